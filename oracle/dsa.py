@@ -1,0 +1,165 @@
+"""Reference semantics of the dynamic-sparse attention path, written as plain definitions.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): only tests, the smoke check and
+the benchmark's CPU-baseline leg may use it.
+
+[DSA-page] = "国产AI芯片完成前沿大模型Day-0适配:稀疏注意力与混合精度推理全解析" (ruibaoantu.com).
+
+Readings taken where the page leaves a step open (each is also listed with its reason in
+the design notes):
+  * the indexer score is a plain int8 x int8 dot product accumulated exactly, with no scale,
+    activation or per-head weight (§2.1 names only a "preliminary Q-K similarity");
+  * one selection per (sequence, query token, KV-head group); the query heads of a group
+    share it (§2.4 keeps selection state per head);
+  * ties in score go to the lower token index; the selected list is returned in ascending
+    token order and padded with -1 (the page states neither);
+  * the forced prefix of §2.4 does not count toward K, and its keys are not scored;
+  * query i of a block sits at position seq_len - q_tail + i and may attend to every cached
+    key at or before its own position (the decode token is already in the cache);
+  * query head h reads KV head h // (H_q / H_kv).
+
+Parity pins (tests/test_oracle.py): index_scores against a pure-Python integer loop and
+the int8 extreme closed form; topk_select against a brute-force full sort and the order
+invariants; index_list against the prefix rule and a hand-worked golden case; attend
+against closed forms (single key, constant V, identical keys, one-hot V rows giving the
+probabilities), scipy's logsumexp, and a full-matrix masked softmax for the dense case;
+page_rows against an unpaged copy under a random page permutation. No function is
+"parity unpinned".
+"""
+import numpy as np
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly: a bf16 is the top half of a float32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def query_position(seq_len: int, q_tail: int, i: int) -> int:
+    """Position of query i of a block whose first query sits q_tail tokens before the end.
+
+    A full prefill has q_tail = T (so pos = i); a decode step has q_tail = 1 (pos = T - 1).
+    """
+    return int(seq_len) - int(q_tail) + int(i)
+
+
+def group_query_heads(kv_head: int, num_q_heads: int, num_kv_heads: int) -> range:
+    """Query heads sharing KV head `kv_head`: contiguous groups of H_q / H_kv heads."""
+    g = int(num_q_heads) // int(num_kv_heads)
+    return range(int(kv_head) * g, (int(kv_head) + 1) * g)
+
+
+def forced_keys(pos: int, prefix_len: int) -> np.ndarray:
+    """[DSA-page] §2.4: the prefix tokens the query can see are always attended."""
+    return np.arange(0, min(int(prefix_len), int(pos) + 1), dtype=np.int64)
+
+
+def candidate_keys(pos: int, prefix_len: int) -> np.ndarray:
+    """[DSA-page] §2.1/§2.4: causal keys outside the forced prefix enter the screening."""
+    return np.arange(int(prefix_len), int(pos) + 1, dtype=np.int64)
+
+
+def page_rows(pool, page_table_row, page_size: int, head: int, t) -> np.ndarray:
+    """[DSA-page] §2.2: token t of a sequence lives in block page_table[t // page_size] at slot
+    t % page_size. `pool` is indexed [page][head][slot] -> row (any object with numpy-style
+    fancy indexing that returns arrays)."""
+    t = np.asarray(t, dtype=np.int64)
+    table = np.asarray(page_table_row, dtype=np.int64)
+    phys = table[t // page_size]
+    slot = t % page_size
+    return np.asarray(pool[phys, head, slot])
+
+
+def index_scores(q_idx_vec, k_rows) -> np.ndarray:
+    """[DSA-page] §2.1: similarity of one indexer query with each candidate key.
+
+    Exact integer dot products (int64), sigma(t) = sum_j q[j] * k[t, j].
+    """
+    q = np.asarray(q_idx_vec, dtype=np.int64)
+    k = np.asarray(k_rows, dtype=np.int64)
+    return k @ q
+
+
+def topk_select(scores, t, k: int) -> np.ndarray:
+    """[DSA-page] §2.1: keep the K best-scoring candidates.
+
+    `t` lists the candidate token indices in ascending order and `scores` their scores.
+    The K largest by (score descending, index ascending) are kept; with K or fewer candidates
+    all are kept. Returned in ascending token order.
+
+    Steps: tau = the K-th largest score; every candidate scoring above tau is kept; the
+    remaining places go to candidates scoring exactly tau, lowest index first.
+    """
+    scores = np.asarray(scores, dtype=np.int64)
+    t = np.asarray(t, dtype=np.int64)
+    n = scores.shape[0]
+    if n <= k:
+        return t.copy()
+    tau = np.partition(scores, n - k)[n - k]
+    above = scores > tau
+    need = k - int(above.sum())
+    at_tau = np.nonzero(scores == tau)[0][:need]
+    keep = np.zeros(n, dtype=bool)
+    keep[above] = True
+    keep[at_tau] = True
+    return t[keep]
+
+
+def index_list(pos: int, prefix_len: int, top_k: int, width: int, score_fn) -> np.ndarray:
+    """The key list one (query, KV-head group) attends to: the forced prefix followed by the
+    top-K candidates, ascending, padded with -1 to `width` (= prefix_len + top_k).
+
+    `score_fn(t)` returns the indexer scores of candidate tokens t.
+    """
+    f = forced_keys(pos, prefix_len)
+    c = candidate_keys(pos, prefix_len)
+    sel = topk_select(score_fn(c), c, top_k) if c.size else c
+    keys = np.sort(np.concatenate([f, sel]))
+    out = np.full(width, -1, dtype=np.int64)
+    out[:keys.size] = keys
+    return out
+
+
+def attend(q_heads, k_rows, v_rows, sm_scale: float):
+    """Softmax attention of each query head over the given key/value rows, in float64.
+
+    z_t = sm_scale * q . k_t;  O = sum_t softmax(z)_t v_t;  LSE = log sum_t exp(z_t).
+    Returns (O [heads][d], LSE [heads]).
+    """
+    q = np.asarray(q_heads, dtype=np.float64)
+    k = np.asarray(k_rows, dtype=np.float64)
+    v = np.asarray(v_rows, dtype=np.float64)
+    z = float(sm_scale) * (q @ k.T)
+    m = z.max(axis=1)
+    e = np.exp(z - m[:, None])
+    s = e.sum(axis=1)
+    o = (e @ v) / s[:, None]
+    return o, m + np.log(s)
+
+
+def dsa_query(*, q_bits, q_idx_vec, kidx_pool, k_pool, v_pool, page_table_row, page_size,
+              kv_head, idx_head, pos, prefix_len, top_k, sm_scale):
+    """One (query token, KV-head group) through the whole path of [DSA-page] §2.
+
+    q_bits      bf16 bits of the group's query heads, [G][d]
+    q_idx_vec   int8 indexer query of this token and indexer head, [d_idx]
+    *_pool      [page][head][slot][...] pools (K/V as bf16 bits, indexer keys as int8)
+    Returns (index list [P+K] int64 with -1 padding, O [G][d] f64, LSE [G] f64).
+    """
+    def score_fn(c):
+        return index_scores(q_idx_vec, page_rows(kidx_pool, page_table_row, page_size, idx_head, c))
+
+    idx = index_list(pos, prefix_len, top_k, prefix_len + top_k, score_fn)
+    keys = idx[idx >= 0]
+    k_rows = bf16_to_f64(page_rows(k_pool, page_table_row, page_size, kv_head, keys))
+    v_rows = bf16_to_f64(page_rows(v_pool, page_table_row, page_size, kv_head, keys))
+    o, lse = attend(bf16_to_f64(q_bits), k_rows, v_rows, sm_scale)
+    return idx, o, lse
+
+
+def dense_query(*, q_bits, k_pool, v_pool, page_table_row, page_size, kv_head, pos, sm_scale):
+    """Dense causal attention of one query token's group: every key 0..pos is attended."""
+    keys = np.arange(0, int(pos) + 1, dtype=np.int64)
+    k_rows = bf16_to_f64(page_rows(k_pool, page_table_row, page_size, kv_head, keys))
+    v_rows = bf16_to_f64(page_rows(v_pool, page_table_row, page_size, kv_head, keys))
+    return attend(bf16_to_f64(q_bits), k_rows, v_rows, sm_scale)

@@ -1,0 +1,272 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test checks the oracle against something it does not compute itself: a brute-force
+enumeration, a closed form, a library routine, or a hand-worked example. A plausible slip
+in the oracle (lowest instead of highest scores, ties to the higher index, a dropped
+softmax scale, a transposed operand, a wrong page lookup, the prefix counted inside K)
+fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bits(x):
+    """float -> bf16 bits for values that are exactly representable (tests only)."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value is not bf16-exact"
+    return (u >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------- conversions / positions
+
+def test_bf16_bits_known_values():
+    bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0x0000, 0x8000, 0x3FC0], dtype=np.uint16)
+    want = [1.0, -2.0, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127, 0.0, -0.0, 1.5]
+    got = oracle.bf16_to_f64(bits)
+    assert got.dtype == np.float64
+    assert list(got) == want
+
+
+def test_query_position_prefill_and_decode():
+    assert [oracle.query_position(10, 10, i) for i in range(3)] == [0, 1, 2]
+    assert oracle.query_position(131072, 1, 0) == 131071
+    # a block of 4 queries that ends the sequence
+    assert [oracle.query_position(20, 4, i) for i in range(4)] == [16, 17, 18, 19]
+
+
+def test_group_heads_are_contiguous():
+    assert list(oracle.group_query_heads(0, 32, 8)) == [0, 1, 2, 3]
+    assert list(oracle.group_query_heads(7, 32, 8)) == [28, 29, 30, 31]
+    assert list(oracle.group_query_heads(0, 4, 1)) == [0, 1, 2, 3]
+
+
+# ---------------------------------------------------------------- indexer scores
+
+@pytest.mark.parametrize("d_idx", [1, 32, 64, 128])
+def test_index_scores_brute_force(d_idx):
+    rng = np.random.default_rng(d_idx)
+    q = rng.integers(-128, 128, size=d_idx).astype(np.int8)
+    k = rng.integers(-128, 128, size=(37, d_idx)).astype(np.int8)
+    got = oracle.index_scores(q, k)
+    want = [sum(int(q[j]) * int(k[t, j]) for j in range(d_idx)) for t in range(k.shape[0])]
+    assert got.dtype == np.int64
+    assert list(got) == want
+
+
+def test_index_scores_int8_extremes():
+    q = np.full(64, -128, dtype=np.int8)
+    assert list(oracle.index_scores(q, np.full((1, 64), -128, np.int8))) == [2 ** 20]
+    assert list(oracle.index_scores(q, np.full((1, 64), 127, np.int8))) == [-64 * 128 * 127]
+    q2 = np.full(128, -128, dtype=np.int8)
+    assert list(oracle.index_scores(q2, np.full((1, 128), -128, np.int8))) == [2 ** 21]
+
+
+# ---------------------------------------------------------------- top-K
+
+def _brute_topk(scores, t, k):
+    order = sorted(range(len(t)), key=lambda j: (-int(scores[j]), int(t[j])))
+    return sorted(int(t[j]) for j in order[:k])
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topk_matches_full_sort(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(0, 60))
+    k = int(rng.integers(1, 70))
+    span = int(rng.choice([2, 3, 5, 100, 10 ** 6]))  # small spans force many ties
+    scores = rng.integers(-span, span + 1, size=n)
+    t = np.sort(rng.choice(10 ** 4, size=n, replace=False)) if n else np.zeros(0, np.int64)
+    got = oracle.topk_select(scores, t, k)
+    assert list(got) == _brute_topk(scores, t, k)
+
+
+def test_topk_invariants_large():
+    rng = np.random.default_rng(7)
+    n, k = 50_000, 2048
+    scores = rng.integers(-40, 41, size=n)          # ~1200 copies of each value
+    t = np.arange(100, 100 + n)
+    sel = oracle.topk_select(scores, t, k)
+    assert sel.size == k and np.all(np.diff(sel) > 0)
+    chosen = np.isin(t, sel)
+    tau = scores[chosen].min()
+    assert scores[~chosen].max() <= tau
+    # among scores equal to tau, every chosen index is below every unchosen one
+    eq = scores == tau
+    assert t[eq & chosen].max() < t[eq & ~chosen].min()
+
+
+def test_topk_all_equal_takes_lowest_indices():
+    t = np.arange(5, 105)
+    assert list(oracle.topk_select(np.zeros(100, np.int64), t, 7)) == list(range(5, 12))
+
+
+def test_topk_few_candidates_keeps_all():
+    t = np.array([3, 9, 11])
+    assert list(oracle.topk_select([5, -1, 2], t, 3)) == [3, 9, 11]
+    assert list(oracle.topk_select([5, -1, 2], t, 8)) == [3, 9, 11]
+    assert list(oracle.topk_select([5, -1, 2], t, 2)) == [3, 11]
+
+
+# ---------------------------------------------------------------- index lists / prefix
+
+@pytest.mark.parametrize("prefix_len", [0, 1, 5, 196])
+def test_index_list_prefix_always_present(prefix_len):
+    rng = np.random.default_rng(prefix_len)
+    top_k = 16
+    width = prefix_len + top_k
+    for pos in [0, 1, 3, prefix_len - 1, prefix_len, prefix_len + 3, prefix_len + 40, 500]:
+        if pos < 0:
+            continue
+        scores = rng.integers(-5, 6, size=pos + 1)
+
+        def score_fn(c):
+            assert c.size == 0 or c.min() >= prefix_len  # prefix keys are never scored
+            return scores[c]
+        lst = oracle.index_list(pos, prefix_len, top_k, width, score_fn)
+        assert lst.shape == (width,)
+        keys = lst[lst >= 0]
+        assert np.all(lst[keys.size:] == -1)
+        assert np.all(np.diff(keys) > 0)
+        visible_prefix = list(range(min(prefix_len, pos + 1)))
+        assert list(keys[:len(visible_prefix)]) == visible_prefix
+        n_cand = max(0, pos + 1 - prefix_len)
+        assert keys.size == len(visible_prefix) + min(top_k, n_cand)  # prefix is outside K
+        assert keys.max() <= pos
+
+
+def test_index_list_ignores_prefix_scores():
+    # Even if prefix keys would outscore everything, they occupy no top-K place.
+    scores = np.array([10 ** 6] * 4 + list(range(20)))
+
+    def score_fn(c):
+        return scores[c]
+    lst = oracle.index_list(23, 4, 3, 7, score_fn)
+    assert list(lst) == [0, 1, 2, 3, 21, 22, 23]
+
+
+# ---------------------------------------------------------------- paging
+
+def test_page_rows_follow_the_page_table():
+    rng = np.random.default_rng(3)
+    T, ps, H, D = 200, 16, 3, 5
+    pages = -(-T // ps)
+    logical = rng.standard_normal((pages * ps, H, D))
+    perm = rng.permutation(pages + 4)[:pages]          # spare physical pages too
+    pool = np.zeros((pages + 4, H, ps, D))
+    for p in range(pages):
+        pool[perm[p]] = logical[p * ps:(p + 1) * ps].transpose(1, 0, 2)
+    t = rng.integers(0, T, size=50)
+    for h in range(H):
+        assert np.array_equal(oracle.page_rows(pool, perm, ps, h, t), logical[t, h])
+
+
+# ---------------------------------------------------------------- attention closed forms
+
+def test_attend_single_key():
+    q = np.array([[0.5, -1.0, 2.0], [1.0, 1.0, 1.0]])
+    k = np.array([[2.0, 1.0, 0.25]])
+    v = np.array([[3.0, -4.0, 5.0]])
+    o, lse = oracle.attend(q, k, v, 0.75)
+    assert np.array_equal(o, np.repeat(v, 2, axis=0))
+    assert np.allclose(lse, 0.75 * (q @ k[0]), rtol=0, atol=1e-15)
+
+
+def test_attend_constant_v_and_identical_keys():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((4, 8))
+    k = rng.standard_normal((9, 8))
+    v_const = np.tile(rng.standard_normal(8), (9, 1))
+    o, _ = oracle.attend(q, k, v_const, 0.3)
+    assert np.allclose(o, v_const[:4], rtol=0, atol=1e-14)
+    k_same = np.tile(k[0], (9, 1))
+    v = rng.standard_normal((9, 8))
+    o, lse = oracle.attend(q, k_same, v, 0.3)
+    assert np.allclose(o, np.tile(v.mean(axis=0), (4, 1)), rtol=0, atol=1e-14)
+    assert np.allclose(lse, 0.3 * (q @ k[0]) + math.log(9), rtol=0, atol=1e-13)
+
+
+def test_attend_probabilities_sum_to_one_and_match_logsumexp():
+    rng = np.random.default_rng(1)
+    n, d = 33, 16
+    q = rng.standard_normal((3, d)) * 4
+    k = rng.standard_normal((n, d))
+    scale = 1 / math.sqrt(d)
+    p, lse = oracle.attend(q, k, np.eye(n), scale)   # one-hot V rows expose the weights
+    z = scale * (q @ k.T)
+    assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.allclose(lse, scipy.special.logsumexp(z, axis=1), rtol=0, atol=1e-12)
+    assert np.allclose(p, np.exp(z - lse[:, None]), rtol=0, atol=1e-12)
+    assert np.allclose(p, scipy.special.softmax(z, axis=1), rtol=0, atol=1e-12)
+
+
+def test_dense_is_top_k_of_everything_and_masked_softmax():
+    """K >= context reproduces dense causal attention, computed here as one full masked
+    softmax(QK^T)V over the whole sequence."""
+    rng = np.random.default_rng(5)
+    T, d, ps, G = 70, 16, 16, 2
+    pages = -(-T // ps)
+    qf = rng.standard_normal((T, G, d)).astype(np.float32)
+    kf = rng.standard_normal((pages * ps, d)).astype(np.float32)
+    vf = rng.standard_normal((pages * ps, d)).astype(np.float32)
+    qb = (qf.view(np.uint32) >> 16).astype(np.uint16)   # truncation: any bf16 values do
+    kb = (kf.view(np.uint32) >> 16).astype(np.uint16)
+    vb = (vf.view(np.uint32) >> 16).astype(np.uint16)
+    table = np.arange(pages)
+    k_pool = kb.reshape(pages, 1, ps, d)
+    v_pool = vb.reshape(pages, 1, ps, d)
+    kidx = rng.integers(-127, 128, size=(pages, 1, ps, 8)).astype(np.int8)
+    qidx = rng.integers(-127, 128, size=(T, 8)).astype(np.int8)
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd = (oracle.bf16_to_f64(x) for x in (qb, kb[:T], vb[:T]))
+    z = scale * np.einsum("igd,td->git", qd, kd)
+    z = np.where(np.arange(T)[None, None, :] <= np.arange(T)[None, :, None], z, -np.inf)
+    want = np.einsum("git,td->igd", scipy.special.softmax(z, axis=2), vd)
+    for i in [0, 1, 15, 16, 17, 40, 69]:
+        idx, o, lse = oracle.dsa_query(q_bits=qb[i], q_idx_vec=qidx[i], kidx_pool=kidx, k_pool=k_pool,
+                                       v_pool=v_pool, page_table_row=table, page_size=ps, kv_head=0,
+                                       idx_head=0, pos=i, prefix_len=0, top_k=T, sm_scale=scale)
+        assert list(idx[idx >= 0]) == list(range(i + 1))
+        assert np.allclose(o, want[i], rtol=0, atol=1e-12)
+        od, lsed = oracle.dense_query(q_bits=qb[i], k_pool=k_pool, v_pool=v_pool, page_table_row=table,
+                                      page_size=ps, kv_head=0, pos=i, sm_scale=scale)
+        assert np.allclose(od, want[i], rtol=0, atol=1e-12)
+        assert np.allclose(lsed, lse, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- hand-worked golden case
+
+def test_golden_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_dsa_8tok.json")))
+    ps = g["page_size"]
+    table = np.array(g["page_table"])
+    n_pages = len(table)
+
+    def paged(rows, dtype):
+        rows = np.asarray(rows)
+        pool = np.zeros((n_pages, 1, ps, rows.shape[1]), dtype=dtype)
+        for t in range(rows.shape[0]):
+            pool[table[t // ps], 0, t % ps] = rows[t]
+        return pool
+    kidx = paged(np.array(g["k_idx_logical"], dtype=np.int8), np.int8)
+    k_pool = paged(_bits(g["k_logical"]), np.uint16)
+    v_pool = paged(_bits(g["v_logical"]), np.uint16)
+    env = {"e": math.e, "log": math.log}
+    for case in g["cases"]:
+        idx, o, lse = oracle.dsa_query(
+            q_bits=_bits([g["q"]]), q_idx_vec=np.array(g["q_idx"], np.int8), kidx_pool=kidx,
+            k_pool=k_pool, v_pool=v_pool, page_table_row=table, page_size=ps, kv_head=0, idx_head=0,
+            pos=case["pos"], prefix_len=g["prefix_len"], top_k=g["top_k"], sm_scale=g["sm_scale"])
+        assert list(idx) == case["index_list"], case["pos"]
+        assert abs(o[0, 0] - eval(case["o0"], env)) < 1e-12, case["pos"]
+        assert abs(o[0, 1] - eval(case["o1"], env)) < 1e-12, case["pos"]
+        assert abs(lse[0] - eval(case["lse"], env)) < 1e-12, case["pos"]
