@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the dynamic-sparse attention path on one MI355X.
+
+Headline workload: one decode step at 128K context -- B=8 sequences, 32 query / 8 KV heads,
+d=128, 64-token pages with a shuffled page table, int8 indexer d_idx=64, top-K=2048 per
+(sequence, KV group). A step is the whole path: indexer over every cached key, exact top-K,
+paged gather + split-K attention + merge. Inputs are seeded synthetic data resident in HBM.
+
+Prints one JSON line. `value` is decode tokens/s (= sequences per step / step time); the
+same line carries HBM GB/s of the step's compulsory bytes, dense causal prefill TFLOP/s
+(B=4, 32/8 heads, S=8192, d=128), the roofline of the dominant kernel (the indexer) and
+the CPU oracle timed on a bounded sample on this host.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+MIB = 1 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = auto)")
+    ap.add_argument("--warm-cache", action="store_true",
+                    help="do not evict the caches between timed steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (for counter calibration)")
+    ap.add_argument("--seed", type=int, default=3)
+    return ap.parse_args()
+
+
+def step_bytes(w):
+    """Compulsory HBM bytes of one decode step (see the design notes for the derivation)."""
+    B, Hkv, Hq, d, T = w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, w.seq_len
+    kidx = B * Hkv * T * w.idx_dim
+    gather = B * Hkv * w.top_k * 2 * d * 2
+    small = (B * Hkv * w.idx_dim            # q_idx
+             + B * Hq * d * 2 * 2            # q + out
+             + B * Hq * 4                    # lse
+             + B * Hkv * w.index_width * 4 * 2  # index list written + read
+             + B * (T // w.page_size) * 4)   # page table
+    return kidx + gather + small
+
+
+def index_kernel_bytes(w):
+    """Algorithmic bytes of one indexer launch: every indexer key, the queries, the scores."""
+    B, Hkv, T = w.batch, w.num_kv_heads, w.seq_len
+    return B * Hkv * T * w.idx_dim + B * Hkv * w.idx_dim + B * Hkv * T * 4 + B * (T // w.page_size) * 4
+
+
+def traffic_for(kernel_file: str, key: str):
+    """Counter-measured HBM bytes per launch, if taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(key)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "flash_attention_int8_amd", "csrc", kernel_file)
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, w, budget_s=12.0):
+    """The oracle, untuned, on host copies of whole sequences of the decode workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    B, Hkv, G = w.batch, w.num_kv_heads, w.group
+    table = inp.page_table.cpu().numpy()
+    q_bits = inp.q.view(torch.int16).cpu().numpy().view(np.uint16)
+    q_idx = inp.q_idx.cpu().numpy()
+    done, t_total = 0, 0.0
+    for b in range(B):
+        pages = torch.as_tensor(table[b], dtype=torch.long, device=inp.k_pool.device)
+        kp = inp.k_pool[pages].view(torch.int16).cpu().numpy().view(np.uint16)
+        vp = inp.v_pool[pages].view(torch.int16).cpu().numpy().view(np.uint16)
+        ip = inp.kidx_pool[pages].cpu().numpy()
+        local = np.arange(len(pages))
+        pos = w.seq_len - 1
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            for g in range(Hkv):
+                oracle.dsa_query(q_bits=q_bits[b, 0, g * G:(g + 1) * G], q_idx_vec=q_idx[b, 0, g],
+                                 kidx_pool=ip, k_pool=kp, v_pool=vp, page_table_row=local,
+                                 page_size=w.page_size, kv_head=g, idx_head=g, pos=pos,
+                                 prefix_len=w.prefix_len, top_k=w.top_k,
+                                 sm_scale=1 / math.sqrt(w.head_dim))
+            t_total += time.perf_counter() - t0
+        done += 1
+        del kp, vp, ip
+        if t_total >= budget_s:
+            break
+    return {"value": done / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {B} sequences of one 128K decode step (all {Hkv} KV groups each: "
+                      f"scores over {w.seq_len} keys, top-{w.top_k}, attention), fp64 numpy, "
+                      f"{t_total:.1f} s"}
+
+
+def bench_prefill(fa, reps):
+    import torch
+
+    from synthetic import CONFIGS, make_inputs
+    w = CONFIGS["dense_prefill_8k"]
+    inp = make_inputs(w, seed=2, device="cuda")
+    kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, page_table=inp.page_table,
+                    seq_lens=inp.seq_lens, max_seq_len=w.seq_len)
+    out = torch.empty_like(inp.q)
+    lse = torch.empty((w.batch, w.q_len, w.num_q_heads), dtype=torch.float32, device="cuda")
+    scale = 1 / math.sqrt(w.head_dim)
+
+    def run():
+        fa.sparse_attn_fwd_prefill(kv, inp.q, w.num_q_heads, w.q_len, w.q_len, None, 0, scale, out, lse)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 4.0 * w.batch * w.num_q_heads * w.head_dim * w.q_len * (w.q_len + 1) / 2
+    del inp, out, lse
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms": ms, "tflops": flops / ms / 1e9,
+            "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS, "flop": flops}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import flash_attention_int8_amd as fa
+    from synthetic import CONFIGS, make_inputs
+
+    fa.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = CONFIGS["sparse_decode_128k"]
+    inp = make_inputs(w, seed=args.seed, device="cuda")
+    kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
+                    page_table=inp.page_table, seq_lens=inp.seq_lens, max_seq_len=w.seq_len,
+                    prefix_len=w.prefix_len)
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    stride = w.seq_len
+    scores = torch.empty((B, 1, Hkv, stride), dtype=torch.int32, device="cuda")
+    indices = torch.empty((B, 1, Hkv, w.index_width), dtype=torch.int32, device="cuda")
+    q = inp.q[:, 0].contiguous()
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    tk_ws_n = fa.sparse_attn_topk_workspace_size(kv, 1, w.top_k)
+    tk_ws = torch.empty(max(tk_ws_n, 16), dtype=torch.uint8, device="cuda")
+    dec_ws_n = fa.sparse_attn_decode_workspace_size(kv, Hq, w.index_width, args.splits)
+    dec_ws = torch.empty(max(dec_ws_n, 16), dtype=torch.uint8, device="cuda")
+    idx_view = indices[:, 0]
+    scale = 1 / math.sqrt(d)
+    flush = None if args.warm_cache else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fa.sparse_attn_index(kv, inp.q_idx, 1, 1, scores, stride)
+        if ev:
+            ev[1].record()
+        fa.sparse_attn_topk(kv, scores, stride, 1, 1, w.top_k, indices, tk_ws, tk_ws_n)
+        if ev:
+            ev[2].record()
+        fa.sparse_attn_fwd_decode(kv, q, Hq, idx_view, w.index_width, scale, args.splits, dec_ws,
+                                  dec_ws_n, out, lse)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.zero_()  # evict L2 and the 256 MB Infinity Cache, outside the timed events
+        step(evs[k])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    seg = [[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(3)] for k in range(args.steps)]
+    ms_step = sum(sum(s) for s in seg) / args.steps
+    ms_index = sum(s[0] for s in seg) / args.steps
+    ms_topk = sum(s[1] for s in seg) / args.steps
+    ms_attn = sum(s[2] for s in seg) / args.steps
+
+    if args.copy_calibration:
+        a = torch.empty(256 * MIB, dtype=torch.uint8, device="cuda")
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+
+    sb = step_bytes(w)
+    ib = index_kernel_bytes(w)
+    achieved = ib / (ms_index * 1e-3) / 1e9
+    result = {
+        "metric": "decode tokens/s + HBM GB/s at 128K ctx top-K=2048; prefill TFLOP/s",
+        "value": B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 indexer + bf16 attention (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "context": w.seq_len, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "idx_dim": w.idx_dim, "top_k": w.top_k,
+                   "page_size": w.page_size, "cache": "warm" if args.warm_cache else "cold"},
+        "hbm_gbps": sb / (ms_step * 1e-3) / 1e9,
+        "hbm_frac": sb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "step_bytes": sb,
+        "breakdown_us": {"index": ms_index * 1e3, "topk": ms_topk * 1e3, "attention": ms_attn * 1e3},
+        "wall_s_timed_loop": t_wall,
+        "roofline": {"kernel": "k_index_stream<64> (indexer)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic_for("sa_index.hip", "k_index_stream<64>")},
+    }
+    if not args.no_prefill:
+        del scores
+        torch.cuda.empty_cache()
+        pf = bench_prefill(fa, args.prefill_reps)
+        result["prefill_tflops"] = pf["tflops"]
+        result["prefill"] = pf
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+// Host side of the C ABI in include/sparse_attn.h: argument validation, then kernel launch.
+// Every check runs before anything is enqueued, so an error return launches nothing.
+#include <hip/hip_runtime.h>
+
+#include "../../include/sparse_attn.h"
+#include "sa_common.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int64_t x) {
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+
+enum Need : unsigned { NEED_KV = 1u, NEED_IDX = 2u };
+
+// Validates the descriptor for the pools a call uses and flattens it.
+int32_t check_kv(const sa_paged_kv* kv, unsigned need, sa::KvView* v) {
+  if (kv == nullptr) return SA_ERR_NULL;
+  if (kv->abi_version != SA_ABI_VERSION) return SA_ERR_ABI;
+  if (kv->page_table == nullptr || kv->seq_lens == nullptr) return SA_ERR_NULL;
+  if ((need & NEED_KV) && (kv->k_pool == nullptr || kv->v_pool == nullptr)) return SA_ERR_NULL;
+  if ((need & NEED_IDX) && kv->kidx_pool == nullptr) return SA_ERR_NULL;
+  if (kv->batch < 1 || kv->num_kv_heads < 1 || kv->max_pages_per_seq < 1 || kv->num_pages < 1 ||
+      kv->max_seq_len < 1 || kv->prefix_len < 0)
+    return SA_ERR_SHAPE;
+  if (!pow2(kv->page_size) || kv->page_size < 64 || kv->page_size > (1 << 24))
+    return SA_ERR_UNSUPPORTED;
+  if ((int64_t)kv->max_seq_len > (int64_t)kv->max_pages_per_seq * kv->page_size) return SA_ERR_SHAPE;
+  if (kv->num_idx_heads != kv->num_kv_heads && kv->num_idx_heads != 1) return SA_ERR_SHAPE;
+  if ((need & NEED_KV) && kv->head_dim != 64 && kv->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if ((need & NEED_IDX) && kv->idx_dim != 32 && kv->idx_dim != 64 && kv->idx_dim != 128)
+    return SA_ERR_UNSUPPORTED;
+  if (!aligned16(kv->page_table) || !aligned16(kv->seq_lens)) return SA_ERR_ALIGN;
+  if ((need & NEED_KV) && (!aligned16(kv->k_pool) || !aligned16(kv->v_pool))) return SA_ERR_ALIGN;
+  if ((need & NEED_IDX) && !aligned16(kv->kidx_pool)) return SA_ERR_ALIGN;
+  v->k_pool = kv->k_pool;
+  v->v_pool = kv->v_pool;
+  v->kidx_pool = kv->kidx_pool;
+  v->page_table = kv->page_table;
+  v->seq_lens = kv->seq_lens;
+  v->num_pages = kv->num_pages;
+  v->batch = kv->batch;
+  v->num_kv_heads = kv->num_kv_heads;
+  v->head_dim = kv->head_dim;
+  v->num_idx_heads = kv->num_idx_heads;
+  v->idx_dim = kv->idx_dim;
+  v->page_size = kv->page_size;
+  v->page_shift = log2i(kv->page_size);
+  v->max_pages_per_seq = kv->max_pages_per_seq;
+  v->max_seq_len = kv->max_seq_len;
+  v->prefix_len = kv->prefix_len;
+  return SA_OK;
+}
+
+int32_t check_block(const sa::KvView& v, int32_t q_len, int32_t q_tail) {
+  if (q_len < 1 || q_tail < q_len || q_tail > v.max_seq_len) return SA_ERR_SHAPE;
+  return SA_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t sparse_attn_abi_version(void) { return SA_ABI_VERSION; }
+
+const char* sparse_attn_status_string(int32_t status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_NULL: return "a required pointer is NULL";
+    case SA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case SA_ERR_UNSUPPORTED: return "size not supported by the kernels";
+    case SA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SA_ERR_HIP: return "HIP runtime rejected a launch";
+    case SA_ERR_ABI: return "descriptor ABI version mismatch";
+    case SA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int32_t sparse_attn_index(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
+                          int32_t q_tail, int32_t* scores, int64_t score_row_stride,
+                          void* stream) {
+  sa::KvView v;
+  int32_t st = check_kv(kv, NEED_IDX, &v);
+  if (st != SA_OK) return st;
+  if ((st = check_block(v, q_len, q_tail)) != SA_OK) return st;
+  if (q_idx == nullptr || scores == nullptr) return SA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(scores)) return SA_ERR_ALIGN;
+  if (score_row_stride < v.max_seq_len || (score_row_stride & 3) != 0) return SA_ERR_SHAPE;
+  return hip_status(sa::launch_index(v, q_idx, q_len, q_tail, scores, score_row_stride,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t sparse_attn_topk_workspace_size(const sa_paged_kv* kv, int32_t q_len, int32_t top_k) {
+  sa::KvView v;
+  if (check_kv(kv, 0, &v) != SA_OK || q_len < 1 || top_k < 1) return 0;
+  return sa::topk_workspace_bytes(v, q_len, top_k);
+}
+
+int32_t sparse_attn_topk(const sa_paged_kv* kv, const int32_t* scores, int64_t score_row_stride,
+                         int32_t q_len, int32_t q_tail, int32_t top_k, int32_t* indices,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  sa::KvView v;
+  int32_t st = check_kv(kv, 0, &v);
+  if (st != SA_OK) return st;
+  if ((st = check_block(v, q_len, q_tail)) != SA_OK) return st;
+  if (scores == nullptr || indices == nullptr) return SA_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(indices)) return SA_ERR_ALIGN;
+  if (top_k < 1 || (int64_t)top_k + v.prefix_len > (1 << 30)) return SA_ERR_SHAPE;
+  if (score_row_stride < v.max_seq_len || (score_row_stride & 3) != 0) return SA_ERR_SHAPE;
+  const size_t need = sa::topk_workspace_bytes(v, q_len, top_k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return SA_ERR_ALIGN;
+  return hip_status(sa::launch_topk(v, scores, score_row_stride, q_len, q_tail, top_k, indices,
+                                    workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_t num_q_heads,
+                                int32_t q_len, int32_t q_tail, const int32_t* indices,
+                                int32_t index_width, float sm_scale, uint16_t* out, float* lse,
+                                void* stream) {
+  sa::KvView v;
+  int32_t st = check_kv(kv, NEED_KV, &v);
+  if (st != SA_OK) return st;
+  if ((st = check_block(v, q_len, q_tail)) != SA_OK) return st;
+  if (q == nullptr || out == nullptr) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (lse != nullptr && !aligned16(lse))) return SA_ERR_ALIGN;
+  if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0) return SA_ERR_SHAPE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (indices == nullptr)
+    return hip_status(sa::launch_attn_dense(v, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, s));
+  const int group = num_q_heads / v.num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return SA_ERR_UNSUPPORTED;
+  if (index_width < 1) return SA_ERR_SHAPE;
+  if (!aligned16(indices)) return SA_ERR_ALIGN;
+  return hip_status(sa::launch_attn_gather(v, q, num_q_heads, q_len, q_tail, indices, index_width,
+                                           sm_scale, 1, nullptr, out, lse, s));
+}
+
+size_t sparse_attn_decode_workspace_size(const sa_paged_kv* kv, int32_t num_q_heads,
+                                         int32_t index_width, int32_t num_splits) {
+  sa::KvView v;
+  if (check_kv(kv, 0, &v) != SA_OK || num_q_heads < 1 || index_width < 1) return 0;
+  if (num_q_heads % v.num_kv_heads != 0 || (v.head_dim != 64 && v.head_dim != 128)) return 0;
+  if (num_splits < 0 || num_splits > 256) return 0;
+  const int64_t units = (int64_t)v.batch * v.num_kv_heads;
+  int splits = num_splits > 0 ? num_splits : sa::auto_splits(units, index_width);
+  if (splits > index_width) splits = index_width;
+  return sa::gather_workspace_bytes(units, num_q_heads / v.num_kv_heads, v.head_dim, splits);
+}
+
+int32_t sparse_attn_fwd_decode(const sa_paged_kv* kv, const uint16_t* q, int32_t num_q_heads,
+                               const int32_t* indices, int32_t index_width, float sm_scale,
+                               int32_t num_splits, void* workspace, size_t workspace_bytes,
+                               uint16_t* out, float* lse, void* stream) {
+  sa::KvView v;
+  int32_t st = check_kv(kv, NEED_KV, &v);
+  if (st != SA_OK) return st;
+  if (q == nullptr || out == nullptr || indices == nullptr) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(indices) || (lse != nullptr && !aligned16(lse)))
+    return SA_ERR_ALIGN;
+  if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0) return SA_ERR_SHAPE;
+  const int group = num_q_heads / v.num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return SA_ERR_UNSUPPORTED;
+  if (index_width < 1 || num_splits < 0 || num_splits > 256) return SA_ERR_SHAPE;
+  const int64_t units = (int64_t)v.batch * v.num_kv_heads;
+  int splits = num_splits > 0 ? num_splits : sa::auto_splits(units, index_width);
+  if (splits > index_width) splits = index_width;
+  const size_t need = sa::gather_workspace_bytes(units, group, v.head_dim, splits);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SA_ERR_ALIGN;
+  }
+  return hip_status(sa::launch_attn_gather(v, q, num_q_heads, 1, 1, indices, index_width, sm_scale,
+                                           splits, static_cast<float*>(workspace), out, lse,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

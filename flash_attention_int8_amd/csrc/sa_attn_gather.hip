@@ -1,0 +1,314 @@
+// Attention over per-query index lists: the decode path (split-K + exact merge) and the
+// sparse prefill path (one unit per query token and KV group).
+//
+// [DSA-page] = "国产AI芯片完成前沿大模型Day-0适配:稀疏注意力与混合精度推理全解析":
+//   §2.2  the selected rows are gathered out of fixed-size KV pages;
+//   §2.3  decode is memory-bound, so only the active rows are loaded, straight into
+//         registers; prefill overlaps the gather of the next rows with compute.
+//
+// A unit is one (sequence, query token, KV group); its G = H_q/H_kv query heads share the
+// index list, so every gathered K/V row is used by G heads. A workgroup of 4 waves takes a
+// contiguous chunk of the list (a "split"). In a wave, d/8 lanes cover one key row (16 bytes
+// of bf16 each), so a wave holds 64/(d/8) keys at once ("lane groups"). Each wave works in
+// batches: it loads NB list entries per lane group, resolves their pages, issues all K and
+// V row loads of the batch, then computes: G dot products per key (8 FMAs per lane + a DPP
+// butterfly over the lane group), one running-max update per batch and G x 8 FMAs per key
+// for the V accumulation. Every lane group keeps its own online-softmax state (max m, sum
+// l, weighted V sum in fp32, base-2 exponent with log2(e) folded into the query); states
+// are merged across lane groups and waves at the end, then either normalised and stored
+// (one split) or written as partials for k_merge_splits (several splits). All merges run in
+// a fixed order, so results are deterministic.
+#include "sa_common.h"
+
+namespace sa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNB = 4;  // keys per lane group per batch
+
+struct SoftmaxState {
+  float m, l;
+};
+
+__device__ __forceinline__ float safe_scale(float m_old, float m_new) {
+  return (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_attn_gather(KvView kv, const uint16_t* __restrict__ q,
+                                                     int num_q_heads, int q_len, int q_tail,
+                                                     const int32_t* __restrict__ indices, int W,
+                                                     float qscale, int num_splits,
+                                                     int keys_per_split, float* __restrict__ ws,
+                                                     uint16_t* __restrict__ out,
+                                                     float* __restrict__ lse) {
+  constexpr int LPK = D / 8;        // lanes per key row
+  constexpr int KPW = 64 / LPK;     // keys a wave holds at once (lane groups)
+  constexpr int NW = 4;
+  __shared__ float sh_m[NW][G];
+  __shared__ float sh_l[NW][G];
+  __shared__ float sh_acc[NW][G][D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane / LPK;       // lane group = key slot
+  const int part = lane % LPK;      // dims part*8 .. part*8+7
+  const int64_t unit = blockIdx.x / num_splits;  // (b * q_len + i) * H_kv + g
+  const int split = (int)(blockIdx.x - unit * num_splits);
+  const int g = (int)(unit % kv.num_kv_heads);
+  const int64_t bi = unit / kv.num_kv_heads;
+  const int b = (int)(bi / q_len);
+  const int i = (int)(bi - (int64_t)b * q_len);
+  const int pos = min(kv.seq_lens[b], kv.max_seq_len) - q_tail + i;
+  const int gi = (kv.num_idx_heads == 1) ? 0 : g;
+  const int32_t* ilist = indices + (bi * kv.num_idx_heads + gi) * (int64_t)W;
+
+  // Query fragments, pre-scaled by sm_scale * log2(e).
+  float qf[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 w = *reinterpret_cast<const uint4*>(
+        q + (bi * num_q_heads + (int64_t)g * G + h) * D + part * 8);
+    qf[h][0] = bf16_lo(w.x) * qscale; qf[h][1] = bf16_hi(w.x) * qscale;
+    qf[h][2] = bf16_lo(w.y) * qscale; qf[h][3] = bf16_hi(w.y) * qscale;
+    qf[h][4] = bf16_lo(w.z) * qscale; qf[h][5] = bf16_hi(w.z) * qscale;
+    qf[h][6] = bf16_lo(w.w) * qscale; qf[h][7] = bf16_hi(w.w) * qscale;
+  }
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+
+  const int k_begin = split * keys_per_split;
+  const int k_end = min(W, k_begin + keys_per_split);
+  const int64_t head_stride = (int64_t)kv.page_size * D;            // one head of one page
+  const int64_t page_stride = head_stride * kv.num_kv_heads;
+
+  // Batches: the workgroup covers NW * KPW * kNB consecutive list entries per batch; wave w
+  // takes entries [w*KPW*kNB, (w+1)*KPW*kNB) of it, lane group grp every KPW-th one.
+  for (int base = k_begin; base < k_end; base += NW * KPW * kNB) {
+    int tok[kNB];
+    int64_t off[kNB];
+    bool ok[kNB];
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {
+      const int j = base + wave * KPW * kNB + u * KPW + grp;
+      tok[u] = (j < k_end) ? ilist[j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {
+      const int t = tok[u];
+      const int64_t ph = (t >= 0 && t <= pos) ? phys_page(kv, b, t) : -1;
+      ok[u] = ph >= 0;
+      off[u] = ok[u] ? ph * page_stride + g * head_stride +
+                           (int64_t)(t & (kv.page_size - 1)) * D + part * 8
+                     : 0;
+    }
+    uint4 kr[kNB], vr[kNB];
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {
+      if (ok[u]) {
+        kr[u] = *reinterpret_cast<const uint4*>(kv.k_pool + off[u]);
+        vr[u] = *reinterpret_cast<const uint4*>(kv.v_pool + off[u]);
+      } else {
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    // scores
+    float s[kNB][G];
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {
+      float kf[8];
+      kf[0] = bf16_lo(kr[u].x); kf[1] = bf16_hi(kr[u].x);
+      kf[2] = bf16_lo(kr[u].y); kf[3] = bf16_hi(kr[u].y);
+      kf[4] = bf16_lo(kr[u].z); kf[5] = bf16_hi(kr[u].z);
+      kf[6] = bf16_lo(kr[u].w); kf[7] = bf16_hi(kr[u].w);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
+        s[u][h] = group_sum_f<LPK>(d);
+      }
+    }
+    // online softmax update, one rescale per batch
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mb = m[h];
+#pragma unroll
+      for (int u = 0; u < kNB; ++u) mb = ok[u] ? fmaxf(mb, s[u][h]) : mb;
+      const float sc = safe_scale(m[h], mb);
+      l[h] *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= sc;
+      m[h] = mb;
+#pragma unroll
+      for (int u = 0; u < kNB; ++u) {
+        const float p = ok[u] ? exp2f(s[u][h] - mb) : 0.f;
+        l[h] += p;
+        acc[h][0] = fmaf(p, bf16_lo(vr[u].x), acc[h][0]);
+        acc[h][1] = fmaf(p, bf16_hi(vr[u].x), acc[h][1]);
+        acc[h][2] = fmaf(p, bf16_lo(vr[u].y), acc[h][2]);
+        acc[h][3] = fmaf(p, bf16_hi(vr[u].y), acc[h][3]);
+        acc[h][4] = fmaf(p, bf16_lo(vr[u].z), acc[h][4]);
+        acc[h][5] = fmaf(p, bf16_hi(vr[u].z), acc[h][5]);
+        acc[h][6] = fmaf(p, bf16_lo(vr[u].w), acc[h][6]);
+        acc[h][7] = fmaf(p, bf16_hi(vr[u].w), acc[h][7]);
+      }
+    }
+  }
+
+  // merge the lane groups of this wave (groups differ in lane bits >= log2(LPK))
+#pragma unroll
+  for (int mask = LPK; mask < 64; mask <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], mask, 64);
+      const float lo = __shfl_xor(l[h], mask, 64);
+      const float mn = fmaxf(m[h], mo);
+      const float s_self = safe_scale(m[h], mn);
+      const float s_oth = safe_scale(mo, mn);
+      l[h] = l[h] * s_self + lo * s_oth;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ao = __shfl_xor(acc[h][e], mask, 64);
+        acc[h][e] = acc[h][e] * s_self + ao * s_oth;
+      }
+      m[h] = mn;
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (part == 0) {
+        sh_m[wave][h] = m[h];
+        sh_l[wave][h] = l[h];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh_acc[wave][h][part * 8 + e] = acc[h][e];
+    }
+  }
+  __syncthreads();
+
+  // merge the waves: thread -> (head, dim) pairs
+  for (int x = threadIdx.x; x < G * D; x += 256) {
+    const int h = x / D;
+    const int dd = x - h * D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, sh_m[w][h]);
+    float ll = 0.f, aa = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sc = safe_scale(sh_m[w][h], mm);
+      ll += sh_l[w][h] * sc;
+      aa += sh_acc[w][h][dd] * sc;
+    }
+    const int64_t qh = bi * num_q_heads + (int64_t)g * G + h;  // output row (b, i, head)
+    if (num_splits == 1) {
+      const float o = (ll > 0.f) ? aa / ll : 0.f;
+      out[qh * D + dd] = (uint16_t)f32_to_bf16(o);
+      if (lse != nullptr && dd == 0) lse[qh] = (ll > 0.f) ? (mm + log2f(ll)) * kLn2 : -INFINITY;
+    } else {
+      // partials: ws_acc [units][splits][G][D], then ws_ml [units][splits][G][2]
+      const int64_t slot = unit * num_splits + split;
+      ws[(slot * G + h) * D + dd] = aa;
+      if (dd == 0) {
+        float* ml = ws + (int64_t)gridDim.x * G * D;  // gridDim.x = units * num_splits
+        ml[(slot * G + h) * 2 + 0] = mm;
+        ml[(slot * G + h) * 2 + 1] = ll;
+      }
+    }
+  }
+}
+
+// Exact merge of split partials. grid.x = units, 256 threads over (head, dim).
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_merge_splits(const float* __restrict__ ws, int64_t units,
+                                                      int num_splits, int num_q_heads,
+                                                      int num_kv_heads, uint16_t* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  const int64_t unit = blockIdx.x;
+  const float* ml = ws + units * num_splits * G * D;
+  const int g = (int)(unit % num_kv_heads);
+  const int64_t bi = unit / num_kv_heads;
+  for (int x = threadIdx.x; x < G * D; x += 256) {
+    const int h = x / D;
+    const int dd = x - h * D;
+    float mm = -INFINITY;
+    for (int s = 0; s < num_splits; ++s) mm = fmaxf(mm, ml[((unit * num_splits + s) * G + h) * 2]);
+    float ll = 0.f, aa = 0.f;
+    for (int s = 0; s < num_splits; ++s) {
+      const int64_t slot = unit * num_splits + s;
+      const float sc = safe_scale(ml[(slot * G + h) * 2], mm);
+      ll += ml[(slot * G + h) * 2 + 1] * sc;
+      aa += ws[(slot * G + h) * D + dd] * sc;
+    }
+    const int64_t qh = bi * num_q_heads + (int64_t)g * G + h;
+    out[qh * D + dd] = (uint16_t)f32_to_bf16((ll > 0.f) ? aa / ll : 0.f);
+    if (lse != nullptr && dd == 0) lse[qh] = (ll > 0.f) ? (mm + log2f(ll)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, int G>
+hipError_t launch_dg(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len, int q_tail,
+                     const int32_t* indices, int W, float sm_scale, int num_splits, float* ws,
+                     uint16_t* out, float* lse, hipStream_t stream) {
+  const int64_t units = (int64_t)kv.batch * q_len * kv.num_kv_heads;
+  const int kps = (W + num_splits - 1) / num_splits;
+  dim3 grid((unsigned)(units * num_splits));
+  hipLaunchKernelGGL((k_attn_gather<D, G>), grid, dim3(256), 0, stream, kv, q, num_q_heads, q_len,
+                     q_tail, indices, W, sm_scale * kLog2e, num_splits, kps, ws, out, lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || num_splits == 1) return e;
+  hipLaunchKernelGGL((k_merge_splits<D, G>), dim3((unsigned)units), dim3(256), 0, stream, ws, units,
+                     num_splits, num_q_heads, kv.num_kv_heads, out, lse);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len, int q_tail,
+                    const int32_t* indices, int W, float sm_scale, int num_splits, float* ws,
+                    uint16_t* out, float* lse, hipStream_t stream) {
+  switch (num_q_heads / kv.num_kv_heads) {
+    case 1: return launch_dg<D, 1>(kv, q, num_q_heads, q_len, q_tail, indices, W, sm_scale, num_splits, ws, out, lse, stream);
+    case 2: return launch_dg<D, 2>(kv, q, num_q_heads, q_len, q_tail, indices, W, sm_scale, num_splits, ws, out, lse, stream);
+    case 4: return launch_dg<D, 4>(kv, q, num_q_heads, q_len, q_tail, indices, W, sm_scale, num_splits, ws, out, lse, stream);
+    case 8: return launch_dg<D, 8>(kv, q, num_q_heads, q_len, q_tail, indices, W, sm_scale, num_splits, ws, out, lse, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t gather_workspace_bytes(int64_t units, int group, int head_dim, int num_splits) {
+  if (num_splits <= 1) return 0;
+  return (size_t)units * num_splits * group * (head_dim + 2) * sizeof(float);
+}
+
+int auto_splits(int64_t units, int index_width) {
+  // Aim for >= 1024 workgroups, with at least 128 list entries per split.
+  int s = 1;
+  while (units * s < 1024 && (index_width + 2 * s - 1) / (2 * s) >= 128 && s < 256) s *= 2;
+  return s;
+}
+
+hipError_t launch_attn_gather(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
+                              int q_tail, const int32_t* indices, int index_width, float sm_scale,
+                              int num_splits, float* ws, uint16_t* out, float* lse,
+                              hipStream_t stream) {
+  if (kv.head_dim == 128)
+    return launch_d<128>(kv, q, num_q_heads, q_len, q_tail, indices, index_width, sm_scale, num_splits, ws, out, lse, stream);
+  if (kv.head_dim == 64)
+    return launch_d<64>(kv, q, num_q_heads, q_len, q_tail, indices, index_width, sm_scale, num_splits, ws, out, lse, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa

@@ -1,0 +1,114 @@
+// Internal helpers shared by the gfx950 kernels and the host layer of the sparse-attention
+// library. Not part of the public ABI (include/sparse_attn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+// The descriptor after host-side validation, flattened into kernel arguments.
+struct KvView {
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int8_t* kidx_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int64_t num_pages;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t num_idx_heads;
+  int32_t idx_dim;
+  int32_t page_size;
+  int32_t page_shift;  // log2(page_size)
+  int32_t max_pages_per_seq;
+  int32_t max_seq_len;
+  int32_t prefix_len;
+};
+
+// Physical page of token t of sequence b, or -1 when the table entry is out of range.
+__device__ __forceinline__ int64_t phys_page(const KvView& kv, int b, int t) {
+  const int lp = t >> kv.page_shift;
+  if (lp < 0 || lp >= kv.max_pages_per_seq) return -1;
+  const int64_t p = kv.page_table[(int64_t)b * kv.max_pages_per_seq + lp];
+  return (p >= 0 && p < kv.num_pages) ? p : -1;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Two bf16 packed in a 32-bit word -> floats.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// DPP lane moves (within rows of 16 lanes).
+enum : int {
+  DPP_QUAD_XOR1 = 0xB1,      // quad_perm [1,0,3,2]
+  DPP_QUAD_XOR2 = 0x4E,      // quad_perm [2,3,0,1]
+  DPP_ROW_HALF_MIRROR = 0x141,
+  DPP_ROW_MIRROR = 0x140,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, true);
+}
+
+// Sum over aligned groups of N lanes (N = 1, 2, 4, 8, 16); every lane of a group gets the sum.
+template <int N>
+__device__ __forceinline__ int group_sum_i(int v) {
+  if constexpr (N >= 2) v += dpp_i<DPP_QUAD_XOR1>(v);
+  if constexpr (N >= 4) v += dpp_i<DPP_QUAD_XOR2>(v);
+  if constexpr (N >= 8) v += dpp_i<DPP_ROW_HALF_MIRROR>(v);
+  if constexpr (N >= 16) v += dpp_i<DPP_ROW_MIRROR>(v);
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum_f(float v) {
+  if constexpr (N >= 2) v += dpp_f<DPP_QUAD_XOR1>(v);
+  if constexpr (N >= 4) v += dpp_f<DPP_QUAD_XOR2>(v);
+  if constexpr (N >= 8) v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  if constexpr (N >= 16) v += dpp_f<DPP_ROW_MIRROR>(v);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace sa
+
+// Kernel launchers (defined in the .hip files; return hipSuccess or the launch error).
+namespace sa {
+hipError_t launch_index(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail,
+                        int32_t* scores, int64_t row_stride, hipStream_t stream);
+hipError_t launch_topk(const KvView& kv, const int32_t* scores, int64_t row_stride, int q_len,
+                       int q_tail, int top_k, int32_t* indices, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+size_t topk_workspace_bytes(const KvView& kv, int q_len, int top_k);
+hipError_t launch_attn_gather(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
+                              int q_tail, const int32_t* indices, int index_width, float sm_scale,
+                              int num_splits, float* ws, uint16_t* out, float* lse,
+                              hipStream_t stream);
+size_t gather_workspace_bytes(int64_t units, int group, int head_dim, int num_splits);
+int auto_splits(int64_t units, int index_width);
+hipError_t launch_attn_dense(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
+                             int q_tail, float sm_scale, uint16_t* out, float* lse,
+                             hipStream_t stream);
+}  // namespace sa

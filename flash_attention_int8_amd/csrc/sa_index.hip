@@ -1,0 +1,238 @@
+// Indexer kernels: exact int8 x int8 -> int32 scores of every candidate key.
+//
+// [DSA-page] = "国产AI芯片完成前沿大模型Day-0适配:稀疏注意力与混合精度推理全解析", §2.1: the
+// indexer runs on the GPU and scores each cached key against the query before the top-K.
+//
+// Two kernels, chosen by how many queries share the keys:
+//  * k_index_stream (few queries per sequence, i.e. decode): HBM-bound streaming of the
+//    indexer keys. A wave reads one 64-token block of one indexer head (64*d_idx contiguous
+//    bytes) with 16-byte loads, so every load instruction moves 1 KiB of consecutive bytes.
+//    d_idx/16 neighbouring lanes hold one token's key; each does 4 v_dot4_i32_i8 against the
+//    matching 16 query bytes, and a DPP butterfly sums the lane group. After the reduction
+//    lane l keeps the token of load (l mod d_idx/16), so a wave stores 64 consecutive scores
+//    with one instruction.
+//  * k_index_mfma (many queries, i.e. prefill): scores are a causal int8 GEMM
+//    S^T = K_idx * Q_idx^T on v_mfma_i32_16x16x32_i8. Keys are the M side so each lane's four
+//    accumulator rows are four consecutive tokens of one query: one 16-byte store each.
+#include "sa_common.h"
+
+namespace sa {
+namespace {
+
+constexpr int kStreamBlocksPerWave = 4;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int dot16(const v4i a, const v4i b) {
+  int acc = 0;
+  acc = __builtin_amdgcn_sdot4(a.x, b.x, acc, false);
+  acc = __builtin_amdgcn_sdot4(a.y, b.y, acc, false);
+  acc = __builtin_amdgcn_sdot4(a.z, b.z, acc, false);
+  acc = __builtin_amdgcn_sdot4(a.w, b.w, acc, false);
+  return acc;
+}
+
+// grid: x = ceil(token blocks / (4 waves * kStreamBlocksPerWave)), y = batch * H_idx.
+template <int D>
+__global__ __launch_bounds__(256) void k_index_stream(KvView kv, const int8_t* __restrict__ q_idx,
+                                                      int q_len, int q_tail,
+                                                      int32_t* __restrict__ scores,
+                                                      int64_t row_stride) {
+  constexpr int LPT = D / 16;   // lanes holding one token's key
+  constexpr int TPL = 64 / LPT; // tokens covered by one 1 KiB load instruction
+  constexpr int R = LPT;        // load instructions per 64-token block
+  constexpr int U = kStreamBlocksPerWave;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.y;
+  const int b = row / kv.num_idx_heads;
+  const int gi = row - b * kv.num_idx_heads;
+  const int T = min(kv.seq_lens[b], kv.max_seq_len);
+  const int P = kv.prefix_len;
+  const int pos0 = T - q_tail;               // position of query 0
+  const int pmax = pos0 + q_len - 1;
+  if (pmax < P || pmax < 0) return;
+  const int blk_first = P >> 6;
+  const int blk_last = pmax >> 6;
+  const int blk0 = blk_first + (blockIdx.x * 4 + wave) * U;
+  if (blk0 > blk_last) return;
+
+  const int part = lane % LPT;               // which 16-byte chunk of a key row
+  const int my_tok = part * TPL + lane / LPT; // token (within the block) this lane stores
+
+  v4i kd[U][R];
+  bool ok[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int blk = blk0 + u;
+    const int64_t phys = (blk <= blk_last) ? phys_page(kv, b, blk << 6) : -1;
+    ok[u] = phys >= 0;
+    if (phys >= 0) {
+      const int slot0 = (blk << 6) & (kv.page_size - 1);
+      const int8_t* base = kv.kidx_pool +
+          ((phys * kv.num_idx_heads + gi) * kv.page_size + slot0) * (int64_t)D;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        kd[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(base + r * 1024 + lane * 16));
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) kd[u][r] = v4i{0, 0, 0, 0};
+    }
+  }
+
+  for (int i = 0; i < q_len; ++i) {
+    const int pos = pos0 + i;
+    if (pos < P) continue;
+    const v4i qf = *reinterpret_cast<const v4i*>(
+        q_idx + (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * D + part * 16);
+    int32_t* srow = scores + (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * row_stride;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int blk = blk0 + u;
+      if (blk > blk_last) break;
+      int mine = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int s = group_sum_i<LPT>(dot16(qf, kd[u][r]));
+        if (part == r) mine = s;
+      }
+      const int t = (blk << 6) + my_tok;
+      if (ok[u] && t >= P && t <= pos) srow[t] = mine;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// MFMA indexer. Wave tile: 64 keys (one 64-token block) x 64 queries. grid.x enumerates
+// (query tile, key chunk) pairs, 4 per workgroup (one per wave); grid.y = batch * H_idx.
+typedef long i64x1;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+constexpr int kMfmaKeyBlocksPerWave = 8;  // 512 keys per wave item
+
+template <int D>
+__global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __restrict__ q_idx,
+                                                    int q_len, int q_tail,
+                                                    int32_t* __restrict__ scores,
+                                                    int64_t row_stride, int n_qtiles,
+                                                    int n_kchunks) {
+  constexpr int KS = D / 32;   // k-steps of the 16x16x32 MFMA
+  constexpr int CH = D / 4;    // bytes of a row held by one lane group (l / 16)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= n_qtiles * n_kchunks) return;
+  const int qt = item / n_kchunks;
+  const int kc = item - qt * n_kchunks;
+  const int row = blockIdx.y;
+  const int b = row / kv.num_idx_heads;
+  const int gi = row - b * kv.num_idx_heads;
+  const int T = min(kv.seq_lens[b], kv.max_seq_len);
+  const int P = kv.prefix_len;
+  const int pos0 = T - q_tail;
+  const int i0 = qt * 64;
+  const int i_end = min(q_len, i0 + 64);
+  const int pmax = pos0 + i_end - 1;
+  const int pmin = pos0 + i0;
+  if (pmax < P) return;
+  const int blk_first = (P >> 6) + kc * kMfmaKeyBlocksPerWave;
+  const int blk_last = min(pmax >> 6, blk_first + kMfmaKeyBlocksPerWave - 1);
+  if (blk_first > blk_last) return;
+
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+
+  // B operand: 4 query blocks of 16, lane holds query (n*16 + l16), bytes lg*CH .. +CH.
+  i64x1 qb[4][KS];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int i = i0 + n * 16 + l16;
+    if (i < q_len) {
+      const int8_t* qp = q_idx + (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * D + lg * CH;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qb[n][ks] = *reinterpret_cast<const i64x1*>(qp + ks * 8);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qb[n][ks] = 0;
+    }
+  }
+
+  for (int blk = blk_first; blk <= blk_last; ++blk) {
+    const int t0 = blk << 6;
+    const int64_t phys = phys_page(kv, b, t0);
+    if (phys < 0) continue;
+    const int slot0 = t0 & (kv.page_size - 1);
+    const int8_t* kbase = kv.kidx_pool +
+        ((phys * kv.num_idx_heads + gi) * kv.page_size + slot0) * (int64_t)D;
+    // A operand: 4 key blocks of 16, lane holds key (m*16 + l16), bytes lg*CH .. +CH.
+    i64x1 ka[4][KS];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int8_t* kp = kbase + (m * 16 + l16) * D + lg * CH;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[m][ks] = *reinterpret_cast<const i64x1*>(kp + ks * 8);
+    }
+    const bool full = (t0 >= P) && (t0 + 63 <= pmin);  // every (key, query) pair is a candidate
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka[m][ks], qb[n][ks], acc, 0, 0, 0);
+        // acc[j] = score(key m*16 + lg*4 + j, query n*16 + l16)
+        const int i = i0 + n * 16 + l16;
+        if (i >= q_len) continue;
+        const int pos = pos0 + i;
+        const int t = t0 + m * 16 + lg * 4;
+        int32_t* dst = scores + (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * row_stride + t;
+        if (full) {
+          *reinterpret_cast<i32x4*>(dst) = acc;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (t + j >= P && t + j <= pos) dst[j] = acc[j];
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_index_d(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail,
+                          int32_t* scores, int64_t row_stride, hipStream_t stream) {
+  const int rows = kv.batch * kv.num_idx_heads;
+  const int pmax = kv.max_seq_len - q_tail + q_len - 1;  // largest position any query can have
+  if (pmax < kv.prefix_len) return hipSuccess;
+  const int blocks = (pmax >> 6) - (kv.prefix_len >> 6) + 1;
+  if (q_len < 16) {
+    const int per_wg = 4 * kStreamBlocksPerWave;
+    dim3 grid((blocks + per_wg - 1) / per_wg, rows);
+    hipLaunchKernelGGL(k_index_stream<D>, grid, dim3(256), 0, stream, kv, q_idx, q_len, q_tail,
+                       scores, row_stride);
+  } else {
+    const int n_qtiles = (q_len + 63) / 64;
+    const int n_kchunks = (blocks + kMfmaKeyBlocksPerWave - 1) / kMfmaKeyBlocksPerWave;
+    const int64_t items = (int64_t)n_qtiles * n_kchunks;
+    dim3 grid((unsigned)((items + 3) / 4), rows);
+    hipLaunchKernelGGL(k_index_mfma<D>, grid, dim3(256), 0, stream, kv, q_idx, q_len, q_tail,
+                       scores, row_stride, n_qtiles, n_kchunks);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail,
+                        int32_t* scores, int64_t row_stride, hipStream_t stream) {
+  switch (kv.idx_dim) {
+    case 32: return launch_index_d<32>(kv, q_idx, q_len, q_tail, scores, row_stride, stream);
+    case 64: return launch_index_d<64>(kv, q_idx, q_len, q_tail, scores, row_stride, stream);
+    case 128: return launch_index_d<128>(kv, q_idx, q_len, q_tail, scores, row_stride, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sa

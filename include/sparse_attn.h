@@ -1,0 +1,191 @@
+/*
+ * sparse_attn.h -- C ABI of a dynamic-sparse ("DSA"-style) attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method follows the page "国产AI芯片完成前沿大模型Day-0适配:稀疏注意力与混合精度推理
+ * 全解析" (ruibaoantu.com), section 2, cited below as [DSA-page]:
+ *   §2.1  an indexer scores every cached key against each query on the GPU, and a
+ *         reduction keeps the top-K key indices per query;
+ *   §2.2  the KV cache is stored in fixed blocks (pages) of contiguous tokens and the
+ *         selected rows are gathered out of them before computing;
+ *   §2.3  prefill and decode run the selection + gather + attention with different
+ *         parallel shapes (prefill overlaps the next block's gather with compute; decode
+ *         loads only the active rows);
+ *   §2.4  vision tokens form a prefix that is always attended in full and never enters the
+ *         sparse screening.
+ * Dense causal attention is the special case where every causal key is selected
+ * (sparse_attn_fwd_prefill with indices == NULL).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Ownership   The caller owns every buffer. All array pointers are DEVICE pointers, except
+ *              the descriptor itself, which is read on the host during the call and may be
+ *              freed as soon as the call returns. The library keeps no state between calls
+ *              and allocates no memory.
+ *  Streams     `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *              enqueues work on it and returns; nothing synchronises.
+ *  Errors      Each call returns SA_OK (0) or an SA_ERR_* code. All argument checks run on
+ *              the host before anything is enqueued; on an error nothing is launched and no
+ *              output is touched. SA_ERR_HIP means a launch was rejected by the runtime;
+ *              earlier launches of the same call may then already be enqueued.
+ *  Device data The CONTENTS of device arrays (page ids, sequence lengths, indices) are the
+ *              caller's contract and are not validated. Kernels still never read or write
+ *              out of bounds: a page id outside [0, num_pages) or an index outside the
+ *              query's causal range is skipped, which makes the result unspecified but safe.
+ *  Alignment   Every array pointer must be 16-byte aligned (SA_ERR_ALIGN otherwise).
+ *  Threads     Calls are re-entrant; concurrent calls on different streams are safe as long
+ *              as their output and workspace buffers do not overlap.
+ *
+ * Positions   A call processes a block of q_len query tokens per sequence. Query i of
+ *             sequence b sits at position  pos = seq_lens[b] - q_tail + i  (q_tail >= q_len
+ *             is the distance from the block's first query to the end of the sequence:
+ *             q_tail = T for a whole prefill, q_tail = 1 for a decode step). The cache holds
+ *             seq_lens[b] tokens including the queries themselves; a query attends to keys
+ *             0..pos.
+ * Selection   Forced keys F = {t : 0 <= t < min(P, pos+1)}; candidate keys
+ *             C = {t : P <= t <= pos}. The index list of a (sequence, query, KV group) is
+ *             F followed by the top-K of C by (indexer score descending, token ascending),
+ *             all in ascending token order and padded with -1 to width P + K. Query head h
+ *             belongs to KV group h / (H_q / H_kv).
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+enum sa_status {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,         /* a required pointer is NULL */
+  SA_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes */
+  SA_ERR_UNSUPPORTED = 3,  /* a size the kernels are not built for (e.g. head_dim 96) */
+  SA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the *_workspace_size value */
+  SA_ERR_HIP = 5,          /* the HIP runtime rejected a launch */
+  SA_ERR_ABI = 6,          /* descriptor abi_version differs from SA_ABI_VERSION */
+  SA_ERR_ALIGN = 7         /* a pointer is not 16-byte aligned */
+};
+
+/*
+ * Paged KV-cache descriptor ([DSA-page] §2.2: fixed-size blocks of contiguous tokens).
+ *
+ * Pools are indexed [page][head][slot][...]: one page holds page_size consecutive tokens of
+ * every head, and within a page each head's rows are contiguous, so one head of one page is
+ * a single contiguous (page_size x row) block.
+ *   k_pool, v_pool  bf16 (raw uint16 bits) [num_pages][num_kv_heads][page_size][head_dim]
+ *   kidx_pool       int8                   [num_pages][num_idx_heads][page_size][idx_dim]
+ *   page_table      int32 [batch][max_pages_per_seq]; logical page p of sequence b is
+ *                   physical page page_table[b * max_pages_per_seq + p]
+ *   seq_lens        int32 [batch]; tokens cached per sequence, each in [1, max_seq_len]
+ * A contiguous cache is the same descriptor with page_size = the sequence length and an
+ * identity page table.
+ * kidx_pool may be NULL for calls that do not score (attention only); k_pool/v_pool may be
+ * NULL for calls that only score/select.
+ */
+typedef struct sa_paged_kv {
+  int32_t abi_version;        /* must be SA_ABI_VERSION */
+  int32_t batch;              /* B >= 1 */
+  int32_t num_kv_heads;       /* H_kv >= 1 */
+  int32_t head_dim;           /* d: 64 or 128 */
+  int32_t num_idx_heads;      /* H_idx: num_kv_heads, or 1 (one indexer key shared by all groups) */
+  int32_t idx_dim;            /* d_idx: 32, 64 or 128 (ignored when kidx_pool is NULL) */
+  int32_t page_size;          /* tokens per page: a power of two, >= 64 */
+  int32_t max_pages_per_seq;  /* row length of page_table */
+  int64_t num_pages;          /* pages in each pool */
+  int32_t max_seq_len;        /* host-side bound on seq_lens[b]; <= max_pages_per_seq * page_size */
+  int32_t prefix_len;         /* P >= 0: forced always-attended prefix ([DSA-page] §2.4) */
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int8_t* kidx_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+} sa_paged_kv;
+
+/* SA_ABI_VERSION of the built library. */
+int32_t sparse_attn_abi_version(void);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char* sparse_attn_status_string(int32_t status);
+
+/*
+ * Indexer ([DSA-page] §2.1): exact int8 scores of every candidate key.
+ *
+ *   scores[b][i][gi][t] = sum_j q_idx[b][i][gi][j] * kidx(b, t, gi)[j]   for P <= t <= pos
+ *
+ * accumulated in int32 (exact: |score| <= idx_dim * 2^14 <= 2^21).
+ *   q_idx   int8  [batch][q_len][num_idx_heads][idx_dim]
+ *   scores  int32 [batch][q_len][num_idx_heads][score_row_stride]; only the candidate
+ *           columns are written, the rest of each row is left untouched.
+ * Requires kidx_pool, page_table, seq_lens; score_row_stride >= max_seq_len and a multiple
+ * of 4; 1 <= q_len <= q_tail <= max_seq_len.
+ */
+int32_t sparse_attn_index(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
+                          int32_t q_tail, int32_t* scores, int64_t score_row_stride,
+                          void* stream);
+
+/*
+ * Top-K selection ([DSA-page] §2.1, with the forced prefix of §2.4).
+ *
+ * For every (b, i, gi) writes the index list described in the header comment:
+ *   indices int32 [batch][q_len][num_idx_heads][prefix_len + top_k]
+ * Ties are broken by the lower token index, so the result is unique and deterministic.
+ *   scores  as written by sparse_attn_index (same q_len/q_tail/row stride); only the
+ *           candidate columns are read.
+ * workspace: at least sparse_attn_topk_workspace_size(...) bytes of device memory (may be
+ * NULL when that size is 0). Its contents on entry do not matter.
+ */
+size_t sparse_attn_topk_workspace_size(const sa_paged_kv* kv, int32_t q_len, int32_t top_k);
+int32_t sparse_attn_topk(const sa_paged_kv* kv, const int32_t* scores, int64_t score_row_stride,
+                         int32_t q_len, int32_t q_tail, int32_t top_k, int32_t* indices,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Prefill attention ([DSA-page] §2.3, prefill): online-softmax attention of a block of
+ * queries over their index lists, or dense causal attention when indices == NULL.
+ *
+ *   q        bf16 [batch][q_len][num_q_heads][head_dim]
+ *   indices  int32 [batch][q_len][num_idx_heads][index_width] lists as written by
+ *            sparse_attn_topk (ascending, -1 padded), or NULL for dense causal attention
+ *            (every key 0..pos; index_width is then ignored)
+ *   out      bf16 [batch][q_len][num_q_heads][head_dim]
+ *   lse      float [batch][q_len][num_q_heads] (natural-log sum of exp of the scaled
+ *            logits), or NULL
+ * For each query head h:  z_t = sm_scale * q_h . K[t];  out = sum_t softmax(z)_t V[t].
+ * fp32 accumulation; out is rounded to bf16 (nearest-even). num_q_heads must be a multiple
+ * of num_kv_heads with group size H_q/H_kv in {1, 2, 4, 8} for the sparse path.
+ */
+int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_t num_q_heads,
+                                int32_t q_len, int32_t q_tail, const int32_t* indices,
+                                int32_t index_width, float sm_scale, uint16_t* out, float* lse,
+                                void* stream);
+
+/*
+ * Decode attention ([DSA-page] §2.3, decode): one query token per sequence (pos =
+ * seq_lens[b] - 1) attends to its index list. Each (b, KV group) list is cut into
+ * num_splits chunks processed in parallel; partial softmax states (max, sum, weighted V in
+ * fp32) are merged exactly in a fixed order, so results are deterministic.
+ *
+ *   q        bf16 [batch][num_q_heads][head_dim]
+ *   indices  int32 [batch][num_idx_heads][index_width]
+ *   out      bf16 [batch][num_q_heads][head_dim];  lse float [batch][num_q_heads] or NULL
+ *   num_splits  0 = choose automatically, else 1..256
+ * workspace: sparse_attn_decode_workspace_size(kv, num_q_heads, index_width, num_splits)
+ * bytes of device memory.
+ */
+size_t sparse_attn_decode_workspace_size(const sa_paged_kv* kv, int32_t num_q_heads,
+                                         int32_t index_width, int32_t num_splits);
+int32_t sparse_attn_fwd_decode(const sa_paged_kv* kv, const uint16_t* q, int32_t num_q_heads,
+                               const int32_t* indices, int32_t index_width, float sm_scale,
+                               int32_t num_splits, void* workspace, size_t workspace_bytes,
+                               uint16_t* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

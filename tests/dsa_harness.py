@@ -1,0 +1,178 @@
+"""Test plumbing: run the HIP path through the binding, and feed the same inputs to the oracle.
+
+The oracle reads device pools through DevicePool, which fancy-indexes the torch tensor drawn
+by the `synthetic` generator and copies the requested rows to host memory. No oracle input
+comes from the HIP library.
+"""
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+import flash_attention_int8_amd as fa
+import oracle
+from synthetic import Inputs
+
+MAX_ABS = 2e-2     # bf16 output vs fp64 oracle, max over elements
+MEAN_ABS = 2e-3    # ... mean over elements
+LSE_ABS = 2e-3     # fp32 log-sum-exp vs fp64
+
+
+class DevicePool:
+    """pool[phys, head, slot] -> numpy rows (bf16 bits as uint16, int8 as int8)."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+
+    def __getitem__(self, key):
+        phys, head, slot = key
+        dev = self.t.device
+        p = torch.as_tensor(np.asarray(phys), device=dev, dtype=torch.long)
+        s = torch.as_tensor(np.asarray(slot), device=dev, dtype=torch.long)
+        rows = self.t[p, int(head), s]
+        if rows.dtype == torch.bfloat16:
+            return rows.view(torch.int16).cpu().numpy().view(np.uint16)
+        return rows.cpu().numpy()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def make_kv(inp: Inputs) -> fa.PagedKV:
+    w = inp.workload
+    return fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
+                      page_table=inp.page_table, seq_lens=inp.seq_lens,
+                      max_seq_len=max(inp.seq_lens_host), prefix_len=w.prefix_len,
+                      num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                      idx_dim=w.idx_dim if not w.dense else 0, num_idx_heads=inp.num_idx_heads,
+                      page_size=w.page_size, num_pages=inp.num_pages)
+
+
+class GpuRun:
+    def __init__(self):
+        self.scores = []       # list of (q0, scores chunk)
+        self.indices = None
+        self.out = None
+        self.lse = None
+
+
+def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
+            keep_scores: bool = False) -> GpuRun:
+    """The whole path on the device: index -> top-K -> attention (or dense attention)."""
+    w = inp.workload
+    kv = make_kv(inp)
+    r = GpuRun()
+    B, S = w.batch, w.q_len
+    if w.dense:
+        r.out, r.lse = fa.prefill(kv, inp.q, q_tail=S)
+        return r
+    if S == 1:
+        scores = fa.index(kv, inp.q_idx, 1, 1)
+        idx = fa.topk(kv, scores, 1, 1, w.top_k)
+        r.indices = idx
+        if keep_scores:
+            r.scores.append((0, scores))
+        r.out, r.lse = fa.decode(kv, inp.q[:, 0].contiguous(), idx[:, 0].contiguous(),
+                                 num_splits=num_splits)
+        r.out = r.out.unsqueeze(1)
+        r.lse = r.lse.unsqueeze(1)
+        return r
+    q_chunk = q_chunk or S
+    T = max(inp.seq_lens_host)
+    r.indices = torch.empty((B, S, inp.num_idx_heads, w.index_width), dtype=torch.int32, device=inp.q.device)
+    r.out = torch.empty_like(inp.q)
+    r.lse = torch.empty((B, S, w.num_q_heads), dtype=torch.float32, device=inp.q.device)
+    for q0 in range(0, S, q_chunk):
+        c = min(q_chunk, S - q0)
+        tail = S - q0
+        qi = inp.q_idx[:, q0:q0 + c].contiguous()
+        scores = fa.index(kv, qi, c, tail)
+        idx = fa.topk(kv, scores, c, tail, w.top_k)
+        out, lse = fa.prefill(kv, inp.q[:, q0:q0 + c].contiguous(), q_tail=tail, indices=idx)
+        r.indices[:, q0:q0 + c] = idx
+        r.out[:, q0:q0 + c] = out
+        r.lse[:, q0:q0 + c] = lse
+        if keep_scores:
+            r.scores.append((q0, scores))
+    del T
+    return r
+
+
+class OracleView:
+    """Host-side views of one workload's inputs for the oracle."""
+
+    def __init__(self, inp: Inputs, host_copy: bool = True):
+        self.inp = inp
+        self.w = inp.workload
+        if host_copy:
+            self.k_pool = bits(inp.k_pool)
+            self.v_pool = bits(inp.v_pool)
+            self.kidx = None if inp.kidx_pool is None else inp.kidx_pool.cpu().numpy()
+        else:
+            self.k_pool = DevicePool(inp.k_pool)
+            self.v_pool = DevicePool(inp.v_pool)
+            self.kidx = None if inp.kidx_pool is None else DevicePool(inp.kidx_pool)
+        self.table = inp.page_table.cpu().numpy()
+        self._q = inp.q
+        self._q_idx = inp.q_idx
+
+    def query(self, b: int, i: int, g: int):
+        """(index list or None, O [G][d], LSE [G]) of query token i of sequence b, KV group g."""
+        w = self.w
+        heads = list(oracle.group_query_heads(g, w.num_q_heads, w.num_kv_heads))
+        qb = bits(self._q[b, i, heads[0]:heads[-1] + 1])
+        pos = oracle.query_position(self.inp.seq_lens_host[b], w.q_len, i)
+        scale = 1.0 / math.sqrt(w.head_dim)
+        if w.dense:
+            o, lse = oracle.dense_query(q_bits=qb, k_pool=self.k_pool, v_pool=self.v_pool,
+                                        page_table_row=self.table[b], page_size=w.page_size,
+                                        kv_head=g, pos=pos, sm_scale=scale)
+            return None, o, lse
+        gi = 0 if self.inp.num_idx_heads == 1 else g
+        qi = self._q_idx[b, i, gi].cpu().numpy()
+        return oracle.dsa_query(q_bits=qb, q_idx_vec=qi, kidx_pool=self.kidx, k_pool=self.k_pool,
+                                v_pool=self.v_pool, page_table_row=self.table[b],
+                                page_size=w.page_size, kv_head=g, idx_head=gi, pos=pos,
+                                prefix_len=w.prefix_len, top_k=w.top_k, sm_scale=scale)
+
+    def scores_row(self, b: int, i: int, gi: int) -> np.ndarray:
+        """Oracle indexer scores of every candidate key of (b, i, gi), with their tokens."""
+        w = self.w
+        pos = oracle.query_position(self.inp.seq_lens_host[b], w.q_len, i)
+        c = oracle.candidate_keys(pos, w.prefix_len)
+        k = oracle.page_rows(self.kidx, self.table[b], w.page_size, gi, c)
+        return c, oracle.index_scores(self._q_idx[b, i, gi].cpu().numpy(), k)
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def compare_rows(gpu: GpuRun, ov: OracleView, rows, check_lse: bool = True):
+    """Checks the given (b, i, g) rows; returns (max_abs, mean_abs, max_lse) over them."""
+    w = ov.w
+    G = w.group
+    errs, lse_errs = [], []
+    for (b, i, g) in rows:
+        idx, o, lse = ov.query(b, i, g)
+        if idx is not None:
+            gi = 0 if ov.inp.num_idx_heads == 1 else g
+            got = gpu.indices[b, i, gi].cpu().numpy()
+            assert np.array_equal(got, idx), (b, i, g, got[:16], idx[:16])
+        og = f64(gpu.out[b, i, g * G:(g + 1) * G])
+        errs.append(np.abs(og - o).ravel())
+        if check_lse and gpu.lse is not None:
+            lg = gpu.lse[b, i, g * G:(g + 1) * G].double().cpu().numpy()
+            lse_errs.append(np.abs(lg - lse))
+    e = np.concatenate(errs)
+    le = float(np.concatenate(lse_errs).max()) if lse_errs else 0.0
+    return float(e.max()), float(e.mean()), le
+
+
+def assert_close(stats):
+    mx, mean, lse = stats
+    assert mx <= MAX_ABS, f"max abs error {mx}"
+    assert mean <= MEAN_ABS, f"mean abs error {mean}"
+    assert lse <= LSE_ABS, f"lse error {lse}"

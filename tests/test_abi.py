@@ -1,0 +1,190 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, the ctypes
+descriptor matches the C struct, and invalid arguments return their documented status
+before anything is launched.
+
+Every validation case below carries at least one invalid argument, so no call here ever
+reaches a kernel launch (the fake device addresses are never dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import flash_attention_int8_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sparse_attn_\w+)", out))
+    assert set(names) <= exported
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.sparse_attn_abi_version() == fa.SA_ABI_VERSION == 1
+    for code in range(8):
+        assert lib.sparse_attn_status_string(code)
+    assert lib.sparse_attn_status_string(0) == b"ok"
+    assert lib.sparse_attn_status_string(99) == b"unknown status"
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    fields = [f for f, _ in fa.sa_paged_kv._fields_]
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(sa_paged_kv, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "sparse_attn.h"\n'
+                   "int main(void) {\n" + body + '\n  printf("size %zu\\n", sizeof(sa_paged_kv));\n'
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(fa.sa_paged_kv, f).offset, f
+    assert int(got["size"]) == ctypes.sizeof(fa.sa_paged_kv)
+
+
+# ----------------------------------------------------------------------------- validation
+
+A = 0x7f0000000000  # a 16-byte aligned fake device address; never dereferenced
+
+
+def desc(**over):
+    d = fa.sa_paged_kv()
+    vals = dict(abi_version=1, batch=2, num_kv_heads=8, head_dim=128, num_idx_heads=8, idx_dim=64,
+                page_size=64, max_pages_per_seq=16, num_pages=32, max_seq_len=1024, prefix_len=0,
+                k_pool=A, v_pool=A + 0x1000, kidx_pool=A + 0x2000, page_table=A + 0x3000,
+                seq_lens=A + 0x4000)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(d, k, v)
+    return d
+
+
+def call_index(lib, d, q_idx=A, q_len=1, q_tail=1, scores=A, stride=1024):
+    return lib.sparse_attn_index(ctypes.byref(d) if d is not None else None, q_idx, q_len, q_tail,
+                                 scores, stride, None)
+
+
+def call_topk(lib, d, scores=A, stride=1024, q_len=1, q_tail=1, k=64, idx=A, ws=None, ws_bytes=0):
+    return lib.sparse_attn_topk(ctypes.byref(d), scores, stride, q_len, q_tail, k, idx, ws, ws_bytes, None)
+
+
+def call_prefill(lib, d, q=A, hq=32, q_len=16, q_tail=16, idx=A, width=64, out=A, lse=None):
+    return lib.sparse_attn_fwd_prefill(ctypes.byref(d), q, hq, q_len, q_tail, idx, width, 0.1, out, lse, None)
+
+
+def call_decode(lib, d, q=A, hq=32, idx=A, width=2048, splits=4, ws=A, ws_bytes=1 << 30, out=A, lse=None):
+    return lib.sparse_attn_fwd_decode(ctypes.byref(d), q, hq, idx, width, 0.1, splits, ws, ws_bytes,
+                                      out, lse, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(d=None), fa.SA_ERR_NULL),
+    (dict(d=desc(abi_version=2)), fa.SA_ERR_ABI),
+    (dict(d=desc(page_table=None)), fa.SA_ERR_NULL),
+    (dict(d=desc(seq_lens=None)), fa.SA_ERR_NULL),
+    (dict(d=desc(kidx_pool=None)), fa.SA_ERR_NULL),
+    (dict(q_idx=None), fa.SA_ERR_NULL),
+    (dict(scores=None), fa.SA_ERR_NULL),
+    (dict(d=desc(idx_dim=48)), fa.SA_ERR_UNSUPPORTED),
+    (dict(d=desc(page_size=96)), fa.SA_ERR_UNSUPPORTED),
+    (dict(d=desc(page_size=32)), fa.SA_ERR_UNSUPPORTED),
+    (dict(d=desc(num_idx_heads=3)), fa.SA_ERR_SHAPE),
+    (dict(d=desc(batch=0)), fa.SA_ERR_SHAPE),
+    (dict(d=desc(max_seq_len=1025)), fa.SA_ERR_SHAPE),    # more than 16 pages x 64
+    (dict(d=desc(prefix_len=-1)), fa.SA_ERR_SHAPE),
+    (dict(q_len=0), fa.SA_ERR_SHAPE),
+    (dict(q_len=4, q_tail=3), fa.SA_ERR_SHAPE),
+    (dict(q_tail=1025), fa.SA_ERR_SHAPE),
+    (dict(stride=1000), fa.SA_ERR_SHAPE),
+    (dict(stride=1026), fa.SA_ERR_SHAPE),                   # not a multiple of 4
+    (dict(scores=A + 4), fa.SA_ERR_ALIGN),
+    (dict(d=desc(kidx_pool=A + 8)), fa.SA_ERR_ALIGN),
+    (dict(d=desc(page_table=A + 4)), fa.SA_ERR_ALIGN),
+])
+def test_index_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_index(lib, d, **case) == code
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(k=0), fa.SA_ERR_SHAPE),
+    (dict(scores=None), fa.SA_ERR_NULL),
+    (dict(idx=None), fa.SA_ERR_NULL),
+    (dict(idx=A + 4), fa.SA_ERR_ALIGN),
+    (dict(stride=512), fa.SA_ERR_SHAPE),
+    (dict(q_len=2, q_tail=1), fa.SA_ERR_SHAPE),
+])
+def test_topk_validation(lib, case, code):
+    assert call_topk(lib, desc(), **case) == code
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(d=desc(head_dim=96)), fa.SA_ERR_UNSUPPORTED),
+    (dict(d=desc(k_pool=None)), fa.SA_ERR_NULL),
+    (dict(d=desc(v_pool=None)), fa.SA_ERR_NULL),
+    (dict(q=None), fa.SA_ERR_NULL),
+    (dict(out=None), fa.SA_ERR_NULL),
+    (dict(hq=30), fa.SA_ERR_SHAPE),                          # not a multiple of H_kv
+    (dict(hq=24), fa.SA_ERR_UNSUPPORTED),                    # group of 3, sparse path
+    (dict(hq=128), fa.SA_ERR_UNSUPPORTED),                   # group of 16, sparse path
+    (dict(width=0), fa.SA_ERR_SHAPE),
+    (dict(q=A + 2), fa.SA_ERR_ALIGN),
+    (dict(out=A + 8), fa.SA_ERR_ALIGN),
+    (dict(lse=A + 4), fa.SA_ERR_ALIGN),
+    (dict(q_len=16, q_tail=2000), fa.SA_ERR_SHAPE),
+])
+def test_prefill_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_prefill(lib, d, **case) == code
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(splits=-1), fa.SA_ERR_SHAPE),
+    (dict(splits=257), fa.SA_ERR_SHAPE),
+    (dict(ws=None), fa.SA_ERR_WORKSPACE),
+    (dict(ws_bytes=16), fa.SA_ERR_WORKSPACE),
+    (dict(ws=A + 4), fa.SA_ERR_ALIGN),
+    (dict(idx=None), fa.SA_ERR_NULL),
+    (dict(hq=24), fa.SA_ERR_UNSUPPORTED),
+    (dict(width=0), fa.SA_ERR_SHAPE),
+    (dict(d=desc(head_dim=32)), fa.SA_ERR_UNSUPPORTED),
+])
+def test_decode_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_decode(lib, d, **case) == code
+
+
+def test_decode_workspace_size(lib):
+    d = desc()
+    # explicit splits: units (B * H_kv) * splits * G * (d + 2) floats
+    assert lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 32, 2048, 4) == 2 * 8 * 4 * 4 * 130 * 4
+    assert lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 32, 2048, 1) == 0
+    # more splits than list entries are clamped to one entry per split
+    assert lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 32, 3, 16) == 2 * 8 * 3 * 4 * 130 * 4
+    auto = lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 32, 2048, 0)
+    assert auto > 0 and auto % (2 * 8 * 4 * 130 * 4) == 0
+    assert lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 30, 2048, 0) == 0

@@ -1,0 +1,244 @@
+"""Parity of the HIP path with the fp64 oracle on seeded inputs (needs an MI355X).
+
+Bars: selected index lists and indexer scores bit-exact; bf16 outputs within max-abs 2e-2
+and mean-abs 2e-3 of the fp64 oracle; fp32 LSE within 2e-3.
+Small cases check every row and cover ragged lengths, shuffled pages with spare pages,
+a forced prefix longer than some sequences, shared indexer heads, every group size, both
+head dims, all indexer widths, split counts and heavy score ties.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import flash_attention_int8_amd as fa
+from synthetic import CONFIGS, Workload, make_inputs
+from dsa_harness import (OracleView, assert_close, compare_rows, make_kv, run_gpu, f64)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def all_rows(inp):
+    w = inp.workload
+    return [(b, i, g) for b in range(w.batch) for i in range(w.q_len) for g in range(w.num_kv_heads)]
+
+
+def W(**kw) -> Workload:
+    base = dict(name="case", batch=1, num_q_heads=8, num_kv_heads=2, head_dim=128, seq_len=256,
+                q_len=256, idx_dim=64, top_k=32, prefix_len=0, page_size=64, shuffled_pages=True,
+                qkv_source="bf16")
+    base.update(kw)
+    return Workload(**base)
+
+
+def _banner(msg):
+    print(f"\n[parity] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ small cases, every row
+
+SMALL = {
+    "tiny_sparse_prefill": (CONFIGS["tiny_sparse_prefill"], {}),
+    "tiny_dense": (CONFIGS["tiny_sparse_prefill"].with_(top_k=0, idx_dim=0), {}),
+    "ragged_prefill_prefix": (W(batch=2, seq_len=300, q_len=250, top_k=40, prefix_len=5),
+                              dict(seq_lens=[300, 250], spare_pages=3)),
+    "prefill_g1_d64_didx32": (W(num_q_heads=2, num_kv_heads=2, head_dim=64, idx_dim=32, seq_len=200,
+                                q_len=200, top_k=16), {}),
+    "prefill_g8_didx128": (W(num_q_heads=16, num_kv_heads=2, idx_dim=128, seq_len=192, q_len=130,
+                             top_k=24, prefix_len=3), dict(seq_lens=[192])),
+    "prefill_shared_indexer": (W(batch=2, seq_len=160, q_len=160, top_k=20), dict(num_idx_heads=1)),
+    "prefill_ties": (W(seq_len=320, q_len=320, top_k=50, prefix_len=7), dict(idx_values=(-1, 0, 1))),
+    "dense_ragged_paged": (W(batch=2, seq_len=300, q_len=300, idx_dim=0, top_k=0),
+                           dict(seq_lens=[300, 301], spare_pages=2)),
+    "dense_d64_g2": (W(num_q_heads=4, head_dim=64, idx_dim=0, top_k=0, seq_len=257, q_len=257,
+                       page_size=128), {}),
+    "dense_contiguous_g4": (W(idx_dim=0, top_k=0, seq_len=512, q_len=512, page_size=512,
+                              shuffled_pages=False), {}),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_every_row(name):
+    w, kw = SMALL[name]
+    _banner(f"small case {name}: {w}")
+    inp = make_inputs(w, seed=11, device="cpu", **kw).to(DEV)
+    gpu = run_gpu(inp, q_chunk=96 if w.q_len > 200 else None)
+    torch.cuda.synchronize()
+    ov = OracleView(inp)
+    assert_close(compare_rows(gpu, ov, all_rows(inp)))
+
+
+DECODE = {
+    "decode_ragged_prefix": (W(batch=4, num_q_heads=16, num_kv_heads=2, head_dim=64, idx_dim=128,
+                               seq_len=1000, q_len=1, top_k=100, prefix_len=13),
+                             dict(seq_lens=[1000, 64, 777, 10], spare_pages=5)),
+    "decode_g4_d128": (W(batch=3, num_q_heads=16, num_kv_heads=4, seq_len=5000, q_len=1, top_k=256),
+                       dict(seq_lens=[5000, 4097, 300])),
+    "decode_g2_shared_indexer": (W(batch=2, num_q_heads=4, seq_len=3000, q_len=1, top_k=64,
+                                   idx_dim=32), dict(num_idx_heads=1)),
+    "decode_ties": (W(batch=2, seq_len=4000, q_len=1, top_k=300, prefix_len=2),
+                    dict(idx_values=(-1, 0, 1))),
+    "decode_g1": (W(batch=2, num_q_heads=2, num_kv_heads=2, seq_len=2000, q_len=1, top_k=128), {}),
+}
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 16])
+@pytest.mark.parametrize("name", list(DECODE))
+def test_decode_every_row(name, splits):
+    w, kw = DECODE[name]
+    _banner(f"decode case {name} splits={splits}")
+    inp = make_inputs(w, seed=5, device="cpu", **kw).to(DEV)
+    gpu = run_gpu(inp, num_splits=splits)
+    torch.cuda.synchronize()
+    assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
+
+
+def test_scores_exact_prefill_and_decode():
+    for w, kw in [SMALL["ragged_prefill_prefix"], DECODE["decode_ragged_prefix"],
+                  SMALL["prefill_g8_didx128"]]:
+        _banner(f"scores {w}")
+        inp = make_inputs(w, seed=3, device="cpu", **kw).to(DEV)
+        gpu = run_gpu(inp, keep_scores=True, q_chunk=64)
+        torch.cuda.synchronize()
+        ov = OracleView(inp)
+        for q0, sc in gpu.scores:
+            sc = sc.cpu().numpy()
+            for b in range(w.batch):
+                for ic in range(sc.shape[1]):
+                    for gi in range(inp.num_idx_heads):
+                        c, want = ov.scores_row(b, q0 + ic, gi)
+                        assert np.array_equal(sc[b, ic, gi, c], want), (b, q0 + ic, gi)
+
+
+# ------------------------------------------------------------------ invariances
+
+def _repack(inp, seed):
+    """Same logical K/V/indexer content under a different page permutation."""
+    w = inp.workload
+    n = inp.num_pages
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(seed)).to(DEV)
+    new = make_inputs(w, seed=0, device="cpu", seq_lens=inp.seq_lens_host,
+                      num_idx_heads=inp.num_idx_heads, spare_pages=n - sum(
+                          -(-t // w.page_size) for t in inp.seq_lens_host)).to(DEV)
+    new.q, new.q_idx = inp.q, inp.q_idx
+    new.k_pool = torch.empty_like(inp.k_pool)
+    new.v_pool = torch.empty_like(inp.v_pool)
+    new.k_pool[perm] = inp.k_pool
+    new.v_pool[perm] = inp.v_pool
+    if inp.kidx_pool is not None:
+        new.kidx_pool = torch.empty_like(inp.kidx_pool)
+        new.kidx_pool[perm] = inp.kidx_pool
+    tbl = inp.page_table.long()
+    new.page_table = torch.where(tbl >= 0, perm[tbl.clamp(min=0)], tbl).to(torch.int32)
+    return new
+
+
+@pytest.mark.parametrize("name", ["ragged_prefill_prefix", "dense_ragged_paged"])
+def test_page_permutation_is_bit_identical(name):
+    w, kw = SMALL[name]
+    inp = make_inputs(w, seed=2, device="cpu", **kw).to(DEV)
+    a = run_gpu(inp)
+    b = run_gpu(_repack(inp, 99))
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.lse, b.lse)
+    if a.indices is not None:
+        assert torch.equal(a.indices, b.indices)
+
+
+def test_decode_permutation_and_determinism():
+    w, kw = DECODE["decode_g4_d128"]
+    inp = make_inputs(w, seed=8, device="cpu", **kw).to(DEV)
+    a = run_gpu(inp, num_splits=4)
+    a2 = run_gpu(inp, num_splits=4)
+    b = run_gpu(_repack(inp, 5), num_splits=4)
+    torch.cuda.synchronize()
+    for x in (a2, b):
+        assert torch.equal(a.indices, x.indices)
+        assert torch.equal(a.out, x.out)
+        assert torch.equal(a.lse, x.lse)
+
+
+def test_decode_matches_last_prefill_row():
+    """Decode at position T-1 equals row T-1 of a prefill over the same cache."""
+    w = W(batch=2, seq_len=700, q_len=700, top_k=64, prefix_len=4)
+    inp = make_inputs(w, seed=4, device="cpu").to(DEV)
+    pre = run_gpu(inp, q_chunk=128)
+    dec_inp = make_inputs(w.with_(q_len=1), seed=4, device="cpu").to(DEV)
+    dec_inp.q = inp.q[:, -1:].contiguous()
+    dec_inp.q_idx = inp.q_idx[:, -1:].contiguous()
+    for splits in (1, 5):
+        dec = run_gpu(dec_inp, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(dec.indices[:, 0], pre.indices[:, -1])
+        d = (f64(dec.out[:, 0]) - f64(pre.out[:, -1]))
+        assert np.abs(d).max() <= 1e-2
+
+
+def test_lse_matches_definition_dense():
+    """Dense LSE equals log-sum-exp of the scaled logits computed by the oracle."""
+    w = SMALL["dense_contiguous_g4"][0]
+    inp = make_inputs(w, seed=1, device="cpu").to(DEV)
+    gpu = run_gpu(inp)
+    torch.cuda.synchronize()
+    rows = [(0, i, g) for i in (0, 1, 63, 64, 200, 511) for g in range(w.num_kv_heads)]
+    assert_close(compare_rows(gpu, OracleView(inp), rows))
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sample_queries(S, n, seed):
+    rng = np.random.default_rng(seed)
+    head = list(range(min(S, 4)))
+    tail = list(range(max(0, S - 4), S))
+    mid = sorted(rng.choice(S, size=min(S, n), replace=False).tolist())
+    return sorted(set(head + tail + mid))
+
+
+def test_full_dense_prefill_8k():
+    w = CONFIGS["dense_prefill_8k"]
+    _banner(f"full {w.name}")
+    inp = make_inputs(w, seed=2, device=DEV)
+    gpu = run_gpu(inp)
+    torch.cuda.synchronize()
+    ov = OracleView(inp, host_copy=False)
+    rows = [(b, i, g) for b in range(w.batch) for i in _sample_queries(w.q_len, 6, b)
+            for g in (0, 3, 7)]
+    assert_close(compare_rows(gpu, ov, rows))
+
+
+def test_full_sparse_decode_128k():
+    w = CONFIGS["sparse_decode_128k"]
+    _banner(f"full {w.name}")
+    inp = make_inputs(w, seed=3, device=DEV)
+    gpu = run_gpu(inp)
+    torch.cuda.synchronize()
+    ov = OracleView(inp, host_copy=False)
+    assert_close(compare_rows(gpu, ov, all_rows(inp)))
+
+
+def test_full_sparse_prefill_32k():
+    w = CONFIGS["sparse_prefill_32k"]
+    _banner(f"full {w.name}")
+    inp = make_inputs(w, seed=4, device=DEV)
+    gpu = run_gpu(inp, q_chunk=2048)
+    torch.cuda.synchronize()
+    ov = OracleView(inp, host_copy=False)
+    rows = [(0, i, g) for i in _sample_queries(w.q_len, 10, 4) for g in (0, 5)]
+    assert_close(compare_rows(gpu, ov, rows))
+
+
+def test_full_sparse_decode_1m_prefix():
+    w = CONFIGS["sparse_decode_1m_prefix"]
+    _banner(f"full {w.name}")
+    inp = make_inputs(w, seed=5, device=DEV)
+    gpu = run_gpu(inp)
+    torch.cuda.synchronize()
+    ov = OracleView(inp, host_copy=False)
+    rows = [(b, 0, g) for b in range(w.batch) for g in (0, 3, 7)]
+    assert_close(compare_rows(gpu, ov, rows))
+    # every list starts with the forced prefix 0..195
+    idx = gpu.indices[:, 0].cpu().numpy()
+    assert np.all(idx[..., :196] == np.arange(196))
