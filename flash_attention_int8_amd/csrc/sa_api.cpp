@@ -30,6 +30,7 @@ int32_t check_kv(const sa_paged_kv* kv, unsigned need, sa::KvView* v) {
   if (!pow2(kv->page_size) || kv->page_size < 64 || kv->page_size > (1 << 24))
     return SA_ERR_UNSUPPORTED;
   if ((int64_t)kv->max_seq_len > (int64_t)kv->max_pages_per_seq * kv->page_size) return SA_ERR_SHAPE;
+  if (kv->num_pages * (int64_t)kv->page_size > INT32_MAX) return SA_ERR_UNSUPPORTED;  // row ids are int32
   if (kv->num_idx_heads != kv->num_kv_heads && kv->num_idx_heads != 1) return SA_ERR_SHAPE;
   if ((need & NEED_KV) && kv->head_dim != 64 && kv->head_dim != 128) return SA_ERR_UNSUPPORTED;
   if ((need & NEED_IDX) && kv->idx_dim != 32 && kv->idx_dim != 64 && kv->idx_dim != 128)

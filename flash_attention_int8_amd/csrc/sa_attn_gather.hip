@@ -25,11 +25,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kNB = 4;  // keys per lane group per batch
-
-struct SoftmaxState {
-  float m, l;
-};
+constexpr int kSeg = 2048;  // list entries resolved into LDS at a time
 
 __device__ __forceinline__ float safe_scale(float m_old, float m_new) {
   return (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
@@ -46,6 +42,9 @@ __global__ __launch_bounds__(256) void k_attn_gather(KvView kv, const uint16_t* 
   constexpr int LPK = D / 8;        // lanes per key row
   constexpr int KPW = 64 / LPK;     // keys a wave holds at once (lane groups)
   constexpr int NW = 4;
+  constexpr int STRIDE = NW * KPW;  // list entries covered by one load round of the workgroup
+  constexpr int kNB = G <= 2 ? 8 : (G == 4 ? 4 : 2);  // keys per lane group per batch
+  __shared__ int32_t sh_rid[kSeg];  // resolved rows (phys_page * page_size + slot) or -1
   __shared__ float sh_m[NW][G];
   __shared__ float sh_l[NW][G];
   __shared__ float sh_acc[NW][G][D];
@@ -63,18 +62,17 @@ __global__ __launch_bounds__(256) void k_attn_gather(KvView kv, const uint16_t* 
   const int pos = min(kv.seq_lens[b], kv.max_seq_len) - q_tail + i;
   const int gi = (kv.num_idx_heads == 1) ? 0 : g;
   const int32_t* ilist = indices + (bi * kv.num_idx_heads + gi) * (int64_t)W;
+  const int64_t head_stride = (int64_t)kv.page_size * D;  // one head of one page
+  const int64_t page_stride = head_stride * kv.num_kv_heads;
+  const uint16_t* kbase = kv.k_pool + g * head_stride + part * 8;
+  const uint16_t* vbase = kv.v_pool + g * head_stride + part * 8;
 
-  // Query fragments, pre-scaled by sm_scale * log2(e).
-  float qf[G][8];
+  // Query fragments stay packed bf16 (converted per use); the softmax scale sm_scale*log2(e)
+  // is applied to the reduced dot products.
+  uint4 qw[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 w = *reinterpret_cast<const uint4*>(
-        q + (bi * num_q_heads + (int64_t)g * G + h) * D + part * 8);
-    qf[h][0] = bf16_lo(w.x) * qscale; qf[h][1] = bf16_hi(w.x) * qscale;
-    qf[h][2] = bf16_lo(w.y) * qscale; qf[h][3] = bf16_hi(w.y) * qscale;
-    qf[h][4] = bf16_lo(w.z) * qscale; qf[h][5] = bf16_hi(w.z) * qscale;
-    qf[h][6] = bf16_lo(w.w) * qscale; qf[h][7] = bf16_hi(w.w) * qscale;
-  }
+  for (int h = 0; h < G; ++h)
+    qw[h] = *reinterpret_cast<const uint4*>(q + (bi * num_q_heads + (int64_t)g * G + h) * D + part * 8);
 
   float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -87,80 +85,90 @@ __global__ __launch_bounds__(256) void k_attn_gather(KvView kv, const uint16_t* 
 
   const int k_begin = split * keys_per_split;
   const int k_end = min(W, k_begin + keys_per_split);
-  const int64_t head_stride = (int64_t)kv.page_size * D;            // one head of one page
-  const int64_t page_stride = head_stride * kv.num_kv_heads;
 
-  // Batches: the workgroup covers NW * KPW * kNB consecutive list entries per batch; wave w
-  // takes entries [w*KPW*kNB, (w+1)*KPW*kNB) of it, lane group grp every KPW-th one.
-  for (int base = k_begin; base < k_end; base += NW * KPW * kNB) {
-    int tok[kNB];
-    int64_t off[kNB];
-    bool ok[kNB];
-#pragma unroll
-    for (int u = 0; u < kNB; ++u) {
-      const int j = base + wave * KPW * kNB + u * KPW + grp;
-      tok[u] = (j < k_end) ? ilist[j] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kNB; ++u) {
-      const int t = tok[u];
-      const int64_t ph = (t >= 0 && t <= pos) ? phys_page(kv, b, t) : -1;
-      ok[u] = ph >= 0;
-      off[u] = ok[u] ? ph * page_stride + g * head_stride +
-                           (int64_t)(t & (kv.page_size - 1)) * D + part * 8
-                     : 0;
-    }
-    uint4 kr[kNB], vr[kNB];
-#pragma unroll
-    for (int u = 0; u < kNB; ++u) {
-      if (ok[u]) {
-        kr[u] = *reinterpret_cast<const uint4*>(kv.k_pool + off[u]);
-        vr[u] = *reinterpret_cast<const uint4*>(kv.v_pool + off[u]);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
+  auto row_off = [&](int rid) -> int64_t {
+    return (int64_t)(rid >> kv.page_shift) * page_stride + (int64_t)(rid & (kv.page_size - 1)) * D;
+  };
+
+  for (int seg = k_begin; seg < k_end; seg += kSeg) {
+    const int n_seg = min(kSeg, k_end - seg);
+    // Resolve list entries -> pool rows, cooperatively (one entry per thread per pass).
+    __syncthreads();  // the previous segment's rows are no longer read
+    for (int j = threadIdx.x; j < n_seg; j += 256) {
+      const int t = ilist[seg + j];
+      int rid = -1;
+      if (t >= 0 && t <= pos) {
+        const int64_t ph = phys_page(kv, b, t);
+        if (ph >= 0) rid = (int)(ph * kv.page_size + (t & (kv.page_size - 1)));
       }
+      sh_rid[j] = rid;
     }
-    // scores
-    float s[kNB][G];
-#pragma unroll
-    for (int u = 0; u < kNB; ++u) {
-      float kf[8];
-      kf[0] = bf16_lo(kr[u].x); kf[1] = bf16_hi(kr[u].x);
-      kf[2] = bf16_lo(kr[u].y); kf[3] = bf16_hi(kr[u].y);
-      kf[4] = bf16_lo(kr[u].z); kf[5] = bf16_hi(kr[u].z);
-      kf[6] = bf16_lo(kr[u].w); kf[7] = bf16_hi(kr[u].w);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
-        s[u][h] = group_sum_f<LPK>(d);
-      }
-    }
-    // online softmax update, one rescale per batch
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mb = m[h];
-#pragma unroll
-      for (int u = 0; u < kNB; ++u) mb = ok[u] ? fmaxf(mb, s[u][h]) : mb;
-      const float sc = safe_scale(m[h], mb);
-      l[h] *= sc;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= sc;
-      m[h] = mb;
+    __syncthreads();
+
+    const int n_batches = (n_seg + STRIDE * kNB - 1) / (STRIDE * kNB);
+    for (int bt = 0; bt < n_batches; ++bt) {
+      // every K and V row of the batch is requested before any is used
+      uint4 ck[kNB], cv[kNB];
+      bool cok[kNB];
 #pragma unroll
       for (int u = 0; u < kNB; ++u) {
-        const float p = ok[u] ? exp2f(s[u][h] - mb) : 0.f;
-        l[h] += p;
-        acc[h][0] = fmaf(p, bf16_lo(vr[u].x), acc[h][0]);
-        acc[h][1] = fmaf(p, bf16_hi(vr[u].x), acc[h][1]);
-        acc[h][2] = fmaf(p, bf16_lo(vr[u].y), acc[h][2]);
-        acc[h][3] = fmaf(p, bf16_hi(vr[u].y), acc[h][3]);
-        acc[h][4] = fmaf(p, bf16_lo(vr[u].z), acc[h][4]);
-        acc[h][5] = fmaf(p, bf16_hi(vr[u].z), acc[h][5]);
-        acc[h][6] = fmaf(p, bf16_lo(vr[u].w), acc[h][6]);
-        acc[h][7] = fmaf(p, bf16_hi(vr[u].w), acc[h][7]);
+        const int j = (bt * kNB + u) * STRIDE + wave * KPW + grp;
+        const int rid = (j < n_seg) ? sh_rid[j] : -1;
+        cok[u] = rid >= 0;
+        if (cok[u]) {
+          const int64_t o = row_off(rid);
+          ck[u] = *reinterpret_cast<const uint4*>(kbase + o);
+          cv[u] = *reinterpret_cast<const uint4*>(vbase + o);
+        } else {
+          ck[u] = make_uint4(0, 0, 0, 0);
+          cv[u] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      float s[kNB][G];
+#pragma unroll
+      for (int u = 0; u < kNB; ++u) {
+        float kf[8];
+        kf[0] = bf16_lo(ck[u].x); kf[1] = bf16_hi(ck[u].x);
+        kf[2] = bf16_lo(ck[u].y); kf[3] = bf16_hi(ck[u].y);
+        kf[4] = bf16_lo(ck[u].z); kf[5] = bf16_hi(ck[u].z);
+        kf[6] = bf16_lo(ck[u].w); kf[7] = bf16_hi(ck[u].w);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float d = bf16_lo(qw[h].x) * kf[0];
+          d = fmaf(bf16_hi(qw[h].x), kf[1], d);
+          d = fmaf(bf16_lo(qw[h].y), kf[2], d);
+          d = fmaf(bf16_hi(qw[h].y), kf[3], d);
+          d = fmaf(bf16_lo(qw[h].z), kf[4], d);
+          d = fmaf(bf16_hi(qw[h].z), kf[5], d);
+          d = fmaf(bf16_lo(qw[h].w), kf[6], d);
+          d = fmaf(bf16_hi(qw[h].w), kf[7], d);
+          s[u][h] = group_sum_f<LPK>(d) * qscale;
+        }
+      }
+      // online softmax update, one rescale per batch
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mb = m[h];
+#pragma unroll
+        for (int u = 0; u < kNB; ++u) mb = cok[u] ? fmaxf(mb, s[u][h]) : mb;
+        const float sc = safe_scale(m[h], mb);
+        l[h] *= sc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= sc;
+        m[h] = mb;
+#pragma unroll
+        for (int u = 0; u < kNB; ++u) {
+          const float p = cok[u] ? exp2f(s[u][h] - mb) : 0.f;
+          l[h] += p;
+          acc[h][0] = fmaf(p, bf16_lo(cv[u].x), acc[h][0]);
+          acc[h][1] = fmaf(p, bf16_hi(cv[u].x), acc[h][1]);
+          acc[h][2] = fmaf(p, bf16_lo(cv[u].y), acc[h][2]);
+          acc[h][3] = fmaf(p, bf16_hi(cv[u].y), acc[h][3]);
+          acc[h][4] = fmaf(p, bf16_lo(cv[u].z), acc[h][4]);
+          acc[h][5] = fmaf(p, bf16_hi(cv[u].z), acc[h][5]);
+          acc[h][6] = fmaf(p, bf16_lo(cv[u].w), acc[h][6]);
+          acc[h][7] = fmaf(p, bf16_hi(cv[u].w), acc[h][7]);
+        }
       }
     }
   }
@@ -229,31 +237,55 @@ __global__ __launch_bounds__(256) void k_attn_gather(KvView kv, const uint16_t* 
   }
 }
 
-// Exact merge of split partials. grid.x = units, 256 threads over (head, dim).
+// Exact merge of split partials, one workgroup per unit. The (max, sum) pairs of all splits
+// are staged in LDS with one parallel load; each thread then reads its (head, dim) column of
+// every split with independent loads and combines them in split order.
+constexpr int kMaxSplits = 256;
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_merge_splits(const float* __restrict__ ws, int64_t units,
                                                       int num_splits, int num_q_heads,
                                                       int num_kv_heads, uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
+  __shared__ float s_w[kMaxSplits][G];  // exp2(m_s - M)
+  __shared__ float s_M[G], s_L[G];
   const int64_t unit = blockIdx.x;
-  const float* ml = ws + units * num_splits * G * D;
+  const float* ml = ws + units * num_splits * G * D + unit * num_splits * G * 2;
+  for (int x = threadIdx.x; x < num_splits * G; x += 256) s_w[x / G][x % G] = ml[x * 2];
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < num_splits; ++s) M = fmaxf(M, s_w[s][h]);
+    float L = 0.f;
+    for (int s = 0; s < num_splits; ++s) {
+      const float w = safe_scale(s_w[s][h], M);
+      L += ml[(s * G + h) * 2 + 1] * w;
+      s_w[s][h] = w;
+    }
+    s_M[h] = M;
+    s_L[h] = L;
+  }
+  __syncthreads();
   const int g = (int)(unit % num_kv_heads);
   const int64_t bi = unit / num_kv_heads;
+  const float* acc = ws + unit * num_splits * G * D;
   for (int x = threadIdx.x; x < G * D; x += 256) {
     const int h = x / D;
-    const int dd = x - h * D;
-    float mm = -INFINITY;
-    for (int s = 0; s < num_splits; ++s) mm = fmaxf(mm, ml[((unit * num_splits + s) * G + h) * 2]);
-    float ll = 0.f, aa = 0.f;
-    for (int s = 0; s < num_splits; ++s) {
-      const int64_t slot = unit * num_splits + s;
-      const float sc = safe_scale(ml[(slot * G + h) * 2], mm);
-      ll += ml[(slot * G + h) * 2 + 1] * sc;
-      aa += ws[(slot * G + h) * D + dd] * sc;
+    float aa = 0.f;
+    int s = 0;
+    for (; s + 8 <= num_splits; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = acc[(int64_t)(s + u) * G * D + x];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) aa += v[u] * s_w[s + u][h];
     }
+    for (; s < num_splits; ++s) aa += acc[(int64_t)s * G * D + x] * s_w[s][h];
+    const float L = s_L[h];
     const int64_t qh = bi * num_q_heads + (int64_t)g * G + h;
-    out[qh * D + dd] = (uint16_t)f32_to_bf16((ll > 0.f) ? aa / ll : 0.f);
-    if (lse != nullptr && dd == 0) lse[qh] = (ll > 0.f) ? (mm + log2f(ll)) * kLn2 : -INFINITY;
+    out[qh * D + (x - h * D)] = (uint16_t)f32_to_bf16((L > 0.f) ? aa / L : 0.f);
+    if (lse != nullptr && x - h * D == 0) lse[qh] = (L > 0.f) ? (s_M[h] + log2f(L)) * kLn2 : -INFINITY;
   }
 }
 

@@ -33,6 +33,9 @@ __device__ __forceinline__ int dot16(const v4i a, const v4i b) {
 }
 
 // grid: x = ceil(token blocks / (4 waves * kStreamBlocksPerWave)), y = batch * H_idx.
+// Each wave scores kStreamBlocksPerWave consecutive 64-token blocks of one row. The first
+// query's fragment and the page-table entries are requested before the key loads, and all
+// key loads of the wave are in flight before any is used.
 template <int D>
 __global__ __launch_bounds__(256) void k_index_stream(KvView kv, const int8_t* __restrict__ q_idx,
                                                       int q_len, int q_tail,
@@ -48,6 +51,10 @@ __global__ __launch_bounds__(256) void k_index_stream(KvView kv, const int8_t* _
   const int row = blockIdx.y;
   const int b = row / kv.num_idx_heads;
   const int gi = row - b * kv.num_idx_heads;
+  const int part = lane % LPT;                // which 16-byte chunk of a key row
+  const int my_tok = part * TPL + lane / LPT; // token (within the block) this lane stores
+  const int8_t* qrow = q_idx + ((int64_t)b * q_len * kv.num_idx_heads + gi) * D + part * 16;
+  const v4i q0 = *reinterpret_cast<const v4i*>(qrow);  // query 0, requested first
   const int T = min(kv.seq_lens[b], kv.max_seq_len);
   const int P = kv.prefix_len;
   const int pos0 = T - q_tail;               // position of query 0
@@ -58,20 +65,16 @@ __global__ __launch_bounds__(256) void k_index_stream(KvView kv, const int8_t* _
   const int blk0 = blk_first + (blockIdx.x * 4 + wave) * U;
   if (blk0 > blk_last) return;
 
-  const int part = lane % LPT;               // which 16-byte chunk of a key row
-  const int my_tok = part * TPL + lane / LPT; // token (within the block) this lane stores
-
+  int64_t phys[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) phys[u] = (blk0 + u <= blk_last) ? phys_page(kv, b, (blk0 + u) << 6) : -1;
   v4i kd[U][R];
-  bool ok[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int blk = blk0 + u;
-    const int64_t phys = (blk <= blk_last) ? phys_page(kv, b, blk << 6) : -1;
-    ok[u] = phys >= 0;
-    if (phys >= 0) {
-      const int slot0 = (blk << 6) & (kv.page_size - 1);
+    if (phys[u] >= 0) {
+      const int slot0 = ((blk0 + u) << 6) & (kv.page_size - 1);
       const int8_t* base = kv.kidx_pool +
-          ((phys * kv.num_idx_heads + gi) * kv.page_size + slot0) * (int64_t)D;
+          ((phys[u] * kv.num_idx_heads + gi) * kv.page_size + slot0) * (int64_t)D;
 #pragma unroll
       for (int r = 0; r < R; ++r)
         kd[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(base + r * 1024 + lane * 16));
@@ -84,21 +87,19 @@ __global__ __launch_bounds__(256) void k_index_stream(KvView kv, const int8_t* _
   for (int i = 0; i < q_len; ++i) {
     const int pos = pos0 + i;
     if (pos < P) continue;
-    const v4i qf = *reinterpret_cast<const v4i*>(
-        q_idx + (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * D + part * 16);
+    const v4i qf = (i == 0) ? q0 : *reinterpret_cast<const v4i*>(qrow + (int64_t)i * kv.num_idx_heads * D);
     int32_t* srow = scores + (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * row_stride;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int blk = blk0 + u;
-      if (blk > blk_last) break;
+      if (phys[u] < 0) continue;
       int mine = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int s = group_sum_i<LPT>(dot16(qf, kd[u][r]));
         if (part == r) mine = s;
       }
-      const int t = (blk << 6) + my_tok;
-      if (ok[u] && t >= P && t <= pos) srow[t] = mine;
+      const int t = ((blk0 + u) << 6) + my_tok;
+      if (t >= P && t <= pos) srow[t] = mine;
     }
   }
 }

@@ -184,16 +184,276 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Long rows (decode: a handful of rows of 10^5..10^6 scores) are split over many workgroups
+// of kChunk scores each, in four launches plus a clearing fill:
+//   hist1    per chunk, an LDS histogram of key >> 12, added into the row histogram with
+//            global atomics on non-empty bins (integer sums: the result does not depend on
+//            their order);
+//   find     one workgroup per row finds b1, the bin holding the K-th largest key, and
+//            `above1`, the number of keys in higher bins;
+//   collect  per chunk, the keys in bins >= b1 (every selected key, plus the rest of bin b1)
+//            are compacted in token order into the chunk's own slot range, with their count;
+//   final    one workgroup per row walks those candidates in chunk order: an LDS histogram of
+//            the low digit of the bin-b1 keys gives tau and `need`, then an ordered pass keeps
+//            keys > tau and the first `need` keys == tau, writing them ascending.
+// Typical rows leave about K + |bin b1| candidates, so final touches a few thousand entries;
+// with heavy ties it simply walks more of them. Workspace (int32 words):
+//   hist1 [rows][4096] | state [rows][4] | ccount [rows][chunks] | cand [rows][chunks][kChunk][2]
+constexpr int kChunk = 8192;
+constexpr int kMT = 256;
+constexpr int kLoads = kChunk / (kMT * 4);
+constexpr int kFinalNT = 1024;
+
+struct RowGeom {
+  int pos, nf, n, P, W;
+};
+
+__device__ __forceinline__ RowGeom row_geom(const KvView& kv, int64_t row, int q_len, int q_tail,
+                                            int top_k) {
+  const int64_t bi = row / kv.num_idx_heads;
+  const int b = (int)(bi / q_len);
+  const int i = (int)(bi - (int64_t)b * q_len);
+  RowGeom g;
+  g.P = kv.prefix_len;
+  g.W = g.P + top_k;
+  g.pos = min(kv.seq_lens[b], kv.max_seq_len) - q_tail + i;
+  g.nf = g.pos < 0 ? 0 : min(g.P, g.pos + 1);
+  g.n = g.pos - g.P + 1;
+  return g;
+}
+
+struct MultiWs {
+  uint32_t* hist1;
+  int32_t* state;   // [rows][4]: b1, above1
+  int32_t* ccount;  // [rows][chunks]
+  int2* cand;       // [rows][chunks][kChunk]: (key, token)
+  int chunks;
+};
+
+__device__ __forceinline__ MultiWs multi_ws(void* ws, int64_t rows, int chunks) {
+  MultiWs w;
+  w.hist1 = static_cast<uint32_t*>(ws);
+  w.state = reinterpret_cast<int32_t*>(w.hist1 + rows * kBins);
+  w.ccount = w.state + rows * 4;
+  int64_t off = (int64_t)(rows * (kBins + 4) + rows * chunks);
+  off = (off + 3) & ~(int64_t)3;  // 16-byte alignment for the candidate pairs
+  w.cand = reinterpret_cast<int2*>(static_cast<int32_t*>(ws) + off);
+  w.chunks = chunks;
+  return w;
+}
+
+__global__ __launch_bounds__(256) void k_topk_zero(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (int64_t)gridDim.x * 256)
+    p[j] = 0u;
+}
+
+// Workgroup-exclusive prefix sum (thread order) and total; two barriers.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int32_t* wave_tot, int* total) {
+  const int incl = block_incl_scan<NT>(v, wave_tot, total);
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kMT) void k_topk_hist1(KvView kv, const int32_t* __restrict__ scores,
+                                                    int64_t row_stride, int q_len, int q_tail,
+                                                    int top_k, void* ws, int chunks) {
+  __shared__ uint32_t h[kBins];
+  const int64_t row = blockIdx.y;
+  const RowGeom g = row_geom(kv, row, q_len, q_tail, top_k);
+  const int t_begin = blockIdx.x * kChunk;
+  if (g.n <= top_k || t_begin > g.pos) return;
+  const MultiWs w = multi_ws(ws, gridDim.y, chunks);
+  for (int j = threadIdx.x; j < kBins; j += kMT) h[j] = 0u;
+  __syncthreads();
+  const int32_t* srow = scores + row * row_stride;
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int t = t_begin + j * kMT * 4 + threadIdx.x * 4;
+    if (t <= g.pos) {
+      const int4 v = *reinterpret_cast<const int4*>(srow + t);
+      const int e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (t + u >= g.P && t + u <= g.pos) atomicAdd(&h[score_key(e[u]) >> 12], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* dst = w.hist1 + row * kBins;
+  for (int j = threadIdx.x; j < kBins; j += kMT)
+    if (h[j]) atomicAdd(&dst[j], h[j]);
+}
+
+__global__ __launch_bounds__(kMT) void k_topk_find(KvView kv, int q_len, int q_tail, int top_k,
+                                                   void* ws, int chunks) {
+  __shared__ TopkShared<kMT> sh;
+  const int64_t row = blockIdx.x;
+  const RowGeom g = row_geom(kv, row, q_len, q_tail, top_k);
+  if (g.n <= top_k) return;
+  const MultiWs w = multi_ws(ws, gridDim.x, chunks);
+  const uint32_t* h1 = w.hist1 + row * kBins;
+  for (int j = threadIdx.x; j < kBins; j += kMT) sh.hist[j] = h1[j];
+  if (threadIdx.x == 0) { sh.found_bin = 0; sh.found_above = 0; }
+  __syncthreads();
+  find_bin<kMT>(sh, top_k);
+  if (threadIdx.x == 0) {
+    w.state[row * 4 + 0] = sh.found_bin;
+    w.state[row * 4 + 1] = sh.found_above;
+  }
+}
+
+__global__ __launch_bounds__(kMT) void k_topk_collect(KvView kv, const int32_t* __restrict__ scores,
+                                                      int64_t row_stride, int q_len, int q_tail,
+                                                      int top_k, void* ws, int chunks) {
+  __shared__ int32_t wave_tot[kMT / 64];
+  const int64_t row = blockIdx.y;
+  const int c = blockIdx.x;
+  const RowGeom g = row_geom(kv, row, q_len, q_tail, top_k);
+  if (g.n <= top_k) return;
+  const MultiWs w = multi_ws(ws, gridDim.y, chunks);
+  const int t_begin = c * kChunk;
+  if (t_begin > g.pos) {
+    if (threadIdx.x == 0) w.ccount[row * chunks + c] = 0;
+    return;
+  }
+  const uint32_t b1 = (uint32_t)w.state[row * 4 + 0];
+  int2* dst = w.cand + (row * chunks + c) * (int64_t)kChunk;
+  const int32_t* srow = scores + row * row_stride;
+  int fill = 0;
+  for (int j = 0; j < kLoads; ++j) {
+    const int t = t_begin + j * kMT * 4 + threadIdx.x * 4;
+    int e[4] = {0, 0, 0, 0};
+    if (t <= g.pos) {
+      const int4 v = *reinterpret_cast<const int4*>(srow + t);
+      e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
+    }
+    int n_keep = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = t + u >= g.P && t + u <= g.pos;
+      n_keep += (in && (score_key(e[u]) >> 12) >= b1) ? 1 : 0;
+    }
+    int tile;
+    int slot = fill + block_excl_scan<kMT>(n_keep, wave_tot, &tile);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t key = score_key(e[u]);
+      const bool in = t + u >= g.P && t + u <= g.pos;
+      if (in && (key >> 12) >= b1) dst[slot++] = make_int2((int)key, t + u);
+    }
+    fill += tile;
+  }
+  if (threadIdx.x == 0) w.ccount[row * chunks + c] = fill;
+}
+
+__global__ __launch_bounds__(kFinalNT) void k_topk_final(KvView kv, int q_len, int q_tail,
+                                                         int top_k, void* ws, int chunks,
+                                                         int32_t* __restrict__ indices) {
+  constexpr int NT = kFinalNT;
+  __shared__ TopkShared<NT> sh;
+  __shared__ int32_t s_off[1025];  // exclusive candidate offsets of the chunks (<= 1024 chunks)
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const RowGeom g = row_geom(kv, row, q_len, q_tail, top_k);
+  int32_t* out = indices + row * g.W;
+  for (int j = tid; j < g.nf; j += NT) out[j] = j;
+  if (g.n <= top_k) {
+    const int m = g.n > 0 ? g.n : 0;
+    for (int j = tid; j < m; j += NT) out[g.nf + j] = g.P + j;
+    for (int j = g.nf + m + tid; j < g.W; j += NT) out[j] = -1;
+    return;
+  }
+  const MultiWs w = multi_ws(ws, gridDim.x, chunks);
+  const uint32_t b1 = (uint32_t)w.state[row * 4 + 0];
+  const int above1 = w.state[row * 4 + 1];
+  // chunk offsets (chunks <= NT)
+  {
+    const int v = tid < chunks ? w.ccount[row * chunks + tid] : 0;
+    int total;
+    const int ex = block_excl_scan<NT>(v, sh.wave_tot, &total);
+    if (tid < chunks) s_off[tid] = ex;
+    if (tid == 0) s_off[chunks] = total;
+    for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
+    if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
+    __syncthreads();
+  }
+  const int total = s_off[chunks];
+  const int2* cand = w.cand + row * chunks * (int64_t)kChunk;
+  // candidate number j -> its chunk (binary search over the offsets) and slot
+  auto fetch = [&](int j) -> int2 {
+    int lo = 0, hi = chunks - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    return cand[(int64_t)lo * kChunk + (j - s_off[lo])];
+  };
+  // exact threshold inside bin b1
+  for (int j = tid; j < total; j += NT) {
+    const int2 e = fetch(j);
+    if (((uint32_t)e.x >> 12) == b1) atomicAdd(&sh.hist[(uint32_t)e.x & 0xfff], 1u);
+  }
+  __syncthreads();
+  find_bin<NT>(sh, top_k - above1);
+  const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
+  const int need = top_k - above1 - sh.found_above;
+  // ordered output: candidates are already in token order
+  int eq_seen = 0, sel = 0;
+  for (int j0 = 0; j0 < total; j0 += NT) {
+    const int j = j0 + tid;
+    const int2 e = (j < total) ? fetch(j) : make_int2(0, 0);
+    const bool valid = j < total;
+    const bool gt = valid && (uint32_t)e.x > tau;
+    const bool eq = valid && (uint32_t)e.x == tau;
+    int eq_tile;
+    const int eq_rank = eq_seen + block_excl_scan<NT>(eq ? 1 : 0, sh.wave_tot, &eq_tile);
+    const bool take = gt || (eq && eq_rank < need);
+    int take_tile;
+    const int slot = sel + block_excl_scan<NT>(take ? 1 : 0, sh.wave_tot2, &take_tile);
+    if (take && slot < top_k) out[g.nf + slot] = e.y;
+    eq_seen += eq_tile;
+    sel += take_tile;
+  }
+}
+
+bool use_multi(int64_t rows, int longest) { return longest >= 16384 && rows <= 2048; }
+
+int64_t multi_chunks(const KvView& kv) { return (kv.max_seq_len + kChunk - 1) / kChunk; }
+
 }  // namespace
 
-size_t topk_workspace_bytes(const KvView&, int, int) { return 0; }
+size_t topk_workspace_bytes(const KvView& kv, int q_len, int) {
+  const int64_t rows = (int64_t)kv.batch * q_len * kv.num_idx_heads;
+  if (!use_multi(rows, kv.max_seq_len - kv.prefix_len)) return 0;
+  const int64_t chunks = multi_chunks(kv);
+  const int64_t head = (rows * (kBins + 4) + rows * chunks + 3) & ~(int64_t)3;
+  return (size_t)(head + rows * chunks * kChunk * 2) * sizeof(int32_t);
+}
 
 hipError_t launch_topk(const KvView& kv, const int32_t* scores, int64_t row_stride, int q_len,
-                       int q_tail, int top_k, int32_t* indices, void*, size_t,
+                       int q_tail, int top_k, int32_t* indices, void* ws, size_t,
                        hipStream_t stream) {
   const int64_t rows = (int64_t)kv.batch * q_len * kv.num_idx_heads;
   if (rows == 0) return hipSuccess;
   const int longest = kv.max_seq_len - kv.prefix_len;
+  if (use_multi(rows, longest)) {
+    const int chunks = (int)multi_chunks(kv);
+    if (chunks > 1024) return hipErrorInvalidValue;
+    const int64_t nz = rows * kBins;
+    const int64_t zb = (nz + 255) / 256 < 4096 ? (nz + 255) / 256 : 4096;
+    hipLaunchKernelGGL(k_topk_zero, dim3((unsigned)zb), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ws), nz);
+    const dim3 grid(chunks, (unsigned)rows);
+    hipLaunchKernelGGL(k_topk_hist1, grid, dim3(kMT), 0, stream, kv, scores, row_stride, q_len,
+                       q_tail, top_k, ws, chunks);
+    hipLaunchKernelGGL(k_topk_find, dim3((unsigned)rows), dim3(kMT), 0, stream, kv, q_len, q_tail,
+                       top_k, ws, chunks);
+    hipLaunchKernelGGL(k_topk_collect, grid, dim3(kMT), 0, stream, kv, scores, row_stride, q_len,
+                       q_tail, top_k, ws, chunks);
+    hipLaunchKernelGGL(k_topk_final, dim3((unsigned)rows), dim3(kFinalNT), 0, stream, kv, q_len,
+                       q_tail, top_k, ws, chunks, indices);
+    return hipGetLastError();
+  }
   if (longest > 8192) {
     hipLaunchKernelGGL(k_topk_row<1024>, dim3((unsigned)rows), dim3(1024), 0, stream, kv, scores,
                        row_stride, q_len, q_tail, top_k, indices);

@@ -96,7 +96,7 @@ typedef struct sa_paged_kv {
   int32_t idx_dim;            /* d_idx: 32, 64 or 128 (ignored when kidx_pool is NULL) */
   int32_t page_size;          /* tokens per page: a power of two, >= 64 */
   int32_t max_pages_per_seq;  /* row length of page_table */
-  int64_t num_pages;          /* pages in each pool */
+  int64_t num_pages;          /* pages in each pool; num_pages * page_size < 2^31 */
   int32_t max_seq_len;        /* host-side bound on seq_lens[b]; <= max_pages_per_seq * page_size */
   int32_t prefix_len;         /* P >= 0: forced always-attended prefix ([DSA-page] §2.4) */
   const uint16_t* k_pool;

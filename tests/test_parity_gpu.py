@@ -81,6 +81,13 @@ DECODE = {
     "decode_ties": (W(batch=2, seq_len=4000, q_len=1, top_k=300, prefix_len=2),
                     dict(idx_values=(-1, 0, 1))),
     "decode_g1": (W(batch=2, num_q_heads=2, num_kv_heads=2, seq_len=2000, q_len=1, top_k=128), {}),
+    # rows of >= 16384 candidates take the multi-workgroup selection
+    "decode_long_ragged_prefix": (W(batch=3, seq_len=70000, q_len=1, top_k=500, prefix_len=100),
+                                  dict(seq_lens=[70000, 16500, 40000])),
+    "decode_long_ties": (W(batch=2, seq_len=33000, q_len=1, top_k=700, prefix_len=3),
+                         dict(idx_values=(-1, 0, 1))),
+    "decode_long_shared_indexer": (W(batch=2, num_q_heads=8, seq_len=24576, q_len=1, top_k=2048,
+                                     idx_dim=32), dict(num_idx_heads=1)),
 }
 
 
