@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for counter calibration)")
+    ap.add_argument("--two-step", action="store_true",
+                    help="select with sparse_attn_index then sparse_attn_topk (score rows in HBM) "
+                         "instead of the fused sparse_attn_index_topk")
     ap.add_argument("--seed", type=int, default=3)
     return ap.parse_args()
 
@@ -57,10 +60,35 @@ def step_bytes(w):
     return kidx + gather + small
 
 
-def index_kernel_bytes(w):
-    """Algorithmic bytes of one indexer launch: every indexer key, the queries, the scores."""
+def index_kernel_bytes(w, two_step):
+    """Algorithmic bytes of one launch of the dominant kernel: every indexer key, the
+    queries and the page table; the stand-alone indexer also writes every score."""
     B, Hkv, T = w.batch, w.num_kv_heads, w.seq_len
-    return B * Hkv * T * w.idx_dim + B * Hkv * w.idx_dim + B * Hkv * T * 4 + B * (T // w.page_size) * 4
+    base = B * Hkv * T * w.idx_dim + B * Hkv * w.idx_dim + B * (T // w.page_size) * 4
+    return base + (B * Hkv * T * 4 if two_step else 0)
+
+
+def kernel_ms(args, kv, inp, w, scores, stride, indices, ws, ws_n, flush):
+    """Average duration of the dominant launch, timed with events on its stream: the
+    stand-alone indexer, or the fused selection call (its sample, main and final kernels;
+    the main pass streams every indexer key and carries almost all of the time).
+    """
+    import torch
+    import flash_attention_int8_amd as fa
+    evs = []
+    for _ in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if args.two_step:
+            fa.sparse_attn_index(kv, inp.q_idx, 1, 1, scores, stride)
+        else:
+            fa.sparse_attn_index_topk(kv, inp.q_idx, 1, 1, w.top_k, indices, ws, ws_n)
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
 
 
 def traffic_for(kernel_file: str, key: str):
@@ -176,6 +204,8 @@ def main():
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     tk_ws_n = fa.sparse_attn_topk_workspace_size(kv, 1, w.top_k)
     tk_ws = torch.empty(max(tk_ws_n, 16), dtype=torch.uint8, device="cuda")
+    fu_ws_n = fa.sparse_attn_index_topk_workspace_size(kv, 1, w.top_k)
+    fu_ws = torch.empty(max(fu_ws_n, 16), dtype=torch.uint8, device="cuda")
     dec_ws_n = fa.sparse_attn_decode_workspace_size(kv, Hq, w.index_width, args.splits)
     dec_ws = torch.empty(max(dec_ws_n, 16), dtype=torch.uint8, device="cuda")
     idx_view = indices[:, 0]
@@ -185,16 +215,17 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record()
-        fa.sparse_attn_index(kv, inp.q_idx, 1, 1, scores, stride)
+        if args.two_step:
+            fa.sparse_attn_index(kv, inp.q_idx, 1, 1, scores, stride)
+            fa.sparse_attn_topk(kv, scores, stride, 1, 1, w.top_k, indices, tk_ws, tk_ws_n)
+        else:
+            fa.sparse_attn_index_topk(kv, inp.q_idx, 1, 1, w.top_k, indices, fu_ws, fu_ws_n)
         if ev:
             ev[1].record()
-        fa.sparse_attn_topk(kv, scores, stride, 1, 1, w.top_k, indices, tk_ws, tk_ws_n)
-        if ev:
-            ev[2].record()
         fa.sparse_attn_fwd_decode(kv, q, Hq, idx_view, w.index_width, scale, args.splits, dec_ws,
                                   dec_ws_n, out, lse)
         if ev:
-            ev[3].record()
+            ev[2].record()
 
     for _ in range(args.warmup):
         step()
@@ -214,16 +245,15 @@ def main():
     ms_step = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     # breakdown: a separate pass with an event between every entry point (the extra
     # event records add a few microseconds that the headline does not carry)
-    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for k in range(args.steps):
         if flush is not None:
             flush.zero_()
         step(bev[k])
     torch.cuda.synchronize()
-    seg = [[bev[k][j].elapsed_time(bev[k][j + 1]) for j in range(3)] for k in range(args.steps)]
-    ms_index = sum(s[0] for s in seg) / args.steps
-    ms_topk = sum(s[1] for s in seg) / args.steps
-    ms_attn = sum(s[2] for s in seg) / args.steps
+    seg = [[bev[k][j].elapsed_time(bev[k][j + 1]) for j in range(2)] for k in range(args.steps)]
+    ms_select = sum(s[0] for s in seg) / args.steps
+    ms_attn = sum(s[1] for s in seg) / args.steps
 
     if args.copy_calibration:
         a = torch.empty(256 * MIB, dtype=torch.uint8, device="cuda")
@@ -232,8 +262,12 @@ def main():
         torch.cuda.synchronize()
 
     sb = step_bytes(w)
-    ib = index_kernel_bytes(w)
-    achieved = ib / (ms_index * 1e-3) / 1e9
+    # dominant kernel: the indexer's key stream (fused main pass, or the stand-alone indexer)
+    dom_name = ("k_index_stream<64> (indexer)" if args.two_step else
+                "sparse_attn_index_topk (k_fused_sample + k_fused_main + k_fused_final)")
+    ib = index_kernel_bytes(w, args.two_step)
+    ms_dom = kernel_ms(args, kv, inp, w, scores, stride, indices, fu_ws, fu_ws_n, flush)
+    achieved = ib / (ms_dom * 1e-3) / 1e9
     result = {
         "metric": "decode tokens/s + HBM GB/s at 128K ctx top-K=2048; prefill TFLOP/s",
         "value": B / (ms_step * 1e-3),
@@ -253,12 +287,15 @@ def main():
         "hbm_gbps": sb / (ms_step * 1e-3) / 1e9,
         "hbm_frac": sb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "step_bytes": sb,
-        "breakdown_us": {"index": ms_index * 1e3, "topk": ms_topk * 1e3, "attention": ms_attn * 1e3},
+        "breakdown_us": {"select": ms_select * 1e3, "attention": ms_attn * 1e3,
+                         "dominant_kernel": ms_dom * 1e3},
+        "select_path": "two-step (index, topk)" if args.two_step else "fused index_topk",
         "wall_s_timed_loop": t_wall,
-        "roofline": {"kernel": "k_index_stream<64> (indexer)", "bound": "hbm",
+        "roofline": {"kernel": dom_name, "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic_for("sa_index.hip", "k_index_stream<64>")},
+                     "traffic": traffic_for("sa_index.hip" if args.two_step else "sa_index_topk.hip",
+                                            "k_index_stream<64>" if args.two_step else "fused_select")},
     }
     if not args.no_prefill:
         del scores

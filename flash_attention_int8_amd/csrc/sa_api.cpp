@@ -122,6 +122,53 @@ int32_t sparse_attn_topk(const sa_paged_kv* kv, const int32_t* scores, int64_t s
                                     workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+int64_t score_stride(const sa::KvView& v) { return ((int64_t)v.max_seq_len + 3) & ~(int64_t)3; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the two-step fallback: score rows, then the selection workspace.
+size_t composite_bytes(const sa::KvView& v, int32_t q_len, int32_t top_k) {
+  const size_t scores = (size_t)v.batch * q_len * v.num_idx_heads * score_stride(v) * sizeof(int32_t);
+  return align256(scores) + sa::topk_workspace_bytes(v, q_len, top_k);
+}
+
+}  // namespace
+
+size_t sparse_attn_index_topk_workspace_size(const sa_paged_kv* kv, int32_t q_len, int32_t top_k) {
+  sa::KvView v;
+  if (check_kv(kv, NEED_IDX, &v) != SA_OK || q_len < 1 || top_k < 1) return 0;
+  if (sa::fused_applies(v, q_len)) return sa::fused_workspace_bytes(v);
+  return composite_bytes(v, q_len, top_k);
+}
+
+int32_t sparse_attn_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
+                               int32_t q_tail, int32_t top_k, int32_t* indices, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  sa::KvView v;
+  int32_t st = check_kv(kv, NEED_IDX, &v);
+  if (st != SA_OK) return st;
+  if ((st = check_block(v, q_len, q_tail)) != SA_OK) return st;
+  if (q_idx == nullptr || indices == nullptr) return SA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(indices)) return SA_ERR_ALIGN;
+  if (top_k < 1 || (int64_t)top_k + v.prefix_len > (1 << 30)) return SA_ERR_SHAPE;
+  const bool fused = sa::fused_applies(v, q_len);
+  const size_t need = fused ? sa::fused_workspace_bytes(v) : composite_bytes(v, q_len, top_k);
+  if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SA_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused) return hip_status(sa::launch_index_topk_fused(v, q_idx, q_tail, top_k, indices, workspace, s));
+  int32_t* scores = static_cast<int32_t*>(workspace);
+  const int64_t stride = score_stride(v);
+  void* tk_ws = static_cast<char*>(workspace) +
+                align256((size_t)v.batch * q_len * v.num_idx_heads * stride * sizeof(int32_t));
+  hipError_t e = sa::launch_index(v, q_idx, q_len, q_tail, scores, stride, s);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  return hip_status(sa::launch_topk(v, scores, stride, q_len, q_tail, top_k, indices, tk_ws,
+                                    sa::topk_workspace_bytes(v, q_len, top_k), s));
+}
+
 int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_t num_q_heads,
                                 int32_t q_len, int32_t q_tail, const int32_t* indices,
                                 int32_t index_width, float sm_scale, uint16_t* out, float* lse,

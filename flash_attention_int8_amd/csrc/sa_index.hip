@@ -14,23 +14,14 @@
 //  * k_index_mfma (many queries, i.e. prefill): scores are a causal int8 GEMM
 //    S^T = K_idx * Q_idx^T on v_mfma_i32_16x16x32_i8. Keys are the M side so each lane's four
 //    accumulator rows are four consecutive tokens of one query: one 16-byte store each.
-#include "sa_common.h"
+#include "sa_index_dev.h"
 
 namespace sa {
 namespace {
 
+using namespace idx;
+
 constexpr int kStreamBlocksPerWave = 4;
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ int dot16(const v4i a, const v4i b) {
-  int acc = 0;
-  acc = __builtin_amdgcn_sdot4(a.x, b.x, acc, false);
-  acc = __builtin_amdgcn_sdot4(a.y, b.y, acc, false);
-  acc = __builtin_amdgcn_sdot4(a.z, b.z, acc, false);
-  acc = __builtin_amdgcn_sdot4(a.w, b.w, acc, false);
-  return acc;
-}
 
 // grid: x = ceil(token blocks / (4 waves * kStreamBlocksPerWave)), y = batch * H_idx.
 // Each wave scores kStreamBlocksPerWave consecutive 64-token blocks of one row. The first

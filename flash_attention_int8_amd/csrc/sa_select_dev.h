@@ -1,0 +1,262 @@
+// Device helpers for exact top-K selection over int32 indexer scores (shared by the
+// stand-alone selection kernels and the fused index + selection kernels).
+//
+// Scores are exact int32 with |s| < 2^23 (an int8 indexer bounds them by d_idx * 2^14 <=
+// 2^21), so key = s + 2^23 is a 24-bit unsigned key that preserves order; selection works
+// on two 12-bit digits of it.
+#pragma once
+
+#include "sa_common.h"
+
+namespace sa {
+namespace sel {
+
+constexpr int kBins = 4096;
+
+__device__ __forceinline__ uint32_t score_key(int32_t s) {
+  int64_t k = (int64_t)s + (1 << 23);
+  k = k < 0 ? 0 : (k > 0xffffff ? 0xffffff : k);
+  return (uint32_t)k;
+}
+
+template <int NT>
+struct TopkShared {
+  uint32_t hist[kBins];
+  int32_t wave_tot[NT / 64];
+  int32_t wave_tot2[NT / 64];
+  int32_t found_bin;
+  int32_t found_above;
+};
+
+// Inclusive prefix sum over the workgroup (thread order); returns the inclusive value and
+// writes the workgroup total to *total. Contains two barriers.
+template <int NT>
+__device__ __forceinline__ int block_incl_scan(int v, int32_t* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wave_tot[wave] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int x = wave_tot[w];
+    before += (w < wave) ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return v + before;
+}
+
+// Largest bin b with sum(hist[b..]) >= k; stores b and sum(hist[b+1..]) in shared memory.
+template <int NT>
+__device__ __forceinline__ void find_bin(TopkShared<NT>& sh, int k) {
+  constexpr int C = kBins / NT;
+  const int base = threadIdx.x * C;
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < C; ++j) s += sh.hist[base + j];
+  int total;
+  const int incl = block_incl_scan<NT>(s, sh.wave_tot, &total);
+  int acc = total - incl;  // sum of bins above this thread's range
+  if (acc < k && acc + s >= k) {
+    for (int j = C - 1; j >= 0; --j) {
+      const int h = sh.hist[base + j];
+      if (acc + h >= k) {
+        sh.found_bin = base + j;
+        sh.found_above = acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+}
+
+// Workgroup-exclusive prefix sum (thread order) and total; two barriers.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int32_t* wave_tot, int* total) {
+  const int incl = block_incl_scan<NT>(v, wave_tot, total);
+  return incl - v;
+}
+
+// Exact top-K among candidates that were compacted per chunk, in token order:
+//   cand [chunks][chunk_cap] (key, token) with ccount[chunk] valid entries each.
+// Every selected key must be among them; b1 is the bin (key >> 12) holding the K-th largest
+// key and `above1` the number of keys in higher bins. Candidates below bin b1 may be
+// present and are ignored. Writes the selected tokens, ascending, to out[0..top_k).
+// s_off needs chunks + 1 <= NT + 1 entries.
+//
+// After the threshold (tau, need) is known, each wave owns one contiguous segment of the
+// candidate list: it counts its keys > tau and == tau with ballots, one workgroup scan over
+// the waves gives every segment its output offset and its number of earlier keys == tau,
+// and each wave then writes its taken keys in order. Two barriers instead of two
+// workgroup scans per 1024 candidates.
+template <int NT>
+__device__ __forceinline__ void select_candidates(TopkShared<NT>& sh, int32_t* s_off,
+                                                  const int2* __restrict__ cand,
+                                                  const int32_t* __restrict__ ccount, int chunks,
+                                                  int chunk_cap, uint32_t b1, int above1,
+                                                  int top_k, int32_t* __restrict__ out) {
+  constexpr int NW = NT / 64;
+  constexpr int kPer = 8;  // candidates per lane loaded together
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  {
+    const int v = tid < chunks ? ccount[tid] : 0;
+    int total;
+    const int ex = block_excl_scan<NT>(v, sh.wave_tot, &total);
+    if (tid < chunks) s_off[tid] = ex;
+    if (tid == 0) s_off[chunks] = total;
+    for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
+    if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
+    __syncthreads();
+  }
+  const int total = s_off[chunks];
+  // candidate number j -> its chunk (binary search over the offsets) and slot
+  auto fetch = [&](int j) -> int2 {
+    int lo = 0, hi = chunks - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    return cand[(int64_t)lo * chunk_cap + (j - s_off[lo])];
+  };
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (total <= NT * kPer) {
+    // Fast path: each wave loads its segment once (kPer steps of 64) and keeps it in
+    // registers through the histogram, the counts and the ordered write.
+    const int seg_begin = wave * 64 * kPer;
+    int2 e[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = seg_begin + k * 64 + lane;
+      e[k] = (j < total) ? fetch(j) : make_int2(0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (seg_begin + k * 64 + lane < total && ((uint32_t)e[k].x >> 12) == b1)
+        atomicAdd(&sh.hist[(uint32_t)e[k].x & 0xfff], 1u);
+    __syncthreads();
+    find_bin<NT>(sh, top_k - above1);
+    const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
+    const int need = top_k - above1 - sh.found_above;
+    int gt_w = 0, eq_w = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const bool valid = seg_begin + k * 64 + lane < total;
+      gt_w += __popcll(__ballot(valid && (uint32_t)e[k].x > tau));
+      eq_w += __popcll(__ballot(valid && (uint32_t)e[k].x == tau));
+    }
+    if (lane == 0) {
+      sh.wave_tot[wave] = gt_w;
+      sh.wave_tot2[wave] = eq_w;
+    }
+    __syncthreads();
+    int gt_before = 0, eq_before = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      gt_before += (v < wave) ? sh.wave_tot[v] : 0;
+      eq_before += (v < wave) ? sh.wave_tot2[v] : 0;
+    }
+    int slot = gt_before + min(need, eq_before);
+    int eq_seen = eq_before;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const bool valid = seg_begin + k * 64 + lane < total;
+      const bool gt = valid && (uint32_t)e[k].x > tau;
+      const bool eq = valid && (uint32_t)e[k].x == tau;
+      const uint64_t eq_mask = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + __popcll(eq_mask & lt) < need);
+      const uint64_t take_mask = __ballot(take);
+      const int o = slot + __popcll(take_mask & lt);
+      if (take && o < top_k) out[o] = e[k].y;
+      slot += __popcll(take_mask);
+      eq_seen += __popcll(eq_mask);
+    }
+    return;
+  }
+  // General path (more candidates than the workgroup holds at once): three streamed passes.
+  // exact threshold inside bin b1
+  for (int base = 0; base < total; base += NT * kPer) {
+    int2 e[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = base + k * NT + tid;
+      e[k] = (j < total) ? fetch(j) : make_int2(0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (base + k * NT + tid < total && ((uint32_t)e[k].x >> 12) == b1)
+        atomicAdd(&sh.hist[(uint32_t)e[k].x & 0xfff], 1u);
+  }
+  __syncthreads();
+  find_bin<NT>(sh, top_k - above1);
+  const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
+  const int need = top_k - above1 - sh.found_above;
+
+  // wave segments of whole 64-entry steps
+  const int steps = (total + 63) / 64;
+  const int seg_steps = (steps + NW - 1) / NW;
+  const int seg_begin = wave * seg_steps * 64;
+  const int seg_end = min(total, seg_begin + seg_steps * 64);
+  int gt_w = 0, eq_w = 0;
+  for (int j0 = seg_begin; j0 < seg_end; j0 += 64 * kPer) {
+    int2 e[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = j0 + k * 64 + lane;
+      e[k] = (j < seg_end) ? fetch(j) : make_int2(0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const bool valid = j0 + k * 64 + lane < seg_end;
+      gt_w += __popcll(__ballot(valid && (uint32_t)e[k].x > tau));
+      eq_w += __popcll(__ballot(valid && (uint32_t)e[k].x == tau));
+    }
+  }
+  if (lane == 0) {
+    sh.wave_tot[wave] = gt_w;
+    sh.wave_tot2[wave] = eq_w;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    gt_before += (v < wave) ? sh.wave_tot[v] : 0;
+    eq_before += (v < wave) ? sh.wave_tot2[v] : 0;
+  }
+  // keys == tau are taken in token order: the segments before this one took min(need, eq_before)
+  int slot = gt_before + min(need, eq_before);
+  int eq_seen = eq_before;
+  for (int j0 = seg_begin; j0 < seg_end; j0 += 64 * kPer) {
+    int2 e[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = j0 + k * 64 + lane;
+      e[k] = (j < seg_end) ? fetch(j) : make_int2(0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const bool valid = j0 + k * 64 + lane < seg_end;
+      const bool gt = valid && (uint32_t)e[k].x > tau;
+      const bool eq = valid && (uint32_t)e[k].x == tau;
+      const uint64_t eq_mask = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + __popcll(eq_mask & lt) < need);
+      const uint64_t take_mask = __ballot(take);
+      const int o = slot + __popcll(take_mask & lt);
+      if (take && o < top_k) out[o] = e[k].y;
+      slot += __popcll(take_mask);
+      eq_seen += __popcll(eq_mask);
+    }
+  }
+}
+
+}  // namespace sel
+}  // namespace sa

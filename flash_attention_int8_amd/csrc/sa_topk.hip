@@ -17,77 +17,13 @@
 //           list comes out ascending and no atomic decides any order.
 // Histogram counts use LDS atomics, which are order-independent; the result is bit-exact
 // and deterministic.
-#include "sa_common.h"
+#include "sa_select_dev.h"
 
 namespace sa {
 namespace {
 
-constexpr int kBins = 4096;
+using namespace sel;
 
-__device__ __forceinline__ uint32_t score_key(int32_t s) {
-  int64_t k = (int64_t)s + (1 << 23);
-  k = k < 0 ? 0 : (k > 0xffffff ? 0xffffff : k);
-  return (uint32_t)k;
-}
-
-template <int NT>
-struct TopkShared {
-  uint32_t hist[kBins];
-  int32_t wave_tot[NT / 64];
-  int32_t wave_tot2[NT / 64];
-  int32_t found_bin;
-  int32_t found_above;
-};
-
-// Inclusive prefix sum over the workgroup (thread order); returns the inclusive value and
-// writes the workgroup total to *total. Contains two barriers.
-template <int NT>
-__device__ __forceinline__ int block_incl_scan(int v, int32_t* wave_tot, int* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  if (lane == 63) wave_tot[wave] = v;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const int x = wave_tot[w];
-    before += (w < wave) ? x : 0;
-    all += x;
-  }
-  __syncthreads();
-  *total = all;
-  return v + before;
-}
-
-// Largest bin b with sum(hist[b..]) >= k; stores b and sum(hist[b+1..]) in shared memory.
-template <int NT>
-__device__ __forceinline__ void find_bin(TopkShared<NT>& sh, int k) {
-  constexpr int C = kBins / NT;
-  const int base = threadIdx.x * C;
-  int s = 0;
-#pragma unroll
-  for (int j = 0; j < C; ++j) s += sh.hist[base + j];
-  int total;
-  const int incl = block_incl_scan<NT>(s, sh.wave_tot, &total);
-  int acc = total - incl;  // sum of bins above this thread's range
-  if (acc < k && acc + s >= k) {
-    for (int j = C - 1; j >= 0; --j) {
-      const int h = sh.hist[base + j];
-      if (acc + h >= k) {
-        sh.found_bin = base + j;
-        sh.found_above = acc;
-        break;
-      }
-      acc += h;
-    }
-  }
-  __syncthreads();
-}
 
 template <int NT>
 __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __restrict__ scores,
@@ -248,13 +184,6 @@ __global__ __launch_bounds__(256) void k_topk_zero(uint32_t* __restrict__ p, int
     p[j] = 0u;
 }
 
-// Workgroup-exclusive prefix sum (thread order) and total; two barriers.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int32_t* wave_tot, int* total) {
-  const int incl = block_incl_scan<NT>(v, wave_tot, total);
-  return incl - v;
-}
-
 __global__ __launch_bounds__(kMT) void k_topk_hist1(KvView kv, const int32_t* __restrict__ scores,
                                                     int64_t row_stride, int q_len, int q_tail,
                                                     int top_k, void* ws, int chunks) {
@@ -366,54 +295,8 @@ __global__ __launch_bounds__(kFinalNT) void k_topk_final(KvView kv, int q_len, i
   const MultiWs w = multi_ws(ws, gridDim.x, chunks);
   const uint32_t b1 = (uint32_t)w.state[row * 4 + 0];
   const int above1 = w.state[row * 4 + 1];
-  // chunk offsets (chunks <= NT)
-  {
-    const int v = tid < chunks ? w.ccount[row * chunks + tid] : 0;
-    int total;
-    const int ex = block_excl_scan<NT>(v, sh.wave_tot, &total);
-    if (tid < chunks) s_off[tid] = ex;
-    if (tid == 0) s_off[chunks] = total;
-    for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
-    if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
-    __syncthreads();
-  }
-  const int total = s_off[chunks];
-  const int2* cand = w.cand + row * chunks * (int64_t)kChunk;
-  // candidate number j -> its chunk (binary search over the offsets) and slot
-  auto fetch = [&](int j) -> int2 {
-    int lo = 0, hi = chunks - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
-    }
-    return cand[(int64_t)lo * kChunk + (j - s_off[lo])];
-  };
-  // exact threshold inside bin b1
-  for (int j = tid; j < total; j += NT) {
-    const int2 e = fetch(j);
-    if (((uint32_t)e.x >> 12) == b1) atomicAdd(&sh.hist[(uint32_t)e.x & 0xfff], 1u);
-  }
-  __syncthreads();
-  find_bin<NT>(sh, top_k - above1);
-  const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
-  const int need = top_k - above1 - sh.found_above;
-  // ordered output: candidates are already in token order
-  int eq_seen = 0, sel = 0;
-  for (int j0 = 0; j0 < total; j0 += NT) {
-    const int j = j0 + tid;
-    const int2 e = (j < total) ? fetch(j) : make_int2(0, 0);
-    const bool valid = j < total;
-    const bool gt = valid && (uint32_t)e.x > tau;
-    const bool eq = valid && (uint32_t)e.x == tau;
-    int eq_tile;
-    const int eq_rank = eq_seen + block_excl_scan<NT>(eq ? 1 : 0, sh.wave_tot, &eq_tile);
-    const bool take = gt || (eq && eq_rank < need);
-    int take_tile;
-    const int slot = sel + block_excl_scan<NT>(take ? 1 : 0, sh.wave_tot2, &take_tile);
-    if (take && slot < top_k) out[g.nf + slot] = e.y;
-    eq_seen += eq_tile;
-    sel += take_tile;
-  }
+  select_candidates<NT>(sh, s_off, w.cand + row * chunks * (int64_t)kChunk,
+                        w.ccount + row * chunks, chunks, kChunk, b1, above1, top_k, out + g.nf);
 }
 
 bool use_multi(int64_t rows, int longest) { return longest >= 16384 && rows <= 2048; }

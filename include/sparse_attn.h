@@ -145,6 +145,25 @@ int32_t sparse_attn_topk(const sa_paged_kv* kv, const int32_t* scores, int64_t s
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Fused indexer + top-K ([DSA-page] §2.1): the index lists that sparse_attn_index followed by
+ * sparse_attn_topk would produce (bit-identical), without materialising the score rows.
+ *
+ *   q_idx    int8  [batch][q_len][num_idx_heads][idx_dim]
+ *   indices  int32 [batch][q_len][num_idx_heads][prefix_len + top_k]
+ * For decode-shaped calls (q_len == 1, rows of >= 16384 candidates) it scores every key once,
+ * keeps an exact histogram of the scores, and writes only the keys above a sampled
+ * provisional threshold; the threshold is checked against the exact histogram and the row
+ * is rescored if it was too high, so the result never depends on the sample. Other shapes
+ * run the two-step path with the score rows held in the workspace.
+ * workspace: sparse_attn_index_topk_workspace_size(kv, q_len, top_k) bytes of device memory;
+ * its contents on entry do not matter.
+ */
+size_t sparse_attn_index_topk_workspace_size(const sa_paged_kv* kv, int32_t q_len, int32_t top_k);
+int32_t sparse_attn_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
+                               int32_t q_tail, int32_t top_k, int32_t* indices, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * Prefill attention ([DSA-page] §2.3, prefill): online-softmax attention of a block of
  * queries over their index lists, or dense causal attention when indices == NULL.
  *

@@ -59,8 +59,9 @@ class GpuRun:
 
 
 def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
-            keep_scores: bool = False) -> GpuRun:
-    """The whole path on the device: index -> top-K -> attention (or dense attention)."""
+            keep_scores: bool = False, fused: bool = False) -> GpuRun:
+    """The whole path on the device: index -> top-K -> attention (or dense attention).
+    fused=True selects with sparse_attn_index_topk instead of index then topk."""
     w = inp.workload
     kv = make_kv(inp)
     r = GpuRun()
@@ -69,11 +70,14 @@ def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
         r.out, r.lse = fa.prefill(kv, inp.q, q_tail=S)
         return r
     if S == 1:
-        scores = fa.index(kv, inp.q_idx, 1, 1)
-        idx = fa.topk(kv, scores, 1, 1, w.top_k)
+        if fused:
+            idx = fa.index_topk(kv, inp.q_idx, 1, 1, w.top_k)
+        else:
+            scores = fa.index(kv, inp.q_idx, 1, 1)
+            idx = fa.topk(kv, scores, 1, 1, w.top_k)
+            if keep_scores:
+                r.scores.append((0, scores))
         r.indices = idx
-        if keep_scores:
-            r.scores.append((0, scores))
         r.out, r.lse = fa.decode(kv, inp.q[:, 0].contiguous(), idx[:, 0].contiguous(),
                                  num_splits=num_splits)
         r.out = r.out.unsqueeze(1)
@@ -88,14 +92,17 @@ def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
         c = min(q_chunk, S - q0)
         tail = S - q0
         qi = inp.q_idx[:, q0:q0 + c].contiguous()
-        scores = fa.index(kv, qi, c, tail)
-        idx = fa.topk(kv, scores, c, tail, w.top_k)
+        if fused:
+            idx = fa.index_topk(kv, qi, c, tail, w.top_k)
+        else:
+            scores = fa.index(kv, qi, c, tail)
+            idx = fa.topk(kv, scores, c, tail, w.top_k)
+            if keep_scores:
+                r.scores.append((q0, scores))
         out, lse = fa.prefill(kv, inp.q[:, q0:q0 + c].contiguous(), q_tail=tail, indices=idx)
         r.indices[:, q0:q0 + c] = idx
         r.out[:, q0:q0 + c] = out
         r.lse[:, q0:q0 + c] = lse
-        if keep_scores:
-            r.scores.append((q0, scores))
     del T
     return r
 

@@ -188,3 +188,35 @@ def test_decode_workspace_size(lib):
     auto = lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 32, 2048, 0)
     assert auto > 0 and auto % (2 * 8 * 4 * 130 * 4) == 0
     assert lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 30, 2048, 0) == 0
+
+
+def call_index_topk(lib, d, q_idx=A, q_len=1, q_tail=1, k=64, idx=A, ws=A, ws_bytes=1 << 34):
+    return lib.sparse_attn_index_topk(ctypes.byref(d), q_idx, q_len, q_tail, k, idx, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(d=desc(kidx_pool=None)), fa.SA_ERR_NULL),
+    (dict(q_idx=None), fa.SA_ERR_NULL),
+    (dict(idx=None), fa.SA_ERR_NULL),
+    (dict(ws=None), fa.SA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), fa.SA_ERR_WORKSPACE),
+    (dict(ws=A + 8), fa.SA_ERR_ALIGN),
+    (dict(k=0), fa.SA_ERR_SHAPE),
+    (dict(q_len=2, q_tail=1), fa.SA_ERR_SHAPE),
+    (dict(d=desc(idx_dim=16)), fa.SA_ERR_UNSUPPORTED),
+])
+def test_index_topk_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_index_topk(lib, d, **case) == code
+
+
+def test_index_topk_workspace_size(lib):
+    # short rows: two-step fallback holds the score rows (B * q_len * H_idx * stride ints)
+    d = desc()
+    assert lib.sparse_attn_index_topk_workspace_size(ctypes.byref(d), 1, 64) >= 2 * 8 * 1024 * 4
+    # long decode rows: fused path, candidate slots for every (row, 8192-token chunk)
+    d = desc(max_seq_len=131072, max_pages_per_seq=2048, num_pages=4096, batch=2)
+    n = lib.sparse_attn_index_topk_workspace_size(ctypes.byref(d), 1, 2048)
+    assert n >= 2 * 8 * 16 * 8192 * 8
+    assert lib.sparse_attn_index_topk_workspace_size(ctypes.byref(d), 1, 0) == 0

@@ -102,6 +102,43 @@ def test_decode_every_row(name, splits):
     assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
 
 
+@pytest.mark.parametrize("name", ["decode_long_ragged_prefix", "decode_long_ties",
+                                  "decode_long_shared_indexer", "decode_ragged_prefix"])
+def test_fused_index_topk_matches(name):
+    """The fused indexer + top-K gives the oracle's lists, identical to the two-step path."""
+    w, kw = DECODE[name]
+    _banner(f"fused index+topk {name}")
+    inp = make_inputs(w, seed=6, device="cpu", **kw).to(DEV)
+    fused = run_gpu(inp, fused=True)
+    two = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.indices, two.indices)
+    assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
+
+
+def test_fused_index_topk_rescore_fallback():
+    """Scores arranged so that an evenly spaced sample of blocks sees far more high scores
+    than the row holds: every 4th block starting at block 0 (the sampled ones for a
+    1024-block row) gets 24 blocks of maximal keys and everything else small random keys.
+    The sampled threshold then excludes part of the true top-K, and the exact rescore must
+    still produce the oracle's lists."""
+    w = W(batch=2, seq_len=65536, q_len=1, top_k=2048)
+    inp = make_inputs(w, seed=9, device="cpu")
+    inp.q_idx.fill_(1)
+    k = inp.kidx_pool
+    k.copy_(torch.randint(-20, 21, k.shape, generator=torch.Generator().manual_seed(1)).to(torch.int8))
+    table = inp.page_table
+    for b in range(w.batch):
+        for j in range(24):
+            k[table[b, 4 * ((7 * j) % 256)]] = 127
+    inp = inp.to(DEV)
+    fused = run_gpu(inp, fused=True)
+    two = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.indices, two.indices)
+    assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
+
+
 def test_scores_exact_prefill_and_decode():
     for w, kw in [SMALL["ragged_prefill_prefix"], DECODE["decode_ragged_prefix"],
                   SMALL["prefill_g8_didx128"]]:
@@ -220,8 +257,10 @@ def test_full_sparse_decode_128k():
     w = CONFIGS["sparse_decode_128k"]
     _banner(f"full {w.name}")
     inp = make_inputs(w, seed=3, device=DEV)
-    gpu = run_gpu(inp)
+    gpu = run_gpu(inp, fused=True)
+    two = run_gpu(inp)
     torch.cuda.synchronize()
+    assert torch.equal(gpu.indices, two.indices)
     ov = OracleView(inp, host_copy=False)
     assert_close(compare_rows(gpu, ov, all_rows(inp)))
 
@@ -241,8 +280,10 @@ def test_full_sparse_decode_1m_prefix():
     w = CONFIGS["sparse_decode_1m_prefix"]
     _banner(f"full {w.name}")
     inp = make_inputs(w, seed=5, device=DEV)
-    gpu = run_gpu(inp)
+    gpu = run_gpu(inp, fused=True)
+    two = run_gpu(inp)
     torch.cuda.synchronize()
+    assert torch.equal(gpu.indices, two.indices)
     ov = OracleView(inp, host_copy=False)
     rows = [(b, 0, g) for b in range(w.batch) for g in (0, 3, 7)]
     assert_close(compare_rows(gpu, ov, rows))
