@@ -198,7 +198,8 @@ size_t sparse_attn_decode_workspace_size(const sa_paged_kv* kv, int32_t num_q_he
   if (num_q_heads % v.num_kv_heads != 0 || (v.head_dim != 64 && v.head_dim != 128)) return 0;
   if (num_splits < 0 || num_splits > 256) return 0;
   const int64_t units = (int64_t)v.batch * v.num_kv_heads;
-  int splits = num_splits > 0 ? num_splits : sa::auto_splits(units, index_width);
+  int splits = num_splits > 0 ? num_splits
+                             : sa::auto_splits(units, index_width, v.head_dim, num_q_heads / v.num_kv_heads);
   if (splits > index_width) splits = index_width;
   return sa::gather_workspace_bytes(units, num_q_heads / v.num_kv_heads, v.head_dim, splits);
 }
@@ -218,7 +219,7 @@ int32_t sparse_attn_fwd_decode(const sa_paged_kv* kv, const uint16_t* q, int32_t
   if (group != 1 && group != 2 && group != 4 && group != 8) return SA_ERR_UNSUPPORTED;
   if (index_width < 1 || num_splits < 0 || num_splits > 256) return SA_ERR_SHAPE;
   const int64_t units = (int64_t)v.batch * v.num_kv_heads;
-  int splits = num_splits > 0 ? num_splits : sa::auto_splits(units, index_width);
+  int splits = num_splits > 0 ? num_splits : sa::auto_splits(units, index_width, v.head_dim, group);
   if (splits > index_width) splits = index_width;
   const size_t need = sa::gather_workspace_bytes(units, group, v.head_dim, splits);
   if (need > 0) {

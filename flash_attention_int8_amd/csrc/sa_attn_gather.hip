@@ -27,12 +27,33 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSeg = 2048;  // list entries resolved into LDS at a time
 
+// Keys each lane group loads at once: as many as the registers allow with 2 waves per SIMD.
+template <int G>
+struct KeysPerLaneGroup {
+  static constexpr int value = G <= 2 ? 16 : (G == 4 ? 8 : 4);
+};
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+// a.lo * b.lo + a.hi * b.hi + c for two bf16 pairs packed in 32-bit words (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         c, false);
+}
+// (lo half of a, lo half of b) and (hi half of a, hi half of b) as packed pairs.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
 __device__ __forceinline__ float safe_scale(float m_old, float m_new) {
   return (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_attn_gather(KvView kv, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 2) void k_attn_gather(KvView kv, const uint16_t* __restrict__ q,
                                                      int num_q_heads, int q_len, int q_tail,
                                                      const int32_t* __restrict__ indices, int W,
                                                      float qscale, int num_splits,
@@ -43,7 +64,8 @@ __global__ __launch_bounds__(256) void k_attn_gather(KvView kv, const uint16_t* 
   constexpr int KPW = 64 / LPK;     // keys a wave holds at once (lane groups)
   constexpr int NW = 4;
   constexpr int STRIDE = NW * KPW;  // list entries covered by one load round of the workgroup
-  constexpr int kNB = G <= 2 ? 8 : (G == 4 ? 4 : 2);  // keys per lane group per batch
+  constexpr int kNB = KeysPerLaneGroup<G>::value;  // keys per lane group per batch
+  constexpr int kSB = 4;                           // keys per online-softmax update
   __shared__ int32_t sh_rid[kSeg];  // resolved rows (phys_page * page_size + slot) or -1
   __shared__ float sh_m[NW][G];
   __shared__ float sh_l[NW][G];
@@ -124,50 +146,51 @@ __global__ __launch_bounds__(256) void k_attn_gather(KvView kv, const uint16_t* 
           cv[u] = make_uint4(0, 0, 0, 0);
         }
       }
-      float s[kNB][G];
+      // consume the batch in sub-batches of kSB keys: scores, one running-max update, V
 #pragma unroll
-      for (int u = 0; u < kNB; ++u) {
-        float kf[8];
-        kf[0] = bf16_lo(ck[u].x); kf[1] = bf16_hi(ck[u].x);
-        kf[2] = bf16_lo(ck[u].y); kf[3] = bf16_hi(ck[u].y);
-        kf[4] = bf16_lo(ck[u].z); kf[5] = bf16_hi(ck[u].z);
-        kf[6] = bf16_lo(ck[u].w); kf[7] = bf16_hi(ck[u].w);
+      for (int u0 = 0; u0 < kNB; u0 += kSB) {
+        float s[kSB][G];
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+          const uint4 kr = ck[u0 + u];
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float d = dot2_bf16(qw[h].x, kr.x, 0.f);
+            d = dot2_bf16(qw[h].y, kr.y, d);
+            d = dot2_bf16(qw[h].z, kr.z, d);
+            d = dot2_bf16(qw[h].w, kr.w, d);
+            s[u][h] = group_sum_f<LPK>(d) * qscale;
+          }
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          float d = bf16_lo(qw[h].x) * kf[0];
-          d = fmaf(bf16_hi(qw[h].x), kf[1], d);
-          d = fmaf(bf16_lo(qw[h].y), kf[2], d);
-          d = fmaf(bf16_hi(qw[h].y), kf[3], d);
-          d = fmaf(bf16_lo(qw[h].z), kf[4], d);
-          d = fmaf(bf16_hi(qw[h].z), kf[5], d);
-          d = fmaf(bf16_lo(qw[h].w), kf[6], d);
-          d = fmaf(bf16_hi(qw[h].w), kf[7], d);
-          s[u][h] = group_sum_f<LPK>(d) * qscale;
+          float mb = m[h];
+#pragma unroll
+          for (int u = 0; u < kSB; ++u) mb = cok[u0 + u] ? fmaxf(mb, s[u][h]) : mb;
+          const float sc = safe_scale(m[h], mb);
+          l[h] *= sc;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= sc;
+          m[h] = mb;
+#pragma unroll
+          for (int u = 0; u < kSB; ++u) {
+            s[u][h] = cok[u0 + u] ? exp2f(s[u][h] - mb) : 0.f;
+            l[h] += s[u][h];
+          }
         }
-      }
-      // online softmax update, one rescale per batch
+        // P.V over key pairs: (p_u, p_u+1) . (v_u[e], v_u+1[e]) with one dot2 per dim
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mb = m[h];
+        for (int u = 0; u < kSB; u += 2) {
+          const uint4 va = cv[u0 + u], vb = cv[u0 + u + 1];
+          const uint32_t vv[8] = {pair_lo(va.x, vb.x), pair_hi(va.x, vb.x), pair_lo(va.y, vb.y),
+                                  pair_hi(va.y, vb.y), pair_lo(va.z, vb.z), pair_hi(va.z, vb.z),
+                                  pair_lo(va.w, vb.w), pair_hi(va.w, vb.w)};
 #pragma unroll
-        for (int u = 0; u < kNB; ++u) mb = cok[u] ? fmaxf(mb, s[u][h]) : mb;
-        const float sc = safe_scale(m[h], mb);
-        l[h] *= sc;
+          for (int h = 0; h < G; ++h) {
+            const uint32_t pp = pack_bf16x2(s[u][h], s[u + 1][h]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= sc;
-        m[h] = mb;
-#pragma unroll
-        for (int u = 0; u < kNB; ++u) {
-          const float p = cok[u] ? exp2f(s[u][h] - mb) : 0.f;
-          l[h] += p;
-          acc[h][0] = fmaf(p, bf16_lo(cv[u].x), acc[h][0]);
-          acc[h][1] = fmaf(p, bf16_hi(cv[u].x), acc[h][1]);
-          acc[h][2] = fmaf(p, bf16_lo(cv[u].y), acc[h][2]);
-          acc[h][3] = fmaf(p, bf16_hi(cv[u].y), acc[h][3]);
-          acc[h][4] = fmaf(p, bf16_lo(cv[u].z), acc[h][4]);
-          acc[h][5] = fmaf(p, bf16_hi(cv[u].z), acc[h][5]);
-          acc[h][6] = fmaf(p, bf16_lo(cv[u].w), acc[h][6]);
-          acc[h][7] = fmaf(p, bf16_hi(cv[u].w), acc[h][7]);
+            for (int e = 0; e < 8; ++e) acc[h][e] = dot2_bf16(pp, vv[e], acc[h][e]);
+          }
         }
       }
     }
@@ -325,11 +348,12 @@ size_t gather_workspace_bytes(int64_t units, int group, int head_dim, int num_sp
   return (size_t)units * num_splits * group * (head_dim + 2) * sizeof(float);
 }
 
-int auto_splits(int64_t units, int index_width) {
-  // Aim for >= 1024 workgroups, with at least 128 list entries per split.
-  int s = 1;
-  while (units * s < 1024 && (index_width + 2 * s - 1) / (2 * s) >= 128 && s < 256) s *= 2;
-  return s;
+int auto_splits(int64_t units, int index_width, int head_dim, int group) {
+  // One load batch per workgroup: 4 waves x (64 / (d/8)) lane groups x keys per lane group.
+  const int per_wg = 4 * (64 / (head_dim / 8)) * (group <= 2 ? 16 : (group == 4 ? 8 : 4));
+  int s = (index_width + per_wg - 1) / per_wg;
+  (void)units;
+  return s < 1 ? 1 : (s > 256 ? 256 : s);
 }
 
 hipError_t launch_attn_gather(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
