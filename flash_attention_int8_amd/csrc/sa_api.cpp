@@ -180,6 +180,7 @@ int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_
   if (q == nullptr || out == nullptr) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(out) || (lse != nullptr && !aligned16(lse))) return SA_ERR_ALIGN;
   if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0) return SA_ERR_SHAPE;
+  if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return SA_ERR_SHAPE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (indices == nullptr)
     return hip_status(sa::launch_attn_dense(v, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, s));
@@ -218,6 +219,7 @@ int32_t sparse_attn_fwd_decode(const sa_paged_kv* kv, const uint16_t* q, int32_t
   const int group = num_q_heads / v.num_kv_heads;
   if (group != 1 && group != 2 && group != 4 && group != 8) return SA_ERR_UNSUPPORTED;
   if (index_width < 1 || num_splits < 0 || num_splits > 256) return SA_ERR_SHAPE;
+  if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return SA_ERR_SHAPE;
   const int64_t units = (int64_t)v.batch * v.num_kv_heads;
   int splits = num_splits > 0 ? num_splits : sa::auto_splits(units, index_width, v.head_dim, group);
   if (splits > index_width) splits = index_width;

@@ -175,6 +175,7 @@ int32_t sparse_attn_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32
  *   lse      float [batch][q_len][num_q_heads] (natural-log sum of exp of the scaled
  *            logits), or NULL
  * For each query head h:  z_t = sm_scale * q_h . K[t];  out = sum_t softmax(z)_t V[t].
+ * sm_scale must be positive and finite (SA_ERR_SHAPE otherwise; the same holds for decode).
  * fp32 accumulation; out is rounded to bf16 (nearest-even). num_q_heads must be a multiple
  * of num_kv_heads with group size H_q/H_kv in {1, 2, 4, 8} for the sparse path.
  */

@@ -89,12 +89,13 @@ def call_topk(lib, d, scores=A, stride=1024, q_len=1, q_tail=1, k=64, idx=A, ws=
     return lib.sparse_attn_topk(ctypes.byref(d), scores, stride, q_len, q_tail, k, idx, ws, ws_bytes, None)
 
 
-def call_prefill(lib, d, q=A, hq=32, q_len=16, q_tail=16, idx=A, width=64, out=A, lse=None):
-    return lib.sparse_attn_fwd_prefill(ctypes.byref(d), q, hq, q_len, q_tail, idx, width, 0.1, out, lse, None)
+def call_prefill(lib, d, q=A, hq=32, q_len=16, q_tail=16, idx=A, width=64, out=A, lse=None, scale=0.1):
+    return lib.sparse_attn_fwd_prefill(ctypes.byref(d), q, hq, q_len, q_tail, idx, width, scale, out, lse, None)
 
 
-def call_decode(lib, d, q=A, hq=32, idx=A, width=2048, splits=4, ws=A, ws_bytes=1 << 30, out=A, lse=None):
-    return lib.sparse_attn_fwd_decode(ctypes.byref(d), q, hq, idx, width, 0.1, splits, ws, ws_bytes,
+def call_decode(lib, d, q=A, hq=32, idx=A, width=2048, splits=4, ws=A, ws_bytes=1 << 30, out=A, lse=None,
+                scale=0.1):
+    return lib.sparse_attn_fwd_decode(ctypes.byref(d), q, hq, idx, width, scale, splits, ws, ws_bytes,
                                       out, lse, None)
 
 
@@ -154,6 +155,9 @@ def test_topk_validation(lib, case, code):
     (dict(out=A + 8), fa.SA_ERR_ALIGN),
     (dict(lse=A + 4), fa.SA_ERR_ALIGN),
     (dict(q_len=16, q_tail=2000), fa.SA_ERR_SHAPE),
+    (dict(scale=0.0), fa.SA_ERR_SHAPE),
+    (dict(scale=-0.5), fa.SA_ERR_SHAPE),
+    (dict(idx=None, scale=float("nan")), fa.SA_ERR_SHAPE),
 ])
 def test_prefill_validation(lib, case, code):
     case = dict(case)
@@ -171,6 +175,7 @@ def test_prefill_validation(lib, case, code):
     (dict(hq=24), fa.SA_ERR_UNSUPPORTED),
     (dict(width=0), fa.SA_ERR_SHAPE),
     (dict(d=desc(head_dim=32)), fa.SA_ERR_UNSUPPORTED),
+    (dict(scale=float("inf")), fa.SA_ERR_SHAPE),
 ])
 def test_decode_validation(lib, case, code):
     case = dict(case)
