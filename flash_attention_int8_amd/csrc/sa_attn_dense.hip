@@ -25,13 +25,29 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int BN = 64;    // keys per tile
+constexpr int kNumXcd = 8;
+constexpr int kDenseWaves = 8;                    // waves per workgroup (2 per SIMD)
+constexpr int kDenseThreads = 64 * kDenseWaves;  // MI355X: 8 accelerator dies, 32 CUs and one L2 each
+// The running maximum used in the exponent is only moved when a row's maximum grows by more
+// than 2^kRescaleLog2 (in exp2 units); until then P stays below 2^kRescaleLog2, far inside
+// the bf16 and fp32 ranges, and the result is unchanged because O and the row sum use the
+// same stale maximum.
+constexpr float kRescaleLog2 = 8.f;
 constexpr int KPAD = 8;   // bf16 padding of a K row in LDS
 constexpr int VPAD = 4;   // bf16 padding of a V^T row in LDS (row stride 136 B: 16 consecutive rows
                           // hit 16 distinct 8-byte bank pairs)
+
+// max(x[l], x[l ^ 32]) in every lane l: a self-swap of the two 32-lane halves gives both
+// values whichever half moves.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 template <int D>
 struct DenseShared {
@@ -45,33 +61,51 @@ union Frag8 {
   uint2 h[2];
 };
 
-// NQB = 32-query column blocks per wave. With NQB = 2 a wave owns 64 queries, so every K and
-// V^T fragment read from LDS feeds two MFMAs: half the LDS traffic per flop of NQB = 1.
-template <int D, int NQB>
-__global__ __launch_bounds__(256, (NQB == 1 ? 2 : 1)) void k_attn_dense(
+// One workgroup: 4 waves, 128 queries of one query head; each wave owns 32 queries.
+// Software pipeline over 64-key tiles, K one tile ahead of V:
+//   iteration j:  [QK(j+1) on MFMA  ||  softmax(j) on VALU]  ->  [P V(j) on MFMA  ||  stage
+//                 tiles j+2 (K) and j+1 (V) into LDS, mask + row max of S(j+1)]  ->  barrier
+// so that the exponentials of one tile are issued between the matrix instructions of the next
+// instead of after them. LDS holds two K tiles and two V^T tiles.
+template <int D>
+__global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     KvView kv, const uint16_t* __restrict__ q, int num_q_heads, int q_len, int q_tail, float qscale,
     uint16_t* __restrict__ out, float* __restrict__ lse, int n_qblocks) {
   constexpr int KS = D / 16;     // k-steps of QK^T
   constexpr int DB = D / 32;     // 32-dim blocks of O^T
   constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int KPT = D / 32;    // key rows per thread in the tile loader
-  constexpr int QW = 32 * NQB;   // queries per wave
-  constexpr int BMQ = 4 * QW;    // queries per workgroup
+  constexpr int KPT = D / 32;    // key rows per thread in the tile loader (half the workgroup)
+  constexpr int KQ = BN / KPT;   // key groups per tile (16)
+  constexpr int QW = 32;         // queries per wave
+  constexpr int BMQ = kDenseWaves * QW;  // queries per workgroup
   __shared__ DenseShared<D> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // heaviest query blocks first (causal work grows with the block index)
-  const int bh_count = kv.batch * num_q_heads;
-  const int qblk = n_qblocks - 1 - (int)(blockIdx.x / bh_count);
-  const int bh = (int)(blockIdx.x % bh_count);
-  const int b = bh / num_q_heads;
-  const int h = bh - b * num_q_heads;
-  const int g = h / (num_q_heads / kv.num_kv_heads);
+  // Work order. Workgroups are dealt round-robin to the 8 XCDs, each with its own L2; the
+  // remap gives every XCD a contiguous run of the logical order, which is (b, KV head) major,
+  // then query blocks heaviest first (causal work grows with the block index), then the G
+  // query heads of the group. The workgroups resident on one XCD then stream the same KV
+  // prefix and share it in L2.
+  const int G = num_q_heads / kv.num_kv_heads;
+  int wg;
+  {
+    const int total = (int)gridDim.x, bid = (int)blockIdx.x;
+    const int per = total / kNumXcd, extra = total % kNumXcd;
+    const int xcd = bid % kNumXcd, r = bid / kNumXcd;
+    wg = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + r;
+  }
+  const int per_pair = n_qblocks * G;
+  const int pair = wg / per_pair;
+  const int rem = wg - pair * per_pair;
+  const int qblk = n_qblocks - 1 - rem / G;
+  const int b = pair / kv.num_kv_heads;
+  const int g = pair - b * kv.num_kv_heads;
+  const int h = g * G + rem % G;
   const int seq_len = min(kv.seq_lens[b], kv.max_seq_len);
   const int pos0 = seq_len - q_tail;              // position of query 0
   const int i_blk = qblk * BMQ;
@@ -81,82 +115,72 @@ __global__ __launch_bounds__(256, (NQB == 1 ? 2 : 1)) void k_attn_dense(
   const int blk_pos_max = pos0 + i_last_blk;
   if (blk_pos_max < 0) return;
   const int n_tiles = blk_pos_max / BN + 1;
+  const int last_w = wave_pos_max >= 0 ? wave_pos_max / BN : -1;  // last tile this wave attends
 
-  // per column block nb: this lane's query, its position and validity
-  int my_i[NQB], my_pos[NQB];
-  bool my_valid[NQB];
-#pragma unroll
-  for (int nb = 0; nb < NQB; ++nb) {
-    my_i[nb] = i_w + nb * 32 + l32;
-    my_pos[nb] = pos0 + my_i[nb];
-    my_valid[nb] = my_i[nb] < q_len;
-  }
+  const int my_i = i_w + l32;
+  const int my_pos = pos0 + my_i;
+  const bool my_valid = my_i < q_len;
 
-  // Q^T fragments (B operand): lane holds query l32 of block nb, dims ks*16 + hi*8 .. +8.
-  Frag8 qf[NQB][KS];
-#pragma unroll
-  for (int nb = 0; nb < NQB; ++nb) {
-    const int qi = my_valid[nb] ? my_i[nb] : i_blk;  // any valid row; never stored
+  // Q^T fragments (B operand): lane holds query l32, dims ks*16 + hi*8 .. +8.
+  Frag8 qf[KS];
+  {
+    const int qi = my_valid ? my_i : i_blk;  // any valid row; never stored
     const uint16_t* qp = q + (((int64_t)b * q_len + qi) * num_q_heads + h) * D + hi * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[nb][ks].u = *reinterpret_cast<const uint4*>(qp + ks * 16);
+    for (int ks = 0; ks < KS; ++ks) qf[ks].u = *reinterpret_cast<const uint4*>(qp + ks * 16);
   }
 
-  f32x16 o[DB][NQB];
+  f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int nb = 0; nb < NQB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][nb][r] = 0.f;
-  float m_run[NQB], l_run[NQB];
-#pragma unroll
-  for (int nb = 0; nb < NQB; ++nb) {
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
-  // Tile loader mappings. K: dims chunk ld_c (8 dims) of key rows ld_kq*KPT .. +KPT, so 16
-  // neighbouring lanes store 256 contiguous bytes of a row. V (stored transposed): each group
-  // of 16 lanes shares one dims chunk and walks the 16 key groups, so a transposed store of
-  // one dim writes 16 contiguous KPT-key runs instead of 16 rows that share a bank.
-  const int ld_c = tid % CPR;
-  const int ld_kq = tid / CPR;
-  constexpr int KQ = BN / KPT;                       // key groups per tile (16)
-  const int lv_c = (tid / KQ) % CPR;                 // V dims chunk
-  const int lv_kq = tid % KQ;                        // V key group
+  // Tile loaders: waves 0-3 stage K, waves 4-7 stage V (each SIMD runs one of each). K: dims
+  // chunk ld_c (8 dims) of key rows ld_kq*KPT .. +KPT, so 16 neighbouring lanes store 256
+  // contiguous bytes of a row. V (stored transposed): each group of 16 lanes shares one dims
+  // chunk and walks the 16 key groups, so a transposed store of one dim writes 16 contiguous
+  // KPT-key runs instead of 16 rows that share a bank.
+  const bool k_loader = wave < kDenseWaves / 2;  // wave-uniform
+  const int ltid = tid & (kDenseThreads / 2 - 1);
+  const int ld_c = ltid % CPR;
+  const int ld_kq = ltid / CPR;
+  const int lv_c = (ltid / KQ) % CPR;
+  const int lv_kq = ltid % KQ;
   const int64_t head_stride = (int64_t)kv.page_size * D;
   const int64_t page_stride = head_stride * kv.num_kv_heads;
 
-  uint4 pk[KPT], pv[KPT];
-  auto load_tile = [&](int tile) {
+  // Global -> registers for one tile of K or V; rows past the end of the sequence, or of a
+  // page missing from the table, are never attended and are loaded as zeros. The tile base is
+  // wave-uniform; each lane adds one 32-bit offset (its first row and dims chunk).
+  const uint32_t k_off = (uint32_t)(ld_kq * KPT * D + ld_c * 8);
+  const uint32_t v_off = (uint32_t)(lv_kq * KPT * D + lv_c * 8);
+  auto load_rows = [&](const uint16_t* pool, int tile, int64_t ph, uint32_t lane_off, int row0,
+                       uint4 (&dst)[KPT]) {
     const int t0 = tile * BN;
-    const int64_t ph = phys_page(kv, b, t0);
-    if (ph < 0) {
+    const uint16_t* tp = pool + ((ph < 0 ? 0 : ph) * page_stride + g * head_stride +
+                                 (int64_t)(t0 & (kv.page_size - 1)) * D);
+    if (ph >= 0 && t0 + BN <= seq_len) {
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) { pk[r] = make_uint4(0, 0, 0, 0); pv[r] = make_uint4(0, 0, 0, 0); }
+      for (int r = 0; r < KPT; ++r) dst[r] = *reinterpret_cast<const uint4*>(tp + lane_off + r * D);
       return;
     }
-    const int64_t base = ph * page_stride + g * head_stride + (int64_t)(t0 & (kv.page_size - 1)) * D;
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int krow = ld_kq * KPT + r;
-      const int vrow = lv_kq * KPT + r;
-      // rows past the end of the sequence are never attended; they are kept finite
-      pk[r] = (t0 + krow < seq_len) ? *reinterpret_cast<const uint4*>(kv.k_pool + base + (int64_t)krow * D + ld_c * 8)
-                                    : make_uint4(0, 0, 0, 0);
-      pv[r] = (t0 + vrow < seq_len) ? *reinterpret_cast<const uint4*>(kv.v_pool + base + (int64_t)vrow * D + lv_c * 8)
-                                    : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
+    const int lim = ph < 0 ? 0 : seq_len - t0;
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
-      *reinterpret_cast<uint4*>(&sh.k[buf][ld_kq * KPT + r][ld_c * 8]) = pk[r];
-    // transpose V: for each of the 8 dims, write the KPT keys as one run
+      dst[r] = (row0 + r < lim) ? *reinterpret_cast<const uint4*>(tp + lane_off + r * D)
+                                : make_uint4(0, 0, 0, 0);
+  };
+  auto store_k = [&](int buf, const uint4 (&src)[KPT]) {
+#pragma unroll
+    for (int r = 0; r < KPT; ++r)
+      *reinterpret_cast<uint4*>(&sh.k[buf][ld_kq * KPT + r][ld_c * 8]) = src[r];
+  };
+  auto store_v = [&](int buf, const uint4 (&src)[KPT]) {  // transpose: KPT-key runs per dim
     const uint32_t* w[KPT];
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) w[r] = reinterpret_cast<const uint32_t*>(&pv[r]);
+    for (int r = 0; r < KPT; ++r) w[r] = reinterpret_cast<const uint32_t*>(&src[r]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       uint16_t vals[KPT];
@@ -174,134 +198,231 @@ __global__ __launch_bounds__(256, (NQB == 1 ? 2 : 1)) void k_attn_dense(
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < n_tiles) load_tile(tile + 1);
+  // S^T = K Q^T for the K tile in buffer buf. s[mb][j*4+i] is key mb*32 + j*8 + hi*4 + i of the
+  // tile, query column l32.
+  auto qk = [&](int buf, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        Frag8 a;
+        a.u = *reinterpret_cast<const uint4*>(&sh.k[buf][mb * 32 + l32][ks * 16 + hi * 8]);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, qf[ks].v, s[mb], 0, 0, 0);
+      }
+  };
+  // Causal mask (only tiles that reach past the wave's first query need it), row max, and the
+  // move of the running maximum with its rescale of O and the row sum (the scale is positive,
+  // so it is applied in the exponent).
+  auto mask_and_max = [&](int tile, f32x16 (&s)[2]) {
     const int t0 = tile * BN;
-    if (t0 <= wave_pos_max) {
-      // S^T = K Q^T: 32-key blocks mb x 32-query blocks nb; each K fragment feeds NQB MFMAs
-      f32x16 s[2][NQB];
+    if (t0 + BN - 1 > pos0 + i_w) {
+      const int lim = my_pos - t0 - hi * 4;  // key offsets above lim are masked
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NQB; ++nb)
+        for (int r = 0; r < 16; ++r)
+          if (mb * 32 + (r >> 2) * 8 + (r & 3) > lim) s[mb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[mb][nb][r] = 0.f;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          Frag8 a;
-          a.u = *reinterpret_cast<const uint4*>(&sh.k[buf][mb * 32 + l32][ks * 16 + hi * 8]);
-#pragma unroll
-          for (int nb = 0; nb < NQB; ++nb)
-            s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, qf[nb][ks].v, s[mb][nb], 0, 0, 0);
-        }
-      // causal mask and row max on the raw scores (the scale is positive, so it is applied in
-      // the exponent). s[mb][nb][j*4+i] is key t0 + mb*32 + j*8 + hi*4 + i, query column l32.
-      const bool diag = (t0 + BN - 1) > (pos0 + i_w);
-      Frag8 pf[NQB][4];
-#pragma unroll
-      for (int nb = 0; nb < NQB; ++nb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if (diag) {
-              const int key = t0 + mb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-              if (key > my_pos[nb]) s[mb][nb][r] = -INFINITY;
-            }
-            mx = fmaxf(mx, s[mb][nb][r]);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[nb], mx);
-        // Rescale the running sum and O only when some lane's maximum grew (wave-uniform test).
-        if (__any(m_new > m_run[nb])) {
-          const float alpha =
-              (m_run[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run[nb] - m_new) * qscale);
-          l_run[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][nb][r] *= alpha;
-          m_run[nb] = m_new;
-        }
-        const float mq = (m_run[nb] == -INFINITY) ? 0.f : m_run[nb] * qscale;
-        float psum = 0.f;
-        // P^T as B operands: step (mb, kk) takes j = 2kk, 2kk+1 of block mb (8 values)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p[e] = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][kk * 8 + e], qscale, -mq));
-              psum += p[e];
-            }
-            Frag8& f = pf[nb][mb * 2 + kk];
-            f.u.x = pack_bf16x2(p[0], p[1]);
-            f.u.y = pack_bf16x2(p[2], p[3]);
-            f.u.z = pack_bf16x2(p[4], p[5]);
-            f.u.w = pack_bf16x2(p[6], p[7]);
-          }
-        l_run[nb] += psum;
-      }
-      // O^T += V^T P^T. Step st = (mb, kk) covers keys mb*32 + kk*16 + {hi*4 + 0..3, 8 + hi*4 + 0..3};
-      // each V^T fragment feeds NQB MFMAs.
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    // wave-uniform test; -inf - -inf is NaN and compares false
+    if (__any((m_new - m_run) * qscale > kRescaleLog2)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * qscale);
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int kb = (st >> 1) * 32 + (st & 1) * 16 + hi * 4;
-          const uint16_t* vrow = &sh.vt[buf][db * 32 + l32][0];
-          Frag8 a;
-          a.h[0] = *reinterpret_cast<const uint2*>(vrow + kb);
-          a.h[1] = *reinterpret_cast<const uint2*>(vrow + kb + 8);
-#pragma unroll
-          for (int nb = 0; nb < NQB; ++nb)
-            o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, pf[nb][st].v, o[db][nb], 0, 0, 0);
-        }
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_run = m_new;
     }
-    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+  // P^T as B operands: step (mb, kk) takes j = 2kk, 2kk+1 of block mb (8 values). The row sum
+  // adds the bf16-rounded P, the same values the P V product sees.
+  auto softmax = [&](const f32x16 (&s)[2], Frag8 (&pf)[4]) {
+    const float mq = (m_run == -INFINITY) ? 0.f : m_run * qscale;
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[mb][kk * 8 + e], qscale, -mq));
+        Frag8& f = pf[mb * 2 + kk];
+        f.u.x = pack_bf16x2(p[0], p[1]);
+        f.u.y = pack_bf16x2(p[2], p[3]);
+        f.u.z = pack_bf16x2(p[4], p[5]);
+        f.u.w = pack_bf16x2(p[6], p[7]);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.x), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.y), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.z), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.w), ones, psum, false);
+      }
+    l_run += psum;
+  };
+  // QK(next tile) and softmax(current tile) in lock step: k-step ks issues the two MFMAs of
+  // S_next (K fragments read one step ahead) and then exponentiates 32/KS of the current
+  // scores; a scheduling barrier closes every step, so each step's VALU work sits between
+  // matrix instructions instead of after all of them.
+  auto qk_softmax = [&](int buf, f32x16 (&sn)[2], const f32x16 (&sc)[2], Frag8 (&pf)[4]) {
+    constexpr int EPS = 32 / KS;  // score elements per step (4 for d = 128, 8 for d = 64)
+    const float mq = (m_run == -INFINITY) ? 0.f : m_run * qscale;
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[mb][r] = 0.f;
+    Frag8 ka[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+      ka[0][mb].u = *reinterpret_cast<const uint4*>(&sh.k[buf][mb * 32 + l32][hi * 8]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          ka[(ks + 1) & 1][mb].u =
+              *reinterpret_cast<const uint4*>(&sh.k[buf][mb * 32 + l32][(ks + 1) * 16 + hi * 8]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        sn[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][mb].v, qf[ks].v, sn[mb], 0, 0, 0);
+      // elements u = ks*EPS .. +EPS of the current tile; u -> (mb, kk, e) = (u/16, (u/8)%2, u%8)
+#pragma unroll
+      for (int u2 = 0; u2 < EPS; u2 += 2) {
+        const int u = ks * EPS + u2;
+        const int mb = u >> 4, kk = (u >> 3) & 1, e = u & 7;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[mb][kk * 8 + e], qscale, -mq));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[mb][kk * 8 + e + 1], qscale, -mq));
+        const uint32_t w = pack_bf16x2(p0, p1);
+        uint32_t* fw = reinterpret_cast<uint32_t*>(&pf[mb * 2 + kk].u);
+        fw[e >> 1] = w;
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, psum, false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += psum;
+  };
+  // O^T += V^T P^T. Step st = (mb, kk) covers keys mb*32 + kk*16 + {hi*4 + 0..3, 8 + hi*4 + 0..3},
+  // the key permutation of the P^T fragments.
+  auto pv = [&](int buf, const Frag8 (&pf)[4]) {
+    auto vfrag = [&](int i) {  // i = st * DB + db; st outer: step st needs the first 8(st+1) exps
+      const int st = i / DB, db = i % DB;
+      const int kb = (st >> 1) * 32 + (st & 1) * 16 + hi * 4;
+      const uint16_t* vrow = &sh.vt[buf][db * 32 + l32][0];
+      Frag8 a;
+      a.h[0] = *reinterpret_cast<const uint2*>(vrow + kb);
+      a.h[1] = *reinterpret_cast<const uint2*>(vrow + kb + 8);
+      return a;
+    };
+    // V^T fragments are read kVPre steps ahead into a rolling buffer; a scheduling barrier
+    // after each step keeps the reads ahead of the matrix instructions that consume them.
+    constexpr int kVPre = 4;
+    Frag8 va[kVPre];
+#pragma unroll
+    for (int i = 0; i < kVPre; ++i) va[i] = vfrag(i);
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % kVPre].v, pf[i / DB].v, o[i % DB], 0, 0, 0);
+      if (i + kVPre < 4 * DB) va[i % kVPre] = vfrag(i + kVPre);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Prologue: K(0), V(0) and K(1) in LDS, S(0) computed, masked and its maximum taken.
+  // Each loader role looks its page up one iteration ahead of the load that needs it.
+  uint4 st[KPT];
+  int64_t ph_next;
+  if (k_loader) {
+    load_rows(kv.k_pool, 0, phys_page(kv, b, 0), k_off, ld_kq * KPT, st);
+    store_k(0, st);
+    if (n_tiles > 1) {
+      load_rows(kv.k_pool, 1, phys_page(kv, b, BN), k_off, ld_kq * KPT, st);
+      store_k(1, st);
+    }
+    ph_next = phys_page(kv, b, 2 * BN);
+  } else {
+    load_rows(kv.v_pool, 0, phys_page(kv, b, 0), v_off, lv_kq * KPT, st);
+    store_v(0, st);
+    ph_next = phys_page(kv, b, BN);
+  }
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (last_w >= 0) {
+    qk(0, sa);
+    mask_and_max(0, sa);
   }
 
-  // finalize: O^T[db*32 + j*8 + hi*4 + i][query l32 of block nb]
-#pragma unroll
-  for (int nb = 0; nb < NQB; ++nb) {
-    const float l_tot = l_run[nb] + __shfl_xor(l_run[nb], 32, 64);
-    if (!my_valid[nb]) continue;
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    const int64_t orow = (((int64_t)b * q_len + my_i[nb]) * num_q_heads + h) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint2 w;
-        w.x = pack_bf16x2(o[db][nb][j * 4 + 0] * inv, o[db][nb][j * 4 + 1] * inv);
-        w.y = pack_bf16x2(o[db][nb][j * 4 + 2] * inv, o[db][nb][j * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(out + orow + db * 32 + j * 8 + hi * 4) = w;
-      }
-    if (lse != nullptr && hi == 0)
-      lse[((int64_t)b * q_len + my_i[nb]) * num_q_heads + h] =
-          (l_tot > 0.f) ? (m_run[nb] * qscale + log2f(l_tot)) * kLn2 : -INFINITY;
+  // Iteration j: on entry K buffer (j+1)&1 holds K(j+1), V buffer j&1 holds V(j), sc holds the
+  // masked S(j) and m_run its running maximum. K loaders fetch K(j+2) into registers while the
+  // tile is computed and store it to K buffer j&1; V loaders do the same with V(j+1) and V
+  // buffer (j+1)&1. Neither buffer is read during iteration j.
+  auto iter = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int ltile = k_loader ? j + 2 : j + 1;
+    const bool more = ltile < n_tiles;
+    const int64_t ph = ph_next;
+    ph_next = phys_page(kv, b, (ltile + 1) * BN);
+    if (more) {
+      if (k_loader) load_rows(kv.k_pool, ltile, ph, k_off, ld_kq * KPT, st);
+      else load_rows(kv.v_pool, ltile, ph, v_off, lv_kq * KPT, st);
+    }
+    if (j <= last_w) {
+      // S(j+1) is computed unconditionally (one extra tile at the wave's end, never used) so
+      // that its matrix instructions share a basic block with the exponentials of S(j).
+      Frag8 pf[4];
+      qk_softmax((j + 1) & 1, sn, sc, pf);
+      pv(j & 1, pf);
+    }
+    if (more) {
+      if (k_loader) store_k(j & 1, st);
+      else store_v((j + 1) & 1, st);
+    }
+    if (j + 1 <= last_w) mask_and_max(j + 1, sn);
+    __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    iter(j, sa, sb);
+    if (j + 1 < n_tiles) iter(j + 1, sb, sa);
   }
+
+  // finalize: O^T[db*32 + j*8 + hi*4 + i][query l32]
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!my_valid) return;
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  const int64_t orow = (((int64_t)b * q_len + my_i) * num_q_heads + h) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint2 w;
+      w.x = pack_bf16x2(o[db][j * 4 + 0] * inv, o[db][j * 4 + 1] * inv);
+      w.y = pack_bf16x2(o[db][j * 4 + 2] * inv, o[db][j * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(out + orow + db * 32 + j * 8 + hi * 4) = w;
+    }
+  if (lse != nullptr && hi == 0)
+    lse[((int64_t)b * q_len + my_i) * num_q_heads + h] =
+        (l_tot > 0.f) ? (m_run * qscale + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-template <int D, int NQB>
+template <int D>
 hipError_t launch_dense_d(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                           int q_tail, float sm_scale, uint16_t* out, float* lse,
                           hipStream_t stream) {
-  constexpr int BMQ = 4 * 32 * NQB;
+  constexpr int BMQ = kDenseWaves * 32;
   const int nqb = (q_len + BMQ - 1) / BMQ;
   const int64_t wgs = (int64_t)nqb * kv.batch * num_q_heads;
-  hipLaunchKernelGGL((k_attn_dense<D, NQB>), dim3((unsigned)wgs), dim3(256), 0, stream, kv, q,
+  hipLaunchKernelGGL((k_attn_dense<D>), dim3((unsigned)wgs), dim3(kDenseThreads), 0, stream, kv, q,
                      num_q_heads, q_len, q_tail, sm_scale * kLog2e, out, lse, nqb);
   return hipGetLastError();
 }
@@ -311,15 +432,10 @@ hipError_t launch_dense_d(const KvView& kv, const uint16_t* q, int num_q_heads, 
 hipError_t launch_attn_dense(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                              int q_tail, float sm_scale, uint16_t* out, float* lse,
                              hipStream_t stream) {
-  // 64 queries per wave halves LDS traffic per flop but leaves one wave per SIMD, which loses
-  // more (no overlap of one wave's softmax with another's MFMAs) than it gains on MI355X.
-  const bool wide = false;
   if (kv.head_dim == 128)
-    return wide ? launch_dense_d<128, 2>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, stream)
-                : launch_dense_d<128, 1>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, stream);
+    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, stream);
   if (kv.head_dim == 64)
-    return wide ? launch_dense_d<64, 2>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, stream)
-                : launch_dense_d<64, 1>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, stream);
+    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, stream);
   return hipErrorInvalidValue;
 }
 
