@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   const int b = pair / kv.num_kv_heads;
   const int g = pair - b * kv.num_kv_heads;
   const int h = g * G + rem % G;
-  const int seq_len = min(kv.seq_lens[b], kv.max_seq_len);
+  const int seq_len = __builtin_amdgcn_readfirstlane(min(kv.seq_lens[b], kv.max_seq_len));
   const int pos0 = seq_len - q_tail;              // position of query 0
   const int i_blk = qblk * BMQ;
   const int i_w = i_blk + wave * QW;              // first query of this wave
@@ -138,39 +138,40 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   float m_run = -INFINITY, l_run = 0.f;
 
   // Tile loaders: waves 0-3 stage K, waves 4-7 stage V (each SIMD runs one of each). K: dims
-  // chunk ld_c (8 dims) of key rows ld_kq*KPT .. +KPT, so 16 neighbouring lanes store 256
-  // contiguous bytes of a row. V (stored transposed): each group of 16 lanes shares one dims
-  // chunk and walks the 16 key groups, so a transposed store of one dim writes 16 contiguous
-  // KPT-key runs instead of 16 rows that share a bank.
+  // chunk ld_c (8 dims) of key rows ld_kq*KPT .. +KPT, so 16 neighbouring lanes load and store
+  // 256 contiguous bytes of a row. V (stored transposed): 4 neighbouring lanes cover 64
+  // contiguous bytes of a row (dims chunks 4*c_hi .. +3) and the next lanes walk the key
+  // groups, so one load touches 16 row segments of 64 B, and a transposed store of one dim by
+  // a half-wave hits 32 distinct 8-byte bank pairs (V^T row stride 136 B).
   const bool k_loader = wave < kDenseWaves / 2;  // wave-uniform
   const int ltid = tid & (kDenseThreads / 2 - 1);
   const int ld_c = ltid % CPR;
   const int ld_kq = ltid / CPR;
-  const int lv_c = (ltid / KQ) % CPR;
-  const int lv_kq = ltid % KQ;
+  const int lv_kq = (ltid / 4) % KQ;
+  const int lv_c = (ltid / (4 * KQ)) * 4 + ltid % 4;
   const int64_t head_stride = (int64_t)kv.page_size * D;
   const int64_t page_stride = head_stride * kv.num_kv_heads;
 
-  // Global -> registers for one tile of K or V; rows past the end of the sequence, or of a
-  // page missing from the table, are never attended and are loaded as zeros. The tile base is
+  // Global -> registers for one tile of K or V. The loads are unconditional and always in
+  // bounds: a tile never crosses a page, and a page missing from the table reads page 0. Rows
+  // that must not be attended (past the end of the sequence, or of a missing page) are zeroed
+  // when the tile is stored to LDS, so the loads stay in flight until then. The tile base is
   // wave-uniform; each lane adds one 32-bit offset (its first row and dims chunk).
   const uint32_t k_off = (uint32_t)(ld_kq * KPT * D + ld_c * 8);
   const uint32_t v_off = (uint32_t)(lv_kq * KPT * D + lv_c * 8);
-  auto load_rows = [&](const uint16_t* pool, int tile, int64_t ph, uint32_t lane_off, int row0,
-                       uint4 (&dst)[KPT]) {
+  auto load_rows = [&](const uint16_t* pool, int tile, int64_t ph, uint32_t lane_off, uint4 (&dst)[KPT]) {
     const int t0 = tile * BN;
     const uint16_t* tp = pool + ((ph < 0 ? 0 : ph) * page_stride + g * head_stride +
                                  (int64_t)(t0 & (kv.page_size - 1)) * D);
-    if (ph >= 0 && t0 + BN <= seq_len) {
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) dst[r] = *reinterpret_cast<const uint4*>(tp + lane_off + r * D);
-      return;
-    }
-    const int lim = ph < 0 ? 0 : seq_len - t0;
+    for (int r = 0; r < KPT; ++r) dst[r] = *reinterpret_cast<const uint4*>(tp + lane_off + r * D);
+  };
+  // rows of tile `tile` that hold attendable keys (wave-uniform)
+  auto valid_rows = [&](int tile, int64_t ph) { return ph < 0 ? 0 : seq_len - tile * BN; };
+  auto mask_rows = [&](uint4 (&v)[KPT], int row0, int lim) {
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
-      dst[r] = (row0 + r < lim) ? *reinterpret_cast<const uint4*>(tp + lane_off + r * D)
-                                : make_uint4(0, 0, 0, 0);
+      if (row0 + r >= lim) v[r] = make_uint4(0, 0, 0, 0);
   };
   auto store_k = [&](int buf, const uint4 (&src)[KPT]) {
 #pragma unroll
@@ -345,15 +346,24 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   uint4 st[KPT];
   int64_t ph_next;
   if (k_loader) {
-    load_rows(kv.k_pool, 0, phys_page(kv, b, 0), k_off, ld_kq * KPT, st);
+    int64_t ph = phys_page(kv, b, 0);
+    load_rows(kv.k_pool, 0, ph, k_off, st);
+    int lim = valid_rows(0, ph);
+    if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
     store_k(0, st);
     if (n_tiles > 1) {
-      load_rows(kv.k_pool, 1, phys_page(kv, b, BN), k_off, ld_kq * KPT, st);
+      ph = phys_page(kv, b, BN);
+      load_rows(kv.k_pool, 1, ph, k_off, st);
+      lim = valid_rows(1, ph);
+      if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
       store_k(1, st);
     }
     ph_next = phys_page(kv, b, 2 * BN);
   } else {
-    load_rows(kv.v_pool, 0, phys_page(kv, b, 0), v_off, lv_kq * KPT, st);
+    const int64_t ph = phys_page(kv, b, 0);
+    load_rows(kv.v_pool, 0, ph, v_off, st);
+    const int lim = valid_rows(0, ph);
+    if (lim < BN) mask_rows(st, lv_kq * KPT, lim);
     store_v(0, st);
     ph_next = phys_page(kv, b, BN);
   }
@@ -369,14 +379,14 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   // tile is computed and store it to K buffer j&1; V loaders do the same with V(j+1) and V
   // buffer (j+1)&1. Neither buffer is read during iteration j.
   auto iter = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    // the load past the last tile re-reads the last one (in bounds) and is never stored
     const int ltile = k_loader ? j + 2 : j + 1;
     const bool more = ltile < n_tiles;
-    const int64_t ph = ph_next;
+    const int lt = more ? ltile : n_tiles - 1;
+    const int64_t ph = more ? ph_next : phys_page(kv, b, lt * BN);
     ph_next = phys_page(kv, b, (ltile + 1) * BN);
-    if (more) {
-      if (k_loader) load_rows(kv.k_pool, ltile, ph, k_off, ld_kq * KPT, st);
-      else load_rows(kv.v_pool, ltile, ph, v_off, lv_kq * KPT, st);
-    }
+    load_rows(k_loader ? kv.k_pool : kv.v_pool, lt, ph, k_loader ? k_off : v_off, st);
+    const int lim = valid_rows(lt, ph);
     if (j <= last_w) {
       // S(j+1) is computed unconditionally (one extra tile at the wave's end, never used) so
       // that its matrix instructions share a basic block with the exponentials of S(j).
@@ -385,6 +395,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
       pv(j & 1, pf);
     }
     if (more) {
+      if (lim < BN) mask_rows(st, k_loader ? ld_kq * KPT : lv_kq * KPT, lim);
       if (k_loader) store_k(j & 1, st);
       else store_v((j + 1) & 1, st);
     }
