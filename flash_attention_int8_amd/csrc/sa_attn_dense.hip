@@ -4,9 +4,11 @@
 // [DSA-page] = "国产AI芯片完成前沿大模型Day-0适配:稀疏注意力与混合精度推理全解析" §2.3: prefill
 // is the compute-heavy phase and runs on the matrix units.
 //
-// Workgroup: 4 waves, 128 queries of one query head (32 per wave), streaming 64-key tiles
-// of the KV head through LDS with a two-stage buffer (the next tile's global loads are in
-// flight while the current tile is computed).
+// Workgroup: 8 waves, 256 queries of one query head (32 per wave, two waves per SIMD),
+// streaming 64-key tiles of the KV head through LDS. K runs one tile ahead of V so that each
+// iteration issues the QK^T matrix instructions of the next tile between the exponentials of
+// the current one (software pipeline, see the loop). Waves 0-3 stage K tiles, waves 4-7 stage
+// V tiles; global loads stay in flight across the compute and land in LDS at its end.
 // Per wave and tile, with v_mfma_f32_32x32x16_bf16:
 //   S^T = K * Q^T   (A = K tile rows from LDS, B = the wave's Q^T held in registers).
 //                   The accumulator layout gives each lane 32 of the 64 scores of ONE query
@@ -15,9 +17,9 @@
 //   O^T += V^T * P^T  (A = V^T from LDS, B = P^T taken straight from the S^T accumulators:
 //                   the 8 scores a lane holds for one 16-key step become its B operand, and
 //                   the V^T reads use the same key permutation, so no shuffle is needed).
-// V is transposed into LDS on the way in: each thread loads D/32 key rows x 8 dims and
-// writes D/32-key runs of each dim. Softmax is base 2 with sm_scale*log2(e) applied to the
-// fp32 scores; Q, K and V stay exact bf16, accumulation is fp32, P is rounded to bf16.
+// V is transposed into LDS on the way in. Softmax is base 2 with sm_scale*log2(e) applied to
+// the fp32 scores; Q, K and V stay exact bf16, accumulation is fp32, P is rounded to bf16 and
+// the row sum adds the rounded P. Workgroups are ordered for L2 reuse across the 8 XCDs.
 #include "sa_common.h"
 
 namespace sa {

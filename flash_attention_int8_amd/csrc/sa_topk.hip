@@ -25,11 +25,15 @@ namespace {
 using namespace sel;
 
 
-template <int NT>
+// STAGE > 0: the row (at most STAGE candidates) is read once, with every thread's loads in
+// flight together, into LDS as 24-bit keys while the high-digit histogram is built; the low
+// digit and the ordered sweep then read LDS. STAGE == 0: all three passes read the scores.
+template <int NT, int STAGE>
 __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __restrict__ scores,
                                                  int64_t row_stride, int q_len, int q_tail,
                                                  int top_k, int32_t* __restrict__ indices) {
   __shared__ TopkShared<NT> sh;
+  __shared__ uint32_t staged[STAGE > 0 ? STAGE : 1];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int64_t bi = row / kv.num_idx_heads;
@@ -50,6 +54,11 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
     for (int j = nf + m + tid; j < W; j += NT) out[j] = -1;
     return;
   }
+  // key of candidate j (token P + j)
+  auto key_at = [&](int j) -> uint32_t {
+    if constexpr (STAGE > 0) return staged[j];
+    else return score_key(srow[P + j]);
+  };
 
   // pass 1: high digit
   if (tid == 0) {
@@ -58,7 +67,25 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
   }
   for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
   __syncthreads();
-  for (int t = P + tid; t <= pos; t += NT) atomicAdd(&sh.hist[score_key(srow[t]) >> 12], 1u);
+  if constexpr (STAGE > 0) {
+    constexpr int PER = STAGE / NT;
+    uint32_t v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = u * NT + tid;
+      v[u] = j < n ? score_key(srow[P + j]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = u * NT + tid;
+      if (j < n) {
+        staged[j] = v[u];
+        atomicAdd(&sh.hist[v[u] >> 12], 1u);
+      }
+    }
+  } else {
+    for (int j = tid; j < n; j += NT) atomicAdd(&sh.hist[key_at(j) >> 12], 1u);
+  }
   __syncthreads();
   find_bin<NT>(sh, top_k);
   const uint32_t b1 = sh.found_bin;
@@ -67,8 +94,8 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
   // pass 2: low digit within bin b1
   for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
   __syncthreads();
-  for (int t = P + tid; t <= pos; t += NT) {
-    const uint32_t key = score_key(srow[t]);
+  for (int j = tid; j < n; j += NT) {
+    const uint32_t key = key_at(j);
     if ((key >> 12) == b1) atomicAdd(&sh.hist[key & 0xfff], 1u);
   }
   __syncthreads();
@@ -76,47 +103,46 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
   const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
   const int need = top_k - above1 - sh.found_above;  // keys equal to tau that are taken
 
-  // pass 3: ordered compaction
+  // pass 3: ordered compaction. Wave w owns the contiguous segment [w*seg, (w+1)*seg) of the
+  // candidates. It counts its keys > tau and == tau (ballots), one exclusive scan over the
+  // waves gives every wave the counts before its segment, and a second sweep places each
+  // taken token at slot = (keys > tau before it) + min(keys == tau before it, need): the list
+  // comes out in token order with one barrier, and no atomic decides any order.
+  constexpr int NW = NT / 64;
   const int lane = tid & 63;
+  const int wv = tid >> 6;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int eq_base = 0, sel_base = 0;
-  for (int t0 = P; t0 <= pos && sel_base < top_k; t0 += NT) {
-    const int t = t0 + tid;
-    const bool valid = t <= pos;
-    const uint32_t key = valid ? score_key(srow[t]) : 0u;
-    const bool gt = valid && key > tau;
-    const bool eq = valid && key == tau;
-    // rank among equal keys, in token order
-    const uint64_t eq_mask = __ballot(eq);
-    const int eq_w = __popcll(eq_mask & lt_mask);
-    if (lane == 0) sh.wave_tot[tid >> 6] = __popcll(eq_mask);
-    __syncthreads();
-    int eq_before = 0, eq_all = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-      const int x = sh.wave_tot[w];
-      eq_before += (w < (tid >> 6)) ? x : 0;
-      eq_all += x;
-    }
-    const bool take = gt || (eq && (eq_base + eq_before + eq_w) < need);
-    const uint64_t tk_mask = __ballot(take);
-    const int tk_w = __popcll(tk_mask & lt_mask);
-    if (lane == 0) sh.wave_tot2[tid >> 6] = __popcll(tk_mask);
-    __syncthreads();
-    int tk_before = 0, tk_all = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-      const int x = sh.wave_tot2[w];
-      tk_before += (w < (tid >> 6)) ? x : 0;
-      tk_all += x;
-    }
-    if (take) {
-      const int slot = sel_base + tk_before + tk_w;
-      if (slot < top_k) out[nf + slot] = t;
-    }
-    eq_base += eq_all;
-    sel_base += tk_all;
-    __syncthreads();  // wave_tot/wave_tot2 are rewritten by the next tile
+  const int seg = ((n + NW * 64 - 1) / (NW * 64)) * 64;
+  const int s0 = wv * seg;
+  const int s1 = min(n, s0 + seg);
+  int gt_w = 0, eq_w = 0;
+  for (int j0 = s0; j0 < s1; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t key = j < s1 ? key_at(j) : 0u;
+    gt_w += __popcll(__ballot(j < s1 && key > tau));
+    eq_w += __popcll(__ballot(j < s1 && key == tau));
+  }
+  if (lane == 0) {
+    sh.wave_tot[wv] = gt_w;
+    sh.wave_tot2[wv] = eq_w;
+  }
+  __syncthreads();
+  int gt_run = 0, eq_run = 0;
+  for (int w = 0; w < wv; ++w) {
+    gt_run += sh.wave_tot[w];
+    eq_run += sh.wave_tot2[w];
+  }
+  for (int j0 = s0; j0 < s1 && gt_run + min(eq_run, need) < top_k; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t key = j < s1 ? key_at(j) : 0u;
+    const bool gt = j < s1 && key > tau;
+    const bool eq = j < s1 && key == tau;
+    const uint64_t gm = __ballot(gt), em = __ballot(eq);
+    const int gt_before = gt_run + __popcll(gm & lt_mask);
+    const int eq_before = eq_run + __popcll(em & lt_mask);
+    if (gt || (eq && eq_before < need)) out[nf + gt_before + min(eq_before, need)] = P + j;
+    gt_run += __popcll(gm);
+    eq_run += __popcll(em);
   }
 }
 
@@ -337,12 +363,16 @@ hipError_t launch_topk(const KvView& kv, const int32_t* scores, int64_t row_stri
                        q_tail, top_k, ws, chunks, indices);
     return hipGetLastError();
   }
-  if (longest > 8192) {
-    hipLaunchKernelGGL(k_topk_row<1024>, dim3((unsigned)rows), dim3(1024), 0, stream, kv, scores,
-                       row_stride, q_len, q_tail, top_k, indices);
+  // rows that fit are staged in LDS (one read of the scores); longer ones take three passes
+  if (longest <= 16384) {
+    hipLaunchKernelGGL((k_topk_row<512, 16384>), dim3((unsigned)rows), dim3(512), 0, stream, kv,
+                       scores, row_stride, q_len, q_tail, top_k, indices);
+  } else if (longest <= 32768) {
+    hipLaunchKernelGGL((k_topk_row<1024, 32768>), dim3((unsigned)rows), dim3(1024), 0, stream, kv,
+                       scores, row_stride, q_len, q_tail, top_k, indices);
   } else {
-    hipLaunchKernelGGL(k_topk_row<256>, dim3((unsigned)rows), dim3(256), 0, stream, kv, scores,
-                       row_stride, q_len, q_tail, top_k, indices);
+    hipLaunchKernelGGL((k_topk_row<1024, 0>), dim3((unsigned)rows), dim3(1024), 0, stream, kv,
+                       scores, row_stride, q_len, q_tail, top_k, indices);
   }
   return hipGetLastError();
 }

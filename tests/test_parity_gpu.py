@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import flash_attention_int8_amd as fa
+import oracle
 from synthetic import CONFIGS, Workload, make_inputs
 from dsa_harness import (OracleView, assert_close, compare_rows, make_kv, run_gpu, f64)
 
@@ -137,6 +138,32 @@ def test_fused_index_topk_rescore_fallback():
     torch.cuda.synchronize()
     assert torch.equal(fused.indices, two.indices)
     assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
+
+
+@pytest.mark.parametrize("seq_len,q_len,prefix,vals", [
+    (16000, 40, 3, 100000),     # rows of <= 16384 candidates: staged in LDS, 512 threads
+    (30000, 24, 0, 3),          # <= 32768 candidates, heavy ties: staged in LDS, 1024 threads
+    (33005, 2050, 5, 40000),    # > 32768 candidates and > 2048 rows: three passes over HBM
+])
+def test_topk_row_paths(seq_len, q_len, prefix, vals):
+    """Stand-alone top-K on score rows written directly (random ints in [-vals, vals)), for
+    each single-row selection path; sampled rows must equal the oracle's index lists."""
+    top_k = 1000
+    _banner(f"topk rows seq_len={seq_len} q_len={q_len} P={prefix} vals={vals}")
+    w = W(num_q_heads=1, num_kv_heads=1, head_dim=64, idx_dim=32, seq_len=seq_len, q_len=q_len,
+          top_k=top_k, prefix_len=prefix)
+    inp = make_inputs(w, seed=21, device=DEV)
+    kv = make_kv(inp)
+    gen = torch.Generator().manual_seed(22)
+    stride = (seq_len + 3) & ~3  # the ABI takes row strides in multiples of 4 scores
+    scores = torch.randint(-vals, vals, (1, q_len, 1, stride), generator=gen, dtype=torch.int32)
+    got = fa.topk(kv, scores.to(DEV), q_len, q_len, top_k).cpu().numpy()
+    rows = range(q_len) if q_len <= 64 else np.linspace(0, q_len - 1, 48).astype(int)
+    host = scores.numpy()
+    for i in rows:
+        pos = oracle.query_position(seq_len, q_len, int(i))
+        want = oracle.index_list(pos, prefix, top_k, prefix + top_k, lambda t: host[0, i, 0, t])
+        assert np.array_equal(got[0, i, 0], want), (i, got[0, i, 0][:8], want[:8])
 
 
 def test_scores_exact_prefill_and_decode():
