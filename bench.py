@@ -37,7 +37,9 @@ def parse():
                     help="do not evict the caches between timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the sparse 32K prefill and the 1M-context decode measurements")
+    ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--two-step", action="store_true",
@@ -118,12 +120,16 @@ def cpu_baseline(inp, w, budget_s=12.0):
     q_bits = inp.q.view(torch.int16).cpu().numpy().view(np.uint16)
     q_idx = inp.q_idx.cpu().numpy()
     done, t_total = 0, 0.0
-    for b in range(B):
-        pages = torch.as_tensor(table[b], dtype=torch.long, device=inp.k_pool.device)
-        kp = inp.k_pool[pages].view(torch.int16).cpu().numpy().view(np.uint16)
-        vp = inp.v_pool[pages].view(torch.int16).cpu().numpy().view(np.uint16)
-        ip = inp.kidx_pool[pages].cpu().numpy()
-        local = np.arange(len(pages))
+    host = {}
+    for n in range(64 * B):  # whole sequences, repeated until the time budget is used
+        b = n % B
+        if b not in host:  # host copies of the sequence's pages, in logical order
+            pages = torch.as_tensor(table[b], dtype=torch.long, device=inp.k_pool.device)
+            host[b] = (inp.k_pool[pages].view(torch.int16).cpu().numpy().view(np.uint16),
+                       inp.v_pool[pages].view(torch.int16).cpu().numpy().view(np.uint16),
+                       inp.kidx_pool[pages].cpu().numpy())
+        kp, vp, ip = host[b]
+        local = np.arange(kp.shape[0])
         pos = w.seq_len - 1
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
@@ -135,13 +141,12 @@ def cpu_baseline(inp, w, budget_s=12.0):
                                  sm_scale=1 / math.sqrt(w.head_dim))
             t_total += time.perf_counter() - t0
         done += 1
-        del kp, vp, ip
         if t_total >= budget_s:
             break
     return {"value": done / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {B} sequences of one 128K decode step (all {Hkv} KV groups each: "
-                      f"scores over {w.seq_len} keys, top-{w.top_k}, attention), fp64 numpy, "
-                      f"{t_total:.1f} s"}
+            "sample": f"{done} sequence-steps (the {B} sequences of the 128K decode step, cycled) "
+                      f"with all {Hkv} KV groups each: scores over {w.seq_len} keys, top-{w.top_k}, "
+                      f"attention; fp64 numpy on one thread, {t_total:.1f} s"}
 
 
 def bench_prefill(fa, reps):
@@ -172,6 +177,113 @@ def bench_prefill(fa, reps):
     torch.cuda.empty_cache()
     return {"workload": w.name, "ms": ms, "tflops": flops / ms / 1e9,
             "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS, "flop": flops}
+
+
+def bench_sparse_prefill(fa, reps, q_chunk=2048):
+    """Whole sparse prefill of 32K tokens (B=1, 32/8 heads, d=128, d_idx=64, top-K=2048): per
+    chunk of q_chunk queries, indexer scores -> top-K -> gathered attention."""
+    import torch
+
+    from synthetic import CONFIGS, make_inputs
+    w = CONFIGS["sparse_prefill_32k"]
+    inp = make_inputs(w, seed=4, device="cuda")
+    kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
+                    page_table=inp.page_table, seq_lens=inp.seq_lens, max_seq_len=w.seq_len,
+                    prefix_len=w.prefix_len)
+    S, Hkv, Hq, d = w.q_len, w.num_kv_heads, w.num_q_heads, w.head_dim
+    stride = (w.seq_len + 3) & ~3
+    scores = torch.empty((1, q_chunk, Hkv, stride), dtype=torch.int32, device="cuda")
+    idx = torch.empty((1, q_chunk, Hkv, w.index_width), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(inp.q)
+    lse = torch.empty((1, S, Hq), dtype=torch.float32, device="cuda")
+    q_idx = [inp.q_idx[:, q0:q0 + q_chunk].contiguous() for q0 in range(0, S, q_chunk)]
+    tk_n = fa.sparse_attn_topk_workspace_size(kv, q_chunk, w.top_k)
+    tk_ws = torch.empty(max(tk_n, 16), dtype=torch.uint8, device="cuda")
+    scale = 1 / math.sqrt(d)
+
+    def run(evs=None):
+        for c, q0 in enumerate(range(0, S, q_chunk)):
+            n, tail = min(q_chunk, S - q0), S - q0
+            if evs:
+                evs[c][0].record()
+            fa.sparse_attn_index(kv, q_idx[c], n, tail, scores, stride)
+            if evs:
+                evs[c][1].record()
+            fa.sparse_attn_topk(kv, scores, stride, n, tail, w.top_k, idx, tk_ws, tk_n)
+            if evs:
+                evs[c][2].record()
+            fa.sparse_attn_fwd_prefill(kv, inp.q[:, q0:q0 + n], Hq, n, tail, idx, w.index_width,
+                                       scale, out[:, q0:q0 + n], lse[:, q0:q0 + n])
+            if evs:
+                evs[c][3].record()
+    run()
+    torch.cuda.synchronize()
+    chunks = (S + q_chunk - 1) // q_chunk
+    stage = [0.0, 0.0, 0.0]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(chunks)]
+    run(evs)
+    torch.cuda.synchronize()
+    for c in range(chunks):
+        for k in range(3):
+            stage[k] += evs[c][k].elapsed_time(evs[c][k + 1])
+    # algorithmic attention flops: 4 heads x (QK + PV) per selected key per (query, group)
+    sel = sum(min(w.top_k, i + 1) for i in range(S))
+    attn_flop = 4.0 * d * Hq * sel
+    del inp, scores, idx, out, lse, q_idx, tk_ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms": ms, "tokens_per_s": S / (ms * 1e-3),
+            "stage_ms": {"index": stage[0], "topk": stage[1], "attention": stage[2]},
+            "attention_tflops": attn_flop / (stage[2] * 1e-3) / 1e12, "q_chunk": q_chunk}
+
+
+def bench_decode_1m(fa, steps, warmup):
+    """One decode step at 1M context with a 196-token forced prefix (B=4, 32/8 heads, d=128,
+    d_idx=64, top-K=2048): fused indexer + top-K, then split-K attention and merge."""
+    import torch
+
+    from synthetic import CONFIGS, make_inputs
+    w = CONFIGS["sparse_decode_1m_prefix"]
+    inp = make_inputs(w, seed=5, device="cuda")
+    kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
+                    page_table=inp.page_table, seq_lens=inp.seq_lens, max_seq_len=w.seq_len,
+                    prefix_len=w.prefix_len)
+    B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
+    idx = torch.empty((B, 1, Hkv, w.index_width), dtype=torch.int32, device="cuda")
+    q = inp.q[:, 0].contiguous()
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    fu_n = fa.sparse_attn_index_topk_workspace_size(kv, 1, w.top_k)
+    fu = torch.empty(max(fu_n, 16), dtype=torch.uint8, device="cuda")
+    dec_n = fa.sparse_attn_decode_workspace_size(kv, Hq, w.index_width, 0)
+    dec = torch.empty(max(dec_n, 16), dtype=torch.uint8, device="cuda")
+    scale = 1 / math.sqrt(w.head_dim)
+
+    def step():
+        fa.sparse_attn_index_topk(kv, inp.q_idx, 1, 1, w.top_k, idx, fu, fu_n)
+        fa.sparse_attn_fwd_decode(kv, q, Hq, idx[:, 0], w.index_width, scale, 0, dec, dec_n, out, lse)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kidx_bytes = B * Hkv * w.seq_len * w.idx_dim
+    gather = B * Hkv * (w.prefix_len + w.top_k) * 2 * w.head_dim * 2
+    del inp, idx, q, out, lse, fu, dec
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms": ms, "tokens_per_s": B / (ms * 1e-3),
+            "hbm_gbps": (kidx_bytes + gather) / (ms * 1e-3) / 1e9, "cache": "warm (back-to-back steps)"}
 
 
 def main():
@@ -310,6 +422,11 @@ def main():
         result["prefill"] = pf
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, w)
+    if not args.no_extra:
+        del inp, evict_buf
+        torch.cuda.empty_cache()
+        result["sparse_prefill"] = bench_sparse_prefill(fa, reps=2)
+        result["decode_1m_prefix"] = bench_decode_1m(fa, steps=10, warmup=3)
     print(json.dumps(result), flush=True)
 
 
