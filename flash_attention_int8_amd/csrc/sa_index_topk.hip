@@ -7,20 +7,18 @@
 // 4-byte score for every 64-byte key into the middle of that read stream costs about a fifth
 // of its time on MI355X.
 //
-// Three launches over rows r = (sequence, indexer head):
-//   sample  one workgroup per row scores an evenly spaced sample of the row's 64-token
-//           blocks (about kSampleBlocks of them) and picks a provisional threshold bin
-//           theta: the highest bin whose sampled tail holds well over the sampled share of
-//           K (twice the expected count plus four standard deviations plus 16). It also
-//           clears the row histogram used by the next pass.
-//   main    per (row, 8192-token chunk): scores every key of the chunk, adds the exact
-//           histogram of key >> 12 into the row histogram, and compacts the keys in bins
-//           >= theta, in token order, into the chunk's candidate slots.
-//   final   one workgroup per row: the exact histogram gives b1, the bin of the K-th largest
-//           key. If b1 >= theta every selected key is a candidate, and the exact selection
-//           runs on the candidates (a few thousand per row). Otherwise (the sample misjudged
-//           the tail) the workgroup rescores the row and collects the keys in bins >= b1
-//           first, so the result stays exact whatever the score distribution.
+// Two launches over rows r = (sequence, indexer head):
+//   main    per (row, 8192-token chunk): scores every key of the chunk; the histogram of key >> 12
+//           over the chunk's first 1024 keys sets the chunk's threshold bin theta_c (the highest
+//           bin whose tail holds well over those keys' share of K), and the keys in bins >=
+//           theta_c are compacted, in token order, into the chunk's candidate slots.
+//   final   one workgroup per row: the histogram of the candidates gives b1, the bin of the
+//           K-th largest candidate. If b1 >= theta_c for every chunk, every key of the row in
+//           a bin >= b1 is a candidate, so the K-th largest key of the row is in bin b1 and the
+//           exact selection runs on the candidates (a few thousand per row). Otherwise (a chunk
+//           holds far more than its share of the top) the workgroup rescores the row: an exact
+//           histogram first, then every key in bins >= the exact b1 is collected, so the
+//           result stays exact whatever the score distribution.
 #include "sa_index_dev.h"
 #include "sa_select_dev.h"
 
@@ -32,24 +30,24 @@ using namespace sel;
 
 constexpr int kFChunk = 8192;             // tokens per main-pass workgroup
 constexpr int kFBlocks = kFChunk / 64;    // 64-token blocks per chunk
-constexpr int kSampleBlocks = 64;         // sampled blocks per row (about)
 constexpr int kFinalNT = 1024;
+constexpr uint32_t kNoKey = 0xffffffffu;  // token outside the candidate range
 
 struct FusedWs {
-  uint32_t* hist1;  // [rows][4096]
-  int32_t* state;   // [rows][4]: theta (a key value), -
-  int32_t* ccount;  // [rows][chunks]
+  int32_t* ccount;  // [rows][chunks]: candidates kept by the chunk
+  int32_t* cth;     // [rows][chunks]: the chunk's threshold bin theta_c
   int2* cand;       // [rows][chunks][kFChunk]: (key, token)
 };
 
+__device__ __forceinline__ int64_t fused_cand_offset(int64_t rows, int chunks) {
+  return (2 * rows * chunks + 3) & ~(int64_t)3;  // int32 units; keeps cand 16-byte aligned
+}
+
 __device__ __forceinline__ FusedWs fused_ws(void* ws, int64_t rows, int chunks) {
   FusedWs w;
-  w.hist1 = static_cast<uint32_t*>(ws);
-  w.state = reinterpret_cast<int32_t*>(w.hist1 + rows * kBins);
-  w.ccount = w.state + rows * 4;
-  int64_t off = rows * (kBins + 4) + rows * chunks;
-  off = (off + 3) & ~(int64_t)3;
-  w.cand = reinterpret_cast<int2*>(static_cast<int32_t*>(ws) + off);
+  w.ccount = static_cast<int32_t*>(ws);
+  w.cth = w.ccount + rows * chunks;
+  w.cand = reinterpret_cast<int2*>(static_cast<int32_t*>(ws) + fused_cand_offset(rows, chunks));
   return w;
 }
 
@@ -80,72 +78,7 @@ __device__ __forceinline__ int64_t block_base(const KvView& kv, int b, int gi, i
   return ((phys * kv.num_idx_heads + gi) * kv.page_size + slot0) * (int64_t)D;
 }
 
-// ---------------------------------------------------------------------------------- sample
-template <int D>
-__global__ __launch_bounds__(kFinalNT) void k_fused_sample(KvView kv, const int8_t* __restrict__ q_idx,
-                                                           int q_tail, int top_k, void* ws,
-                                                           int chunks) {
-  constexpr int NT = kFinalNT;
-  __shared__ TopkShared<NT> sh;
-  const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const FusedWs w = fused_ws(ws, gridDim.x, chunks);
-  const FRow r = frow(kv, row, q_tail, top_k);
-  uint32_t* h1 = w.hist1 + row * kBins;
-  for (int j = threadIdx.x; j < kBins; j += NT) {
-    h1[j] = 0u;
-    sh.hist[j] = 0u;
-  }
-  if (threadIdx.x == 0) { sh.found_bin = 0; sh.found_above = 0; }
-  if (r.n <= top_k) return;  // uniform: the final pass lists every candidate
-  __syncthreads();
-  const v4i qf = *reinterpret_cast<const v4i*>(q_idx + (row * (int64_t)D) + lane_part<D>(lane) * 16);
-  const int n_blk = r.blk_last - r.blk_first + 1;
-  const int stride = max(1, n_blk / kSampleBlocks);
-  constexpr int SU = kSampleBlocks / (NT / 64);  // sampled blocks per wave, loads issued together
-  for (int j0 = wave * SU; j0 * stride < n_blk; j0 += (NT / 64) * SU) {
-    int64_t base[SU];
-    v4i kd[SU][Blk<D>::R];
-#pragma unroll
-    for (int u = 0; u < SU; ++u) {
-      const int j = j0 + u;
-      base[u] = (j * stride < n_blk) ? block_base<D>(kv, r.b, r.gi, r.blk_first + j * stride) : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < SU; ++u) {
-      if (base[u] >= 0) {
-        load_block<D>(kv.kidx_pool + base[u], lane, kd[u]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < Blk<D>::R; ++q) kd[u][q] = v4i{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < SU; ++u) {
-      const int s = to_token_order<D>(score_block<D>(qf, kd[u], lane), lane);
-      const int t = ((r.blk_first + (j0 + u) * stride) << 6) + lane;
-      if (base[u] >= 0 && t >= r.P && t <= r.pos) atomicAdd(&sh.hist[score_key(s) >> 12], 1u);
-    }
-  }
-  __syncthreads();
-  // total sampled keys, and the share of K they should hold above the threshold
-  int cnt = 0;
-  for (int j = threadIdx.x; j < kBins; j += NT) cnt += sh.hist[j];
-  int n_s;
-  block_incl_scan<NT>(cnt, sh.wave_tot, &n_s);
-  const float expect = (float)top_k * (float)n_s / (float)r.n;
-  const int target = (int)(2.f * expect + 4.f * sqrtf(expect) + 16.f);
-  int theta = 0;  // collect everything unless the sample supports a higher bin
-  if (target < n_s) {
-    find_bin<NT>(sh, target);
-    theta = sh.found_bin << 12;
-  }
-  if (threadIdx.x == 0) w.state[row * 4 + 0] = theta;
-}
-
-// ------------------------------------------------------------------------------------ main
-// Compacts, in token order, the keys of one 16-block slab with key >= theta. Wave w holds
+// Compacts, in token order, the keys of one 16-block slab that `keep` marks. Wave w holds
 // blocks u = 0..U-1 at slab positions w*U + u, with lane l holding token l of each block.
 template <int NW, int U>
 __device__ __forceinline__ int compact_slab(const uint32_t (&key)[U], const bool (&keep)[U],
@@ -180,31 +113,36 @@ __device__ __forceinline__ int compact_slab(const uint32_t (&key)[U], const bool
   return fill + total;
 }
 
+// ------------------------------------------------------------------------------------ main
 template <int D>
-__global__ __launch_bounds__(256) void k_fused_main(KvView kv, const int8_t* __restrict__ q_idx,
+__global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv, const int8_t* __restrict__ q_idx,
                                                     int q_tail, int top_k, void* ws, int chunks) {
-  constexpr int NW = 4;
-  constexpr int U = 4;  // blocks per wave per slab; a slab is NW * U = 16 blocks
-  __shared__ uint32_t h[kBins];
-  __shared__ int32_t wave_tot[NW];
+  constexpr int NT = 256;
+  constexpr int NW = NT / 64;
+  constexpr int U = 4;  // blocks per wave per slab; a slab is NW * U = 16 blocks (1024 tokens)
+  __shared__ TopkShared<NT> sh;
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const FusedWs w = fused_ws(ws, gridDim.y, chunks);
   const FRow r = frow(kv, row, q_tail, top_k);
-  if (r.n <= top_k) return;
+  if (r.n <= top_k) return;  // the final pass lists every candidate
   if (c * kFChunk > r.pos) {
-    if (threadIdx.x == 0) w.ccount[row * chunks + c] = 0;
+    if (tid == 0) {
+      w.ccount[row * chunks + c] = 0;
+      w.cth[row * chunks + c] = 0;
+    }
     return;
   }
   const v4i qf = *reinterpret_cast<const v4i*>(q_idx + (row * (int64_t)D) + lane_part<D>(lane) * 16);
-  const uint32_t theta = (uint32_t)w.state[row * 4 + 0];
-  for (int j = threadIdx.x; j < kBins; j += 256) h[j] = 0u;
+  for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
+  if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
   __syncthreads();
   int2* dst = w.cand + (row * chunks + c) * (int64_t)kFChunk;
-  int fill = 0;
-  for (int slab = 0; slab < kFBlocks / (NW * U); ++slab) {
+  // scores slab `slab` of the chunk: key, whether the token is a candidate, token index
+  auto score_slab = [&](int slab, uint32_t (&key)[U], bool (&in)[U], int (&tok)[U]) {
     const int blk0 = c * kFBlocks + slab * NW * U + wave * U;
     int64_t base[U];
 #pragma unroll
@@ -222,24 +160,51 @@ __global__ __launch_bounds__(256) void k_fused_main(KvView kv, const int8_t* __r
         for (int q = 0; q < Blk<D>::R; ++q) kd[u][q] = v4i{0, 0, 0, 0};
       }
     }
-    uint32_t key[U];
-    bool keep[U];
-    int tok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = to_token_order<D>(score_block<D>(qf, kd[u], lane), lane);
       tok[u] = ((blk0 + u) << 6) + lane;
-      const bool in = base[u] >= 0 && tok[u] >= r.P && tok[u] <= r.pos;
+      in[u] = base[u] >= 0 && tok[u] >= r.P && tok[u] <= r.pos;
       key[u] = score_key(s);
-      if (in) atomicAdd(&h[key[u] >> 12], 1u);
-      keep[u] = in && key[u] >= theta;
     }
-    fill = compact_slab<NW, U>(key, keep, tok, wave_tot, dst, fill);
+  };
+  uint32_t key[U];
+  bool in[U], keep[U];
+  int tok[U];
+  // The chunk's threshold from its first slab: the highest bin whose tail holds well over the
+  // slab's share of K (twice the expected count plus three standard deviations plus 8). Any
+  // value is safe: the final pass checks it and rescores the row if it was too high.
+  score_slab(0, key, in, tok);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (in[u]) atomicAdd(&sh.hist[key[u] >> 12], 1u);
+  __syncthreads();
+  uint32_t th = 0;
+  {
+    int cnt = 0;
+    for (int j = tid; j < kBins; j += NT) cnt += sh.hist[j];
+    int n_s;
+    block_incl_scan<NT>(cnt, sh.wave_tot, &n_s);
+    const float expect = (float)top_k * (float)n_s / (float)r.n;
+    const int target = (int)(2.f * expect + 3.f * sqrtf(expect) + 8.f);
+    if (n_s >= 256 && target < n_s) {  // short first slabs (row edges) keep everything
+      find_bin<NT>(sh, target);
+      th = (uint32_t)sh.found_bin;
+    }
   }
-  uint32_t* h1 = w.hist1 + row * kBins;
-  for (int j = threadIdx.x; j < kBins; j += 256)
-    if (h[j]) atomicAdd(&h1[j], h[j]);
-  if (threadIdx.x == 0) w.ccount[row * chunks + c] = fill;
+#pragma unroll
+  for (int u = 0; u < U; ++u) keep[u] = in[u] && (key[u] >> 12) >= th;
+  int fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, 0);
+  for (int slab = 1; slab < kFBlocks / (NW * U); ++slab) {
+    score_slab(slab, key, in, tok);
+#pragma unroll
+    for (int u = 0; u < U; ++u) keep[u] = in[u] && (key[u] >> 12) >= th;
+    fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, fill);
+  }
+  if (tid == 0) {
+    w.ccount[row * chunks + c] = fill;
+    w.cth[row * chunks + c] = (int32_t)th;
+  }
 }
 
 // ----------------------------------------------------------------------------------- final
@@ -251,6 +216,7 @@ __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_
   constexpr int NW = NT / 64;
   __shared__ TopkShared<NT> sh;
   __shared__ int32_t s_off[1025];
+  __shared__ int32_t s_thmax;
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,24 +231,48 @@ __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_
     for (int j = r.nf + m + tid; j < r.W; j += NT) out[j] = -1;
     return;
   }
-  const uint32_t* h1 = w.hist1 + row * kBins;
-  const uint32_t theta = (uint32_t)w.state[row * 4 + 0];
-  for (int j = tid; j < kBins; j += NT) sh.hist[j] = h1[j];
-  if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
+  const int32_t* cc = w.ccount + row * chunks;
+  const int32_t* cth = w.cth + row * chunks;
+  const int2* cand = w.cand + row * chunks * (int64_t)kFChunk;
+  for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
+  if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; s_thmax = 0; }
+  __syncthreads();
+  // highest chunk threshold, and the histogram of the candidates' high digit
+  if (tid < chunks) atomicMax(&s_thmax, cth[tid]);
+  for (int ch = 0; ch < chunks; ++ch) {
+    const int m = cc[ch];
+    for (int j = tid; j < m; j += NT) atomicAdd(&sh.hist[(uint32_t)cand[(int64_t)ch * kFChunk + j].x >> 12], 1u);
+  }
   __syncthreads();
   find_bin<NT>(sh, top_k);
-  const uint32_t b1 = (uint32_t)sh.found_bin;
-  const int above1 = sh.found_above;
-  if ((b1 << 12) < theta) {
-    // The provisional threshold excluded part of bin b1 or above: rescore the row and
-    // collect every key in bins >= b1, chunk by chunk, into the same slots.
+  uint32_t b1 = (uint32_t)sh.found_bin;
+  int above1 = sh.found_above;
+  if ((int)b1 < s_thmax) {
+    // Some chunk kept only bins above b1: the candidates may miss part of the top. Rescore
+    // the row: the exact histogram first, then every key in bins >= the exact b1.
     const v4i qf = *reinterpret_cast<const v4i*>(q_idx + (row * (int64_t)D) + lane_part<D>(lane) * 16);
-    for (int c = 0; c < chunks; ++c) {
-      int2* dst = w.cand + (row * chunks + c) * (int64_t)kFChunk;
+    for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
+    if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
+    __syncthreads();
+    for (int blk = r.blk_first + wave; blk <= r.blk_last; blk += NW) {
+      const int64_t base = block_base<D>(kv, r.b, r.gi, blk);
+      if (base < 0) continue;  // wave-uniform
+      v4i kd[Blk<D>::R];
+      load_block<D>(kv.kidx_pool + base, lane, kd);
+      const int s = to_token_order<D>(score_block<D>(qf, kd, lane), lane);
+      const int tok = (blk << 6) + lane;
+      if (tok >= r.P && tok <= r.pos) atomicAdd(&sh.hist[score_key(s) >> 12], 1u);
+    }
+    __syncthreads();
+    find_bin<NT>(sh, top_k);
+    b1 = (uint32_t)sh.found_bin;
+    above1 = sh.found_above;
+    for (int ch = 0; ch < chunks; ++ch) {
+      int2* dst = w.cand + (row * chunks + ch) * (int64_t)kFChunk;
       int fill = 0;
-      if (c * kFChunk <= r.pos) {
+      if (ch * kFChunk <= r.pos) {
         for (int slab = 0; slab < kFBlocks / NW; ++slab) {
-          const int blk = c * kFBlocks + slab * NW + wave;
+          const int blk = ch * kFBlocks + slab * NW + wave;
           const int64_t base =
               (blk >= r.blk_first && blk <= r.blk_last) ? block_base<D>(kv, r.b, r.gi, blk) : -1;
           v4i kd[1][Blk<D>::R];
@@ -299,14 +289,13 @@ __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_
           fill = compact_slab<NW, 1>(key, keep, tok, sh.wave_tot2, dst, fill);
         }
       }
-      if (tid == 0) w.ccount[row * chunks + c] = fill;
+      if (tid == 0) w.ccount[row * chunks + ch] = fill;
       __syncthreads();
     }
     __threadfence_block();
     __syncthreads();
   }
-  select_candidates<NT>(sh, s_off, w.cand + row * chunks * (int64_t)kFChunk, w.ccount + row * chunks,
-                        chunks, kFChunk, b1, above1, top_k, out + r.nf);
+  select_candidates<NT>(sh, s_off, cand, cc, chunks, kFChunk, b1, above1, top_k, out + r.nf);
 }
 
 template <int D>
@@ -315,8 +304,6 @@ hipError_t launch_d(const KvView& kv, const int8_t* q_idx, int q_tail, int top_k
   const int64_t rows = (int64_t)kv.batch * kv.num_idx_heads;
   const int chunks = (kv.max_seq_len + kFChunk - 1) / kFChunk;
   if (chunks > 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_fused_sample<D>, dim3((unsigned)rows), dim3(kFinalNT), 0, stream, kv, q_idx,
-                     q_tail, top_k, ws, chunks);
   hipLaunchKernelGGL(k_fused_main<D>, dim3(chunks, (unsigned)rows), dim3(256), 0, stream, kv, q_idx,
                      q_tail, top_k, ws, chunks);
   hipLaunchKernelGGL(k_fused_final<D>, dim3((unsigned)rows), dim3(kFinalNT), 0, stream, kv, q_idx,
@@ -335,7 +322,7 @@ bool fused_applies(const KvView& kv, int q_len) {
 size_t fused_workspace_bytes(const KvView& kv) {
   const int64_t rows = (int64_t)kv.batch * kv.num_idx_heads;
   const int64_t chunks = (kv.max_seq_len + kFChunk - 1) / kFChunk;
-  const int64_t head = (rows * (kBins + 4) + rows * chunks + 3) & ~(int64_t)3;
+  const int64_t head = (2 * rows * chunks + 3) & ~(int64_t)3;  // ccount, cth
   return (size_t)(head + rows * chunks * kFChunk * 2) * sizeof(int32_t);
 }
 

@@ -150,11 +150,11 @@ int32_t sparse_attn_topk(const sa_paged_kv* kv, const int32_t* scores, int64_t s
  *
  *   q_idx    int8  [batch][q_len][num_idx_heads][idx_dim]
  *   indices  int32 [batch][q_len][num_idx_heads][prefix_len + top_k]
- * For decode-shaped calls (q_len == 1, rows of >= 16384 candidates) it scores every key once,
- * keeps an exact histogram of the scores, and writes only the keys above a sampled
- * provisional threshold; the threshold is checked against the exact histogram and the row
- * is rescored if it was too high, so the result never depends on the sample. Other shapes
- * run the two-step path with the score rows held in the workspace.
+ * For decode-shaped calls (q_len == 1, rows of >= 16384 candidates) it scores every key once
+ * and writes only the keys above a per-chunk provisional threshold (taken from the chunk's
+ * first 1024 keys); the selection checks that no threshold could have dropped a selected key
+ * and rescores the row exactly if one could, so the result never depends on the thresholds.
+ * Other shapes run the two-step path with the score rows held in the workspace.
  * workspace: sparse_attn_index_topk_workspace_size(kv, q_len, top_k) bytes of device memory;
  * its contents on entry do not matter.
  */

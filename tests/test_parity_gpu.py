@@ -117,12 +117,33 @@ def test_fused_index_topk_matches(name):
     assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
 
 
-def test_fused_index_topk_rescore_fallback():
-    """Scores arranged so that an evenly spaced sample of blocks sees far more high scores
-    than the row holds: every 4th block starting at block 0 (the sampled ones for a
-    1024-block row) gets 24 blocks of maximal keys and everything else small random keys.
-    The sampled threshold then excludes part of the true top-K, and the exact rescore must
-    still produce the oracle's lists."""
+def test_fused_index_topk_concentrated_chunk_rescore():
+    """One 8192-token chunk holds most of the top: its first 1024 tokens get maximal keys
+    (so the chunk's threshold lands in their bin) and its next 1536 tokens keys one bin lower,
+    part of which belong to the top-K. The chunk drops those, the candidates' K-th largest bin
+    falls below its threshold, and the final pass must rescore the row exactly."""
+    w = W(batch=2, seq_len=65536, q_len=1, top_k=2048)
+    inp = make_inputs(w, seed=9, device="cpu")
+    inp.q_idx.fill_(2)
+    k = inp.kidx_pool
+    k.copy_(torch.randint(-20, 21, k.shape, generator=torch.Generator().manual_seed(1)).to(torch.int8))
+    table = inp.page_table
+    for b in range(w.batch):
+        for p in range(256, 272):       # chunk 2, first slab: score 2*127*64 = 16256
+            k[table[b, p]] = 127
+        for p in range(272, 296):       # next 24 blocks: score 2*64*64 = 8192, one bin lower
+            k[table[b, p]] = 64
+    inp = inp.to(DEV)
+    fused = run_gpu(inp, fused=True)
+    two = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.indices, two.indices)
+    assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
+
+
+def test_fused_index_topk_spread_maximal_blocks():
+    """24 blocks of maximal keys spread over the row (every 4th block pattern) among small
+    random keys: the lists must still equal the two-step path and the oracle."""
     w = W(batch=2, seq_len=65536, q_len=1, top_k=2048)
     inp = make_inputs(w, seed=9, device="cpu")
     inp.q_idx.fill_(1)
