@@ -234,20 +234,13 @@ __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_
   const int32_t* cc = w.ccount + row * chunks;
   const int32_t* cth = w.cth + row * chunks;
   const int2* cand = w.cand + row * chunks * (int64_t)kFChunk;
-  for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
-  if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; s_thmax = 0; }
+  if (tid == 0) s_thmax = 0;
   __syncthreads();
-  // highest chunk threshold, and the histogram of the candidates' high digit
-  if (tid < chunks) atomicMax(&s_thmax, cth[tid]);
-  for (int ch = 0; ch < chunks; ++ch) {
-    const int m = cc[ch];
-    for (int j = tid; j < m; j += NT) atomicAdd(&sh.hist[(uint32_t)cand[(int64_t)ch * kFChunk + j].x >> 12], 1u);
-  }
+  if (tid < chunks) atomicMax(&s_thmax, cth[tid]);  // the highest chunk threshold
   __syncthreads();
-  find_bin<NT>(sh, top_k);
-  uint32_t b1 = (uint32_t)sh.found_bin;
-  int above1 = sh.found_above;
-  if ((int)b1 < s_thmax) {
+  // b1 from the candidates, valid when no chunk threshold lies above it
+  if (!select_candidates<NT>(sh, s_off, cand, cc, chunks, kFChunk, 0u, 0, top_k, out + r.nf,
+                             s_thmax)) {
     // Some chunk kept only bins above b1: the candidates may miss part of the top. Rescore
     // the row: the exact histogram first, then every key in bins >= the exact b1.
     const v4i qf = *reinterpret_cast<const v4i*>(q_idx + (row * (int64_t)D) + lane_part<D>(lane) * 16);
@@ -265,8 +258,8 @@ __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_
     }
     __syncthreads();
     find_bin<NT>(sh, top_k);
-    b1 = (uint32_t)sh.found_bin;
-    above1 = sh.found_above;
+    const uint32_t b1 = (uint32_t)sh.found_bin;
+    const int above1 = sh.found_above;
     for (int ch = 0; ch < chunks; ++ch) {
       int2* dst = w.cand + (row * chunks + ch) * (int64_t)kFChunk;
       int fill = 0;
@@ -294,8 +287,8 @@ __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_
     }
     __threadfence_block();
     __syncthreads();
+    select_candidates<NT>(sh, s_off, cand, cc, chunks, kFChunk, b1, above1, top_k, out + r.nf);
   }
-  select_candidates<NT>(sh, s_off, cand, cc, chunks, kFChunk, b1, above1, top_k, out + r.nf);
 }
 
 template <int D>

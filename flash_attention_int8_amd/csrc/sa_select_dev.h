@@ -97,12 +97,18 @@ __device__ __forceinline__ int block_excl_scan(int v, int32_t* wave_tot, int* to
 // the waves gives every segment its output offset and its number of earlier keys == tau,
 // and each wave then writes its taken keys in order. Two barriers instead of two
 // workgroup scans per 1024 candidates.
+//
+// With check_bin >= 0, b1 and above1 are not given: they are taken from the candidates' own
+// histogram, which equals the row's for every bin >= check_bin. If b1 < check_bin that is not
+// enough to know the row's K-th largest key: nothing is written and the call returns false
+// (uniformly). Otherwise, and always with check_bin < 0, it returns true.
 template <int NT>
-__device__ __forceinline__ void select_candidates(TopkShared<NT>& sh, int32_t* s_off,
+__device__ __forceinline__ bool select_candidates(TopkShared<NT>& sh, int32_t* s_off,
                                                   const int2* __restrict__ cand,
                                                   const int32_t* __restrict__ ccount, int chunks,
                                                   int chunk_cap, uint32_t b1, int above1,
-                                                  int top_k, int32_t* __restrict__ out) {
+                                                  int top_k, int32_t* __restrict__ out,
+                                                  int check_bin = -1) {
   constexpr int NW = NT / 64;
   constexpr int kPer = 8;  // candidates per lane loaded together
   const int tid = threadIdx.x;
@@ -138,6 +144,19 @@ __device__ __forceinline__ void select_candidates(TopkShared<NT>& sh, int32_t* s
     for (int k = 0; k < kPer; ++k) {
       const int j = seg_begin + k * 64 + lane;
       e[k] = (j < total) ? fetch(j) : make_int2(0, 0);
+    }
+    if (check_bin >= 0) {  // b1 from the candidates' high digits
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        if (seg_begin + k * 64 + lane < total) atomicAdd(&sh.hist[(uint32_t)e[k].x >> 12], 1u);
+      __syncthreads();
+      find_bin<NT>(sh, top_k);
+      b1 = (uint32_t)sh.found_bin;
+      above1 = sh.found_above;
+      if ((int)b1 < check_bin) return false;
+      for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
+      if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
+      __syncthreads();
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
@@ -180,9 +199,30 @@ __device__ __forceinline__ void select_candidates(TopkShared<NT>& sh, int32_t* s
       slot += __popcll(take_mask);
       eq_seen += __popcll(eq_mask);
     }
-    return;
+    return true;
   }
-  // General path (more candidates than the workgroup holds at once): three streamed passes.
+  // General path (more candidates than the workgroup holds at once): streamed passes.
+  if (check_bin >= 0) {  // b1 from the candidates' high digits
+    for (int base = 0; base < total; base += NT * kPer) {
+      int2 e[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int j = base + k * NT + tid;
+        e[k] = (j < total) ? fetch(j) : make_int2(0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        if (base + k * NT + tid < total) atomicAdd(&sh.hist[(uint32_t)e[k].x >> 12], 1u);
+    }
+    __syncthreads();
+    find_bin<NT>(sh, top_k);
+    b1 = (uint32_t)sh.found_bin;
+    above1 = sh.found_above;
+    if ((int)b1 < check_bin) return false;
+    for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
+    if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
+    __syncthreads();
+  }
   // exact threshold inside bin b1
   for (int base = 0; base < total; base += NT * kPer) {
     int2 e[kPer];
@@ -256,6 +296,7 @@ __device__ __forceinline__ void select_candidates(TopkShared<NT>& sh, int32_t* s
       eq_seen += __popcll(eq_mask);
     }
   }
+  return true;
 }
 
 }  // namespace sel
