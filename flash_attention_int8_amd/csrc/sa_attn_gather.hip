@@ -49,8 +49,15 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
 }
 
 __device__ __forceinline__ float safe_scale(float m_old, float m_new) {
-  return (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
+  return (m_old == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_old - m_new);
 }
+
+// The running maximum used in the exponent moves only when a key's score exceeds it by more
+// than 2^kRescaleLog2 (exp2 units): P stays below 2^kRescaleLog2, far inside bf16 and fp32
+// range, and the result is unchanged because the sum and the V accumulator use the same
+// maximum. Rescaling the accumulator then happens on a few keys per list instead of every
+// sub-batch.
+constexpr float kRescaleLog2 = 8.f;
 
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void k_attn_gather(KvView kv, const uint16_t* __restrict__ q,
@@ -162,19 +169,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_gather(KvView kv, const uint16_
             s[u][h] = group_sum_f<LPK>(d) * qscale;
           }
         }
+        float mb[G];
+        bool grow = false;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          float mb = m[h];
+          mb[h] = m[h];
 #pragma unroll
-          for (int u = 0; u < kSB; ++u) mb = cok[u0 + u] ? fmaxf(mb, s[u][h]) : mb;
-          const float sc = safe_scale(m[h], mb);
-          l[h] *= sc;
+          for (int u = 0; u < kSB; ++u) mb[h] = cok[u0 + u] ? fmaxf(mb[h], s[u][h]) : mb[h];
+          grow = grow || (mb[h] > m[h] + kRescaleLog2);  // false while both are -inf
+        }
+        if (__any(grow)) {  // wave-uniform; rare after the first keys of a list
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] *= sc;
-          m[h] = mb;
+          for (int h = 0; h < G; ++h) {
+            const float mn = (mb[h] > m[h] + kRescaleLog2) ? mb[h] : m[h];
+            const float sc = safe_scale(m[h], mn);
+            l[h] *= sc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] *= sc;
+            m[h] = mn;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
 #pragma unroll
           for (int u = 0; u < kSB; ++u) {
-            s[u][h] = cok[u0 + u] ? exp2f(s[u][h] - mb) : 0.f;
+            s[u][h] = cok[u0 + u] ? __builtin_amdgcn_exp2f(s[u][h] - m[h]) : 0.f;
             l[h] += s[u][h];
           }
         }
