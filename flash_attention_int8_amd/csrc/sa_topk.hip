@@ -25,16 +25,32 @@ namespace {
 using namespace sel;
 
 
-// STAGE > 0: the row (at most STAGE candidates) is read once, with every thread's loads in
-// flight together, into LDS as 24-bit keys while the high-digit histogram is built; the low
-// digit and the ordered sweep then read LDS. STAGE == 0: all three passes read the scores.
-template <int NT, int STAGE>
-__global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __restrict__ scores,
-                                                 int64_t row_stride, int q_len, int q_tail,
-                                                 int top_k, int32_t* __restrict__ indices) {
+// Rows of at most NT * PER candidates are held in registers: candidate j (token P + j) sits
+// in thread j % NT, slot j / NT, so the row is read once with every thread's PER loads in
+// flight together. A strided sample of 1024 keys sets a provisional threshold bin theta (its
+// tail holds 1.5 times the sampled share of K plus three standard deviations plus 8); the keys
+// in bins >= theta are compacted, in token order, into a short list in LDS, and the exact radix
+// select runs on that list. The list is enough when it holds at least K keys and the K-th
+// largest of them lies in a bin >= theta: then every key of the row in a bin >= b1 is on it.
+// Otherwise (or when the list would not fit) the exact select runs over the registers, so the
+// result never depends on the sample. Token order over (slot u, wave, lane) is u-major, so
+// every ordered write takes per-(u, wave) counts and one workgroup scan.
+template <int NT, int PER, int CAND>
+__global__ __launch_bounds__(NT) void k_topk_row_reg(KvView kv, const int32_t* __restrict__ scores,
+                                                     int64_t row_stride, int q_len, int q_tail,
+                                                     int top_k, int32_t* __restrict__ indices) {
+  constexpr int NW = NT / 64;
+  constexpr int kSample = 1024;
+  static_assert(PER * NW <= NT, "one scan entry per thread");
   __shared__ TopkShared<NT> sh;
-  __shared__ uint32_t staged[STAGE > 0 ? STAGE : 1];
+  __shared__ int32_t s_cnt[2][PER * NW];   // per-(u, wave) counts, then exclusive offsets
+  __shared__ uint32_t l_key[CAND];         // short list: keys ...
+  __shared__ uint16_t l_pos[CAND];         // ... and positions j, token order
+  __shared__ int32_t s_total[2];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t row = blockIdx.x;
   const int64_t bi = row / kv.num_idx_heads;
   const int b = (int)(bi / q_len);
@@ -54,71 +70,228 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
     for (int j = nf + m + tid; j < W; j += NT) out[j] = -1;
     return;
   }
-  // key of candidate j (token P + j)
-  auto key_at = [&](int j) -> uint32_t {
-    if constexpr (STAGE > 0) return staged[j];
-    else return score_key(srow[P + j]);
+  uint32_t v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int j = u * NT + tid;
+    v[u] = j < n ? score_key(srow[P + j]) : 0u;
+  }
+  auto clear_hist = [&]() {
+    __syncthreads();  // every wave has read the previous histogram and found_bin/found_above
+    for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
+    if (tid == 0) {
+      sh.found_bin = 0;
+      sh.found_above = 0;
+    }
+    __syncthreads();
+  };
+  // Per-(u, wave) counts of up to two predicates are written to s_cnt[k][u * NW + wave] (by
+  // lane 0); scan_counts turns them, in place, into exclusive offsets in token order and
+  // leaves the totals in s_total.
+  auto scan_counts = [&]() {
+    __syncthreads();
+    const int x0 = tid < PER * NW ? s_cnt[0][tid] : 0;
+    const int x1 = tid < PER * NW ? s_cnt[1][tid] : 0;
+    int t0, t1;
+    const int e0 = block_excl_scan<NT>(x0, sh.wave_tot, &t0);
+    const int e1 = block_excl_scan<NT>(x1, sh.wave_tot2, &t1);
+    if (tid < PER * NW) {
+      s_cnt[0][tid] = e0;
+      s_cnt[1][tid] = e1;
+    }
+    if (tid == 0) {
+      s_total[0] = t0;
+      s_total[1] = t1;
+    }
+    __syncthreads();
+  };
+  // Ordered output from the registers: keys > tau, and the first `need` keys == tau.
+  auto emit_regs = [&](uint32_t tau, int need) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = u * NT + tid;
+      const int cg = __popcll(__ballot(j < n && v[u] > tau));
+      const int ce = __popcll(__ballot(j < n && v[u] == tau));
+      if (lane == 0) {
+        s_cnt[0][u * NW + wv] = cg;
+        s_cnt[1][u * NW + wv] = ce;
+      }
+    }
+    scan_counts();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = u * NT + tid;
+      const bool gt = j < n && v[u] > tau;
+      const bool eq = j < n && v[u] == tau;
+      const int gb = s_cnt[0][u * NW + wv] + __popcll(__ballot(gt) & lt_mask);
+      const int eb = s_cnt[1][u * NW + wv] + __popcll(__ballot(eq) & lt_mask);
+      if (gt || (eq && eb < need)) out[nf + gb + min(eb, need)] = P + j;
+    }
   };
 
-  // pass 1: high digit
+  // provisional threshold from a strided sample (re-read from the row, now in the caches)
+  clear_hist();
+  const int ns = min(kSample, n);
+  for (int s = tid; s < ns; s += NT)
+    atomicAdd(&sh.hist[score_key(srow[P + (int)((int64_t)s * n / ns)]) >> 12], 1u);
+  __syncthreads();
+  const float expect = (float)top_k * (float)ns / (float)n;
+  const int target = (int)(1.5f * expect + 3.f * sqrtf(expect) + 8.f);
+  uint32_t th = 0;
+  if (target < ns) {
+    find_bin<NT>(sh, target);
+    th = (uint32_t)sh.found_bin;
+  }
+  // short list of the keys in bins >= th
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = __popcll(__ballot(u * NT + tid < n && (v[u] >> 12) >= th));
+    if (lane == 0) {
+      s_cnt[0][u * NW + wv] = c;
+      s_cnt[1][u * NW + wv] = 0;
+    }
+  }
+  scan_counts();
+  const int m = s_total[0];
+  bool ok = m >= top_k && m <= CAND;
+  if (ok) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = u * NT + tid;
+      const bool keep = j < n && (v[u] >> 12) >= th;
+      const int o = s_cnt[0][u * NW + wv] + __popcll(__ballot(keep) & lt_mask);
+      if (keep) {
+        l_key[o] = v[u];
+        l_pos[o] = (uint16_t)j;
+      }
+    }
+    clear_hist();  // its barriers also complete the list
+    for (int c = tid; c < m; c += NT) atomicAdd(&sh.hist[l_key[c] >> 12], 1u);
+    __syncthreads();
+    find_bin<NT>(sh, top_k);
+    ok = sh.found_bin >= (int)th;  // uniform
+  }
+  if (ok) {
+    const uint32_t b1 = sh.found_bin;
+    const int above1 = sh.found_above;
+    clear_hist();
+    for (int c = tid; c < m; c += NT)
+      if ((l_key[c] >> 12) == b1) atomicAdd(&sh.hist[l_key[c] & 0xfff], 1u);
+    __syncthreads();
+    find_bin<NT>(sh, top_k - above1);
+    const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
+    const int need = top_k - above1 - sh.found_above;
+    // ordered output over the list: wave segments, counts by ballot, one scan over the waves
+    const int seg = ((m + NW * 64 - 1) / (NW * 64)) * 64;
+    const int s0 = wv * seg, s1 = min(m, s0 + seg);
+    int gt_w = 0, eq_w = 0;
+    for (int c0 = s0; c0 < s1; c0 += 64) {
+      const int c = c0 + lane;
+      const uint32_t key = c < s1 ? l_key[c] : 0u;
+      gt_w += __popcll(__ballot(c < s1 && key > tau));
+      eq_w += __popcll(__ballot(c < s1 && key == tau));
+    }
+    if (lane == 0) {
+      sh.wave_tot[wv] = gt_w;
+      sh.wave_tot2[wv] = eq_w;
+    }
+    __syncthreads();
+    int gt_run = 0, eq_run = 0;
+    for (int w = 0; w < wv; ++w) {
+      gt_run += sh.wave_tot[w];
+      eq_run += sh.wave_tot2[w];
+    }
+    for (int c0 = s0; c0 < s1 && gt_run + min(eq_run, need) < top_k; c0 += 64) {
+      const int c = c0 + lane;
+      const uint32_t key = c < s1 ? l_key[c] : 0u;
+      const bool gt = c < s1 && key > tau;
+      const bool eq = c < s1 && key == tau;
+      const uint64_t gm = __ballot(gt), em = __ballot(eq);
+      const int gt_before = gt_run + __popcll(gm & lt_mask);
+      const int eq_before = eq_run + __popcll(em & lt_mask);
+      if (gt || (eq && eq_before < need)) out[nf + gt_before + min(eq_before, need)] = P + (int)l_pos[c];
+      gt_run += __popcll(gm);
+      eq_run += __popcll(em);
+    }
+    return;
+  }
+  // exact select over the registers
+  clear_hist();
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (u * NT + tid < n) atomicAdd(&sh.hist[v[u] >> 12], 1u);
+  __syncthreads();
+  find_bin<NT>(sh, top_k);
+  const uint32_t b1 = sh.found_bin;
+  const int above1 = sh.found_above;
+  clear_hist();
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (u * NT + tid < n && (v[u] >> 12) == b1) atomicAdd(&sh.hist[v[u] & 0xfff], 1u);
+  __syncthreads();
+  find_bin<NT>(sh, top_k - above1);
+  const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
+  const int need = top_k - above1 - sh.found_above;
+  emit_regs(tau, need);
+}
+
+// Rows longer than the register path holds: three passes over the scores in global memory
+// (high digit, low digit within bin b1, ordered compaction by wave segments).
+template <int NT>
+__global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __restrict__ scores,
+                                                 int64_t row_stride, int q_len, int q_tail,
+                                                 int top_k, int32_t* __restrict__ indices) {
+  constexpr int NW = NT / 64;
+  __shared__ TopkShared<NT> sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t row = blockIdx.x;
+  const int64_t bi = row / kv.num_idx_heads;
+  const int b = (int)(bi / q_len);
+  const int i = (int)(bi - (int64_t)b * q_len);
+  const int P = kv.prefix_len;
+  const int W = P + top_k;
+  const int pos = min(kv.seq_lens[b], kv.max_seq_len) - q_tail + i;
+  const int32_t* srow = scores + row * row_stride;
+  int32_t* out = indices + row * W;
+  const int nf = pos < 0 ? 0 : min(P, pos + 1);
+  for (int j = tid; j < nf; j += NT) out[j] = j;
+  const int n = pos - P + 1;
+  if (n <= top_k) {
+    const int m = n > 0 ? n : 0;
+    for (int j = tid; j < m; j += NT) out[nf + j] = P + j;
+    for (int j = nf + m + tid; j < W; j += NT) out[j] = -1;
+    return;
+  }
   if (tid == 0) {
     sh.found_bin = 0;
     sh.found_above = 0;
   }
   for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
   __syncthreads();
-  if constexpr (STAGE > 0) {
-    constexpr int PER = STAGE / NT;
-    uint32_t v[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int j = u * NT + tid;
-      v[u] = j < n ? score_key(srow[P + j]) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int j = u * NT + tid;
-      if (j < n) {
-        staged[j] = v[u];
-        atomicAdd(&sh.hist[v[u] >> 12], 1u);
-      }
-    }
-  } else {
-    for (int j = tid; j < n; j += NT) atomicAdd(&sh.hist[key_at(j) >> 12], 1u);
-  }
+  for (int j = tid; j < n; j += NT) atomicAdd(&sh.hist[score_key(srow[P + j]) >> 12], 1u);
   __syncthreads();
   find_bin<NT>(sh, top_k);
   const uint32_t b1 = sh.found_bin;
   const int above1 = sh.found_above;
-
-  // pass 2: low digit within bin b1
   for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
   __syncthreads();
   for (int j = tid; j < n; j += NT) {
-    const uint32_t key = key_at(j);
+    const uint32_t key = score_key(srow[P + j]);
     if ((key >> 12) == b1) atomicAdd(&sh.hist[key & 0xfff], 1u);
   }
   __syncthreads();
   find_bin<NT>(sh, top_k - above1);
   const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
-  const int need = top_k - above1 - sh.found_above;  // keys equal to tau that are taken
-
-  // pass 3: ordered compaction. Wave w owns the contiguous segment [w*seg, (w+1)*seg) of the
-  // candidates. It counts its keys > tau and == tau (ballots), one exclusive scan over the
-  // waves gives every wave the counts before its segment, and a second sweep places each
-  // taken token at slot = (keys > tau before it) + min(keys == tau before it, need): the list
-  // comes out in token order with one barrier, and no atomic decides any order.
-  constexpr int NW = NT / 64;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int need = top_k - above1 - sh.found_above;
   const int seg = ((n + NW * 64 - 1) / (NW * 64)) * 64;
-  const int s0 = wv * seg;
-  const int s1 = min(n, s0 + seg);
+  const int s0 = wv * seg, s1 = min(n, s0 + seg);
   int gt_w = 0, eq_w = 0;
   for (int j0 = s0; j0 < s1; j0 += 64) {
     const int j = j0 + lane;
-    const uint32_t key = j < s1 ? key_at(j) : 0u;
+    const uint32_t key = j < s1 ? score_key(srow[P + j]) : 0u;
     gt_w += __popcll(__ballot(j < s1 && key > tau));
     eq_w += __popcll(__ballot(j < s1 && key == tau));
   }
@@ -134,7 +307,7 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
   }
   for (int j0 = s0; j0 < s1 && gt_run + min(eq_run, need) < top_k; j0 += 64) {
     const int j = j0 + lane;
-    const uint32_t key = j < s1 ? key_at(j) : 0u;
+    const uint32_t key = j < s1 ? score_key(srow[P + j]) : 0u;
     const bool gt = j < s1 && key > tau;
     const bool eq = j < s1 && key == tau;
     const uint64_t gm = __ballot(gt), em = __ballot(eq);
@@ -363,16 +536,16 @@ hipError_t launch_topk(const KvView& kv, const int32_t* scores, int64_t row_stri
                        q_tail, top_k, ws, chunks, indices);
     return hipGetLastError();
   }
-  // rows that fit are staged in LDS (one read of the scores); longer ones take three passes
+  // rows that fit are held in registers (one read of the scores); longer ones take three passes
   if (longest <= 16384) {
-    hipLaunchKernelGGL((k_topk_row<512, 16384>), dim3((unsigned)rows), dim3(512), 0, stream, kv,
-                       scores, row_stride, q_len, q_tail, top_k, indices);
+    hipLaunchKernelGGL((k_topk_row_reg<512, 32, 4096>), dim3((unsigned)rows), dim3(512), 0, stream,
+                       kv, scores, row_stride, q_len, q_tail, top_k, indices);
   } else if (longest <= 32768) {
-    hipLaunchKernelGGL((k_topk_row<1024, 32768>), dim3((unsigned)rows), dim3(1024), 0, stream, kv,
-                       scores, row_stride, q_len, q_tail, top_k, indices);
+    hipLaunchKernelGGL((k_topk_row_reg<1024, 32, 8192>), dim3((unsigned)rows), dim3(1024), 0, stream,
+                       kv, scores, row_stride, q_len, q_tail, top_k, indices);
   } else {
-    hipLaunchKernelGGL((k_topk_row<1024, 0>), dim3((unsigned)rows), dim3(1024), 0, stream, kv,
-                       scores, row_stride, q_len, q_tail, top_k, indices);
+    hipLaunchKernelGGL((k_topk_row<1024>), dim3((unsigned)rows), dim3(1024), 0, stream, kv, scores,
+                       row_stride, q_len, q_tail, top_k, indices);
   }
   return hipGetLastError();
 }

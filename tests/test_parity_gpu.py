@@ -163,12 +163,14 @@ def test_fused_index_topk_spread_maximal_blocks():
 
 @pytest.mark.parametrize("seq_len,q_len,prefix,vals", [
     (16000, 40, 3, 100000),     # rows of <= 16384 candidates: staged in LDS, 512 threads
-    (30000, 24, 0, 3),          # <= 32768 candidates, heavy ties: staged in LDS, 1024 threads
+    (30000, 24, 0, 3),          # <= 32768, every key in one bin: the sampled list overflows
+    (30000, 24, 1, -1),         # <= 32768, keys 4096*k + {0,1,2}: short list, ties at tau
     (33005, 2050, 5, 40000),    # > 32768 candidates and > 2048 rows: three passes over HBM
 ])
 def test_topk_row_paths(seq_len, q_len, prefix, vals):
-    """Stand-alone top-K on score rows written directly (random ints in [-vals, vals)), for
-    each single-row selection path; sampled rows must equal the oracle's index lists."""
+    """Stand-alone top-K on score rows written directly (random ints in [-vals, vals), or for
+    vals < 0 multiples of 4096 in [-20, 20) plus 0..2), for each single-row selection path and
+    both outcomes of the sampled short list; sampled rows must equal the oracle's lists."""
     top_k = 1000
     _banner(f"topk rows seq_len={seq_len} q_len={q_len} P={prefix} vals={vals}")
     w = W(num_q_heads=1, num_kv_heads=1, head_dim=64, idx_dim=32, seq_len=seq_len, q_len=q_len,
@@ -177,7 +179,11 @@ def test_topk_row_paths(seq_len, q_len, prefix, vals):
     kv = make_kv(inp)
     gen = torch.Generator().manual_seed(22)
     stride = (seq_len + 3) & ~3  # the ABI takes row strides in multiples of 4 scores
-    scores = torch.randint(-vals, vals, (1, q_len, 1, stride), generator=gen, dtype=torch.int32)
+    if vals > 0:
+        scores = torch.randint(-vals, vals, (1, q_len, 1, stride), generator=gen, dtype=torch.int32)
+    else:
+        scores = (4096 * torch.randint(-20, 20, (1, q_len, 1, stride), generator=gen, dtype=torch.int32)
+                  + torch.randint(0, 3, (1, q_len, 1, stride), generator=gen, dtype=torch.int32))
     got = fa.topk(kv, scores.to(DEV), q_len, q_len, top_k).cpu().numpy()
     rows = range(q_len) if q_len <= 64 else np.linspace(0, q_len - 1, 48).astype(int)
     host = scores.numpy()
