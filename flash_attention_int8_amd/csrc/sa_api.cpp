@@ -188,8 +188,8 @@ int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_
   if (group != 1 && group != 2 && group != 4 && group != 8) return SA_ERR_UNSUPPORTED;
   if (index_width < 1) return SA_ERR_SHAPE;
   if (!aligned16(indices)) return SA_ERR_ALIGN;
-  return hip_status(sa::launch_attn_gather(v, q, num_q_heads, q_len, q_tail, indices, index_width,
-                                           sm_scale, 1, nullptr, out, lse, s));
+  return hip_status(sa::launch_attn_sparse_mfma(v, q, num_q_heads, q_len, q_tail, indices,
+                                                index_width, sm_scale, out, lse, s));
 }
 
 size_t sparse_attn_decode_workspace_size(const sa_paged_kv* kv, int32_t num_q_heads,

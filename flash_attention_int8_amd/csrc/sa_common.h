@@ -115,6 +115,9 @@ bool fused_applies(const KvView& kv, int q_len);
 size_t fused_workspace_bytes(const KvView& kv);
 hipError_t launch_index_topk_fused(const KvView& kv, const int8_t* q_idx, int q_tail, int top_k,
                                    int32_t* indices, void* ws, hipStream_t stream);
+hipError_t launch_attn_sparse_mfma(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
+                                   int q_tail, const int32_t* indices, int index_width,
+                                   float sm_scale, uint16_t* out, float* lse, hipStream_t stream);
 hipError_t launch_attn_dense(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                              int q_tail, float sm_scale, uint16_t* out, float* lse,
                              hipStream_t stream);
