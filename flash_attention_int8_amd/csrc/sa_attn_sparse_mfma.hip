@@ -53,7 +53,7 @@ struct SparseShared {
 };
 
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_attn_sparse_mfma(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_attn_sparse_mfma(
     KvView kv, const uint16_t* __restrict__ q, int num_q_heads, int q_len, int q_tail,
     const int32_t* __restrict__ indices, int W, int top_k, float qscale,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -104,18 +104,22 @@ __global__ __launch_bounds__(64) void k_attn_sparse_mfma(
   for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
 
-  // list entries of tile t -> pool rows (lanes 0..31), and the tile's valid-key mask
-  auto resolve = [&](int t, int slot) -> uint32_t {
-    int rid = -1;
-    if (lane < TK) {
-      const int e = t * TK + lane;
-      const int tok = e < w_valid ? ilist[e] : -1;
-      if (tok >= 0 && tok <= pos) {
-        const int64_t ph = phys_page(kv, b, tok);
-        if (ph >= 0) rid = (int)(ph * kv.page_size + (tok & (kv.page_size - 1)));
-      }
-      sh.rid[slot][lane] = rid;
-    }
+  // List entry -> pool row in three steps, each issued an iteration before its result is used
+  // (lanes 0..31 hold the tile's 32 entries): the entry (token), its page-table entry, and the
+  // row id written to LDS with the tile's valid-key mask.
+  const int32_t* ptab = kv.page_table + (int64_t)b * kv.max_pages_per_seq;
+  auto fetch_tok = [&](int t) -> int {
+    const int e = t * TK + lane;
+    return (lane < TK && e < w_valid) ? ilist[e] : -1;
+  };
+  auto tok_ok = [&](int tok) {
+    return tok >= 0 && tok <= pos && (tok >> kv.page_shift) < kv.max_pages_per_seq;
+  };
+  auto fetch_page = [&](int tok) -> int { return tok_ok(tok) ? ptab[tok >> kv.page_shift] : -1; };
+  auto finish = [&](int tok, int pt, int slot) -> uint32_t {
+    const bool ok = tok_ok(tok) && pt >= 0 && pt < kv.num_pages;
+    const int rid = ok ? pt * kv.page_size + (tok & (kv.page_size - 1)) : -1;
+    if (lane < TK) sh.rid[slot][lane] = rid;
     return (uint32_t)__ballot(lane < TK && rid >= 0);
   };
   auto row_off = [&](int rid) -> int64_t {
@@ -148,36 +152,35 @@ __global__ __launch_bounds__(64) void k_attn_sparse_mfma(
   };
 
   uint32_t vmask = 0, vmask_next = 0;
-  Frag8 kc[2][KS];  // K operands of the tile being computed
+  int tok_n2 = -1;  // list entries of tile t+2
   if (n_tiles > 0) {
-    vmask = resolve(0, 0);
+    int tk = fetch_tok(0);
+    vmask = finish(tk, fetch_page(tk), 0);
+    tk = fetch_tok(1);
+    vmask_next = finish(tk, fetch_page(tk), 1);
+    tok_n2 = fetch_tok(2);
     __syncthreads();
     load_tile(0);
-    if (n_tiles > 1) vmask_next = resolve(1, 1);
     store_v();
     __syncthreads();
   }
   const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
   for (int t = 0; t < n_tiles; ++t) {
     const int cur = t & 1, nxt = cur ^ 1;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kc[hh][ks] = kf[hh][ks];
-    // rows of tile t+1 in flight while tile t is computed; tile t+2's list entries resolved
-    if (t + 1 < n_tiles) load_tile(nxt);
-    uint32_t vmask_after = 0;
-    if (t + 2 < n_tiles) vmask_after = resolve(t + 2, cur);
-
-    // S^T for the two 16-key halves of the tile
+    // S^T for the two 16-key halves of the tile (its K operands were loaded an iteration ago)
     f32x4 s[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[hh][ks].v, qf[ks].v, s[hh], 0, 0, 0);
+        s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[hh][ks].v, qf[ks].v, s[hh], 0, 0, 0);
     }
+    // rows of tile t+1, page entries of tile t+2 and list entries of tile t+3 in flight while
+    // the rest of tile t is computed (the K operand registers are free once S^T is issued)
+    if (t + 1 < n_tiles) load_tile(nxt);
+    const int tok_n3 = fetch_tok(t + 3);
+    const int pt_n2 = fetch_page(tok_n2);
     // keys without a row (padding, past the causal end, missing page) are masked
     float mx = -INFINITY;
 #pragma unroll
@@ -231,11 +234,14 @@ __global__ __launch_bounds__(64) void k_attn_sparse_mfma(
           (__attribute__((address_space(3))) v4s*)(&sh.v[16 + vrow][vcol]));
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, pf.v, o[nb], 0, 0, 0);
     }
+    // tile t+2's rows go to the slot tile t used (its rows were loaded an iteration ago)
+    const uint32_t vmask_after = finish(tok_n2, pt_n2, cur);
+    tok_n2 = tok_n3;
     if (t + 1 < n_tiles) {
       __syncthreads();  // the tile's LDS reads are done
       store_v();
-      __syncthreads();
     }
+    __syncthreads();
     vmask = vmask_next;
     vmask_next = vmask_after;
   }
