@@ -72,7 +72,7 @@ def index_kernel_bytes(w, two_step):
 
 def kernel_ms(args, kv, inp, w, scores, stride, indices, ws, ws_n, evict):
     """Average duration of the dominant launch, timed with events on its stream: the
-    stand-alone indexer, or the fused selection call (its sample, main and final kernels;
+    stand-alone indexer, or the fused selection call (its main and final kernels;
     the main pass streams every indexer key and carries almost all of the time).
     """
     import torch
@@ -381,7 +381,7 @@ def main():
     sb = step_bytes(w)
     # dominant kernel: the indexer's key stream (fused main pass, or the stand-alone indexer)
     dom_name = ("k_index_stream<64> (indexer)" if args.two_step else
-                "sparse_attn_index_topk (k_fused_sample + k_fused_main + k_fused_final)")
+                "sparse_attn_index_topk (k_fused_main + k_fused_final)")
     ib = index_kernel_bytes(w, args.two_step)
     ms_dom = kernel_ms(args, kv, inp, w, scores, stride, indices, fu_ws, fu_ws_n, evict)
     achieved = ib / (ms_dom * 1e-3) / 1e9
