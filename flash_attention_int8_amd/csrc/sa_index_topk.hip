@@ -31,7 +31,6 @@ using namespace sel;
 constexpr int kFChunk = 8192;             // tokens per main-pass workgroup
 constexpr int kFBlocks = kFChunk / 64;    // 64-token blocks per chunk
 constexpr int kFinalNT = 1024;
-constexpr uint32_t kNoKey = 0xffffffffu;  // token outside the candidate range
 
 struct FusedWs {
   int32_t* ccount;  // [rows][chunks]: candidates kept by the chunk
@@ -208,6 +207,219 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
 }
 
 // ----------------------------------------------------------------------------------- final
+constexpr int kRegPer = 24;    // candidates per lane held in registers by the final pass
+constexpr int kRegSpec = 8;    // of those, loaded before the counts are known (one chunk per wave)
+constexpr int kFineBins = 1024;
+constexpr int kFineShift = 8;  // fine bins are 256 key units; 1024 of them span 64 coarse bins
+
+// Wave-uniform search over a histogram held in LDS, highest bin first: lane l owns the PER
+// consecutive bins starting at l * PER. Returns the bin holding the k-th largest element and
+// writes the number of elements in higher bins to *above; returns -1 if the histogram holds
+// fewer than k elements. Every wave may run it at once on the same bins (read only).
+template <int PER>
+__device__ __forceinline__ int wave_find_bin(const uint32_t* hist, int k, int* above) {
+  const int lane = threadIdx.x & 63;
+  uint32_t h[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hist + lane * PER + i);
+    h[i] = v.x; h[i + 1] = v.y; h[i + 2] = v.z; h[i + 3] = v.w;
+  }
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += (int)h[i];
+  const int incl = wave_incl_sum(s);
+  const int all = __builtin_amdgcn_readlane(incl, 63);
+  const int mine_above = all - incl;  // elements in the bins of higher lanes
+  const uint64_t hit = __ballot(mine_above < k && mine_above + s >= k);
+  if (hit == 0) return -1;
+  const int L = __builtin_ctzll(hit);
+  int bin = -1, acc = mine_above, res_above = 0;
+  if (lane == L) {
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (bin < 0 && acc + (int)h[i] >= k) { bin = lane * PER + i; res_above = acc; }
+      acc += (int)h[i];
+    }
+  }
+  *above = __builtin_amdgcn_readlane(res_above, L);
+  return __builtin_amdgcn_readlane(bin, L);
+}
+
+// Exact selection for one row from the candidates held in registers. Wave w owns chunks
+// [w*cpw, (w+1)*cpw) and their candidates, in token order, as e[k] for index k*64 + lane.
+// Every key of the row in a coarse bin (key >> 12) at or above theta_max, the highest chunk
+// threshold, is a candidate; so if at least K candidates lie at or above theta_max << 12, the
+// K largest keys of the row are the K largest of those candidates. A 1024-bin histogram of
+// 256-unit fine bins above that base locates the K-th largest to one fine bin and a 256-entry
+// histogram of that bin gives it exactly. Returns false (uniformly, nothing written) when a
+// wave holds more candidates than its registers, when fewer than K candidates lie above the
+// base, or when the K-th largest lies beyond the fine range; the caller then takes the
+// general path.
+struct RegRow {
+  int2 e[kRegPer];  // the wave's candidates, index k * 64 + lane
+  int ccl, thl;     // lane i < number of the wave's chunks: count and threshold of chunk i
+  int cpw, c0, nch;
+  bool spec;        // e[0 .. kRegSpec) were loaded before the counts were known
+};
+
+// Issues the loads of the register path; they depend on nothing but the row, so they go out
+// before the row's length is known. With one chunk per wave the chunk's first slots are loaded
+// at once (they lie inside its region; entries past its count are ignored).
+template <int NT>
+__device__ __forceinline__ void reg_row_prefetch(const FusedWs& w, int64_t row, int chunks,
+                                                 RegRow& q) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  q.cpw = (chunks + NW - 1) / NW;
+  q.c0 = wave * q.cpw;
+  q.nch = max(0, min(chunks, q.c0 + q.cpw) - q.c0);
+  const int64_t crow = row * chunks;
+  q.spec = (q.cpw == 1 && q.nch == 1);
+  if (q.spec) {
+    const int2* cw = w.cand + (crow + q.c0) * (int64_t)kFChunk;
+#pragma unroll
+    for (int k = 0; k < kRegSpec; ++k) q.e[k] = cw[k * 64 + lane];
+  }
+  q.ccl = lane < q.nch ? w.ccount[crow + q.c0 + lane] : 0;
+  q.thl = lane < q.nch ? w.cth[crow + q.c0 + lane] : 0;
+}
+
+template <int NT>
+__device__ __forceinline__ bool select_row_registers(TopkShared<NT>& sh, const FusedWs& w,
+                                                     int64_t row, int chunks, int top_k,
+                                                     int32_t* __restrict__ out, RegRow& q) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nch = q.nch;
+  const int ccl = q.ccl, thl = q.thl;
+  const bool spec = q.spec;
+  int2 (&e)[kRegPer] = q.e;
+  const int2* cw = w.cand + (row * chunks + q.c0) * (int64_t)kFChunk;  // the wave's first chunk
+  for (int j = tid; j < kFineBins + 256; j += NT) sh.hist[j] = 0u;
+  const int incl = wave_incl_sum(ccl);
+  const int ex = incl - ccl;  // offset of chunk c0 + lane inside the wave's candidates
+  const int wtot = __builtin_amdgcn_readlane(incl, 63);  // wave-uniform: loops below end on it
+  const int thw = __builtin_amdgcn_readlane(wave_incl_max_nonneg(thl), 63);
+  if (lane == 0) {
+    sh.wave_tot[wave] = wtot;
+    sh.wave_tot2[wave] = thw;
+  }
+  __syncthreads();
+  uint32_t thmax = 0;
+  bool over = false;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    thmax = max(thmax, (uint32_t)sh.wave_tot2[v]);
+    over |= sh.wave_tot[v] > kRegPer * 64;
+  }
+  if (over) return false;
+  const int kfirst = spec ? kRegSpec : 0;
+#pragma unroll
+  for (int k = 0; k < kRegPer; ++k) {
+    if (k * 64 >= wtot) break;
+    const int j = k * 64 + lane;
+    if (k >= kfirst && j < wtot) {
+      int ci = 0, off = 0;
+      for (int t = 1; t < nch; ++t) {  // chunk of wave-local candidate j
+        const int o = __builtin_amdgcn_readlane(ex, t);
+        if (j >= o) { ci = t; off = o; }
+      }
+      e[k] = cw[ci * (int64_t)kFChunk + (j - off)];
+    }
+  }
+  const uint32_t base = thmax << 12;
+#pragma unroll
+  for (int k = 0; k < kRegPer; ++k) {
+    if (k * 64 >= wtot) break;
+    const uint32_t key = (uint32_t)e[k].x;
+    if (k * 64 + lane < wtot && key >= base)
+      atomicAdd(&sh.hist[min((key - base) >> kFineShift, (uint32_t)kFineBins - 1)], 1u);
+  }
+  __syncthreads();
+  // The fine bin of the K-th largest: wave w totals bins [64w, 64w + 64), then every wave
+  // finds the segment and the bin inside it.
+  static_assert(kFineBins == NW * 64, "one 64-bin segment per wave");
+  int32_t* seg = reinterpret_cast<int32_t*>(sh.hist + kFineBins + 256);
+  {
+    const int t = wave_incl_sum((int)sh.hist[wave * 64 + lane]);
+    if (lane == 63) seg[wave] = t;
+  }
+  __syncthreads();
+  int fb = -1, above_fb = 0;
+  {
+    const int sv = lane < NW ? seg[lane] : 0;
+    const int incl_s = wave_incl_sum(sv);
+    const int above_s = __builtin_amdgcn_readlane(incl_s, 63) - incl_s;  // in later segments
+    const uint64_t hit = __ballot(lane < NW && above_s < top_k && above_s + sv >= top_k);
+    if (hit != 0) {
+      const int S = __builtin_ctzll(hit);
+      const int base_s = __builtin_amdgcn_readlane(above_s, S);
+      const int hv = (int)sh.hist[S * 64 + lane];
+      const int incl_b = wave_incl_sum(hv);
+      const int ab = base_s + __builtin_amdgcn_readlane(incl_b, 63) - incl_b;  // in higher bins
+      const uint64_t hit2 = __ballot(ab < top_k && ab + hv >= top_k);
+      const int L = __builtin_ctzll(hit2);
+      fb = S * 64 + L;
+      above_fb = __builtin_amdgcn_readlane(ab, L);
+    }
+  }
+  if (fb < 0 || fb == kFineBins - 1) return false;
+  const uint32_t fb_lo = base + ((uint32_t)fb << kFineShift);
+#pragma unroll
+  for (int k = 0; k < kRegPer; ++k) {
+    if (k * 64 >= wtot) break;
+    const uint32_t key = (uint32_t)e[k].x;
+    if (k * 64 + lane < wtot && key >= fb_lo && key < fb_lo + (1u << kFineShift))
+      atomicAdd(&sh.hist[kFineBins + (key & 255u)], 1u);
+  }
+  __syncthreads();
+  int above_sb;
+  const int sb = wave_find_bin<4>(sh.hist + kFineBins, top_k - above_fb, &above_sb);
+  const uint32_t tau = fb_lo + (uint32_t)sb;
+  const int need = top_k - above_fb - above_sb;  // keys == tau to take, in token order
+  int gt_w = 0, eq_w = 0;
+#pragma unroll
+  for (int k = 0; k < kRegPer; ++k) {
+    if (k * 64 >= wtot) break;
+    const bool valid = k * 64 + lane < wtot;
+    gt_w += __popcll(__ballot(valid && (uint32_t)e[k].x > tau));
+    eq_w += __popcll(__ballot(valid && (uint32_t)e[k].x == tau));
+  }
+  if (lane == 0) {
+    sh.wave_tot[wave] = gt_w;
+    sh.wave_tot2[wave] = eq_w;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    gt_before += (v < wave) ? sh.wave_tot[v] : 0;
+    eq_before += (v < wave) ? sh.wave_tot2[v] : 0;
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int slot = gt_before + min(need, eq_before);
+  int eq_seen = eq_before;
+#pragma unroll
+  for (int k = 0; k < kRegPer; ++k) {
+    if (k * 64 >= wtot) break;
+    const bool valid = k * 64 + lane < wtot;
+    const bool gt = valid && (uint32_t)e[k].x > tau;
+    const bool eq = valid && (uint32_t)e[k].x == tau;
+    const uint64_t eq_mask = __ballot(eq);
+    const bool take = gt || (eq && eq_seen + __popcll(eq_mask & lt) < need);
+    const uint64_t take_mask = __ballot(take);
+    const int o = slot + __popcll(take_mask & lt);
+    if (take && o < top_k) out[o] = e[k].y;
+    slot += __popcll(take_mask);
+    eq_seen += __popcll(eq_mask);
+  }
+  return true;
+}
+
 template <int D>
 __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_t* __restrict__ q_idx,
                                                           int q_tail, int top_k, void* ws,
@@ -222,6 +434,8 @@ __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const FusedWs w = fused_ws(ws, gridDim.x, chunks);
+  RegRow q;
+  reg_row_prefetch<NT>(w, row, chunks, q);
   const FRow r = frow(kv, row, q_tail, top_k);
   int32_t* out = indices + row * r.W;
   for (int j = tid; j < r.nf; j += NT) out[j] = j;
@@ -231,9 +445,12 @@ __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_
     for (int j = r.nf + m + tid; j < r.W; j += NT) out[j] = -1;
     return;
   }
+  if (select_row_registers<NT>(sh, w, row, chunks, top_k, out + r.nf, q)) return;
+  // General path: candidates streamed from the workspace.
   const int32_t* cc = w.ccount + row * chunks;
   const int32_t* cth = w.cth + row * chunks;
   const int2* cand = w.cand + row * chunks * (int64_t)kFChunk;
+  __syncthreads();  // every wave is done with the shared arrays of the register path
   if (tid == 0) s_thmax = 0;
   __syncthreads();
   if (tid < chunks) atomicMax(&s_thmax, cth[tid]);  // the highest chunk threshold

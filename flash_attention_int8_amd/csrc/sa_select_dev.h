@@ -21,12 +21,36 @@ __device__ __forceinline__ uint32_t score_key(int32_t s) {
 
 template <int NT>
 struct TopkShared {
-  uint32_t hist[kBins];
+  alignas(16) uint32_t hist[kBins];
   int32_t wave_tot[NT / 64];
   int32_t wave_tot2[NT / 64];
   int32_t found_bin;
   int32_t found_above;
 };
+
+// Inclusive prefix sum / maximum over the 64 lanes of a wave, on DPP: row_shr 1, 2, 4, 8
+// inside each 16-lane row, then row_bcast:15 (rows 1 and 3 add the last lane of the row
+// before) and row_bcast:31 (rows 2 and 3 add lane 31). Lanes shifted in from outside a row
+// read 0 (for the maximum, 0 is the identity on the non-negative values it is used on).
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_max_nonneg(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));
+  return v;
+}
 
 // Inclusive prefix sum over the workgroup (thread order); returns the inclusive value and
 // writes the workgroup total to *total. Contains two barriers.
@@ -34,11 +58,7 @@ template <int NT>
 __device__ __forceinline__ int block_incl_scan(int v, int32_t* wave_tot, int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+  v = wave_incl_sum(v);
   if (lane == 63) wave_tot[wave] = v;
   __syncthreads();
   int before = 0, all = 0;

@@ -161,6 +161,43 @@ def test_fused_index_topk_spread_maximal_blocks():
     assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
 
 
+def test_fused_index_topk_many_chunks_ragged():
+    """Rows of more 8192-token chunks than the final pass has waves (each wave holds several
+    chunks' candidates), ragged lengths so some waves hold none, and a forced prefix."""
+    w = W(batch=3, head_dim=64, seq_len=300000, q_len=1, top_k=2048, prefix_len=7)
+    _banner("fused index+topk 300K rows, ragged")
+    inp = make_inputs(w, seed=12, device="cpu", seq_lens=[300000, 140000, 20000]).to(DEV)
+    fused = run_gpu(inp, fused=True)
+    two = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.indices, two.indices)
+    assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
+
+
+def test_fused_index_topk_top_far_above_thresholds():
+    """The top of each row lies far above every chunk's threshold (blocks of maximal keys
+    outside the chunks' first 1024 tokens, hundreds of coarse bins above the bulk), so the
+    K-th largest falls beyond the final pass's fine histogram; 2560 tied maximal keys also
+    make the tie order decide which 2048 are kept."""
+    w = W(batch=2, seq_len=131072, q_len=1, top_k=2048)
+    _banner("fused index+topk, top far above the chunk thresholds")
+    inp = make_inputs(w, seed=13, device="cpu")
+    inp.q_idx.fill_(127)
+    k = inp.kidx_pool
+    k.copy_(torch.randint(-127, 128, k.shape, generator=torch.Generator().manual_seed(3)).to(torch.int8))
+    table = inp.page_table
+    for b in range(w.batch):
+        for c in range(8):              # 5 blocks in each of chunks 2, 4, .., 16, past the first slab
+            for j in range(5):
+                k[table[b, 128 * (2 * c + 1) + 20 + 17 * j]] = 127
+    inp = inp.to(DEV)
+    fused = run_gpu(inp, fused=True)
+    two = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.indices, two.indices)
+    assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
+
+
 @pytest.mark.parametrize("seq_len,q_len,prefix,vals", [
     (16000, 40, 3, 100000),     # rows of <= 16384 candidates: staged in LDS, 512 threads
     (30000, 24, 0, 3),          # <= 32768, every key in one bin: the sampled list overflows
