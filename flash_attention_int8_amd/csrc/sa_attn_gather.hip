@@ -18,6 +18,8 @@
 // are merged across lane groups and waves at the end, then either normalised and stored
 // (one split) or written as partials for k_merge_splits (several splits). All merges run in
 // a fixed order, so results are deterministic.
+#include <type_traits>
+
 #include "sa_common.h"
 
 namespace sa {
@@ -216,24 +218,27 @@ __global__ __launch_bounds__(256, 2) void k_attn_gather(KvView kv, const uint16_
   }
 
   // merge the lane groups of this wave (groups differ in lane bits >= log2(LPK))
-#pragma unroll
-  for (int mask = LPK; mask < 64; mask <<= 1) {
+  auto merge_pairs = [&](auto mask_c) {
+    constexpr int M = decltype(mask_c)::value;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], mask, 64);
-      const float lo = __shfl_xor(l[h], mask, 64);
-      const float mn = fmaxf(m[h], mo);
-      const float s_self = safe_scale(m[h], mn);
-      const float s_oth = safe_scale(mo, mn);
-      l[h] = l[h] * s_self + lo * s_oth;
+      const FPair mp = lane_pair<M>(m[h]);
+      const FPair lp = lane_pair<M>(l[h]);
+      const float mn = fmaxf(mp.lo, mp.hi);
+      const float s_lo = safe_scale(mp.lo, mn);
+      const float s_hi = safe_scale(mp.hi, mn);
+      l[h] = lp.lo * s_lo + lp.hi * s_hi;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float ao = __shfl_xor(acc[h][e], mask, 64);
-        acc[h][e] = acc[h][e] * s_self + ao * s_oth;
+        const FPair ap = lane_pair<M>(acc[h][e]);
+        acc[h][e] = ap.lo * s_lo + ap.hi * s_hi;
       }
       m[h] = mn;
     }
-  }
+  };
+  if constexpr (LPK <= 8) merge_pairs(std::integral_constant<int, 8>{});
+  merge_pairs(std::integral_constant<int, 16>{});
+  merge_pairs(std::integral_constant<int, 32>{});
   if (grp == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -368,10 +373,12 @@ size_t gather_workspace_bytes(int64_t units, int group, int head_dim, int num_sp
 }
 
 int auto_splits(int64_t units, int index_width, int head_dim, int group) {
-  // One load batch per workgroup: 4 waves x (64 / (d/8)) lane groups x keys per lane group.
-  const int per_wg = 4 * (64 / (head_dim / 8)) * (group <= 2 ? 16 : (group == 4 ? 8 : 4));
-  int s = (index_width + per_wg - 1) / per_wg;
-  (void)units;
+  // A load batch of a workgroup is 4 waves x (64 / (d/8)) lane groups x keys per lane group.
+  // Two batches per workgroup measured faster than one (fewer partials to merge, every
+  // workgroup resident at once) as long as that still gives every CU a workgroup.
+  const int batch = 4 * (64 / (head_dim / 8)) * (group <= 2 ? 16 : (group == 4 ? 8 : 4));
+  int s = (index_width + 2 * batch - 1) / (2 * batch);
+  if (units * s < 256) s = (index_width + batch - 1) / batch;
   return s < 1 ? 1 : (s > 256 ? 256 : s);
 }
 

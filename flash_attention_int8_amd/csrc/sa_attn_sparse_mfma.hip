@@ -191,8 +191,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
         if (!((vmask >> key) & 1u)) s[hh][r] = -INFINITY;
         mx = fmaxf(mx, s[hh][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    {
+      const FPair p16 = lane_pair<16>(mx);
+      const FPair p32 = lane_pair<32>(fmaxf(p16.lo, p16.hi));
+      mx = fmaxf(p32.lo, p32.hi);
+    }
     const float m_new = fmaxf(m_run, mx);
     if (__any((m_new - m_run) * qscale > kRescaleLog2)) {  // wave-uniform, rare
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * qscale);
@@ -247,8 +250,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
   }
 
   // l over the 4 lanes of each head; O^T[dim nb*16 + 4g + r][head col] sits in o[nb][r]
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const FPair l16 = lane_pair<16>(l_part);
+  const FPair l32 = lane_pair<32>(l16.lo + l16.hi);
+  const float l_tot = l32.lo + l32.hi;
   if (col >= G) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t qh = bi * num_q_heads + (int64_t)g * G + col;

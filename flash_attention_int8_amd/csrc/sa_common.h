@@ -95,6 +95,29 @@ __device__ __forceinline__ float group_sum_f(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// The values of a lane pair {l, l ^ M}, lower lane first, in both lanes of the pair: row
+// rotation by 8 inside 16-lane rows (M = 8), self-swap of odd and even 16-lane rows (M = 16)
+// or of the two 32-lane halves (M = 32). VALU only (no LDS round trip); both lanes get the
+// same ordered pair, so anything computed from it is identical in both.
+struct FPair {
+  float lo, hi;
+};
+template <int M>
+__device__ __forceinline__ FPair lane_pair(float x) {
+  static_assert(M == 8 || M == 16 || M == 32, "lane_pair supports M = 8, 16, 32");
+  if constexpr (M == 8) {
+    const float o = __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x128, 0xf, 0xf, false));
+    const bool upper = (__lane_id() & 8) != 0;
+    return FPair{upper ? o : x, upper ? x : o};
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return FPair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return FPair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+  }
+}
+
 }  // namespace sa
 
 // Kernel launchers (defined in the .hip files; return hipSuccess or the launch error).
