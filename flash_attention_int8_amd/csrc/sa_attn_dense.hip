@@ -170,6 +170,17 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   };
   // rows of tile `tile` that hold attendable keys (wave-uniform)
   auto valid_rows = [&](int tile, int64_t ph) { return ph < 0 ? 0 : seq_len - tile * BN; };
+  // Page-table entry of a tile, loaded one iteration before it is needed and checked only
+  // where it is used: the load is unconditional (index clamped into the table) so that no
+  // wait for it is placed next to the load.
+  auto raw_page = [&](int tile) -> int32_t {
+    const int lp = min((tile * BN) >> kv.page_shift, kv.max_pages_per_seq - 1);
+    return kv.page_table[(int64_t)b * kv.max_pages_per_seq + lp];
+  };
+  auto checked_page = [&](int tile, int32_t raw) -> int64_t {
+    const int lp = (tile * BN) >> kv.page_shift;
+    return (lp < kv.max_pages_per_seq && raw >= 0 && raw < kv.num_pages) ? (int64_t)raw : -1;
+  };
   auto mask_rows = [&](uint4 (&v)[KPT], int row0, int lim) {
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
@@ -346,7 +357,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   // Prologue: K(0), V(0) and K(1) in LDS, S(0) computed, masked and its maximum taken.
   // Each loader role looks its page up one iteration ahead of the load that needs it.
   uint4 st[KPT];
-  int64_t ph_next;
+  int32_t raw_next;  // page-table entry of the next tile this wave loads
   if (k_loader) {
     int64_t ph = phys_page(kv, b, 0);
     load_rows(kv.k_pool, 0, ph, k_off, st);
@@ -360,14 +371,14 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
       if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
       store_k(1, st);
     }
-    ph_next = phys_page(kv, b, 2 * BN);
+    raw_next = raw_page(2);
   } else {
     const int64_t ph = phys_page(kv, b, 0);
     load_rows(kv.v_pool, 0, ph, v_off, st);
     const int lim = valid_rows(0, ph);
     if (lim < BN) mask_rows(st, lv_kq * KPT, lim);
     store_v(0, st);
-    ph_next = phys_page(kv, b, BN);
+    raw_next = raw_page(1);
   }
   __syncthreads();
   f32x16 sa[2], sb[2];
@@ -381,12 +392,13 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   // tile is computed and store it to K buffer j&1; V loaders do the same with V(j+1) and V
   // buffer (j+1)&1. Neither buffer is read during iteration j.
   auto iter = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    // the load past the last tile re-reads the last one (in bounds) and is never stored
+    // the load past the last tile reads the last tile's slots of page 0 (in bounds) and is
+    // never stored
     const int ltile = k_loader ? j + 2 : j + 1;
     const bool more = ltile < n_tiles;
     const int lt = more ? ltile : n_tiles - 1;
-    const int64_t ph = more ? ph_next : phys_page(kv, b, lt * BN);
-    ph_next = phys_page(kv, b, (ltile + 1) * BN);
+    const int64_t ph = more ? checked_page(ltile, raw_next) : 0;
+    raw_next = raw_page(ltile + 1);
     load_rows(k_loader ? kv.k_pool : kv.v_pool, lt, ph, k_loader ? k_off : v_off, st);
     const int lim = valid_rows(lt, ph);
     if (j <= last_w) {

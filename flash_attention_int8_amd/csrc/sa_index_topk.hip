@@ -140,14 +140,31 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
   if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
   __syncthreads();
   int2* dst = w.cand + (row * chunks + c) * (int64_t)kFChunk;
+  // Page-table entries of a slab's blocks, requested a slab ahead of their use. The loads are
+  // unconditional (index clamped into the table) so that no wait lands next to them; the
+  // entries are checked in score_slab.
+  auto slab_pages = [&](int slab, int32_t (&raw)[U]) {
+    const int blk0 = c * kFBlocks + slab * NW * U + wave * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int lp = min(((blk0 + u) << 6) >> kv.page_shift, kv.max_pages_per_seq - 1);
+      raw[u] = kv.page_table[(int64_t)r.b * kv.max_pages_per_seq + lp];
+    }
+  };
   // scores slab `slab` of the chunk: key, whether the token is a candidate, token index
-  auto score_slab = [&](int slab, uint32_t (&key)[U], bool (&in)[U], int (&tok)[U]) {
+  auto score_slab = [&](int slab, const int32_t (&raw)[U], uint32_t (&key)[U], bool (&in)[U],
+                        int (&tok)[U]) {
     const int blk0 = c * kFBlocks + slab * NW * U + wave * U;
     int64_t base[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int blk = blk0 + u;
-      base[u] = (blk >= r.blk_first && blk <= r.blk_last) ? block_base<D>(kv, r.b, r.gi, blk) : -1;
+      const int lp = (blk << 6) >> kv.page_shift;
+      const bool ok = blk >= r.blk_first && blk <= r.blk_last && lp < kv.max_pages_per_seq &&
+                      raw[u] >= 0 && raw[u] < kv.num_pages;
+      base[u] = ok ? (((int64_t)raw[u] * kv.num_idx_heads + r.gi) * kv.page_size +
+                      ((blk << 6) & (kv.page_size - 1))) * (int64_t)D
+                   : -1;
     }
     v4i kd[U][Blk<D>::R];
 #pragma unroll
@@ -170,10 +187,13 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
   uint32_t key[U];
   bool in[U], keep[U];
   int tok[U];
+  int32_t raw_cur[U], raw_nxt[U];
+  slab_pages(0, raw_cur);
+  slab_pages(1, raw_nxt);
   // The chunk's threshold from its first slab: the highest bin whose tail holds well over the
   // slab's share of K (twice the expected count plus three standard deviations plus 8). Any
   // value is safe: the final pass checks it and rescores the row if it was too high.
-  score_slab(0, key, in, tok);
+  score_slab(0, raw_cur, key, in, tok);
 #pragma unroll
   for (int u = 0; u < U; ++u)
     if (in[u]) atomicAdd(&sh.hist[key[u] >> 12], 1u);
@@ -195,7 +215,10 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
   for (int u = 0; u < U; ++u) keep[u] = in[u] && (key[u] >> 12) >= th;
   int fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, 0);
   for (int slab = 1; slab < kFBlocks / (NW * U); ++slab) {
-    score_slab(slab, key, in, tok);
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw_cur[u] = raw_nxt[u];
+    slab_pages(slab + 1, raw_nxt);  // past the chunk: clamped, in bounds, never used
+    score_slab(slab, raw_cur, key, in, tok);
 #pragma unroll
     for (int u = 0; u < U; ++u) keep[u] = in[u] && (key[u] >> 12) >= th;
     fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, fill);

@@ -70,12 +70,14 @@ __global__ __launch_bounds__(NT) void k_topk_row_reg(KvView kv, const int32_t* _
     for (int j = nf + m + tid; j < W; j += NT) out[j] = -1;
     return;
   }
+  // Every load is issued before any is used: the index is clamped into the row instead of
+  // guarding the load (a guarded load makes the compiler wait for it on the spot), and the
+  // entries past the row are zeroed afterwards.
   uint32_t v[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int j = u * NT + tid;
-    v[u] = j < n ? score_key(srow[P + j]) : 0u;
-  }
+  for (int u = 0; u < PER; ++u) v[u] = (uint32_t)srow[P + min(u * NT + tid, n - 1)];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) v[u] = u * NT + tid < n ? score_key((int32_t)v[u]) : 0u;
   auto clear_hist = [&]() {
     __syncthreads();  // every wave has read the previous histogram and found_bin/found_above
     for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
@@ -271,16 +273,34 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
   }
   for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
   __syncthreads();
-  for (int j = tid; j < n; j += NT) atomicAdd(&sh.hist[score_key(srow[P + j]) >> 12], 1u);
+  // kLd keys per thread are requested at once (indices clamped into the row, so no load is
+  // guarded) before any is used.
+  constexpr int kLd = 8;
+  auto load_batch = [&](int j0, int step, uint32_t (&k)[kLd]) {
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) k[u] = (uint32_t)srow[P + min(j0 + u * step, n - 1)];
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) k[u] = score_key((int32_t)k[u]);
+  };
+  for (int j0 = tid; j0 < n; j0 += kLd * NT) {
+    uint32_t k[kLd];
+    load_batch(j0, NT, k);
+#pragma unroll
+    for (int u = 0; u < kLd; ++u)
+      if (j0 + u * NT < n) atomicAdd(&sh.hist[k[u] >> 12], 1u);
+  }
   __syncthreads();
   find_bin<NT>(sh, top_k);
   const uint32_t b1 = sh.found_bin;
   const int above1 = sh.found_above;
   for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
   __syncthreads();
-  for (int j = tid; j < n; j += NT) {
-    const uint32_t key = score_key(srow[P + j]);
-    if ((key >> 12) == b1) atomicAdd(&sh.hist[key & 0xfff], 1u);
+  for (int j0 = tid; j0 < n; j0 += kLd * NT) {
+    uint32_t k[kLd];
+    load_batch(j0, NT, k);
+#pragma unroll
+    for (int u = 0; u < kLd; ++u)
+      if (j0 + u * NT < n && (k[u] >> 12) == b1) atomicAdd(&sh.hist[k[u] & 0xfff], 1u);
   }
   __syncthreads();
   find_bin<NT>(sh, top_k - above1);
@@ -289,11 +309,15 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
   const int seg = ((n + NW * 64 - 1) / (NW * 64)) * 64;
   const int s0 = wv * seg, s1 = min(n, s0 + seg);
   int gt_w = 0, eq_w = 0;
-  for (int j0 = s0; j0 < s1; j0 += 64) {
-    const int j = j0 + lane;
-    const uint32_t key = j < s1 ? score_key(srow[P + j]) : 0u;
-    gt_w += __popcll(__ballot(j < s1 && key > tau));
-    eq_w += __popcll(__ballot(j < s1 && key == tau));
+  for (int j0 = s0; j0 < s1; j0 += kLd * 64) {
+    uint32_t k[kLd];
+    load_batch(j0 + lane, 64, k);
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) {
+      const int j = j0 + u * 64 + lane;
+      gt_w += __popcll(__ballot(j < s1 && k[u] > tau));
+      eq_w += __popcll(__ballot(j < s1 && k[u] == tau));
+    }
   }
   if (lane == 0) {
     sh.wave_tot[wv] = gt_w;
@@ -305,17 +329,21 @@ __global__ __launch_bounds__(NT) void k_topk_row(KvView kv, const int32_t* __res
     gt_run += sh.wave_tot[w];
     eq_run += sh.wave_tot2[w];
   }
-  for (int j0 = s0; j0 < s1 && gt_run + min(eq_run, need) < top_k; j0 += 64) {
-    const int j = j0 + lane;
-    const uint32_t key = j < s1 ? score_key(srow[P + j]) : 0u;
-    const bool gt = j < s1 && key > tau;
-    const bool eq = j < s1 && key == tau;
-    const uint64_t gm = __ballot(gt), em = __ballot(eq);
-    const int gt_before = gt_run + __popcll(gm & lt_mask);
-    const int eq_before = eq_run + __popcll(em & lt_mask);
-    if (gt || (eq && eq_before < need)) out[nf + gt_before + min(eq_before, need)] = P + j;
-    gt_run += __popcll(gm);
-    eq_run += __popcll(em);
+  for (int j0 = s0; j0 < s1 && gt_run + min(eq_run, need) < top_k; j0 += kLd * 64) {
+    uint32_t k[kLd];
+    load_batch(j0 + lane, 64, k);
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) {
+      const int j = j0 + u * 64 + lane;
+      const bool gt = j < s1 && k[u] > tau;
+      const bool eq = j < s1 && k[u] == tau;
+      const uint64_t gm = __ballot(gt), em = __ballot(eq);
+      const int gt_before = gt_run + __popcll(gm & lt_mask);
+      const int eq_before = eq_run + __popcll(em & lt_mask);
+      if (gt || (eq && eq_before < need)) out[nf + gt_before + min(eq_before, need)] = P + j;
+      gt_run += __popcll(gm);
+      eq_run += __popcll(em);
+    }
   }
 }
 
