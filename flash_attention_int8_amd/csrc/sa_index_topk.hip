@@ -235,40 +235,6 @@ constexpr int kRegSpec = 8;    // of those, loaded before the counts are known (
 constexpr int kFineBins = 1024;
 constexpr int kFineShift = 8;  // fine bins are 256 key units; 1024 of them span 64 coarse bins
 
-// Wave-uniform search over a histogram held in LDS, highest bin first: lane l owns the PER
-// consecutive bins starting at l * PER. Returns the bin holding the k-th largest element and
-// writes the number of elements in higher bins to *above; returns -1 if the histogram holds
-// fewer than k elements. Every wave may run it at once on the same bins (read only).
-template <int PER>
-__device__ __forceinline__ int wave_find_bin(const uint32_t* hist, int k, int* above) {
-  const int lane = threadIdx.x & 63;
-  uint32_t h[PER];
-#pragma unroll
-  for (int i = 0; i < PER; i += 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(hist + lane * PER + i);
-    h[i] = v.x; h[i + 1] = v.y; h[i + 2] = v.z; h[i + 3] = v.w;
-  }
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) s += (int)h[i];
-  const int incl = wave_incl_sum(s);
-  const int all = __builtin_amdgcn_readlane(incl, 63);
-  const int mine_above = all - incl;  // elements in the bins of higher lanes
-  const uint64_t hit = __ballot(mine_above < k && mine_above + s >= k);
-  if (hit == 0) return -1;
-  const int L = __builtin_ctzll(hit);
-  int bin = -1, acc = mine_above, res_above = 0;
-  if (lane == L) {
-#pragma unroll
-    for (int i = PER - 1; i >= 0; --i) {
-      if (bin < 0 && acc + (int)h[i] >= k) { bin = lane * PER + i; res_above = acc; }
-      acc += (int)h[i];
-    }
-  }
-  *above = __builtin_amdgcn_readlane(res_above, L);
-  return __builtin_amdgcn_readlane(bin, L);
-}
-
 // Exact selection for one row from the candidates held in registers. Wave w owns chunks
 // [w*cpw, (w+1)*cpw) and their candidates, in token order, as e[k] for index k*64 + lane.
 // Every key of the row in a coarse bin (key >> 12) at or above theta_max, the highest chunk
@@ -363,33 +329,10 @@ __device__ __forceinline__ bool select_row_registers(TopkShared<NT>& sh, const F
       atomicAdd(&sh.hist[min((key - base) >> kFineShift, (uint32_t)kFineBins - 1)], 1u);
   }
   __syncthreads();
-  // The fine bin of the K-th largest: wave w totals bins [64w, 64w + 64), then every wave
-  // finds the segment and the bin inside it.
   static_assert(kFineBins == NW * 64, "one 64-bin segment per wave");
-  int32_t* seg = reinterpret_cast<int32_t*>(sh.hist + kFineBins + 256);
-  {
-    const int t = wave_incl_sum((int)sh.hist[wave * 64 + lane]);
-    if (lane == 63) seg[wave] = t;
-  }
-  __syncthreads();
-  int fb = -1, above_fb = 0;
-  {
-    const int sv = lane < NW ? seg[lane] : 0;
-    const int incl_s = wave_incl_sum(sv);
-    const int above_s = __builtin_amdgcn_readlane(incl_s, 63) - incl_s;  // in later segments
-    const uint64_t hit = __ballot(lane < NW && above_s < top_k && above_s + sv >= top_k);
-    if (hit != 0) {
-      const int S = __builtin_ctzll(hit);
-      const int base_s = __builtin_amdgcn_readlane(above_s, S);
-      const int hv = (int)sh.hist[S * 64 + lane];
-      const int incl_b = wave_incl_sum(hv);
-      const int ab = base_s + __builtin_amdgcn_readlane(incl_b, 63) - incl_b;  // in higher bins
-      const uint64_t hit2 = __ballot(ab < top_k && ab + hv >= top_k);
-      const int L = __builtin_ctzll(hit2);
-      fb = S * 64 + L;
-      above_fb = __builtin_amdgcn_readlane(ab, L);
-    }
-  }
+  int above_fb;
+  const int fb = block_find_bin_segments<NW>(sh.hist, reinterpret_cast<int32_t*>(sh.hist + kFineBins + 256),
+                                             top_k, &above_fb);
   if (fb < 0 || fb == kFineBins - 1) return false;
   const uint32_t fb_lo = base + ((uint32_t)fb << kFineShift);
 #pragma unroll

@@ -52,6 +52,70 @@ __device__ __forceinline__ int wave_incl_max_nonneg(int v) {
   return v;
 }
 
+// Wave-uniform search over a histogram held in LDS, highest bin first: lane l owns the PER
+// consecutive bins starting at l * PER. Returns the bin holding the k-th largest element and
+// writes the number of elements in higher bins to *above; returns -1 if the histogram holds
+// fewer than k elements. Every wave may run it at once on the same bins (read only).
+template <int PER>
+__device__ __forceinline__ int wave_find_bin(const uint32_t* hist, int k, int* above) {
+  const int lane = threadIdx.x & 63;
+  uint32_t h[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hist + lane * PER + i);
+    h[i] = v.x; h[i + 1] = v.y; h[i + 2] = v.z; h[i + 3] = v.w;
+  }
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += (int)h[i];
+  const int incl = wave_incl_sum(s);
+  const int all = __builtin_amdgcn_readlane(incl, 63);
+  const int mine_above = all - incl;  // elements in the bins of higher lanes
+  const uint64_t hit = __ballot(mine_above < k && mine_above + s >= k);
+  if (hit == 0) return -1;
+  const int L = __builtin_ctzll(hit);
+  int bin = -1, acc = mine_above, res_above = 0;
+  if (lane == L) {
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (bin < 0 && acc + (int)h[i] >= k) { bin = lane * PER + i; res_above = acc; }
+      acc += (int)h[i];
+    }
+  }
+  *above = __builtin_amdgcn_readlane(res_above, L);
+  return __builtin_amdgcn_readlane(bin, L);
+}
+
+// Bin holding the k-th largest element of a histogram of NW * 64 bins in LDS (wave w totals
+// bins [64w, 64w + 64) into seg[w], one barrier, then every wave finds the segment and the
+// bin inside it on its own, so all waves leave with the same answer). Writes the number of
+// elements in higher bins to *above; returns -1 if the histogram holds fewer than k.
+template <int NW>
+__device__ __forceinline__ int block_find_bin_segments(const uint32_t* hist, int32_t* seg, int k,
+                                                       int* above) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  {
+    const int t = wave_incl_sum((int)hist[wave * 64 + lane]);
+    if (lane == 63) seg[wave] = t;
+  }
+  __syncthreads();
+  const int sv = lane < NW ? seg[lane] : 0;
+  const int incl_s = wave_incl_sum(sv);
+  const int above_s = __builtin_amdgcn_readlane(incl_s, 63) - incl_s;  // in later segments
+  const uint64_t hit = __ballot(lane < NW && above_s < k && above_s + sv >= k);
+  if (hit == 0) return -1;
+  const int S = __builtin_ctzll(hit);
+  const int base_s = __builtin_amdgcn_readlane(above_s, S);
+  const int hv = (int)hist[S * 64 + lane];
+  const int incl_b = wave_incl_sum(hv);
+  const int ab = base_s + __builtin_amdgcn_readlane(incl_b, 63) - incl_b;  // in higher bins
+  const uint64_t hit2 = __ballot(ab < k && ab + hv >= k);
+  const int L = __builtin_ctzll(hit2);
+  *above = __builtin_amdgcn_readlane(ab, L);
+  return S * 64 + L;
+}
+
 // Inclusive prefix sum over the workgroup (thread order); returns the inclusive value and
 // writes the workgroup total to *total. Contains two barriers.
 template <int NT>

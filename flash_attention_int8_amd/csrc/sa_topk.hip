@@ -25,28 +25,31 @@ namespace {
 using namespace sel;
 
 
-// Rows of at most NT * PER candidates are held in registers: candidate j (token P + j) sits
-// in thread j % NT, slot j / NT, so the row is read once with every thread's PER loads in
-// flight together. A strided sample of 1024 keys sets a provisional threshold bin theta (its
-// tail holds 1.5 times the sampled share of K plus three standard deviations plus 8); the keys
-// in bins >= theta are compacted, in token order, into a short list in LDS, and the exact radix
-// select runs on that list. The list is enough when it holds at least K keys and the K-th
-// largest of them lies in a bin >= theta: then every key of the row in a bin >= b1 is on it.
-// Otherwise (or when the list would not fit) the exact select runs over the registers, so the
-// result never depends on the sample. Token order over (slot u, wave, lane) is u-major, so
-// every ordered write takes per-(u, wave) counts and one workgroup scan.
+// Rows of at most NT * PER candidates are held in registers: wave w holds candidates
+// [w * PER * 64, (w + 1) * PER * 64) (candidate j is token P + j), slot u and lane l holding
+// j = w * PER * 64 + u * 64 + l, so the row is read once with every thread's PER loads in
+// flight together, and token order is wave-major: an ordered write needs one scan over the
+// waves, and the offsets inside a wave come from ballots. A strided sample of 1024 keys sets
+// a provisional threshold bin theta (its tail holds 1.5 times the sampled share of K plus
+// three standard deviations plus 8); the keys in bins >= theta are compacted, in token order,
+// into a short list in LDS. When the list holds at least K keys, the K largest keys of the
+// row are the K largest on it (every key of the row at or above theta << 12 is on the list):
+// a histogram of 256-unit fine bins above theta << 12 locates the K-th largest to one fine
+// bin, and a 256-entry histogram of that bin gives it exactly. Otherwise (too few or too many
+// keys on the list, or the K-th largest beyond the fine range) the exact select runs over the
+// registers, so the result never depends on the sample.
 template <int NT, int PER, int CAND>
 __global__ __launch_bounds__(NT) void k_topk_row_reg(KvView kv, const int32_t* __restrict__ scores,
                                                      int64_t row_stride, int q_len, int q_tail,
                                                      int top_k, int32_t* __restrict__ indices) {
   constexpr int NW = NT / 64;
   constexpr int kSample = 1024;
-  static_assert(PER * NW <= NT, "one scan entry per thread");
+  constexpr int kFine = NW * 64;  // fine bins: one 64-bin segment per wave
+  static_assert(kFine + 256 + NW <= kBins, "the fine histograms fit in the shared histogram");
+  static_assert(NT * PER <= 65536, "list positions are 16-bit");
   __shared__ TopkShared<NT> sh;
-  __shared__ int32_t s_cnt[2][PER * NW];   // per-(u, wave) counts, then exclusive offsets
-  __shared__ uint32_t l_key[CAND];         // short list: keys ...
-  __shared__ uint16_t l_pos[CAND];         // ... and positions j, token order
-  __shared__ int32_t s_total[2];
+  __shared__ uint32_t l_key[CAND];  // short list: keys ...
+  __shared__ uint16_t l_pos[CAND];  // ... and positions j, token order
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -70,14 +73,15 @@ __global__ __launch_bounds__(NT) void k_topk_row_reg(KvView kv, const int32_t* _
     for (int j = nf + m + tid; j < W; j += NT) out[j] = -1;
     return;
   }
+  auto jid = [&](int u) { return wv * (PER * 64) + u * 64 + lane; };
   // Every load is issued before any is used: the index is clamped into the row instead of
   // guarding the load (a guarded load makes the compiler wait for it on the spot), and the
   // entries past the row are zeroed afterwards.
   uint32_t v[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) v[u] = (uint32_t)srow[P + min(u * NT + tid, n - 1)];
+  for (int u = 0; u < PER; ++u) v[u] = (uint32_t)srow[P + min(jid(u), n - 1)];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) v[u] = u * NT + tid < n ? score_key((int32_t)v[u]) : 0u;
+  for (int u = 0; u < PER; ++u) v[u] = jid(u) < n ? score_key((int32_t)v[u]) : 0u;
   auto clear_hist = [&]() {
     __syncthreads();  // every wave has read the previous histogram and found_bin/found_above
     for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
@@ -87,47 +91,35 @@ __global__ __launch_bounds__(NT) void k_topk_row_reg(KvView kv, const int32_t* _
     }
     __syncthreads();
   };
-  // Per-(u, wave) counts of up to two predicates are written to s_cnt[k][u * NW + wave] (by
-  // lane 0); scan_counts turns them, in place, into exclusive offsets in token order and
-  // leaves the totals in s_total.
-  auto scan_counts = [&]() {
-    __syncthreads();
-    const int x0 = tid < PER * NW ? s_cnt[0][tid] : 0;
-    const int x1 = tid < PER * NW ? s_cnt[1][tid] : 0;
-    int t0, t1;
-    const int e0 = block_excl_scan<NT>(x0, sh.wave_tot, &t0);
-    const int e1 = block_excl_scan<NT>(x1, sh.wave_tot2, &t1);
-    if (tid < PER * NW) {
-      s_cnt[0][tid] = e0;
-      s_cnt[1][tid] = e1;
-    }
-    if (tid == 0) {
-      s_total[0] = t0;
-      s_total[1] = t1;
-    }
-    __syncthreads();
-  };
   // Ordered output from the registers: keys > tau, and the first `need` keys == tau.
   auto emit_regs = [&](uint32_t tau, int need) {
+    int gt_w = 0, eq_w = 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int j = u * NT + tid;
-      const int cg = __popcll(__ballot(j < n && v[u] > tau));
-      const int ce = __popcll(__ballot(j < n && v[u] == tau));
-      if (lane == 0) {
-        s_cnt[0][u * NW + wv] = cg;
-        s_cnt[1][u * NW + wv] = ce;
-      }
+      gt_w += __popcll(__ballot(jid(u) < n && v[u] > tau));
+      eq_w += __popcll(__ballot(jid(u) < n && v[u] == tau));
     }
-    scan_counts();
+    if (lane == 0) {
+      sh.wave_tot[wv] = gt_w;
+      sh.wave_tot2[wv] = eq_w;
+    }
+    __syncthreads();
+    int gb = 0, eb = 0;
+    for (int w = 0; w < wv; ++w) {
+      gb += sh.wave_tot[w];
+      eb += sh.wave_tot2[w];
+    }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int j = u * NT + tid;
+      const int j = jid(u);
       const bool gt = j < n && v[u] > tau;
       const bool eq = j < n && v[u] == tau;
-      const int gb = s_cnt[0][u * NW + wv] + __popcll(__ballot(gt) & lt_mask);
-      const int eb = s_cnt[1][u * NW + wv] + __popcll(__ballot(eq) & lt_mask);
-      if (gt || (eq && eb < need)) out[nf + gb + min(eb, need)] = P + j;
+      const uint64_t gm = __ballot(gt), em = __ballot(eq);
+      const int g = gb + __popcll(gm & lt_mask);
+      const int e = eb + __popcll(em & lt_mask);
+      if (gt || (eq && e < need)) out[nf + g + min(e, need)] = P + j;
+      gb += __popcll(gm);
+      eb += __popcll(em);
     }
   };
 
@@ -144,84 +136,90 @@ __global__ __launch_bounds__(NT) void k_topk_row_reg(KvView kv, const int32_t* _
     find_bin<NT>(sh, target);
     th = (uint32_t)sh.found_bin;
   }
-  // short list of the keys in bins >= th
+  // short list of the keys in bins >= th; the fine histograms are cleared on the way
+  int cnt_w = 0;
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int c = __popcll(__ballot(u * NT + tid < n && (v[u] >> 12) >= th));
-    if (lane == 0) {
-      s_cnt[0][u * NW + wv] = c;
-      s_cnt[1][u * NW + wv] = 0;
-    }
+  for (int u = 0; u < PER; ++u) cnt_w += __popcll(__ballot(jid(u) < n && (v[u] >> 12) >= th));
+  if (lane == 0) sh.wave_tot[wv] = cnt_w;
+  for (int j = tid; j < kFine + 256; j += NT) sh.hist[j] = 0;
+  __syncthreads();
+  int off = 0, m = 0;
+  for (int w = 0; w < NW; ++w) {
+    const int x = sh.wave_tot[w];
+    off += (w < wv) ? x : 0;
+    m += x;
   }
-  scan_counts();
-  const int m = s_total[0];
-  bool ok = m >= top_k && m <= CAND;
-  if (ok) {
+  if (m >= top_k && m <= CAND) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int j = u * NT + tid;
-      const bool keep = j < n && (v[u] >> 12) >= th;
-      const int o = s_cnt[0][u * NW + wv] + __popcll(__ballot(keep) & lt_mask);
+      const bool keep = jid(u) < n && (v[u] >> 12) >= th;
+      const uint64_t km = __ballot(keep);
+      const int o = off + __popcll(km & lt_mask);
       if (keep) {
         l_key[o] = v[u];
-        l_pos[o] = (uint16_t)j;
+        l_pos[o] = (uint16_t)jid(u);
       }
+      off += __popcll(km);
     }
-    clear_hist();  // its barriers also complete the list
-    for (int c = tid; c < m; c += NT) atomicAdd(&sh.hist[l_key[c] >> 12], 1u);
-    __syncthreads();
-    find_bin<NT>(sh, top_k);
-    ok = sh.found_bin >= (int)th;  // uniform
-  }
-  if (ok) {
-    const uint32_t b1 = sh.found_bin;
-    const int above1 = sh.found_above;
-    clear_hist();
+    __syncthreads();  // the list is complete
+    const uint32_t base = th << 12;
     for (int c = tid; c < m; c += NT)
-      if ((l_key[c] >> 12) == b1) atomicAdd(&sh.hist[l_key[c] & 0xfff], 1u);
+      atomicAdd(&sh.hist[min((l_key[c] - base) >> 8, (uint32_t)kFine - 1)], 1u);
     __syncthreads();
-    find_bin<NT>(sh, top_k - above1);
-    const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
-    const int need = top_k - above1 - sh.found_above;
-    // ordered output over the list: wave segments, counts by ballot, one scan over the waves
-    const int seg = ((m + NW * 64 - 1) / (NW * 64)) * 64;
-    const int s0 = wv * seg, s1 = min(m, s0 + seg);
-    int gt_w = 0, eq_w = 0;
-    for (int c0 = s0; c0 < s1; c0 += 64) {
-      const int c = c0 + lane;
-      const uint32_t key = c < s1 ? l_key[c] : 0u;
-      gt_w += __popcll(__ballot(c < s1 && key > tau));
-      eq_w += __popcll(__ballot(c < s1 && key == tau));
+    int above_fb = 0;
+    const int fb = block_find_bin_segments<NW>(sh.hist, reinterpret_cast<int32_t*>(sh.hist + kFine + 256),
+                                               top_k, &above_fb);
+    if (fb >= 0 && fb < kFine - 1) {  // uniform
+      const uint32_t lo = base + ((uint32_t)fb << 8);
+      for (int c = tid; c < m; c += NT) {
+        const uint32_t key = l_key[c];
+        if (key >= lo && key < lo + 256u) atomicAdd(&sh.hist[kFine + (key & 255u)], 1u);
+      }
+      __syncthreads();
+      int above_sb = 0;
+      const int sb = wave_find_bin<4>(sh.hist + kFine, top_k - above_fb, &above_sb);
+      const uint32_t tau = lo + (uint32_t)sb;
+      const int need = top_k - above_fb - above_sb;
+      // ordered output over the list: wave segments, counts by ballot, one scan over the waves
+      const int seg = ((m + NW * 64 - 1) / (NW * 64)) * 64;
+      const int s0 = wv * seg, s1 = min(m, s0 + seg);
+      int gt_w = 0, eq_w = 0;
+      for (int c0 = s0; c0 < s1; c0 += 64) {
+        const int c = c0 + lane;
+        const uint32_t key = c < s1 ? l_key[c] : 0u;
+        gt_w += __popcll(__ballot(c < s1 && key > tau));
+        eq_w += __popcll(__ballot(c < s1 && key == tau));
+      }
+      if (lane == 0) {
+        sh.wave_tot[wv] = gt_w;
+        sh.wave_tot2[wv] = eq_w;
+      }
+      __syncthreads();
+      int gt_run = 0, eq_run = 0;
+      for (int w = 0; w < wv; ++w) {
+        gt_run += sh.wave_tot[w];
+        eq_run += sh.wave_tot2[w];
+      }
+      for (int c0 = s0; c0 < s1 && gt_run + min(eq_run, need) < top_k; c0 += 64) {
+        const int c = c0 + lane;
+        const uint32_t key = c < s1 ? l_key[c] : 0u;
+        const bool gt = c < s1 && key > tau;
+        const bool eq = c < s1 && key == tau;
+        const uint64_t gm = __ballot(gt), em = __ballot(eq);
+        const int gt_before = gt_run + __popcll(gm & lt_mask);
+        const int eq_before = eq_run + __popcll(em & lt_mask);
+        if (gt || (eq && eq_before < need)) out[nf + gt_before + min(eq_before, need)] = P + (int)l_pos[c];
+        gt_run += __popcll(gm);
+        eq_run += __popcll(em);
+      }
+      return;
     }
-    if (lane == 0) {
-      sh.wave_tot[wv] = gt_w;
-      sh.wave_tot2[wv] = eq_w;
-    }
-    __syncthreads();
-    int gt_run = 0, eq_run = 0;
-    for (int w = 0; w < wv; ++w) {
-      gt_run += sh.wave_tot[w];
-      eq_run += sh.wave_tot2[w];
-    }
-    for (int c0 = s0; c0 < s1 && gt_run + min(eq_run, need) < top_k; c0 += 64) {
-      const int c = c0 + lane;
-      const uint32_t key = c < s1 ? l_key[c] : 0u;
-      const bool gt = c < s1 && key > tau;
-      const bool eq = c < s1 && key == tau;
-      const uint64_t gm = __ballot(gt), em = __ballot(eq);
-      const int gt_before = gt_run + __popcll(gm & lt_mask);
-      const int eq_before = eq_run + __popcll(em & lt_mask);
-      if (gt || (eq && eq_before < need)) out[nf + gt_before + min(eq_before, need)] = P + (int)l_pos[c];
-      gt_run += __popcll(gm);
-      eq_run += __popcll(em);
-    }
-    return;
   }
   // exact select over the registers
   clear_hist();
 #pragma unroll
   for (int u = 0; u < PER; ++u)
-    if (u * NT + tid < n) atomicAdd(&sh.hist[v[u] >> 12], 1u);
+    if (jid(u) < n) atomicAdd(&sh.hist[v[u] >> 12], 1u);
   __syncthreads();
   find_bin<NT>(sh, top_k);
   const uint32_t b1 = sh.found_bin;
@@ -229,7 +227,7 @@ __global__ __launch_bounds__(NT) void k_topk_row_reg(KvView kv, const int32_t* _
   clear_hist();
 #pragma unroll
   for (int u = 0; u < PER; ++u)
-    if (u * NT + tid < n && (v[u] >> 12) == b1) atomicAdd(&sh.hist[v[u] & 0xfff], 1u);
+    if (jid(u) < n && (v[u] >> 12) == b1) atomicAdd(&sh.hist[v[u] & 0xfff], 1u);
   __syncthreads();
   find_bin<NT>(sh, top_k - above1);
   const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;

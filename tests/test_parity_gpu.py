@@ -203,11 +203,14 @@ def test_fused_index_topk_top_far_above_thresholds():
     (30000, 24, 0, 3),          # <= 32768, every key in one bin: the sampled list overflows
     (30000, 24, 1, -1),         # <= 32768, keys 4096*k + {0,1,2}: short list, ties at tau
     (33005, 2050, 5, 40000),    # > 32768 candidates and > 2048 rows: three passes over HBM
+    (30000, 24, 2, -2),         # <= 32768, the top far above the sampled threshold: the list
+                                # holds it, but beyond the fine bins, so the registers decide
 ])
 def test_topk_row_paths(seq_len, q_len, prefix, vals):
-    """Stand-alone top-K on score rows written directly (random ints in [-vals, vals), or for
-    vals < 0 multiples of 4096 in [-20, 20) plus 0..2), for each single-row selection path and
-    both outcomes of the sampled short list; sampled rows must equal the oracle's lists."""
+    """Stand-alone top-K on score rows written directly (random ints in [-vals, vals); for
+    vals == -1 multiples of 4096 in [-20, 20) plus 0..2; for vals == -2 ints in [-2000, 2000)
+    with 1500 tokens per row raised to 600000 plus 0..49), for each single-row selection path
+    and every outcome of the sampled short list; sampled rows must equal the oracle's lists."""
     top_k = 1000
     _banner(f"topk rows seq_len={seq_len} q_len={q_len} P={prefix} vals={vals}")
     w = W(num_q_heads=1, num_kv_heads=1, head_dim=64, idx_dim=32, seq_len=seq_len, q_len=q_len,
@@ -218,6 +221,11 @@ def test_topk_row_paths(seq_len, q_len, prefix, vals):
     stride = (seq_len + 3) & ~3  # the ABI takes row strides in multiples of 4 scores
     if vals > 0:
         scores = torch.randint(-vals, vals, (1, q_len, 1, stride), generator=gen, dtype=torch.int32)
+    elif vals == -2:
+        scores = torch.randint(-2000, 2000, (1, q_len, 1, stride), generator=gen, dtype=torch.int32)
+        for i in range(q_len):
+            hot = torch.randperm(seq_len - 3 * q_len, generator=gen)[:1500]
+            scores[0, i, 0, hot] = 600000 + torch.randint(0, 50, (1500,), generator=gen, dtype=torch.int32)
     else:
         scores = (4096 * torch.randint(-20, 20, (1, q_len, 1, stride), generator=gen, dtype=torch.int32)
                   + torch.randint(0, 3, (1, q_len, 1, stride), generator=gen, dtype=torch.int32))
