@@ -150,21 +150,31 @@ __global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __r
     }
   }
 
-  for (int blk = blk_first; blk <= blk_last; ++blk) {
-    const int t0 = blk << 6;
-    const int64_t phys = phys_page(kv, b, t0);
-    if (phys < 0) continue;
-    const int slot0 = t0 & (kv.page_size - 1);
+  // Block k of the item is loaded one step before it is multiplied, and its page-table entry
+  // one step before that. All of these loads are unconditional (a missing page reads page 0;
+  // the page-table index is clamped) so that none is waited for where it is issued; a block
+  // without a page is skipped at compute time.
+  auto raw_page = [&](int blk) -> int32_t {
+    const int lp = min((blk << 6) >> kv.page_shift, kv.max_pages_per_seq - 1);
+    return kv.page_table[(int64_t)b * kv.max_pages_per_seq + lp];
+  };
+  // A operand: 4 key blocks of 16, lane holds key (m*16 + l16), bytes lg*CH .. +CH.
+  auto load_k = [&](int blk, int32_t raw, i64x1 (&ka)[4][KS]) -> bool {
+    const int lp = (blk << 6) >> kv.page_shift;
+    const bool ok = lp < kv.max_pages_per_seq && raw >= 0 && raw < kv.num_pages;
+    const int64_t phys = ok ? raw : 0;
     const int8_t* kbase = kv.kidx_pool +
-        ((phys * kv.num_idx_heads + gi) * kv.page_size + slot0) * (int64_t)D;
-    // A operand: 4 key blocks of 16, lane holds key (m*16 + l16), bytes lg*CH .. +CH.
-    i64x1 ka[4][KS];
+        ((phys * kv.num_idx_heads + gi) * kv.page_size + ((blk << 6) & (kv.page_size - 1))) * (int64_t)D;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int8_t* kp = kbase + (m * 16 + l16) * D + lg * CH;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) ka[m][ks] = *reinterpret_cast<const i64x1*>(kp + ks * 8);
     }
+    return ok;
+  };
+  auto compute = [&](int blk, const i64x1 (&ka)[4][KS]) {
+    const int t0 = blk << 6;
     const bool full = (t0 >= P) && (t0 + 63 <= pmin);  // every (key, query) pair is a candidate
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -189,6 +199,18 @@ __global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __r
         }
       }
     }
+  };
+  i64x1 ka0[4][KS], ka1[4][KS];
+  int32_t r_next = raw_page(blk_first + 1);
+  bool ok0 = load_k(blk_first, raw_page(blk_first), ka0), ok1 = false;
+  for (int blk = blk_first; blk <= blk_last; blk += 2) {
+    int32_t r_after = raw_page(blk + 2);
+    if (blk + 1 <= blk_last) ok1 = load_k(blk + 1, r_next, ka1);
+    if (ok0) compute(blk, ka0);
+    if (blk + 1 > blk_last) break;
+    r_next = raw_page(blk + 3);
+    if (blk + 2 <= blk_last) ok0 = load_k(blk + 2, r_after, ka0);
+    if (ok1) compute(blk + 1, ka1);
   }
 }
 
