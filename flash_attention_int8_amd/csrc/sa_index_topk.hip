@@ -151,49 +151,58 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
       raw[u] = kv.page_table[(int64_t)r.b * kv.max_pages_per_seq + lp];
     }
   };
-  // scores slab `slab` of the chunk: key, whether the token is a candidate, token index
-  auto score_slab = [&](int slab, const int32_t (&raw)[U], uint32_t (&key)[U], bool (&in)[U],
-                        int (&tok)[U]) {
+  // Requests the keys of slab `slab` (its page-table entries in `raw`): unconditional loads, a
+  // block without a page reading page 0 and flagged in `ok`, so that the loads can stay in
+  // flight across the compaction of the previous slab.
+  auto issue_slab = [&](int slab, const int32_t (&raw)[U], v4i (&kd)[U][Blk<D>::R], bool (&ok)[U]) {
     const int blk0 = c * kFBlocks + slab * NW * U + wave * U;
-    int64_t base[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int blk = blk0 + u;
       const int lp = (blk << 6) >> kv.page_shift;
-      const bool ok = blk >= r.blk_first && blk <= r.blk_last && lp < kv.max_pages_per_seq &&
-                      raw[u] >= 0 && raw[u] < kv.num_pages;
-      base[u] = ok ? (((int64_t)raw[u] * kv.num_idx_heads + r.gi) * kv.page_size +
-                      ((blk << 6) & (kv.page_size - 1))) * (int64_t)D
-                   : -1;
+      ok[u] = blk >= r.blk_first && blk <= r.blk_last && lp < kv.max_pages_per_seq &&
+              raw[u] >= 0 && raw[u] < kv.num_pages;
+      const int64_t base = (((int64_t)(ok[u] ? raw[u] : 0) * kv.num_idx_heads + r.gi) * kv.page_size +
+                            ((blk << 6) & (kv.page_size - 1))) * (int64_t)D;
+      load_block<D>(kv.kidx_pool + base, lane, kd[u]);
     }
-    v4i kd[U][Blk<D>::R];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (base[u] >= 0) {
-        load_block<D>(kv.kidx_pool + base[u], lane, kd[u]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < Blk<D>::R; ++q) kd[u][q] = v4i{0, 0, 0, 0};
-      }
-    }
+  };
+  // scores a loaded slab: key, whether the token is a candidate, token index
+  auto score_slab = [&](int slab, const v4i (&kd)[U][Blk<D>::R], const bool (&ok)[U], uint32_t (&key)[U],
+                        bool (&in)[U], int (&tok)[U]) {
+    const int blk0 = c * kFBlocks + slab * NW * U + wave * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = to_token_order<D>(score_block<D>(qf, kd[u], lane), lane);
       tok[u] = ((blk0 + u) << 6) + lane;
-      in[u] = base[u] >= 0 && tok[u] >= r.P && tok[u] <= r.pos;
+      in[u] = ok[u] && tok[u] >= r.P && tok[u] <= r.pos;
       key[u] = score_key(s);
     }
   };
+  constexpr int kSlabs = kFBlocks / (NW * U);
   uint32_t key[U];
-  bool in[U], keep[U];
+  bool in[U], keep[U], ok[U];
   int tok[U];
   int32_t raw_cur[U], raw_nxt[U];
+  v4i kd[U][Blk<D>::R];
   slab_pages(0, raw_cur);
   slab_pages(1, raw_nxt);
+  issue_slab(0, raw_cur, kd, ok);
+  // After a slab is scored its registers take the next slab's loads, which stay in flight
+  // while the slab is compacted (and, for the first slab, while the threshold is found).
+  auto next_slab = [&](int slab) {
+    if (slab + 1 < kSlabs) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) raw_cur[u] = raw_nxt[u];
+      slab_pages(slab + 2, raw_nxt);  // past the chunk: clamped, in bounds, never used
+      issue_slab(slab + 1, raw_cur, kd, ok);
+    }
+  };
   // The chunk's threshold from its first slab: the highest bin whose tail holds well over the
   // slab's share of K (twice the expected count plus three standard deviations plus 8). Any
   // value is safe: the final pass checks it and rescores the row if it was too high.
-  score_slab(0, raw_cur, key, in, tok);
+  score_slab(0, kd, ok, key, in, tok);
+  next_slab(0);
 #pragma unroll
   for (int u = 0; u < U; ++u)
     if (in[u]) atomicAdd(&sh.hist[key[u] >> 12], 1u);
@@ -214,11 +223,9 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
 #pragma unroll
   for (int u = 0; u < U; ++u) keep[u] = in[u] && (key[u] >> 12) >= th;
   int fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, 0);
-  for (int slab = 1; slab < kFBlocks / (NW * U); ++slab) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) raw_cur[u] = raw_nxt[u];
-    slab_pages(slab + 1, raw_nxt);  // past the chunk: clamped, in bounds, never used
-    score_slab(slab, raw_cur, key, in, tok);
+  for (int slab = 1; slab < kSlabs; ++slab) {
+    score_slab(slab, kd, ok, key, in, tok);
+    next_slab(slab);
 #pragma unroll
     for (int u = 0; u < U; ++u) keep[u] = in[u] && (key[u] >> 12) >= th;
     fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, fill);
