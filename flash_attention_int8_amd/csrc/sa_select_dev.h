@@ -86,17 +86,29 @@ __device__ __forceinline__ int wave_find_bin(const uint32_t* hist, int k, int* a
   return __builtin_amdgcn_readlane(bin, L);
 }
 
-// Bin holding the k-th largest element of a histogram of NW * 64 bins in LDS (wave w totals
-// bins [64w, 64w + 64) into seg[w], one barrier, then every wave finds the segment and the
-// bin inside it on its own, so all waves leave with the same answer). Writes the number of
-// elements in higher bins to *above; returns -1 if the histogram holds fewer than k.
-template <int NW>
+// Bin holding the k-th largest element of a histogram of NW * 64 * BPL bins in LDS (wave w
+// totals bins [w * 64 * BPL, (w + 1) * 64 * BPL) into seg[w], one barrier, then every wave
+// finds the segment and the bin inside it on its own, so all waves leave with the same
+// answer). Writes the number of elements in higher bins to *above; returns -1 if the
+// histogram holds fewer than k. BPL is 1 or a multiple of 4.
+template <int NW, int BPL = 1>
 __device__ __forceinline__ int block_find_bin_segments(const uint32_t* hist, int32_t* seg, int k,
                                                        int* above) {
+  static_assert(BPL == 1 || BPL % 4 == 0, "bins per lane: 1 or a multiple of 4");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   {
-    const int t = wave_incl_sum((int)hist[wave * 64 + lane]);
+    int v = 0;
+    if constexpr (BPL == 1) {
+      v = (int)hist[wave * 64 + lane];
+    } else {
+#pragma unroll
+      for (int i = 0; i < BPL; i += 4) {
+        const uint4 q = *reinterpret_cast<const uint4*>(hist + (wave * 64 + lane) * BPL + i);
+        v += (int)(q.x + q.y + q.z + q.w);
+      }
+    }
+    const int t = wave_incl_sum(v);
     if (lane == 63) seg[wave] = t;
   }
   __syncthreads();
@@ -107,13 +119,20 @@ __device__ __forceinline__ int block_find_bin_segments(const uint32_t* hist, int
   if (hit == 0) return -1;
   const int S = __builtin_ctzll(hit);
   const int base_s = __builtin_amdgcn_readlane(above_s, S);
-  const int hv = (int)hist[S * 64 + lane];
-  const int incl_b = wave_incl_sum(hv);
-  const int ab = base_s + __builtin_amdgcn_readlane(incl_b, 63) - incl_b;  // in higher bins
-  const uint64_t hit2 = __ballot(ab < k && ab + hv >= k);
-  const int L = __builtin_ctzll(hit2);
-  *above = __builtin_amdgcn_readlane(ab, L);
-  return S * 64 + L;
+  if constexpr (BPL == 1) {
+    const int hv = (int)hist[S * 64 + lane];
+    const int incl_b = wave_incl_sum(hv);
+    const int ab = base_s + __builtin_amdgcn_readlane(incl_b, 63) - incl_b;  // in higher bins
+    const uint64_t hit2 = __ballot(ab < k && ab + hv >= k);
+    const int L = __builtin_ctzll(hit2);
+    *above = __builtin_amdgcn_readlane(ab, L);
+    return S * 64 + L;
+  } else {
+    int ab = 0;
+    const int bin = wave_find_bin<BPL>(hist + S * 64 * BPL, k - base_s, &ab);
+    *above = base_s + ab;
+    return S * 64 * BPL + bin;
+  }
 }
 
 // Inclusive prefix sum over the workgroup (thread order); returns the inclusive value and

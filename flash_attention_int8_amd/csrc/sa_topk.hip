@@ -25,31 +25,36 @@ namespace {
 using namespace sel;
 
 
-// Rows of at most NT * PER candidates are held in registers: wave w holds candidates
-// [w * PER * 64, (w + 1) * PER * 64) (candidate j is token P + j), slot u and lane l holding
-// j = w * PER * 64 + u * 64 + l, so the row is read once with every thread's PER loads in
-// flight together, and token order is wave-major: an ordered write needs one scan over the
-// waves, and the offsets inside a wave come from ballots. A strided sample of 1024 keys sets
-// a provisional threshold bin theta (its tail holds 1.5 times the sampled share of K plus
-// three standard deviations plus 8); the keys in bins >= theta are compacted, in token order,
-// into a short list in LDS. When the list holds at least K keys, the K largest keys of the
-// row are the K largest on it (every key of the row at or above theta << 12 is on the list):
-// a histogram of 256-unit fine bins above theta << 12 locates the K-th largest to one fine
-// bin, and a 256-entry histogram of that bin gives it exactly. Otherwise (too few or too many
-// keys on the list, or the K-th largest beyond the fine range) the exact select runs over the
-// registers, so the result never depends on the sample.
-template <int NT, int PER, int CAND>
-__global__ __launch_bounds__(NT) void k_topk_row_reg(KvView kv, const int32_t* __restrict__ scores,
-                                                     int64_t row_stride, int q_len, int q_tail,
-                                                     int top_k, int32_t* __restrict__ indices) {
+// Rows of up to 32768 candidates, streamed from the score row by one 256-thread workgroup
+// per row: few registers and about 39 KB of LDS, so four rows are in flight per CU and their
+// latencies overlap. Wave w streams the contiguous quarter [w * Q, (w + 1) * Q) of the row
+// (Q a multiple of 64), so token order is wave-major.
+//   sample    1024 keys at evenly spaced positions give a threshold bin theta (its tail holds
+//             1.25 times the sampled share of K plus three standard deviations plus 8);
+//   stream    every key at or above T = theta << 12 is appended, in token order, to its wave's
+//             list in LDS (ballots only, no barrier); the next batch of loads is in flight while
+//             one is appended;
+//   select    when the lists hold at least K keys and none overflowed, the K largest keys of the
+//             row are the K largest on the lists (every key >= T is on one): a 256-bin histogram
+//             of 512-unit bins above T and a 512-entry histogram of the bin holding the K-th
+//             largest give it exactly, and the output is written from the lists in order;
+//   fallback  otherwise the exact two-digit radix select streams the row again, its 4096-bin
+//             histograms held in the list space.
+constexpr int kStrNT = 256;
+constexpr int kStrCap = 1536;  // list entries per wave
+constexpr int kStrLd = 8;      // keys per lane per batch
+
+__global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int32_t* __restrict__ scores,
+                                                          int64_t row_stride, int q_len, int q_tail,
+                                                          int top_k, int32_t* __restrict__ indices) {
+  constexpr int NT = kStrNT;
   constexpr int NW = NT / 64;
-  constexpr int kSample = 1024;
-  constexpr int kFine = NW * 64;  // fine bins: one 64-bin segment per wave
-  static_assert(kFine + 256 + NW <= kBins, "the fine histograms fit in the shared histogram");
-  static_assert(NT * PER <= 65536, "list positions are 16-bit");
-  __shared__ TopkShared<NT> sh;
-  __shared__ uint32_t l_key[CAND];  // short list: keys ...
-  __shared__ uint16_t l_pos[CAND];  // ... and positions j, token order
+  constexpr int kBatch = 64 * kStrLd;
+  static_assert(NW * kStrCap >= kBins, "the list space holds a 4096-bin histogram");
+  __shared__ __align__(16) uint32_t l_key[NW * kStrCap];  // per-wave lists (or a histogram)
+  __shared__ uint16_t l_pos[NW * kStrCap];
+  __shared__ __align__(16) uint32_t s_hist[768];          // fine (256) and sub (512) bins
+  __shared__ int32_t s_cnt[NW], s_cnt2[NW], s_seg[NW];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -73,166 +78,193 @@ __global__ __launch_bounds__(NT) void k_topk_row_reg(KvView kv, const int32_t* _
     for (int j = nf + m + tid; j < W; j += NT) out[j] = -1;
     return;
   }
-  auto jid = [&](int u) { return wv * (PER * 64) + u * 64 + lane; };
-  // Every load is issued before any is used: the index is clamped into the row instead of
-  // guarding the load (a guarded load makes the compiler wait for it on the spot), and the
-  // entries past the row are zeroed afterwards.
-  uint32_t v[PER];
+  out += nf;
+  const int Q = ((n + NW * 64 - 1) / (NW * 64)) * 64;
+  const int j_begin = wv * Q, j_end = min(n, j_begin + Q);  // this wave's candidates
+  // kStrLd keys of the row per lane, requested together (index clamped into the row, so no
+  // load is guarded and none is waited for where it is issued)
+  auto load_batch = [&](int j0, uint32_t (&k)[kStrLd]) {
 #pragma unroll
-  for (int u = 0; u < PER; ++u) v[u] = (uint32_t)srow[P + min(jid(u), n - 1)];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) v[u] = jid(u) < n ? score_key((int32_t)v[u]) : 0u;
-  auto clear_hist = [&]() {
-    __syncthreads();  // every wave has read the previous histogram and found_bin/found_above
-    for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
-    if (tid == 0) {
-      sh.found_bin = 0;
-      sh.found_above = 0;
-    }
-    __syncthreads();
+    for (int u = 0; u < kStrLd; ++u) k[u] = (uint32_t)srow[P + min(j0 + u * 64 + lane, n - 1)];
   };
-  // Ordered output from the registers: keys > tau, and the first `need` keys == tau.
-  auto emit_regs = [&](uint32_t tau, int need) {
-    int gt_w = 0, eq_w = 0;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      gt_w += __popcll(__ballot(jid(u) < n && v[u] > tau));
-      eq_w += __popcll(__ballot(jid(u) < n && v[u] == tau));
-    }
-    if (lane == 0) {
-      sh.wave_tot[wv] = gt_w;
-      sh.wave_tot2[wv] = eq_w;
-    }
-    __syncthreads();
-    int gb = 0, eb = 0;
-    for (int w = 0; w < wv; ++w) {
-      gb += sh.wave_tot[w];
-      eb += sh.wave_tot2[w];
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int j = jid(u);
-      const bool gt = j < n && v[u] > tau;
-      const bool eq = j < n && v[u] == tau;
-      const uint64_t gm = __ballot(gt), em = __ballot(eq);
-      const int g = gb + __popcll(gm & lt_mask);
-      const int e = eb + __popcll(em & lt_mask);
-      if (gt || (eq && e < need)) out[nf + g + min(e, need)] = P + j;
-      gb += __popcll(gm);
-      eb += __popcll(em);
+  // visits every key of this wave's range in order: f(j0, keys) per batch, loads one batch ahead
+  auto stream = [&](auto&& f) {
+    uint32_t ka[kStrLd], kb[kStrLd];
+    int j0 = j_begin;
+    if (j0 < j_end) load_batch(j0, ka);
+    for (; j0 < j_end; j0 += 2 * kBatch) {
+      const int j1 = j0 + kBatch;
+      if (j1 < j_end) load_batch(j1, kb);
+      f(j0, ka);
+      if (j1 >= j_end) break;
+      if (j1 + kBatch < j_end) load_batch(j1 + kBatch, ka);
+      f(j1, kb);
     }
   };
 
-  // provisional threshold from a strided sample (re-read from the row, now in the caches)
-  clear_hist();
-  const int ns = min(kSample, n);
-  for (int s = tid; s < ns; s += NT)
-    atomicAdd(&sh.hist[score_key(srow[P + (int)((int64_t)s * n / ns)]) >> 12], 1u);
+  // sample: 1024 evenly spaced keys into a 4096-bin histogram (in the list space)
+  for (int j = tid; j < kBins; j += NT) l_key[j] = 0u;
+  __syncthreads();
+  const int ns = min(1024, n);
+  {
+    uint32_t sk[1024 / NT];
+#pragma unroll
+    for (int t = 0; t < 1024 / NT; ++t)
+      sk[t] = (uint32_t)srow[P + (int)((int64_t)min(tid + t * NT, ns - 1) * n / ns)];
+#pragma unroll
+    for (int t = 0; t < 1024 / NT; ++t)
+      if (tid + t * NT < ns) atomicAdd(&l_key[score_key((int32_t)sk[t]) >> 12], 1u);
+  }
   __syncthreads();
   const float expect = (float)top_k * (float)ns / (float)n;
-  const int target = (int)(1.5f * expect + 3.f * sqrtf(expect) + 8.f);
-  uint32_t th = 0;
+  const int target = (int)(1.25f * expect + 3.f * sqrtf(expect) + 8.f);
+  uint32_t T = 0u;
   if (target < ns) {
-    find_bin<NT>(sh, target);
-    th = (uint32_t)sh.found_bin;
+    int ab = 0;
+    T = (uint32_t)block_find_bin_segments<NW, 16>(l_key, s_seg, target, &ab) << 12;
   }
-  // short list of the keys in bins >= th; the fine histograms are cleared on the way
-  int cnt_w = 0;
+  for (int j = tid; j < 768; j += NT) s_hist[j] = 0u;
+  __syncthreads();  // the sample histogram is no longer read
+
+  // stream the row into the per-wave lists
+  uint32_t* lk = l_key + wv * kStrCap;
+  uint16_t* lp = l_pos + wv * kStrCap;
+  int cnt = 0;
+  stream([&](int j0, const uint32_t (&k)[kStrLd]) {
 #pragma unroll
-  for (int u = 0; u < PER; ++u) cnt_w += __popcll(__ballot(jid(u) < n && (v[u] >> 12) >= th));
-  if (lane == 0) sh.wave_tot[wv] = cnt_w;
-  for (int j = tid; j < kFine + 256; j += NT) sh.hist[j] = 0;
-  __syncthreads();
-  int off = 0, m = 0;
-  for (int w = 0; w < NW; ++w) {
-    const int x = sh.wave_tot[w];
-    off += (w < wv) ? x : 0;
-    m += x;
-  }
-  if (m >= top_k && m <= CAND) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const bool keep = jid(u) < n && (v[u] >> 12) >= th;
+    for (int u = 0; u < kStrLd; ++u) {
+      const int j = j0 + u * 64 + lane;
+      const uint32_t key = score_key((int32_t)k[u]);
+      const bool keep = j < j_end && key >= T;
       const uint64_t km = __ballot(keep);
-      const int o = off + __popcll(km & lt_mask);
-      if (keep) {
-        l_key[o] = v[u];
-        l_pos[o] = (uint16_t)jid(u);
+      const int o = cnt + __popcll(km & lt_mask);
+      if (keep && o < kStrCap) {
+        lk[o] = key;
+        lp[o] = (uint16_t)j;
       }
-      off += __popcll(km);
+      cnt += __popcll(km);
     }
-    __syncthreads();  // the list is complete
-    const uint32_t base = th << 12;
-    for (int c = tid; c < m; c += NT)
-      atomicAdd(&sh.hist[min((l_key[c] - base) >> 8, (uint32_t)kFine - 1)], 1u);
+  });
+  if (lane == 0) s_cnt[wv] = cnt;
+  __syncthreads();
+  int m = 0;
+  bool over = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    m += s_cnt[w];
+    over = over || s_cnt[w] > kStrCap;
+  }
+  if (m >= top_k && !over) {
+    for (int c = lane; c < cnt; c += 64) atomicAdd(&s_hist[min((lk[c] - T) >> 9, 255u)], 1u);
     __syncthreads();
     int above_fb = 0;
-    const int fb = block_find_bin_segments<NW>(sh.hist, reinterpret_cast<int32_t*>(sh.hist + kFine + 256),
-                                               top_k, &above_fb);
-    if (fb >= 0 && fb < kFine - 1) {  // uniform
-      const uint32_t lo = base + ((uint32_t)fb << 8);
-      for (int c = tid; c < m; c += NT) {
-        const uint32_t key = l_key[c];
-        if (key >= lo && key < lo + 256u) atomicAdd(&sh.hist[kFine + (key & 255u)], 1u);
+    const int fb = block_find_bin_segments<NW, 1>(s_hist, s_seg, top_k, &above_fb);
+    if (fb >= 0 && fb < 255) {  // uniform
+      const uint32_t lo = T + ((uint32_t)fb << 9);
+      for (int c = lane; c < cnt; c += 64) {
+        const uint32_t key = lk[c];
+        if (key >= lo && key < lo + 512u) atomicAdd(&s_hist[256 + (key - lo)], 1u);
       }
       __syncthreads();
       int above_sb = 0;
-      const int sb = wave_find_bin<4>(sh.hist + kFine, top_k - above_fb, &above_sb);
+      const int sb = wave_find_bin<8>(s_hist + 256, top_k - above_fb, &above_sb);
       const uint32_t tau = lo + (uint32_t)sb;
       const int need = top_k - above_fb - above_sb;
-      // ordered output over the list: wave segments, counts by ballot, one scan over the waves
-      const int seg = ((m + NW * 64 - 1) / (NW * 64)) * 64;
-      const int s0 = wv * seg, s1 = min(m, s0 + seg);
       int gt_w = 0, eq_w = 0;
-      for (int c0 = s0; c0 < s1; c0 += 64) {
+      for (int c0 = 0; c0 < cnt; c0 += 64) {
         const int c = c0 + lane;
-        const uint32_t key = c < s1 ? l_key[c] : 0u;
-        gt_w += __popcll(__ballot(c < s1 && key > tau));
-        eq_w += __popcll(__ballot(c < s1 && key == tau));
+        const uint32_t key = c < cnt ? lk[c] : 0u;
+        gt_w += __popcll(__ballot(c < cnt && key > tau));
+        eq_w += __popcll(__ballot(c < cnt && key == tau));
       }
       if (lane == 0) {
-        sh.wave_tot[wv] = gt_w;
-        sh.wave_tot2[wv] = eq_w;
+        s_cnt[wv] = gt_w;
+        s_cnt2[wv] = eq_w;
       }
       __syncthreads();
       int gt_run = 0, eq_run = 0;
       for (int w = 0; w < wv; ++w) {
-        gt_run += sh.wave_tot[w];
-        eq_run += sh.wave_tot2[w];
+        gt_run += s_cnt[w];
+        eq_run += s_cnt2[w];
       }
-      for (int c0 = s0; c0 < s1 && gt_run + min(eq_run, need) < top_k; c0 += 64) {
+      for (int c0 = 0; c0 < cnt && gt_run + min(eq_run, need) < top_k; c0 += 64) {
         const int c = c0 + lane;
-        const uint32_t key = c < s1 ? l_key[c] : 0u;
-        const bool gt = c < s1 && key > tau;
-        const bool eq = c < s1 && key == tau;
+        const uint32_t key = c < cnt ? lk[c] : 0u;
+        const bool gt = c < cnt && key > tau;
+        const bool eq = c < cnt && key == tau;
         const uint64_t gm = __ballot(gt), em = __ballot(eq);
         const int gt_before = gt_run + __popcll(gm & lt_mask);
         const int eq_before = eq_run + __popcll(em & lt_mask);
-        if (gt || (eq && eq_before < need)) out[nf + gt_before + min(eq_before, need)] = P + (int)l_pos[c];
+        if (gt || (eq && eq_before < need)) out[gt_before + min(eq_before, need)] = P + (int)lp[c];
         gt_run += __popcll(gm);
         eq_run += __popcll(em);
       }
       return;
     }
   }
-  // exact select over the registers
-  clear_hist();
-#pragma unroll
-  for (int u = 0; u < PER; ++u)
-    if (jid(u) < n) atomicAdd(&sh.hist[v[u] >> 12], 1u);
+  // exact two-digit radix select, streamed; the histograms live in the list space
+  uint32_t* hist = l_key;
+  __syncthreads();  // the lists are no longer read
+  for (int j = tid; j < kBins; j += NT) hist[j] = 0u;
   __syncthreads();
-  find_bin<NT>(sh, top_k);
-  const uint32_t b1 = sh.found_bin;
-  const int above1 = sh.found_above;
-  clear_hist();
+  stream([&](int j0, const uint32_t (&k)[kStrLd]) {
 #pragma unroll
-  for (int u = 0; u < PER; ++u)
-    if (jid(u) < n && (v[u] >> 12) == b1) atomicAdd(&sh.hist[v[u] & 0xfff], 1u);
+    for (int u = 0; u < kStrLd; ++u)
+      if (j0 + u * 64 + lane < j_end) atomicAdd(&hist[score_key((int32_t)k[u]) >> 12], 1u);
+  });
   __syncthreads();
-  find_bin<NT>(sh, top_k - above1);
-  const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
-  const int need = top_k - above1 - sh.found_above;
-  emit_regs(tau, need);
+  int above1 = 0;
+  const uint32_t b1 = (uint32_t)block_find_bin_segments<NW, 16>(hist, s_seg, top_k, &above1);
+  __syncthreads();
+  for (int j = tid; j < kBins; j += NT) hist[j] = 0u;
+  __syncthreads();
+  stream([&](int j0, const uint32_t (&k)[kStrLd]) {
+#pragma unroll
+    for (int u = 0; u < kStrLd; ++u) {
+      const uint32_t key = score_key((int32_t)k[u]);
+      if (j0 + u * 64 + lane < j_end && (key >> 12) == b1) atomicAdd(&hist[key & 0xfff], 1u);
+    }
+  });
+  __syncthreads();
+  int above2 = 0;
+  const uint32_t b2 = (uint32_t)block_find_bin_segments<NW, 16>(hist, s_seg, top_k - above1, &above2);
+  const uint32_t tau = (b1 << 12) | b2;
+  const int need = top_k - above1 - above2;
+  int gt_w = 0, eq_w = 0;
+  stream([&](int j0, const uint32_t (&k)[kStrLd]) {
+#pragma unroll
+    for (int u = 0; u < kStrLd; ++u) {
+      const bool valid = j0 + u * 64 + lane < j_end;
+      const uint32_t key = score_key((int32_t)k[u]);
+      gt_w += __popcll(__ballot(valid && key > tau));
+      eq_w += __popcll(__ballot(valid && key == tau));
+    }
+  });
+  if (lane == 0) {
+    s_cnt[wv] = gt_w;
+    s_cnt2[wv] = eq_w;
+  }
+  __syncthreads();
+  int gt_run = 0, eq_run = 0;
+  for (int w = 0; w < wv; ++w) {
+    gt_run += s_cnt[w];
+    eq_run += s_cnt2[w];
+  }
+  stream([&](int j0, const uint32_t (&k)[kStrLd]) {
+#pragma unroll
+    for (int u = 0; u < kStrLd; ++u) {
+      const int j = j0 + u * 64 + lane;
+      const uint32_t key = score_key((int32_t)k[u]);
+      const bool gt = j < j_end && key > tau;
+      const bool eq = j < j_end && key == tau;
+      const uint64_t gm = __ballot(gt), em = __ballot(eq);
+      const int gt_before = gt_run + __popcll(gm & lt_mask);
+      const int eq_before = eq_run + __popcll(em & lt_mask);
+      if (gt || (eq && eq_before < need)) out[gt_before + min(eq_before, need)] = P + j;
+      gt_run += __popcll(gm);
+      eq_run += __popcll(em);
+    }
+  });
 }
 
 // Rows longer than the register path holds: three passes over the scores in global memory
@@ -563,11 +595,8 @@ hipError_t launch_topk(const KvView& kv, const int32_t* scores, int64_t row_stri
     return hipGetLastError();
   }
   // rows that fit are held in registers (one read of the scores); longer ones take three passes
-  if (longest <= 16384) {
-    hipLaunchKernelGGL((k_topk_row_reg<512, 32, 4096>), dim3((unsigned)rows), dim3(512), 0, stream,
-                       kv, scores, row_stride, q_len, q_tail, top_k, indices);
-  } else if (longest <= 32768) {
-    hipLaunchKernelGGL((k_topk_row_reg<1024, 32, 8192>), dim3((unsigned)rows), dim3(1024), 0, stream,
+  if (longest <= 32768) {
+    hipLaunchKernelGGL(k_topk_row_stream, dim3((unsigned)rows), dim3(kStrNT), 0, stream,
                        kv, scores, row_stride, q_len, q_tail, top_k, indices);
   } else {
     hipLaunchKernelGGL((k_topk_row<1024>), dim3((unsigned)rows), dim3(1024), 0, stream, kv, scores,

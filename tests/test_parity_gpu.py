@@ -199,12 +199,13 @@ def test_fused_index_topk_top_far_above_thresholds():
 
 
 @pytest.mark.parametrize("seq_len,q_len,prefix,vals", [
-    (16000, 40, 3, 100000),     # rows of <= 16384 candidates: staged in LDS, 512 threads
-    (30000, 24, 0, 3),          # <= 32768, every key in one bin: the sampled list overflows
-    (30000, 24, 1, -1),         # <= 32768, keys 4096*k + {0,1,2}: short list, ties at tau
+    (16000, 40, 3, 100000),     # rows of <= 32768 candidates, streamed: sampled lists
+    (30000, 24, 0, 3),          # <= 32768, every key in one bin: the lists overflow, so the
+                                # streamed two-digit radix select decides
+    (30000, 24, 1, -1),         # <= 32768, keys 4096*k + {0,1,2}: short lists, ties at tau
     (33005, 2050, 5, 40000),    # > 32768 candidates and > 2048 rows: three passes over HBM
-    (30000, 24, 2, -2),         # <= 32768, the top far above the sampled threshold: the list
-                                # holds it, but beyond the fine bins, so the registers decide
+    (30000, 24, 2, -2),         # <= 32768, the top far above the sampled threshold: the lists
+                                # hold it, but beyond the fine bins, so the radix select decides
 ])
 def test_topk_row_paths(seq_len, q_len, prefix, vals):
     """Stand-alone top-K on score rows written directly (random ints in [-vals, vals); for
