@@ -228,10 +228,12 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, qf[ks].v, s[mb], 0, 0, 0);
       }
   };
-  // Causal mask (only tiles that reach past the wave's first query need it), row max, and the
-  // move of the running maximum with its rescale of O and the row sum (the scale is positive,
-  // so it is applied in the exponent).
-  auto mask_and_max = [&](int tile, f32x16 (&s)[2]) {
+  // Causal mask (only tiles that reach past the wave's first query need it). The row maximum
+  // of the masked tile is taken a few elements per step inside the P V product of the tile
+  // before (so its VALU work sits between matrix instructions); finish_max combines the two
+  // halves of the row and moves the running maximum, rescaling O and the row sum (the scale
+  // is positive, so it is applied in the exponent).
+  auto mask_tile = [&](int tile, f32x16 (&s)[2]) {
     const int t0 = tile * BN;
     if (t0 + BN - 1 > pos0 + i_w) {
       const int lim = my_pos - t0 - hi * 4;  // key offsets above lim are masked
@@ -241,11 +243,8 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
         for (int r = 0; r < 16; ++r)
           if (mb * 32 + (r >> 2) * 8 + (r & 3) > lim) s[mb][r] = -INFINITY;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+  };
+  auto finish_max = [&](float mx) {
     mx = halves_max(mx);
     const float m_new = fmaxf(m_run, mx);
     // wave-uniform test; -inf - -inf is NaN and compares false
@@ -330,7 +329,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   };
   // O^T += V^T P^T. Step st = (mb, kk) covers keys mb*32 + kk*16 + {hi*4 + 0..3, 8 + hi*4 + 0..3},
   // the key permutation of the P^T fragments.
-  auto pv = [&](int buf, const Frag8 (&pf)[4]) {
+  auto pv = [&](int buf, const Frag8 (&pf)[4], const f32x16 (&sm)[2], float& mx, bool do_max) {
     auto vfrag = [&](int i) {  // i = st * DB + db; st outer: step st needs the first 8(st+1) exps
       const int st = i / DB, db = i % DB;
       const int kb = (st >> 1) * 32 + (st & 1) * 16 + hi * 4;
@@ -350,6 +349,10 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     for (int i = 0; i < 4 * DB; ++i) {
       o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % kVPre].v, pf[i / DB].v, o[i % DB], 0, 0, 0);
       if (i + kVPre < 4 * DB) va[i % kVPre] = vfrag(i + kVPre);
+      if (do_max) {
+#pragma unroll
+        for (int e = i * (32 / (4 * DB)); e < (i + 1) * (32 / (4 * DB)); ++e) mx = fmaxf(mx, sm[e >> 4][e & 15]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -384,7 +387,11 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   f32x16 sa[2], sb[2];
   if (last_w >= 0) {
     qk(0, sa);
-    mask_and_max(0, sa);
+    mask_tile(0, sa);
+    float mx0 = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) mx0 = fmaxf(mx0, sa[e >> 4][e & 15]);
+    finish_max(mx0);
   }
 
   // Iteration j: on entry K buffer (j+1)&1 holds K(j+1), V buffer j&1 holds V(j), sc holds the
@@ -401,19 +408,21 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     raw_next = raw_page(ltile + 1);
     load_rows(k_loader ? kv.k_pool : kv.v_pool, lt, ph, k_loader ? k_off : v_off, st);
     const int lim = valid_rows(lt, ph);
+    float mx = -INFINITY;
     if (j <= last_w) {
       // S(j+1) is computed unconditionally (one extra tile at the wave's end, never used) so
       // that its matrix instructions share a basic block with the exponentials of S(j).
       Frag8 pf[4];
       qk_softmax((j + 1) & 1, sn, sc, pf);
-      pv(j & 1, pf);
+      if (j + 1 <= last_w) mask_tile(j + 1, sn);
+      pv(j & 1, pf, sn, mx, j + 1 <= last_w);
     }
     if (more) {
       if (lim < BN) mask_rows(st, k_loader ? ld_kq * KPT : lv_kq * KPT, lim);
       if (k_loader) store_k(j & 1, st);
       else store_v((j + 1) & 1, st);
     }
-    if (j + 1 <= last_w) mask_and_max(j + 1, sn);
+    if (j + 1 <= last_w) finish_max(mx);
     __syncthreads();
   };
   for (int j = 0; j < n_tiles; j += 2) {
