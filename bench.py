@@ -181,7 +181,9 @@ def bench_prefill(fa, reps):
 
 def bench_sparse_prefill(fa, reps, q_chunk=2048):
     """Whole sparse prefill of 32K tokens (B=1, 32/8 heads, d=128, d_idx=64, top-K=2048): per
-    chunk of q_chunk queries, indexer scores -> top-K -> gathered attention."""
+    chunk of q_chunk queries, indexer scores -> top-K -> attention on masked dense tiles
+    (sparse_attn_fwd_prefill_masked). The gathered-row attention (sparse_attn_fwd_prefill with
+    the lists) is timed on the same lists in a separate pass."""
     import torch
 
     from synthetic import CONFIGS, make_inputs
@@ -199,9 +201,11 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048):
     q_idx = [inp.q_idx[:, q0:q0 + q_chunk].contiguous() for q0 in range(0, S, q_chunk)]
     tk_n = fa.sparse_attn_topk_workspace_size(kv, q_chunk, w.top_k)
     tk_ws = torch.empty(max(tk_n, 16), dtype=torch.uint8, device="cuda")
+    mk_n = fa.sparse_attn_prefill_masked_workspace_size(kv, q_chunk)
+    mk_ws = torch.empty(max(mk_n, 16), dtype=torch.uint8, device="cuda")
     scale = 1 / math.sqrt(d)
 
-    def run(evs=None):
+    def run(evs=None, gather=False):
         for c, q0 in enumerate(range(0, S, q_chunk)):
             n, tail = min(q_chunk, S - q0), S - q0
             if evs:
@@ -212,8 +216,13 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048):
             fa.sparse_attn_topk(kv, scores, stride, n, tail, w.top_k, idx, tk_ws, tk_n)
             if evs:
                 evs[c][2].record()
-            fa.sparse_attn_fwd_prefill(kv, inp.q[:, q0:q0 + n], Hq, n, tail, idx, w.index_width,
-                                       scale, out[:, q0:q0 + n], lse[:, q0:q0 + n])
+            if gather:
+                fa.sparse_attn_fwd_prefill(kv, inp.q[:, q0:q0 + n], Hq, n, tail, idx, w.index_width,
+                                           scale, out[:, q0:q0 + n], lse[:, q0:q0 + n])
+            else:
+                fa.sparse_attn_fwd_prefill_masked(kv, inp.q[:, q0:q0 + n], Hq, n, tail, idx,
+                                                  w.index_width, scale, mk_ws, mk_n,
+                                                  out[:, q0:q0 + n], lse[:, q0:q0 + n])
             if evs:
                 evs[c][3].record()
     run()
@@ -233,14 +242,24 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048):
     for c in range(chunks):
         for k in range(3):
             stage[k] += evs[c][k].elapsed_time(evs[c][k + 1])
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(chunks)]
+    run(gev, gather=True)
+    torch.cuda.synchronize()
+    gather_ms = sum(gev[c][2].elapsed_time(gev[c][3]) for c in range(chunks))
     # algorithmic attention flops: 4 heads x (QK + PV) per selected key per (query, group)
     sel = sum(min(w.top_k, i + 1) for i in range(S))
     attn_flop = 4.0 * d * Hq * sel
-    del inp, scores, idx, out, lse, q_idx, tk_ws
+    # the masked dense tiles compute every causal (query, key) pair
+    causal_flop = 4.0 * d * Hq * S * (S + 1) / 2
+    del inp, scores, idx, out, lse, q_idx, tk_ws, mk_ws
     torch.cuda.empty_cache()
     return {"workload": w.name, "ms": ms, "tokens_per_s": S / (ms * 1e-3),
             "stage_ms": {"index": stage[0], "topk": stage[1], "attention": stage[2]},
-            "attention_tflops": attn_flop / (stage[2] * 1e-3) / 1e12, "q_chunk": q_chunk}
+            "attention": "masked dense tiles (sparse_attn_fwd_prefill_masked)",
+            "attention_tflops": attn_flop / (stage[2] * 1e-3) / 1e12,
+            "attention_mfma_tflops": causal_flop / (stage[2] * 1e-3) / 1e12,
+            "attention_gathered_ms": gather_ms,
+            "q_chunk": q_chunk}
 
 
 def bench_decode_1m(fa, steps, warmup):

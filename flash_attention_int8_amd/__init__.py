@@ -26,7 +26,9 @@ SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_H
 EXPORTS = ["sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_index",
            "sparse_attn_topk_workspace_size", "sparse_attn_topk",
            "sparse_attn_index_topk_workspace_size", "sparse_attn_index_topk",
-           "sparse_attn_fwd_prefill", "sparse_attn_decode_workspace_size", "sparse_attn_fwd_decode"]
+           "sparse_attn_fwd_prefill", "sparse_attn_prefill_masked_workspace_size",
+           "sparse_attn_fwd_prefill_masked", "sparse_attn_decode_workspace_size",
+           "sparse_attn_fwd_decode"]
 
 
 class SparseAttnError(RuntimeError):
@@ -81,6 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sparse_attn_index_topk_workspace_size": (SZ, [KV, I32, I32]),
         "sparse_attn_index_topk": (I32, [KV, P, I32, I32, I32, P, P, SZ, P]),
         "sparse_attn_fwd_prefill": (I32, [KV, P, I32, I32, I32, P, I32, F32, P, P, P]),
+        "sparse_attn_prefill_masked_workspace_size": (SZ, [KV, I32]),
+        "sparse_attn_fwd_prefill_masked": (I32, [KV, P, I32, I32, I32, P, I32, F32, P, SZ, P, P, P]),
         "sparse_attn_decode_workspace_size": (SZ, [KV, I32, I32, I32]),
         "sparse_attn_fwd_decode": (I32, [KV, P, I32, P, I32, F32, I32, P, SZ, P, P, P]),
     }
@@ -196,6 +200,20 @@ def sparse_attn_fwd_prefill(kv: PagedKV, q, num_q_heads, q_len, q_tail, indices,
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
 
 
+def sparse_attn_prefill_masked_workspace_size(kv: PagedKV, q_len) -> int:
+    return int(load().sparse_attn_prefill_masked_workspace_size(kv.ref, q_len))
+
+
+def sparse_attn_fwd_prefill_masked(kv: PagedKV, q, num_q_heads, q_len, q_tail, indices, index_width,
+                                   sm_scale, workspace, workspace_bytes, out, lse=None, stream=None):
+    lib = load()
+    _check("sparse_attn_fwd_prefill_masked", lib.sparse_attn_fwd_prefill_masked(
+        kv.ref, _ptr(q, torch.bfloat16, "q"), num_q_heads, q_len, q_tail,
+        _ptr(indices, torch.int32, "indices"), index_width, float(sm_scale),
+        _ptr(workspace, None, "workspace"), workspace_bytes,
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
 def sparse_attn_decode_workspace_size(kv: PagedKV, num_q_heads, index_width, num_splits=0) -> int:
     return int(load().sparse_attn_decode_workspace_size(kv.ref, num_q_heads, index_width, num_splits))
 
@@ -268,6 +286,26 @@ def prefill(kv: PagedKV, q, q_tail, indices=None, sm_scale=None, out=None, lse=N
         lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
     width = 0 if indices is None else int(indices.shape[-1])
     sparse_attn_fwd_prefill(kv, q, Hq, q_len, q_tail, indices, width, sm_scale, out, lse, stream)
+    return out, lse
+
+
+def prefill_masked(kv: PagedKV, q, q_tail, indices, sm_scale=None, out=None, lse=None,
+                   workspace=None, want_lse=True, stream=None):
+    """Sparse prefill on dense matrix tiles: the same result as prefill(..., indices) (each
+    listed key counted once), computed over every causal key with the unselected ones masked."""
+    B, q_len, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+    need = sparse_attn_prefill_masked_workspace_size(kv, q_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    sparse_attn_fwd_prefill_masked(kv, q, Hq, q_len, q_tail, indices, int(indices.shape[-1]), sm_scale,
+                                   workspace, workspace.numel() * workspace.element_size(), out, lse,
+                                   stream)
     return out, lse
 
 

@@ -192,6 +192,35 @@ int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_
                                                 index_width, sm_scale, out, lse, s));
 }
 
+size_t sparse_attn_prefill_masked_workspace_size(const sa_paged_kv* kv, int32_t q_len) {
+  sa::KvView v;
+  if (check_kv(kv, 0, &v) != SA_OK || q_len < 1) return 0;
+  return sa::sel_workspace_bytes(v, q_len);
+}
+
+int32_t sparse_attn_fwd_prefill_masked(const sa_paged_kv* kv, const uint16_t* q,
+                                       int32_t num_q_heads, int32_t q_len, int32_t q_tail,
+                                       const int32_t* indices, int32_t index_width, float sm_scale,
+                                       void* workspace, size_t workspace_bytes, uint16_t* out,
+                                       float* lse, void* stream) {
+  sa::KvView v;
+  int32_t st = check_kv(kv, NEED_KV, &v);
+  if (st != SA_OK) return st;
+  if ((st = check_block(v, q_len, q_tail)) != SA_OK) return st;
+  if (q == nullptr || out == nullptr || indices == nullptr) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(indices) || (lse != nullptr && !aligned16(lse)))
+    return SA_ERR_ALIGN;
+  if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0) return SA_ERR_SHAPE;
+  if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return SA_ERR_SHAPE;
+  if (index_width < 1) return SA_ERR_SHAPE;
+  const size_t need = sa::sel_workspace_bytes(v, q_len);
+  if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SA_ERR_ALIGN;
+  return hip_status(sa::launch_attn_masked(v, q, num_q_heads, q_len, q_tail, indices, index_width,
+                                           sm_scale, workspace, out, lse,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t sparse_attn_decode_workspace_size(const sa_paged_kv* kv, int32_t num_q_heads,
                                          int32_t index_width, int32_t num_splits) {
   sa::KvView v;

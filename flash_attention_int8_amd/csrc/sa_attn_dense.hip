@@ -69,10 +69,11 @@ union Frag8 {
 //                 tiles j+2 (K) and j+1 (V) into LDS, mask + row max of S(j+1)]  ->  barrier
 // so that the exponentials of one tile are issued between the matrix instructions of the next
 // instead of after them. LDS holds two K tiles and two V^T tiles.
-template <int D>
+template <int D, bool MASKED>
 __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     KvView kv, const uint16_t* __restrict__ q, int num_q_heads, int q_len, int q_tail, float qscale,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int n_qblocks) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int n_qblocks,
+    const uint64_t* __restrict__ sel, int sel_qblocks, int sel_tiles) {
   constexpr int KS = D / 16;     // k-steps of QK^T
   constexpr int DB = D / 32;     // 32-dim blocks of O^T
   constexpr int CPR = D / 8;     // 16-byte chunks per row
@@ -122,6 +123,14 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   const int my_i = i_w + l32;
   const int my_pos = pos0 + my_i;
   const bool my_valid = my_i < q_len;
+  // Selection masks of this wave's 32 queries (masked mode): one 256-byte record per 64-key
+  // tile, 32 lane masks in the order of the S^T accumulator elements.
+  const uint64_t* selw = nullptr;
+  if constexpr (MASKED) {
+    const int gi = kv.num_idx_heads == 1 ? 0 : g;
+    const int qb = qblk * kDenseWaves + wave;
+    selw = sel + (((int64_t)b * kv.num_idx_heads + gi) * sel_qblocks + qb) * (int64_t)sel_tiles * 32;
+  }
 
   // Q^T fragments (B operand): lane holds query l32, dims ks*16 + hi*8 .. +8.
   Frag8 qf[KS];
@@ -233,7 +242,23 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   // before (so its VALU work sits between matrix instructions); finish_max combines the two
   // halves of the row and moves the running maximum, rescaling O and the row sum (the scale
   // is positive, so it is applied in the exponent).
+  // Masked mode: every key outside the query's selection (a subset of 0..pos) gets -inf, one
+  // v_cndmask per score with the tile record's lane masks (scalar loads) as the condition.
+  auto apply_sel = [&](const uint64_t (&mw)[32], f32x16 (&s)[2]) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s[mb][r] = __builtin_amdgcn_inverse_ballot_w64(mw[mb * 16 + r]) ? s[mb][r] : -INFINITY;
+  };
   auto mask_tile = [&](int tile, f32x16 (&s)[2]) {
+    if constexpr (MASKED) {  // the prologue's tile; the loop uses apply_sel
+      uint64_t mw[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) mw[k] = selw[(int64_t)tile * 32 + k];
+      apply_sel(mw, s);
+      return;
+    }
     const int t0 = tile * BN;
     if (t0 + BN - 1 > pos0 + i_w) {
       const int lim = my_pos - t0 - hi * 4;  // key offsets above lim are masked
@@ -413,8 +438,19 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
       // S(j+1) is computed unconditionally (one extra tile at the wave's end, never used) so
       // that its matrix instructions share a basic block with the exponentials of S(j).
       Frag8 pf[4];
+      // masked mode: the record of tile j+1 is requested before the QK^T of that tile so that
+      // the scalar loads are back when its scores are masked (clamped: in bounds, unused)
+      uint64_t mw[32];
+      if constexpr (MASKED) {
+        const uint64_t* w = selw + (int64_t)min(j + 1, last_w) * 32;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) mw[k] = w[k];
+      }
       qk_softmax((j + 1) & 1, sn, sc, pf);
-      if (j + 1 <= last_w) mask_tile(j + 1, sn);
+      // (masked mode applies the record unconditionally: S(j+1) is not used past last_w, and
+      // a conditional use would let the compiler sink the loads to it)
+      if constexpr (MASKED) apply_sel(mw, sn);
+      else if (j + 1 <= last_w) mask_tile(j + 1, sn);
       pv(j & 1, pf, sn, mx, j + 1 <= last_w);
     }
     if (more) {
@@ -452,24 +488,111 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
 template <int D>
 hipError_t launch_dense_d(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                           int q_tail, float sm_scale, uint16_t* out, float* lse,
-                          hipStream_t stream) {
+                          const uint64_t* sel, hipStream_t stream) {
   constexpr int BMQ = kDenseWaves * 32;
   const int nqb = (q_len + BMQ - 1) / BMQ;
   const int64_t wgs = (int64_t)nqb * kv.batch * num_q_heads;
-  hipLaunchKernelGGL((k_attn_dense<D>), dim3((unsigned)wgs), dim3(kDenseThreads), 0, stream, kv, q,
-                     num_q_heads, q_len, q_tail, sm_scale * kLog2e, out, lse, nqb);
+  if (sel == nullptr) {
+    hipLaunchKernelGGL((k_attn_dense<D, false>), dim3((unsigned)wgs), dim3(kDenseThreads), 0, stream,
+                       kv, q, num_q_heads, q_len, q_tail, sm_scale * kLog2e, out, lse, nqb,
+                       (const uint64_t*)nullptr, 0, 0);
+  } else {
+    hipLaunchKernelGGL((k_attn_dense<D, true>), dim3((unsigned)wgs), dim3(kDenseThreads), 0, stream,
+                       kv, q, num_q_heads, q_len, q_tail, sm_scale * kLog2e, out, lse, nqb, sel,
+                       sel_query_blocks(q_len), sel_tiles(kv));
+  }
   return hipGetLastError();
 }
 
+// Selection masks from index lists. One workgroup per (sequence, indexer head, block of 32
+// queries) builds the block's records for a range of up to kSelRange tiles in LDS (bits set
+// with LDS atomics, which commute) and writes them out whole, so every record of the
+// workspace is written, zeros included (queries past q_len, keys never selected).
+constexpr int kSelRange = 512;   // tiles per LDS pass: 512 x 256 B = 128 KiB
+constexpr int kSelThreads = 1024;
+
+__global__ __launch_bounds__(kSelThreads) void k_sel_masks(KvView kv, int q_len, int q_tail,
+                                                           const int32_t* __restrict__ indices, int W,
+                                                           uint64_t* __restrict__ sel, int n_qb,
+                                                           int n_tiles) {
+  __shared__ uint32_t bits[kSelRange * 64];  // [tile - j0][element w][lane half]
+  const int qb = blockIdx.x;
+  const int bg = blockIdx.y;  // b * H_idx + gi
+  const int b = bg / kv.num_idx_heads;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  constexpr int NW = kSelThreads / 64;
+  const int seq_len = min(kv.seq_lens[b], kv.max_seq_len);
+  uint64_t* dst = sel + ((int64_t)bg * n_qb + qb) * (int64_t)n_tiles * 32;
+  for (int j0 = 0; j0 < n_tiles; j0 += kSelRange) {
+    const int nt = min(kSelRange, n_tiles - j0);
+    for (int k = tid; k < nt * 16; k += kSelThreads)
+      reinterpret_cast<uint4*>(bits)[k] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    const int key_lo = j0 * BN, key_hi = (j0 + nt) * BN;  // keys of this range: [key_lo, key_hi)
+    for (int ql = wave; ql < 32; ql += NW) {
+      const int i = qb * 32 + ql;
+      if (i >= q_len) continue;  // wave-uniform
+      const int pos = seq_len - q_tail + i;
+      const int lim = min(pos + 1, min(seq_len, key_hi));  // keys >= lim are never attended
+      const int32_t* list = indices + (((int64_t)b * q_len + i) * kv.num_idx_heads +
+                                       (bg - b * kv.num_idx_heads)) * (int64_t)W;
+#pragma unroll 8
+      for (int e = lane; e < W; e += 64) {
+        const int t = list[e];
+        if (t >= key_lo && t < lim) {
+          const int o = t & (BN - 1);
+          const int o2 = o & 31;
+          const int w = (o >> 5) * 16 + (o2 >> 3) * 4 + (o2 & 3);
+          atomicOr(&bits[((t >> 6) - j0) * 64 + w * 2 + ((o2 >> 2) & 1)], 1u << ql);
+        }
+      }
+    }
+    __syncthreads();
+    uint4* d4 = reinterpret_cast<uint4*>(dst + (int64_t)j0 * 32);
+    for (int k = tid; k < nt * 16; k += kSelThreads) d4[k] = reinterpret_cast<const uint4*>(bits)[k];
+    __syncthreads();
+  }
+}
+
 }  // namespace
+
+int sel_query_blocks(int q_len) {
+  constexpr int BMQ = kDenseWaves * 32;
+  return (q_len + BMQ - 1) / BMQ * kDenseWaves;
+}
+
+int sel_tiles(const KvView& kv) { return (kv.max_seq_len + BN - 1) / BN; }
+
+size_t sel_workspace_bytes(const KvView& kv, int q_len) {
+  return (size_t)kv.batch * kv.num_idx_heads * sel_query_blocks(q_len) * sel_tiles(kv) * 256;
+}
 
 hipError_t launch_attn_dense(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                              int q_tail, float sm_scale, uint16_t* out, float* lse,
                              hipStream_t stream) {
   if (kv.head_dim == 128)
-    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, stream);
+    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, nullptr, stream);
   if (kv.head_dim == 64)
-    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, stream);
+    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, nullptr, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_masked(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
+                              int q_tail, const int32_t* indices, int index_width, float sm_scale,
+                              void* ws, uint16_t* out, float* lse, hipStream_t stream) {
+  uint64_t* sel = static_cast<uint64_t*>(ws);
+  const int n_qb = sel_query_blocks(q_len), n_tiles = sel_tiles(kv);
+  hipLaunchKernelGGL(k_sel_masks, dim3((unsigned)n_qb, (unsigned)(kv.batch * kv.num_idx_heads)),
+                     dim3(kSelThreads), 0, stream, kv, q_len, q_tail, indices, index_width, sel, n_qb,
+                     n_tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (kv.head_dim == 128)
+    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, stream);
+  if (kv.head_dim == 64)
+    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, stream);
   return hipErrorInvalidValue;
 }
 

@@ -144,4 +144,12 @@ hipError_t launch_attn_sparse_mfma(const KvView& kv, const uint16_t* q, int num_
 hipError_t launch_attn_dense(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                              int q_tail, float sm_scale, uint16_t* out, float* lse,
                              hipStream_t stream);
+// Masked-dense sparse prefill: selection masks built from index lists in the workspace, then
+// the dense kernel with every unselected score set to -inf.
+int sel_query_blocks(int q_len);
+int sel_tiles(const KvView& kv);
+size_t sel_workspace_bytes(const KvView& kv, int q_len);
+hipError_t launch_attn_masked(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
+                              int q_tail, const int32_t* indices, int index_width, float sm_scale,
+                              void* ws, uint16_t* out, float* lse, hipStream_t stream);
 }  // namespace sa

@@ -185,6 +185,30 @@ int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_
                                 void* stream);
 
 /*
+ * Sparse prefill on dense matrix tiles ([DSA-page] §2.3, prefill): the result of
+ * sparse_attn_fwd_prefill with the same index lists, computed by the dense causal kernel
+ * over every key 0..pos with each key that is not in the query's list masked out of the
+ * softmax. Its cost follows the causal length, not top_k, so it pays off when the lists are
+ * a large share of the causal keys or the gather is the bottleneck (long prefill blocks:
+ * matrix tiles instead of one 512-byte row gather per selected key).
+ *   q, out, lse  as for sparse_attn_fwd_prefill
+ *   indices      int32 [batch][q_len][num_idx_heads][index_width], entries -1 or token ids;
+ *                ids outside 0..min(pos, seq_len-1) are skipped, and a key listed more than
+ *                once counts once (lists from sparse_attn_topk never repeat a key)
+ * A query whose list holds no key gets out = 0 and lse = -inf.
+ * workspace: sparse_attn_prefill_masked_workspace_size(kv, q_len) bytes of device memory
+ * (one 64-bit lane mask per (32 queries, 64-key tile, score slot): batch * num_idx_heads *
+ * 8 * ceil(q_len / 256) * ceil(max_seq_len / 64) * 256 bytes); its contents on entry do not
+ * matter. head_dim 64 or 128; any group size H_q/H_kv.
+ */
+size_t sparse_attn_prefill_masked_workspace_size(const sa_paged_kv* kv, int32_t q_len);
+int32_t sparse_attn_fwd_prefill_masked(const sa_paged_kv* kv, const uint16_t* q,
+                                       int32_t num_q_heads, int32_t q_len, int32_t q_tail,
+                                       const int32_t* indices, int32_t index_width, float sm_scale,
+                                       void* workspace, size_t workspace_bytes, uint16_t* out,
+                                       float* lse, void* stream);
+
+/*
  * Decode attention ([DSA-page] §2.3, decode): one query token per sequence (pos =
  * seq_lens[b] - 1) attends to its index list. Each (b, KV group) list is cut into
  * num_splits chunks processed in parallel; partial softmax states (max, sum, weighted V in

@@ -16,7 +16,11 @@ from synthetic import Inputs
 
 MAX_ABS = 2e-2     # bf16 output vs fp64 oracle, max over elements
 MEAN_ABS = 2e-3    # ... mean over elements
-LSE_ABS = 2e-3     # fp32 log-sum-exp vs fp64
+# fp32 log-sum-exp vs fp64. The kernels round each P to bf16 before P.V and add those rounded
+# values into the row sum (so O is an exact convex combination of the weights P.V saw); a
+# rounded P is off by at most 2^-8 of itself, so the sum, and exp(LSE), by at most 2^-8:
+# |LSE error| <= ln(1 + 2^-8) = 3.9e-3, reached when one key dominates a short list.
+LSE_ABS = 4e-3
 
 
 class DevicePool:
@@ -59,9 +63,10 @@ class GpuRun:
 
 
 def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
-            keep_scores: bool = False, fused: bool = False) -> GpuRun:
+            keep_scores: bool = False, fused: bool = False, masked: bool = False) -> GpuRun:
     """The whole path on the device: index -> top-K -> attention (or dense attention).
-    fused=True selects with sparse_attn_index_topk instead of index then topk."""
+    fused=True selects with sparse_attn_index_topk instead of index then topk; masked=True
+    runs the prefill attention on masked dense tiles (sparse_attn_fwd_prefill_masked)."""
     w = inp.workload
     kv = make_kv(inp)
     r = GpuRun()
@@ -99,7 +104,11 @@ def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
             idx = fa.topk(kv, scores, c, tail, w.top_k)
             if keep_scores:
                 r.scores.append((q0, scores))
-        out, lse = fa.prefill(kv, inp.q[:, q0:q0 + c].contiguous(), q_tail=tail, indices=idx)
+        qc = inp.q[:, q0:q0 + c].contiguous()
+        if masked:
+            out, lse = fa.prefill_masked(kv, qc, q_tail=tail, indices=idx)
+        else:
+            out, lse = fa.prefill(kv, qc, q_tail=tail, indices=idx)
         r.indices[:, q0:q0 + c] = idx
         r.out[:, q0:q0 + c] = out
         r.lse[:, q0:q0 + c] = lse

@@ -93,6 +93,44 @@ def call_prefill(lib, d, q=A, hq=32, q_len=16, q_tail=16, idx=A, width=64, out=A
     return lib.sparse_attn_fwd_prefill(ctypes.byref(d), q, hq, q_len, q_tail, idx, width, scale, out, lse, None)
 
 
+def call_masked(lib, d, q=A, hq=32, q_len=16, q_tail=16, idx=A, width=64, ws=A, ws_bytes=1 << 30,
+                out=A, lse=None, scale=0.1):
+    return lib.sparse_attn_fwd_prefill_masked(ctypes.byref(d), q, hq, q_len, q_tail, idx, width, scale,
+                                              ws, ws_bytes, out, lse, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(q=None), fa.SA_ERR_NULL),
+    (dict(idx=None), fa.SA_ERR_NULL),
+    (dict(out=None), fa.SA_ERR_NULL),
+    (dict(d=desc(k_pool=None)), fa.SA_ERR_NULL),
+    (dict(hq=12), fa.SA_ERR_SHAPE),                      # not a multiple of H_kv = 8
+    (dict(width=0), fa.SA_ERR_SHAPE),
+    (dict(scale=0.0), fa.SA_ERR_SHAPE),
+    (dict(scale=float("nan")), fa.SA_ERR_SHAPE),
+    (dict(q_len=17, q_tail=16), fa.SA_ERR_SHAPE),
+    (dict(ws=None), fa.SA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), fa.SA_ERR_WORKSPACE),
+    (dict(ws=A + 8), fa.SA_ERR_ALIGN),
+    (dict(idx=A + 4), fa.SA_ERR_ALIGN),
+    (dict(d=desc(head_dim=96)), fa.SA_ERR_UNSUPPORTED),
+])
+def test_prefill_masked_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_masked(lib, d, **case) == code
+
+
+def test_prefill_masked_workspace_size(lib):
+    d = desc()  # B=2, H_idx=8, max_seq_len=1024 -> 16 tiles
+    for q_len, blocks in [(1, 1), (256, 1), (257, 2), (1000, 4)]:
+        want = 2 * 8 * 8 * blocks * 16 * 256
+        assert lib.sparse_attn_prefill_masked_workspace_size(ctypes.byref(d), q_len) == want
+    assert lib.sparse_attn_prefill_masked_workspace_size(ctypes.byref(d), 0) == 0
+    d1 = desc(num_idx_heads=1)
+    assert lib.sparse_attn_prefill_masked_workspace_size(ctypes.byref(d1), 256) == 2 * 8 * 16 * 256
+
+
 def call_decode(lib, d, q=A, hq=32, idx=A, width=2048, splits=4, ws=A, ws_bytes=1 << 30, out=A, lse=None,
                 scale=0.1):
     return lib.sparse_attn_fwd_decode(ctypes.byref(d), q, hq, idx, width, scale, splits, ws, ws_bytes,
