@@ -538,15 +538,27 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_masks(KvView kv, int q_len,
       const int lim = min(pos + 1, min(seq_len, key_hi));  // keys >= lim are never attended
       const int32_t* list = indices + (((int64_t)b * q_len + i) * kv.num_idx_heads +
                                        (bg - b * kv.num_idx_heads)) * (int64_t)W;
-#pragma unroll 8
-      for (int e = lane; e < W; e += 64) {
-        const int t = list[e];
+      auto set = [&](int t) {
         if (t >= key_lo && t < lim) {
           const int o = t & (BN - 1);
           const int o2 = o & 31;
           const int w = (o >> 5) * 16 + (o2 >> 3) * 4 + (o2 & 3);
           atomicOr(&bits[((t >> 6) - j0) * 64 + w * 2 + ((o2 >> 2) & 1)], 1u << ql);
         }
+      };
+      if ((W & 3) == 0) {  // rows start 16-byte aligned: four entries per load
+        const int4* l4 = reinterpret_cast<const int4*>(list);
+#pragma unroll 8
+        for (int e = lane; e < (W >> 2); e += 64) {
+          const int4 v = l4[e];
+          set(v.x);
+          set(v.y);
+          set(v.z);
+          set(v.w);
+        }
+      } else {
+#pragma unroll 8
+        for (int e = lane; e < W; e += 64) set(list[e]);
       }
     }
     __syncthreads();

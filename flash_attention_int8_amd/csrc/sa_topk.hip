@@ -26,18 +26,20 @@ using namespace sel;
 
 
 // Rows of up to 32768 candidates, streamed from the score row by one 256-thread workgroup
-// per row: few registers and about 39 KB of LDS, so four rows are in flight per CU and their
+// per row: few registers and about 26 KB of LDS, so six rows are in flight per CU and their
 // latencies overlap. Wave w streams the contiguous quarter [w * Q, (w + 1) * Q) of the row
 // (Q a multiple of 64), so token order is wave-major.
 //   sample    1024 keys at evenly spaced positions give a threshold bin theta (its tail holds
 //             1.25 times the sampled share of K plus three standard deviations plus 8);
 //   stream    every key at or above T = theta << 12 is appended, in token order, to its wave's
-//             list in LDS (ballots only, no barrier); the next batch of loads is in flight while
-//             one is appended;
+//             list in LDS (ballots only, no barrier) as one word: its offset above T (clamped
+//             to 65535) in the high half, its candidate index in the low half; the next batch
+//             of loads is in flight while one is appended;
 //   select    when the lists hold at least K keys and none overflowed, the K largest keys of the
 //             row are the K largest on the lists (every key >= T is on one): a 256-bin histogram
-//             of 512-unit bins above T and a 512-entry histogram of the bin holding the K-th
-//             largest give it exactly, and the output is written from the lists in order;
+//             of 256-unit bins above T and a 256-entry histogram of the bin holding the K-th
+//             largest give it exactly (the top bin, which holds the clamped offsets, must not
+//             be that bin), and the output is written from the lists in order;
 //   fallback  otherwise the exact two-digit radix select streams the row again, its 4096-bin
 //             histograms held in the list space.
 constexpr int kStrNT = 256;
@@ -51,9 +53,9 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
   constexpr int NW = NT / 64;
   constexpr int kBatch = 64 * kStrLd;
   static_assert(NW * kStrCap >= kBins, "the list space holds a 4096-bin histogram");
-  __shared__ __align__(16) uint32_t l_key[NW * kStrCap];  // per-wave lists (or a histogram)
-  __shared__ uint16_t l_pos[NW * kStrCap];
-  __shared__ __align__(16) uint32_t s_hist[768];          // fine (256) and sub (512) bins
+  // per-wave lists, entry = min(key - T, 65535) << 16 | candidate index (or a histogram)
+  __shared__ __align__(16) uint32_t l_key[NW * kStrCap];
+  __shared__ __align__(16) uint32_t s_hist[512];          // fine (256) and sub (256) bins
   __shared__ int32_t s_cnt[NW], s_cnt2[NW], s_seg[NW];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,12 +125,11 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
     int ab = 0;
     T = (uint32_t)block_find_bin_segments<NW, 16>(l_key, s_seg, target, &ab) << 12;
   }
-  for (int j = tid; j < 768; j += NT) s_hist[j] = 0u;
+  for (int j = tid; j < 512; j += NT) s_hist[j] = 0u;
   __syncthreads();  // the sample histogram is no longer read
 
   // stream the row into the per-wave lists
   uint32_t* lk = l_key + wv * kStrCap;
-  uint16_t* lp = l_pos + wv * kStrCap;
   int cnt = 0;
   stream([&](int j0, const uint32_t (&k)[kStrLd]) {
 #pragma unroll
@@ -138,10 +139,7 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
       const bool keep = j < j_end && key >= T;
       const uint64_t km = __ballot(keep);
       const int o = cnt + __popcll(km & lt_mask);
-      if (keep && o < kStrCap) {
-        lk[o] = key;
-        lp[o] = (uint16_t)j;
-      }
+      if (keep && o < kStrCap) lk[o] = (min(key - T, 65535u) << 16) | (uint32_t)j;
       cnt += __popcll(km);
     }
   });
@@ -155,25 +153,26 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
     over = over || s_cnt[w] > kStrCap;
   }
   if (m >= top_k && !over) {
-    for (int c = lane; c < cnt; c += 64) atomicAdd(&s_hist[min((lk[c] - T) >> 9, 255u)], 1u);
+    for (int c = lane; c < cnt; c += 64) atomicAdd(&s_hist[lk[c] >> 24], 1u);
     __syncthreads();
     int above_fb = 0;
     const int fb = block_find_bin_segments<NW, 1>(s_hist, s_seg, top_k, &above_fb);
     if (fb >= 0 && fb < 255) {  // uniform
-      const uint32_t lo = T + ((uint32_t)fb << 9);
+      // offsets (key - T) from here on; the clamped ones all lie in bin 255, above tau
+      const uint32_t lo = (uint32_t)fb << 8;
       for (int c = lane; c < cnt; c += 64) {
-        const uint32_t key = lk[c];
-        if (key >= lo && key < lo + 512u) atomicAdd(&s_hist[256 + (key - lo)], 1u);
+        const uint32_t off = lk[c] >> 16;
+        if (off >= lo && off < lo + 256u) atomicAdd(&s_hist[256 + (off - lo)], 1u);
       }
       __syncthreads();
       int above_sb = 0;
-      const int sb = wave_find_bin<8>(s_hist + 256, top_k - above_fb, &above_sb);
+      const int sb = wave_find_bin<4>(s_hist + 256, top_k - above_fb, &above_sb);
       const uint32_t tau = lo + (uint32_t)sb;
       const int need = top_k - above_fb - above_sb;
       int gt_w = 0, eq_w = 0;
       for (int c0 = 0; c0 < cnt; c0 += 64) {
         const int c = c0 + lane;
-        const uint32_t key = c < cnt ? lk[c] : 0u;
+        const uint32_t key = c < cnt ? lk[c] >> 16 : 0u;
         gt_w += __popcll(__ballot(c < cnt && key > tau));
         eq_w += __popcll(__ballot(c < cnt && key == tau));
       }
@@ -189,13 +188,14 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
       }
       for (int c0 = 0; c0 < cnt && gt_run + min(eq_run, need) < top_k; c0 += 64) {
         const int c = c0 + lane;
-        const uint32_t key = c < cnt ? lk[c] : 0u;
+        const uint32_t e = c < cnt ? lk[c] : 0u;
+        const uint32_t key = e >> 16;
         const bool gt = c < cnt && key > tau;
         const bool eq = c < cnt && key == tau;
         const uint64_t gm = __ballot(gt), em = __ballot(eq);
         const int gt_before = gt_run + __popcll(gm & lt_mask);
         const int eq_before = eq_run + __popcll(em & lt_mask);
-        if (gt || (eq && eq_before < need)) out[gt_before + min(eq_before, need)] = P + (int)lp[c];
+        if (gt || (eq && eq_before < need)) out[gt_before + min(eq_before, need)] = P + (int)(e & 0xffffu);
         gt_run += __popcll(gm);
         eq_run += __popcll(em);
       }
