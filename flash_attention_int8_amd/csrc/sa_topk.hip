@@ -29,8 +29,8 @@ using namespace sel;
 // per row: few registers and about 26 KB of LDS, so six rows are in flight per CU and their
 // latencies overlap. Wave w streams the contiguous quarter [w * Q, (w + 1) * Q) of the row
 // (Q a multiple of 64), so token order is wave-major.
-//   sample    1024 keys at evenly spaced positions give a threshold bin theta (its tail holds
-//             1.25 times the sampled share of K plus three standard deviations plus 8);
+//   sample    1024 keys (16 evenly spaced runs of 64) give a threshold bin theta (its tail
+//             holds 1.25 times the sampled share of K plus three standard deviations plus 8);
 //   stream    every key at or above T = theta << 12 is appended, in token order, to its wave's
 //             list in LDS (ballots only, no barrier) as one word: its offset above T (clamped
 //             to 65535) in the high half, its candidate index in the low half; the next batch
@@ -104,15 +104,21 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
     }
   };
 
-  // sample: 1024 evenly spaced keys into a 4096-bin histogram (in the list space)
+  // sample: 1024 keys into a 4096-bin histogram (in the list space), taken as 16 runs of 64
+  // consecutive keys at evenly spaced starts (2 cache lines each, so the sample reads about
+  // 1/16 of a long row instead of every line of it), or evenly spaced keys in rows under 2048
   for (int j = tid; j < kBins; j += NT) l_key[j] = 0u;
   __syncthreads();
   const int ns = min(1024, n);
   {
     uint32_t sk[1024 / NT];
 #pragma unroll
-    for (int t = 0; t < 1024 / NT; ++t)
-      sk[t] = (uint32_t)srow[P + (int)((int64_t)min(tid + t * NT, ns - 1) * n / ns)];
+    for (int t = 0; t < 1024 / NT; ++t) {
+      const int sidx = min(tid + t * NT, ns - 1);
+      const int js = n >= 2048 ? (int)((int64_t)(sidx >> 6) * n / 16) + (sidx & 63)
+                               : (int)((int64_t)sidx * n / ns);
+      sk[t] = (uint32_t)srow[P + js];
+    }
 #pragma unroll
     for (int t = 0; t < 1024 / NT; ++t)
       if (tid + t * NT < ns) atomicAdd(&l_key[score_key((int32_t)sk[t]) >> 12], 1u);
