@@ -13,7 +13,8 @@
 //    with one instruction.
 //  * k_index_mfma (many queries, i.e. prefill): scores are a causal int8 GEMM
 //    S^T = K_idx * Q_idx^T on v_mfma_i32_16x16x32_i8. Keys are the M side so each lane's four
-//    accumulator rows are four consecutive tokens of one query: one 16-byte store each.
+//    accumulator rows are four consecutive tokens of one query; a 16-query x 64-key tile goes
+//    through LDS and out as whole 256-byte row segments.
 #include "sa_index_dev.h"
 
 namespace sa {
@@ -102,6 +103,7 @@ typedef long i64x1;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
 constexpr int kMfmaKeyBlocksPerWave = 8;  // 512 keys per wave item
+constexpr int kStageStride = 68;          // ints per staged score row (64 + 4 of padding)
 
 template <int D>
 __global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __restrict__ q_idx,
@@ -134,6 +136,7 @@ __global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __r
 
   const int l16 = lane & 15;
   const int lg = lane >> 4;
+  __shared__ __align__(16) int32_t s_stage[4][16][kStageStride];
 
   // B operand: 4 query blocks of 16, lane holds query (n*16 + l16), bytes lg*CH .. +CH.
   i64x1 qb[4][KS];
@@ -173,29 +176,50 @@ __global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __r
     }
     return ok;
   };
+  // Score rows of a full block leave through the wave's LDS tile so that every store
+  // instruction writes whole 256-byte row segments (4 rows of 64 keys) instead of 64-byte
+  // pieces of 16 rows.
+  int32_t (&stg)[16][kStageStride] = s_stage[wave];
   auto compute = [&](int blk, const i64x1 (&ka)[4][KS]) {
     const int t0 = blk << 6;
     const bool full = (t0 >= P) && (t0 + 63 <= pmin);  // every (key, query) pair is a candidate
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int n = 0; n < 4; ++n) {
+      i32x4 acc[4];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        i32x4 acc = {0, 0, 0, 0};
+      for (int m = 0; m < 4; ++m) {
+        acc[m] = i32x4{0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka[m][ks], qb[n][ks], acc, 0, 0, 0);
-        // acc[j] = score(key m*16 + lg*4 + j, query n*16 + l16)
+          acc[m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka[m][ks], qb[n][ks], acc[m], 0, 0, 0);
+      }
+      // acc[m][j] = score(key m*16 + lg*4 + j, query n*16 + l16)
+      if (full) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) *reinterpret_cast<i32x4*>(&stg[l16][m * 16 + lg * 4]) = acc[m];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int qr = rr * 4 + (lane >> 4);  // query of the n-block; lanes 16k..16k+15 cover its 64 keys
+          const int c = lane & 15;
+          const i32x4 v = *reinterpret_cast<const i32x4*>(&stg[qr][c * 4]);
+          const int iq = i0 + n * 16 + qr;
+          if (iq < q_len)
+            *reinterpret_cast<i32x4*>(scores + (((int64_t)b * q_len + iq) * kv.num_idx_heads + gi) *
+                                                   row_stride + t0 + c * 4) = v;
+        }
+        __builtin_amdgcn_wave_barrier();  // the tile is read before the next n-block writes it
+      } else {
         const int i = i0 + n * 16 + l16;
         if (i >= q_len) continue;
         const int pos = pos0 + i;
-        const int t = t0 + m * 16 + lg * 4;
-        int32_t* dst = scores + (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * row_stride + t;
-        if (full) {
-          *reinterpret_cast<i32x4*>(dst) = acc;
-        } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int t = t0 + m * 16 + lg * 4;
+          int32_t* dst = scores + (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * row_stride + t;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (t + j >= P && t + j <= pos) dst[j] = acc[j];
+            if (t + j >= P && t + j <= pos) dst[j] = acc[m][j];
         }
       }
     }
