@@ -181,9 +181,10 @@ def bench_prefill(fa, reps):
 
 def bench_sparse_prefill(fa, reps, q_chunk=2048):
     """Whole sparse prefill of 32K tokens (B=1, 32/8 heads, d=128, d_idx=64, top-K=2048): per
-    chunk of q_chunk queries, indexer scores -> top-K -> attention on masked dense tiles
-    (sparse_attn_fwd_prefill_masked). The gathered-row attention (sparse_attn_fwd_prefill with
-    the lists) is timed on the same lists in a separate pass."""
+    chunk of q_chunk queries, the fused selection (sparse_attn_index_topk: indexer keys ->
+    exact top-K lists) then attention on masked dense tiles (sparse_attn_fwd_prefill_masked).
+    Separate passes time the two-step selection (sparse_attn_index, then sparse_attn_topk on
+    int32 score rows) and the gathered-row attention (sparse_attn_fwd_prefill with the lists)."""
     import torch
 
     from synthetic import CONFIGS, make_inputs
@@ -194,28 +195,32 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048):
                     prefix_len=w.prefix_len)
     S, Hkv, Hq, d = w.q_len, w.num_kv_heads, w.num_q_heads, w.head_dim
     stride = (w.seq_len + 3) & ~3
-    scores = torch.empty((1, q_chunk, Hkv, stride), dtype=torch.int32, device="cuda")
     idx = torch.empty((1, q_chunk, Hkv, w.index_width), dtype=torch.int32, device="cuda")
     out = torch.empty_like(inp.q)
     lse = torch.empty((1, S, Hq), dtype=torch.float32, device="cuda")
     q_idx = [inp.q_idx[:, q0:q0 + q_chunk].contiguous() for q0 in range(0, S, q_chunk)]
+    fu_n = fa.sparse_attn_index_topk_workspace_size(kv, q_chunk, w.top_k)
+    fu_ws = torch.empty(max(fu_n, 16), dtype=torch.uint8, device="cuda")
     tk_n = fa.sparse_attn_topk_workspace_size(kv, q_chunk, w.top_k)
     tk_ws = torch.empty(max(tk_n, 16), dtype=torch.uint8, device="cuda")
     mk_n = fa.sparse_attn_prefill_masked_workspace_size(kv, q_chunk)
     mk_ws = torch.empty(max(mk_n, 16), dtype=torch.uint8, device="cuda")
     scale = 1 / math.sqrt(d)
+    # the two-step pass keeps its int32 score rows in the fused call's workspace
+    scores = fu_ws[: q_chunk * Hkv * stride * 4].view(torch.int32).view(1, q_chunk, Hkv, stride)
 
-    def run(evs=None, gather=False):
+    def run(evs=None, gather=False, two_step=False):
         for c, q0 in enumerate(range(0, S, q_chunk)):
             n, tail = min(q_chunk, S - q0), S - q0
             if evs:
                 evs[c][0].record()
-            fa.sparse_attn_index(kv, q_idx[c], n, tail, scores, stride)
+            if two_step:
+                fa.sparse_attn_index(kv, q_idx[c], n, tail, scores, stride)
+                fa.sparse_attn_topk(kv, scores, stride, n, tail, w.top_k, idx, tk_ws, tk_n)
+            else:
+                fa.sparse_attn_index_topk(kv, q_idx[c], n, tail, w.top_k, idx, fu_ws, fu_n)
             if evs:
                 evs[c][1].record()
-            fa.sparse_attn_topk(kv, scores, stride, n, tail, w.top_k, idx, tk_ws, tk_n)
-            if evs:
-                evs[c][2].record()
             if gather:
                 fa.sparse_attn_fwd_prefill(kv, inp.q[:, q0:q0 + n], Hq, n, tail, idx, w.index_width,
                                            scale, out[:, q0:q0 + n], lse[:, q0:q0 + n])
@@ -224,11 +229,10 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048):
                                                   w.index_width, scale, mk_ws, mk_n,
                                                   out[:, q0:q0 + n], lse[:, q0:q0 + n])
             if evs:
-                evs[c][3].record()
+                evs[c][2].record()
     run()
     torch.cuda.synchronize()
     chunks = (S + q_chunk - 1) // q_chunk
-    stage = [0.0, 0.0, 0.0]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -236,28 +240,29 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(chunks)]
-    run(evs)
-    torch.cuda.synchronize()
-    for c in range(chunks):
-        for k in range(3):
-            stage[k] += evs[c][k].elapsed_time(evs[c][k + 1])
-    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(chunks)]
-    run(gev, gather=True)
-    torch.cuda.synchronize()
-    gather_ms = sum(gev[c][2].elapsed_time(gev[c][3]) for c in range(chunks))
+
+    def staged(**kw):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(chunks)]
+        run(evs, **kw)
+        torch.cuda.synchronize()
+        return [sum(evs[c][k].elapsed_time(evs[c][k + 1]) for c in range(chunks)) for k in range(2)]
+    stage = staged()
+    two_sel = staged(two_step=True)[0]
+    gather_ms = staged(gather=True)[1]
     # algorithmic attention flops: 4 heads x (QK + PV) per selected key per (query, group)
     sel = sum(min(w.top_k, i + 1) for i in range(S))
     attn_flop = 4.0 * d * Hq * sel
     # the masked dense tiles compute every causal (query, key) pair
     causal_flop = 4.0 * d * Hq * S * (S + 1) / 2
-    del inp, scores, idx, out, lse, q_idx, tk_ws, mk_ws
+    del inp, scores, idx, out, lse, q_idx, tk_ws, mk_ws, fu_ws
     torch.cuda.empty_cache()
     return {"workload": w.name, "ms": ms, "tokens_per_s": S / (ms * 1e-3),
-            "stage_ms": {"index": stage[0], "topk": stage[1], "attention": stage[2]},
+            "stage_ms": {"select": stage[0], "attention": stage[1]},
+            "select": "sparse_attn_index_topk (16-bit indexer keys, exact ties)",
             "attention": "masked dense tiles (sparse_attn_fwd_prefill_masked)",
-            "attention_tflops": attn_flop / (stage[2] * 1e-3) / 1e12,
-            "attention_mfma_tflops": causal_flop / (stage[2] * 1e-3) / 1e12,
+            "attention_tflops": attn_flop / (stage[1] * 1e-3) / 1e12,
+            "attention_mfma_tflops": causal_flop / (stage[1] * 1e-3) / 1e12,
+            "select_two_step_ms": two_sel,
             "attention_gathered_ms": gather_ms,
             "q_chunk": q_chunk}
 

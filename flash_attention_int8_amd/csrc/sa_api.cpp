@@ -159,6 +159,15 @@ int32_t sparse_attn_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32
   if (!aligned16(workspace)) return SA_ERR_ALIGN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (fused) return hip_status(sa::launch_index_topk_fused(v, q_idx, q_tail, top_k, indices, workspace, s));
+  if (sa::topk_coarse_applies(v, q_len)) {
+    // many-query blocks of rows up to 32K: 16-bit keys (half the traffic of int32 scores) in the
+    // score space of the workspace, row stride a multiple of 8 keys
+    uint16_t* keys = static_cast<uint16_t*>(workspace);
+    const int64_t kstride = ((int64_t)v.max_seq_len + 7) & ~(int64_t)7;
+    hipError_t e = sa::launch_index_coarse(v, q_idx, q_len, q_tail, keys, kstride, s);
+    if (e != hipSuccess) return SA_ERR_HIP;
+    return hip_status(sa::launch_topk_coarse(v, keys, kstride, q_len, q_tail, top_k, q_idx, indices, s));
+  }
   int32_t* scores = static_cast<int32_t*>(workspace);
   const int64_t stride = score_stride(v);
   void* tk_ws = static_cast<char*>(workspace) +

@@ -144,6 +144,14 @@ hipError_t launch_attn_sparse_mfma(const KvView& kv, const uint16_t* q, int num_
 hipError_t launch_attn_dense(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                              int q_tail, float sm_scale, uint16_t* out, float* lse,
                              hipStream_t stream);
+// Fused prefill selection on 16-bit order-preserving indexer keys (exact: ties in a key are
+// settled by recomputed int8 scores).
+hipError_t launch_index_coarse(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail,
+                               uint16_t* keys, int64_t row_stride, hipStream_t stream);
+bool topk_coarse_applies(const KvView& kv, int q_len);
+hipError_t launch_topk_coarse(const KvView& kv, const uint16_t* keys, int64_t row_stride, int q_len,
+                              int q_tail, int top_k, const int8_t* q_idx, int32_t* indices,
+                              hipStream_t stream);
 // Masked-dense sparse prefill: selection masks built from index lists in the workspace, then
 // the dense kernel with every unselected score set to -inf.
 int sel_query_blocks(int q_len);

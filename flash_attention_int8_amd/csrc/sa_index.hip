@@ -105,12 +105,27 @@ typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 constexpr int kMfmaKeyBlocksPerWave = 8;  // 512 keys per wave item
 constexpr int kStageStride = 68;          // ints per staged score row (64 + 4 of padding)
 
+// Coarse 16-bit keys (used by the fused prefill selection): c(s) = min((s + B) >> shift, 65535)
+// with B = D * 2^14 >= |s| and shift = log2(D) - 1, so c is order-preserving (s1 > s2 whenever
+// c(s1) > c(s2)) and a key of c carries the exact score in [c * 2^shift - B, (c + 1) * 2^shift - B].
 template <int D>
+struct Coarse {
+  static constexpr int kShift = D == 32 ? 4 : (D == 64 ? 5 : 6);
+  static constexpr int kBias = D << 14;
+};
+template <int D>
+__device__ __forceinline__ uint16_t coarse_key(int s) {
+  return (uint16_t)min((s + Coarse<D>::kBias) >> Coarse<D>::kShift, 65535);
+}
+
+template <int D, bool COARSE>
 __global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __restrict__ q_idx,
                                                     int q_len, int q_tail,
-                                                    int32_t* __restrict__ scores,
+                                                    void* __restrict__ scores_out,
                                                     int64_t row_stride, int n_qtiles,
                                                     int n_kchunks) {
+  int32_t* __restrict__ scores = static_cast<int32_t*>(scores_out);
+  uint16_t* __restrict__ ckeys = static_cast<uint16_t*>(scores_out);
   constexpr int KS = D / 32;   // k-steps of the 16x16x32 MFMA
   constexpr int CH = D / 4;    // bytes of a row held by one lane group (l / 16)
   const int lane = threadIdx.x & 63;
@@ -136,7 +151,7 @@ __global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __r
 
   const int l16 = lane & 15;
   const int lg = lane >> 4;
-  __shared__ __align__(16) int32_t s_stage[4][16][kStageStride];
+  __shared__ __align__(16) int32_t s_stage[4][16][kStageStride];  // (coarse: 16-bit rows of 72)
 
   // B operand: 4 query blocks of 16, lane holds query (n*16 + l16), bytes lg*CH .. +CH.
   i64x1 qb[4][KS];
@@ -194,7 +209,29 @@ __global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __r
           acc[m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka[m][ks], qb[n][ks], acc[m], 0, 0, 0);
       }
       // acc[m][j] = score(key m*16 + lg*4 + j, query n*16 + l16)
-      if (full) {
+      if (full && COARSE) {
+        // 16-bit keys: a 64-key row segment is 128 bytes, 8 lanes of 16 bytes; 8 rows per store
+        uint16_t (*stg16)[72] = reinterpret_cast<uint16_t (*)[72]>(&stg[0][0]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          uint2 w;
+          w.x = (uint32_t)coarse_key<D>(acc[m][0]) | ((uint32_t)coarse_key<D>(acc[m][1]) << 16);
+          w.y = (uint32_t)coarse_key<D>(acc[m][2]) | ((uint32_t)coarse_key<D>(acc[m][3]) << 16);
+          *reinterpret_cast<uint2*>(&stg16[l16][m * 16 + lg * 4]) = w;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int qr = rr * 8 + (lane >> 3);
+          const int c = lane & 7;
+          const uint4 v = *reinterpret_cast<const uint4*>(&stg16[qr][c * 8]);
+          const int iq = i0 + n * 16 + qr;
+          if (iq < q_len)
+            *reinterpret_cast<uint4*>(ckeys + (((int64_t)b * q_len + iq) * kv.num_idx_heads + gi) *
+                                                  row_stride + t0 + c * 8) = v;
+        }
+        __builtin_amdgcn_wave_barrier();
+      } else if (full) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) *reinterpret_cast<i32x4*>(&stg[l16][m * 16 + lg * 4]) = acc[m];
         __builtin_amdgcn_wave_barrier();
@@ -216,10 +253,14 @@ __global__ __launch_bounds__(256) void k_index_mfma(KvView kv, const int8_t* __r
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int t = t0 + m * 16 + lg * 4;
-          int32_t* dst = scores + (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * row_stride + t;
+          const int64_t o = (((int64_t)b * q_len + i) * kv.num_idx_heads + gi) * row_stride + t;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (t + j >= P && t + j <= pos) dst[j] = acc[m][j];
+          for (int j = 0; j < 4; ++j) {
+            if (t + j >= P && t + j <= pos) {
+              if constexpr (COARSE) ckeys[o + j] = coarse_key<D>(acc[m][j]);
+              else scores[o + j] = acc[m][j];
+            }
+          }
         }
       }
     }
@@ -255,13 +296,40 @@ hipError_t launch_index_d(const KvView& kv, const int8_t* q_idx, int q_len, int 
     const int n_kchunks = (blocks + kMfmaKeyBlocksPerWave - 1) / kMfmaKeyBlocksPerWave;
     const int64_t items = (int64_t)n_qtiles * n_kchunks;
     dim3 grid((unsigned)((items + 3) / 4), rows);
-    hipLaunchKernelGGL(k_index_mfma<D>, grid, dim3(256), 0, stream, kv, q_idx, q_len, q_tail,
-                       scores, row_stride, n_qtiles, n_kchunks);
+    hipLaunchKernelGGL((k_index_mfma<D, false>), grid, dim3(256), 0, stream, kv, q_idx, q_len, q_tail,
+                       (void*)scores, row_stride, n_qtiles, n_kchunks);
   }
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_index_coarse_d(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail,
+                                 uint16_t* keys, int64_t row_stride, hipStream_t stream) {
+  const int rows = kv.batch * kv.num_idx_heads;
+  const int pmax = kv.max_seq_len - q_tail + q_len - 1;
+  if (pmax < kv.prefix_len) return hipSuccess;
+  const int blocks = (pmax >> 6) - (kv.prefix_len >> 6) + 1;
+  const int n_qtiles = (q_len + 63) / 64;
+  const int n_kchunks = (blocks + kMfmaKeyBlocksPerWave - 1) / kMfmaKeyBlocksPerWave;
+  const int64_t items = (int64_t)n_qtiles * n_kchunks;
+  dim3 grid((unsigned)((items + 3) / 4), rows);
+  hipLaunchKernelGGL((k_index_mfma<D, true>), grid, dim3(256), 0, stream, kv, q_idx, q_len, q_tail,
+                     (void*)keys, row_stride, n_qtiles, n_kchunks);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_index_coarse(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail,
+                               uint16_t* keys, int64_t row_stride, hipStream_t stream) {
+  if (q_len < 16) return hipErrorInvalidValue;  // the many-query (MFMA) indexer only
+  switch (kv.idx_dim) {
+    case 32: return launch_index_coarse_d<32>(kv, q_idx, q_len, q_tail, keys, row_stride, stream);
+    case 64: return launch_index_coarse_d<64>(kv, q_idx, q_len, q_tail, keys, row_stride, stream);
+    case 128: return launch_index_coarse_d<128>(kv, q_idx, q_len, q_tail, keys, row_stride, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_index(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail,
                         int32_t* scores, int64_t row_stride, hipStream_t stream) {

@@ -46,9 +46,21 @@ constexpr int kStrNT = 256;
 constexpr int kStrCap = 1536;  // list entries per wave
 constexpr int kStrLd = 8;      // keys per lane per batch
 
-__global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int32_t* __restrict__ scores,
+//
+// Coarse variant (COARSE = true, used by the fused prefill selection): the row holds the 16-bit
+// order-preserving keys c(s) of the indexer (c(s1) > c(s2) implies s1 > s2; a key c holds
+// exact scores in [c * 2^shift - B, c * 2^shift - B + 2^shift], B = d_idx * 2^14, shift =
+// log2(d_idx) - 1). The lists and the fine histograms run on c as above. Every key with c above
+// the K-th largest key tau_c is taken; when the keys equal to tau_c are more than are needed, their
+// exact scores are recomputed from the int8 query and key rows (r = s - tau_c * 2^shift + B,
+// at most 2^shift + 1 values) and a histogram of r picks them exactly, ties by token. When the
+// lists cannot decide, the streamed exact radix select runs on exact scores computed from the
+// int8 rows.
+template <bool COARSE>
+__global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const void* __restrict__ scores_v,
                                                           int64_t row_stride, int q_len, int q_tail,
-                                                          int top_k, int32_t* __restrict__ indices) {
+                                                          int top_k, int32_t* __restrict__ indices,
+                                                          const int8_t* __restrict__ q_idx) {
   constexpr int NT = kStrNT;
   constexpr int NW = NT / 64;
   constexpr int kBatch = 64 * kStrLd;
@@ -68,8 +80,37 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
   const int P = kv.prefix_len;
   const int W = P + top_k;
   const int pos = min(kv.seq_lens[b], kv.max_seq_len) - q_tail + i;
-  const int32_t* srow = scores + row * row_stride;
+  const int32_t* srow = static_cast<const int32_t*>(scores_v) + row * row_stride;
+  const uint16_t* crow = static_cast<const uint16_t*>(scores_v) + row * row_stride;
   int32_t* out = indices + row * W;
+  // coarse rows: exact int8 score of token t (the row's query against the key's indexer row;
+  // a page missing from the table reads page 0, like the indexer's unspecified case)
+  const int D = kv.idx_dim;
+  const int gi = (int)(row - bi * kv.num_idx_heads);
+  auto exact_score = [&](int t) -> int32_t {
+    const int lp = min(t >> kv.page_shift, kv.max_pages_per_seq - 1);
+    int64_t ph = kv.page_table[(int64_t)b * kv.max_pages_per_seq + lp];
+    ph = (ph >= 0 && ph < kv.num_pages) ? ph : 0;
+    const int8_t* kr = kv.kidx_pool + ((ph * kv.num_idx_heads + gi) * kv.page_size +
+                                       (t & (kv.page_size - 1))) * (int64_t)D;
+    const int8_t* qr = q_idx + row * (int64_t)D;
+    int acc = 0;
+    for (int c = 0; c < D; c += 16) {
+      const int4 a = *reinterpret_cast<const int4*>(qr + c);
+      const int4 k = *reinterpret_cast<const int4*>(kr + c);
+      acc = __builtin_amdgcn_sdot4(a.x, k.x, acc, false);
+      acc = __builtin_amdgcn_sdot4(a.y, k.y, acc, false);
+      acc = __builtin_amdgcn_sdot4(a.z, k.z, acc, false);
+      acc = __builtin_amdgcn_sdot4(a.w, k.w, acc, false);
+    }
+    return acc;
+  };
+  bool exact_mode = false;  // coarse rows: the fallback streams exact scores
+  // selection key of a loaded value: 16-bit coarse key, or the 24-bit key of an exact score
+  auto key_of = [&](uint32_t raw) -> uint32_t {
+    return (COARSE && !exact_mode) ? raw : score_key((int32_t)raw);
+  };
+  constexpr int kShift1 = COARSE ? 4 : 12;  // sample histogram: key >> kShift1, 4096 bins
 
   const int nf = pos < 0 ? 0 : min(P, pos + 1);
   for (int j = tid; j < nf; j += NT) out[j] = j;
@@ -86,8 +127,16 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
   // kStrLd keys of the row per lane, requested together (index clamped into the row, so no
   // load is guarded and none is waited for where it is issued)
   auto load_batch = [&](int j0, uint32_t (&k)[kStrLd]) {
+    if (COARSE && exact_mode) {
 #pragma unroll
-    for (int u = 0; u < kStrLd; ++u) k[u] = (uint32_t)srow[P + min(j0 + u * 64 + lane, n - 1)];
+      for (int u = 0; u < kStrLd; ++u) k[u] = (uint32_t)exact_score(P + min(j0 + u * 64 + lane, n - 1));
+    } else {
+#pragma unroll
+      for (int u = 0; u < kStrLd; ++u) {
+        const int j = P + min(j0 + u * 64 + lane, n - 1);
+        k[u] = COARSE ? (uint32_t)crow[j] : (uint32_t)srow[j];
+      }
+    }
   };
   // visits every key of this wave's range in order: f(j0, keys) per batch, loads one batch ahead
   auto stream = [&](auto&& f) {
@@ -117,11 +166,11 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
       const int sidx = min(tid + t * NT, ns - 1);
       const int js = n >= 2048 ? (int)((int64_t)(sidx >> 6) * n / 16) + (sidx & 63)
                                : (int)((int64_t)sidx * n / ns);
-      sk[t] = (uint32_t)srow[P + js];
+      sk[t] = COARSE ? (uint32_t)crow[P + js] : (uint32_t)srow[P + js];
     }
 #pragma unroll
     for (int t = 0; t < 1024 / NT; ++t)
-      if (tid + t * NT < ns) atomicAdd(&l_key[score_key((int32_t)sk[t]) >> 12], 1u);
+      if (tid + t * NT < ns) atomicAdd(&l_key[key_of(sk[t]) >> kShift1], 1u);
   }
   __syncthreads();
   const float expect = (float)top_k * (float)ns / (float)n;
@@ -129,7 +178,7 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
   uint32_t T = 0u;
   if (target < ns) {
     int ab = 0;
-    T = (uint32_t)block_find_bin_segments<NW, 16>(l_key, s_seg, target, &ab) << 12;
+    T = (uint32_t)block_find_bin_segments<NW, 16>(l_key, s_seg, target, &ab) << kShift1;
   }
   for (int j = tid; j < 512; j += NT) s_hist[j] = 0u;
   __syncthreads();  // the sample histogram is no longer read
@@ -141,7 +190,7 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
 #pragma unroll
     for (int u = 0; u < kStrLd; ++u) {
       const int j = j0 + u * 64 + lane;
-      const uint32_t key = score_key((int32_t)k[u]);
+      const uint32_t key = key_of(k[u]);
       const bool keep = j < j_end && key >= T;
       const uint64_t km = __ballot(keep);
       const int o = cnt + __popcll(km & lt_mask);
@@ -163,7 +212,8 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
     __syncthreads();
     int above_fb = 0;
     const int fb = block_find_bin_segments<NW, 1>(s_hist, s_seg, top_k, &above_fb);
-    if (fb >= 0 && fb < 255) {  // uniform
+    // (coarse offsets are never clamped: every bin is exact)
+    if (fb >= 0 && (COARSE || fb < 255)) {  // uniform
       // offsets (key - T) from here on; the clamped ones all lie in bin 255, above tau
       const uint32_t lo = (uint32_t)fb << 8;
       for (int c = lane; c < cnt; c += 64) {
@@ -187,6 +237,71 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
         s_cnt2[wv] = eq_w;
       }
       __syncthreads();
+      if constexpr (COARSE) {
+        int eq_total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) eq_total += s_cnt2[w];
+        if (eq_total > need) {  // uniform: the keys equal to tau_c are decided by exact scores
+          const int shift = D == 32 ? 4 : (D == 64 ? 5 : 6);
+          const int64_t lo_s = ((int64_t)(T + tau) << shift) - ((int64_t)D << 14);
+          uint32_t* rh = s_hist;  // free again: 256 bins of r
+          for (int j = tid; j < 256; j += NT) rh[j] = 0u;
+          __syncthreads();
+          // one pass computes the exact scores: every entry's high half becomes its class,
+          // 0xffff above tau, 0x100 | r at tau, 0 below
+          for (int c = lane; c < cnt; c += 64) {
+            const uint32_t e = lk[c];
+            const uint32_t off = e >> 16;
+            uint32_t cls = 0u;
+            if (off > tau) {
+              cls = 0xffffu;
+            } else if (off == tau) {
+              const int64_t rr = exact_score(P + (int)(e & 0xffffu)) - lo_s;
+              const uint32_t r = (uint32_t)(rr < 0 ? 0 : (rr > 255 ? 255 : rr));
+              atomicAdd(&rh[r], 1u);
+              cls = 0x100u | r;
+            }
+            lk[c] = (cls << 16) | (e & 0xffffu);
+          }
+          __syncthreads();
+          int above_r = 0;
+          const uint32_t rstar = 0x100u | (uint32_t)wave_find_bin<4>(rh, need, &above_r);
+          const int need_r = need - above_r;  // keys at r* to take, in token order
+          // classes: gt 0xffff; above r* (0x100 | r, r > r*) taken; at r* the first need_r
+          int tk_c = 0, er_c = 0;
+          for (int c0 = 0; c0 < cnt; c0 += 64) {
+            const int c = c0 + lane;
+            const uint32_t cls = c < cnt ? lk[c] >> 16 : 0u;
+            tk_c += __popcll(__ballot(cls > rstar));
+            er_c += __popcll(__ballot(cls == rstar));
+          }
+          __syncthreads();  // every wave has read the first-pass counts
+          if (lane == 0) {
+            s_cnt[wv] = tk_c;
+            s_cnt2[wv] = er_c;
+          }
+          __syncthreads();
+          int taken = 0, er_run = 0;
+          for (int w = 0; w < wv; ++w) {
+            taken += s_cnt[w];
+            er_run += s_cnt2[w];
+          }
+          taken += min(er_run, need_r);
+          for (int c0 = 0; c0 < cnt; c0 += 64) {
+            const int c = c0 + lane;
+            const uint32_t e = c < cnt ? lk[c] : 0u;
+            const uint32_t cls = e >> 16;
+            const bool eqr = c < cnt && cls == rstar;
+            const uint64_t rm = __ballot(eqr);
+            const bool take = (c < cnt && cls > rstar) || (eqr && er_run + __popcll(rm & lt_mask) < need_r);
+            const uint64_t tm = __ballot(take);
+            if (take) out[taken + __popcll(tm & lt_mask)] = P + (int)(e & 0xffffu);
+            taken += __popcll(tm);
+            er_run += __popcll(rm);
+          }
+          return;
+        }
+      }
       int gt_run = 0, eq_run = 0;
       for (int w = 0; w < wv; ++w) {
         gt_run += s_cnt[w];
@@ -208,7 +323,9 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
       return;
     }
   }
-  // exact two-digit radix select, streamed; the histograms live in the list space
+  // exact two-digit radix select, streamed; the histograms live in the list space (coarse
+  // rows stream exact scores recomputed from the int8 rows)
+  exact_mode = true;
   uint32_t* hist = l_key;
   __syncthreads();  // the lists are no longer read
   for (int j = tid; j < kBins; j += NT) hist[j] = 0u;
@@ -216,7 +333,7 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
   stream([&](int j0, const uint32_t (&k)[kStrLd]) {
 #pragma unroll
     for (int u = 0; u < kStrLd; ++u)
-      if (j0 + u * 64 + lane < j_end) atomicAdd(&hist[score_key((int32_t)k[u]) >> 12], 1u);
+      if (j0 + u * 64 + lane < j_end) atomicAdd(&hist[key_of(k[u]) >> 12], 1u);
   });
   __syncthreads();
   int above1 = 0;
@@ -227,7 +344,7 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
   stream([&](int j0, const uint32_t (&k)[kStrLd]) {
 #pragma unroll
     for (int u = 0; u < kStrLd; ++u) {
-      const uint32_t key = score_key((int32_t)k[u]);
+      const uint32_t key = key_of(k[u]);
       if (j0 + u * 64 + lane < j_end && (key >> 12) == b1) atomicAdd(&hist[key & 0xfff], 1u);
     }
   });
@@ -241,7 +358,7 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
 #pragma unroll
     for (int u = 0; u < kStrLd; ++u) {
       const bool valid = j0 + u * 64 + lane < j_end;
-      const uint32_t key = score_key((int32_t)k[u]);
+      const uint32_t key = key_of(k[u]);
       gt_w += __popcll(__ballot(valid && key > tau));
       eq_w += __popcll(__ballot(valid && key == tau));
     }
@@ -260,7 +377,7 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const int
 #pragma unroll
     for (int u = 0; u < kStrLd; ++u) {
       const int j = j0 + u * 64 + lane;
-      const uint32_t key = score_key((int32_t)k[u]);
+      const uint32_t key = key_of(k[u]);
       const bool gt = j < j_end && key > tau;
       const bool eq = j < j_end && key == tau;
       const uint64_t gm = __ballot(gt), em = __ballot(eq);
@@ -602,12 +719,30 @@ hipError_t launch_topk(const KvView& kv, const int32_t* scores, int64_t row_stri
   }
   // rows that fit are held in registers (one read of the scores); longer ones take three passes
   if (longest <= 32768) {
-    hipLaunchKernelGGL(k_topk_row_stream, dim3((unsigned)rows), dim3(kStrNT), 0, stream,
-                       kv, scores, row_stride, q_len, q_tail, top_k, indices);
+    hipLaunchKernelGGL(k_topk_row_stream<false>, dim3((unsigned)rows), dim3(kStrNT), 0, stream,
+                       kv, (const void*)scores, row_stride, q_len, q_tail, top_k, indices,
+                       (const int8_t*)nullptr);
   } else {
     hipLaunchKernelGGL((k_topk_row<1024>), dim3((unsigned)rows), dim3(1024), 0, stream, kv, scores,
                        row_stride, q_len, q_tail, top_k, indices);
   }
+  return hipGetLastError();
+}
+
+bool topk_coarse_applies(const KvView& kv, int q_len) {
+  const int64_t rows = (int64_t)kv.batch * q_len * kv.num_idx_heads;
+  const int longest = kv.max_seq_len - kv.prefix_len;
+  return q_len >= 16 && longest <= 32768 && !use_multi(rows, longest);
+}
+
+hipError_t launch_topk_coarse(const KvView& kv, const uint16_t* keys, int64_t row_stride, int q_len,
+                              int q_tail, int top_k, const int8_t* q_idx, int32_t* indices,
+                              hipStream_t stream) {
+  const int64_t rows = (int64_t)kv.batch * q_len * kv.num_idx_heads;
+  if (rows == 0) return hipSuccess;
+  if (!topk_coarse_applies(kv, q_len)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_topk_row_stream<true>, dim3((unsigned)rows), dim3(kStrNT), 0, stream, kv,
+                     (const void*)keys, row_stride, q_len, q_tail, top_k, indices, q_idx);
   return hipGetLastError();
 }
 

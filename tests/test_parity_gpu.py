@@ -186,6 +186,36 @@ def test_fused_index_topk_matches(name):
     assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
 
 
+FUSED_PREFILL = {
+    **{n: SMALL[n] for n in MASKED_CASES},
+    # rows of > 6144 candidates whose keys fall in a handful of 16-bit keys: the lists overflow
+    # and the exact radix select runs on recomputed scores
+    "prefill_long_ties": (W(seq_len=8000, q_len=32, top_k=300, prefix_len=2),
+                          dict(idx_values=(-1, 0, 1))),
+    "prefill_long_random": (W(batch=2, seq_len=20000, q_len=40, top_k=1000, prefix_len=5),
+                            dict(seq_lens=[20000, 9000])),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED_PREFILL))
+def test_fused_index_topk_prefill_matches(name):
+    """Prefill blocks through sparse_attn_index_topk (16-bit keys, exact scores recomputed for
+    the keys that tie in the K-th largest key): the same lists as index then topk, and the
+    oracle's lists and outputs."""
+    w, kw = FUSED_PREFILL[name]
+    _banner(f"fused index+topk prefill {name}")
+    inp = make_inputs(w, seed=17, device="cpu", **kw).to(DEV)
+    chunk = 96 if w.q_len > 200 else None
+    fused = run_gpu(inp, q_chunk=chunk, fused=True)
+    two = run_gpu(inp, q_chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.indices, two.indices)
+    rows = all_rows(inp)
+    if len(rows) > 400:
+        rows = rows[:: max(1, len(rows) // 400)]
+    assert_close(compare_rows(fused, OracleView(inp), rows))
+
+
 def test_fused_index_topk_concentrated_chunk_rescore():
     """One 8192-token chunk holds most of the top: its first 1024 tokens get maximal keys
     (so the chunk's threshold lands in their bin) and its next 1536 tokens keys one bin lower,
@@ -446,12 +476,16 @@ def test_full_sparse_prefill_32k():
 
 
 def test_full_sparse_prefill_32k_masked():
-    """The 32K sparse prefill with the attention on masked dense tiles, in the bench's launch
-    configuration (2048-query blocks)."""
+    """The 32K sparse prefill as the benchmark runs it: fused selection (16-bit keys) and the
+    attention on masked dense tiles, in 2048-query blocks; lists equal the two-step path's."""
     w = CONFIGS["sparse_prefill_32k"]
-    _banner(f"full {w.name}, masked dense tiles")
+    _banner(f"full {w.name}, fused selection, masked dense tiles")
     inp = make_inputs(w, seed=4, device=DEV)
-    gpu = run_gpu(inp, q_chunk=2048, masked=True)
+    gpu = run_gpu(inp, q_chunk=2048, masked=True, fused=True)
+    two = run_gpu(inp, q_chunk=2048)
+    torch.cuda.synchronize()
+    assert torch.equal(gpu.indices, two.indices)
+    del two
     torch.cuda.synchronize()
     ov = OracleView(inp, host_copy=False)
     rows = [(0, i, g) for i in _sample_queries(w.q_len, 10, 4) for g in (1, 6)]
