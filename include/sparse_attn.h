@@ -154,7 +154,10 @@ int32_t sparse_attn_topk(const sa_paged_kv* kv, const int32_t* scores, int64_t s
  * and writes only the keys above a per-chunk provisional threshold (taken from the chunk's
  * first 1024 keys); the selection checks that no threshold could have dropped a selected key
  * and rescores the row exactly if one could, so the result never depends on the thresholds.
- * Other shapes run the two-step path with the score rows held in the workspace.
+ * Many-query blocks (q_len >= 16) of rows up to 32768 candidates hold 16-bit order-preserving
+ * keys of the scores in the workspace instead (half the traffic) and settle the keys that tie
+ * at the K-th largest by recomputing their exact int8 scores. Other shapes run the two-step
+ * path with the score rows held in the workspace.
  * workspace: sparse_attn_index_topk_workspace_size(kv, q_len, top_k) bytes of device memory;
  * its contents on entry do not matter.
  */
