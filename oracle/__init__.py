@@ -27,6 +27,7 @@ from .dsa import (  # noqa: F401
     candidate_keys,
     forced_keys,
     page_rows,
+    append_rows,
     index_scores,
     topk_select,
     index_list,

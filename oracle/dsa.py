@@ -23,7 +23,8 @@ the int8 extreme closed form; topk_select against a brute-force full sort and th
 invariants; index_list against the prefix rule and a hand-worked golden case; attend
 against closed forms (single key, constant V, identical keys, one-hot V rows giving the
 probabilities), scipy's logsumexp, and a full-matrix masked softmax for the dense case;
-page_rows against an unpaged copy under a random page permutation. No function is
+page_rows against an unpaged copy under a random page permutation; append_rows against
+page_rows (round trip) and an unpaged array write, untouched rows kept. No function is
 "parity unpinned".
 """
 import numpy as np
@@ -68,6 +69,18 @@ def page_rows(pool, page_table_row, page_size: int, head: int, t) -> np.ndarray:
     phys = table[t // page_size]
     slot = t % page_size
     return np.asarray(pool[phys, head, slot])
+
+
+def append_rows(pool, page_table_row, page_size: int, head: int, t, rows) -> None:
+    """[DSA-page] §2.2 / §2.3: a new token t of a sequence is stored in block
+    page_table[t // page_size] at slot t % page_size (the write counterpart of page_rows).
+    `pool` is a numpy array [page][head][slot][...], modified in place; `rows` holds one row
+    per token of `t`. Tokens whose block is missing from the table (entry < 0) are skipped."""
+    t = np.asarray(t, dtype=np.int64)
+    table = np.asarray(page_table_row, dtype=np.int64)
+    phys = table[t // page_size]
+    ok = phys >= 0
+    pool[phys[ok], head, (t % page_size)[ok]] = np.asarray(rows)[ok]
 
 
 def index_scores(q_idx_vec, k_rows) -> np.ndarray:

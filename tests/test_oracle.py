@@ -172,6 +172,37 @@ def test_page_rows_follow_the_page_table():
 
 # ---------------------------------------------------------------- attention closed forms
 
+def test_append_rows_round_trip_and_unpaged_equivalent():
+    """Writing tokens through the page table lands them where page_rows reads them, touches
+    nothing else, equals a plain write into the unpaged (logical-order) array, and skips
+    tokens whose block is missing from the table."""
+    rng = np.random.default_rng(3)
+    page_size, n_pages, heads, d = 4, 6, 2, 3
+    table = rng.permutation(n_pages + 2)[:n_pages]          # spare physical pages
+    pool = rng.integers(-9, 9, size=(n_pages + 2, heads, page_size, d))
+    before = pool.copy()
+    t = np.array([0, 5, 6, 7, 13, 23])
+    rows = rng.integers(100, 200, size=(len(t), d))
+    oracle.append_rows(pool, table, page_size, 1, t, rows)
+    assert np.array_equal(oracle.page_rows(pool, table, page_size, 1, t), rows)
+    # unpaged: logical array [token][head][d] built from the table, written directly
+    def unpaged(p):  # [page][head][slot][d] -> [token][head][d] in logical order
+        return p[table].transpose(0, 2, 1, 3).reshape(n_pages * page_size, heads, d)
+    logical = unpaged(before).copy()
+    logical[t, 1] = rows
+    assert np.array_equal(unpaged(pool), logical)
+    spare = np.setdiff1d(np.arange(n_pages + 2), table)
+    assert np.array_equal(pool[spare], before[spare])       # pages outside the table untouched
+    # a missing block: its tokens are skipped, the others still written
+    table2 = table.copy()
+    table2[1] = -1                                           # tokens 4..7
+    pool2 = before.copy()
+    oracle.append_rows(pool2, table2, page_size, 0, t, rows)
+    ok = (t // page_size) != 1
+    assert np.array_equal(oracle.page_rows(pool2, table, page_size, 0, t[ok]), rows[ok])
+    assert np.array_equal(pool2[table[1]], before[table[1]])
+
+
 def test_attend_single_key():
     q = np.array([[0.5, -1.0, 2.0], [1.0, 1.0, 1.0]])
     k = np.array([[2.0, 1.0, 0.25]])
