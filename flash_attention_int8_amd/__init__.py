@@ -27,8 +27,8 @@ EXPORTS = ["sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_
            "sparse_attn_topk_workspace_size", "sparse_attn_topk",
            "sparse_attn_index_topk_workspace_size", "sparse_attn_index_topk",
            "sparse_attn_fwd_prefill", "sparse_attn_prefill_masked_workspace_size",
-           "sparse_attn_fwd_prefill_masked", "sparse_attn_decode_workspace_size",
-           "sparse_attn_fwd_decode"]
+           "sparse_attn_fwd_prefill_masked", "sparse_attn_kv_append",
+           "sparse_attn_decode_workspace_size", "sparse_attn_fwd_decode"]
 
 
 class SparseAttnError(RuntimeError):
@@ -85,6 +85,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sparse_attn_fwd_prefill": (I32, [KV, P, I32, I32, I32, P, I32, F32, P, P, P]),
         "sparse_attn_prefill_masked_workspace_size": (SZ, [KV, I32]),
         "sparse_attn_fwd_prefill_masked": (I32, [KV, P, I32, I32, I32, P, I32, F32, P, SZ, P, P, P]),
+        "sparse_attn_kv_append": (I32, [KV, P, P, P, I32, P]),
         "sparse_attn_decode_workspace_size": (SZ, [KV, I32, I32, I32]),
         "sparse_attn_fwd_decode": (I32, [KV, P, I32, P, I32, F32, I32, P, SZ, P, P, P]),
     }
@@ -212,6 +213,23 @@ def sparse_attn_fwd_prefill_masked(kv: PagedKV, q, num_q_heads, q_len, q_tail, i
         _ptr(indices, torch.int32, "indices"), index_width, float(sm_scale),
         _ptr(workspace, None, "workspace"), workspace_bytes,
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def sparse_attn_kv_append(kv: PagedKV, k_new, v_new, kidx_new, n_new, stream=None):
+    lib = load()
+    _check("sparse_attn_kv_append", lib.sparse_attn_kv_append(
+        kv.ref, _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+        _ptr(kidx_new, torch.int8, "kidx_new"), n_new, _stream(stream)))
+
+
+def kv_append(kv: PagedKV, k_new=None, v_new=None, kidx_new=None, stream=None):
+    """Write new tokens into the paged pools: k_new/v_new [B][n][H_kv][d] bf16, kidx_new
+    [B][n][H_idx][d_idx] int8 (either may be omitted); positions seq_lens[b] - n + i."""
+    ref = k_new if k_new is not None else kidx_new
+    n_new = int(ref.shape[1])
+    sparse_attn_kv_append(kv, None if k_new is None else k_new.contiguous(),
+                          None if v_new is None else v_new.contiguous(),
+                          None if kidx_new is None else kidx_new.contiguous(), n_new, stream)
 
 
 def sparse_attn_decode_workspace_size(kv: PagedKV, num_q_heads, index_width, num_splits=0) -> int:

@@ -230,6 +230,22 @@ int32_t sparse_attn_fwd_prefill_masked(const sa_paged_kv* kv, const uint16_t* q,
                                            static_cast<hipStream_t>(stream)));
 }
 
+int32_t sparse_attn_kv_append(const sa_paged_kv* kv, const uint16_t* k_new, const uint16_t* v_new,
+                              const int8_t* kidx_new, int32_t n_new, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return SA_ERR_NULL;
+  if (k_new == nullptr && kidx_new == nullptr) return SA_ERR_NULL;
+  sa::KvView v;
+  const unsigned need = (k_new != nullptr ? NEED_KV : 0u) | (kidx_new != nullptr ? NEED_IDX : 0u);
+  int32_t st = check_kv(kv, need, &v);
+  if (st != SA_OK) return st;
+  if (n_new < 1 || n_new > v.max_seq_len) return SA_ERR_SHAPE;
+  if ((k_new != nullptr && (!aligned16(k_new) || !aligned16(v_new))) ||
+      (kidx_new != nullptr && !aligned16(kidx_new)))
+    return SA_ERR_ALIGN;
+  return hip_status(sa::launch_kv_append(v, k_new, v_new, kidx_new, n_new,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 size_t sparse_attn_decode_workspace_size(const sa_paged_kv* kv, int32_t num_q_heads,
                                          int32_t index_width, int32_t num_splits) {
   sa::KvView v;

@@ -152,6 +152,9 @@ bool topk_coarse_applies(const KvView& kv, int q_len);
 hipError_t launch_topk_coarse(const KvView& kv, const uint16_t* keys, int64_t row_stride, int q_len,
                               int q_tail, int top_k, const int8_t* q_idx, int32_t* indices,
                               hipStream_t stream);
+// KV-cache append: new tokens' rows written into the paged pools.
+hipError_t launch_kv_append(const KvView& kv, const uint16_t* k_new, const uint16_t* v_new,
+                            const int8_t* kidx_new, int n_new, hipStream_t stream);
 // Masked-dense sparse prefill: selection masks built from index lists in the workspace, then
 // the dense kernel with every unselected score set to -inf.
 int sel_query_blocks(int q_len);

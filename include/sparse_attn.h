@@ -212,6 +212,22 @@ int32_t sparse_attn_fwd_prefill_masked(const sa_paged_kv* kv, const uint16_t* q,
                                        float* lse, void* stream);
 
 /*
+ * KV-cache append ([DSA-page] §2.2: the cache is kept in fixed blocks of contiguous tokens,
+ * found through the block table; §2.3: each decode step adds its token to the cache before
+ * the selection and attention read it). Writes n_new new tokens per sequence into the pools:
+ * token i of sequence b goes to position seq_lens[b] - n_new + i (seq_lens already counts the
+ * new tokens), i.e. to page page_table[b][pos / page_size], slot pos % page_size.
+ *   k_new, v_new  bf16 [batch][n_new][num_kv_heads][head_dim], both or neither (NULL: the K and
+ *                 V pools are not written)
+ *   kidx_new      int8 [batch][n_new][num_idx_heads][idx_dim], or NULL (indexer keys not written)
+ * At least one of the two must be given. The pools named in the descriptor are written in
+ * place, so they must be writable device memory for this call. Positions below 0 and tokens
+ * whose page entry lies outside [0, num_pages) are skipped. 1 <= n_new <= max_seq_len.
+ */
+int32_t sparse_attn_kv_append(const sa_paged_kv* kv, const uint16_t* k_new, const uint16_t* v_new,
+                              const int8_t* kidx_new, int32_t n_new, void* stream);
+
+/*
  * Decode attention ([DSA-page] §2.3, decode): one query token per sequence (pos =
  * seq_lens[b] - 1) attends to its index list. Each (b, KV group) list is cut into
  * num_splits chunks processed in parallel; partial softmax states (max, sum, weighted V in

@@ -131,6 +131,30 @@ def test_prefill_masked_workspace_size(lib):
     assert lib.sparse_attn_prefill_masked_workspace_size(ctypes.byref(d1), 256) == 2 * 8 * 16 * 256
 
 
+def call_append(lib, d, k=A, v=A + 0x100, ki=A + 0x200, n=4):
+    return lib.sparse_attn_kv_append(ctypes.byref(d), k, v, ki, n, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(v=None), fa.SA_ERR_NULL),                       # K without V
+    (dict(k=None), fa.SA_ERR_NULL),                       # V without K
+    (dict(k=None, v=None, ki=None), fa.SA_ERR_NULL),      # nothing to write
+    (dict(d=desc(kidx_pool=None)), fa.SA_ERR_NULL),       # indexer rows but no indexer pool
+    (dict(d=desc(k_pool=None)), fa.SA_ERR_NULL),
+    (dict(n=0), fa.SA_ERR_SHAPE),
+    (dict(n=1025), fa.SA_ERR_SHAPE),                      # more than max_seq_len
+    (dict(k=A + 2), fa.SA_ERR_ALIGN),
+    (dict(ki=A + 8), fa.SA_ERR_ALIGN),
+    (dict(d=desc(head_dim=96)), fa.SA_ERR_UNSUPPORTED),
+    (dict(d=desc(idx_dim=48)), fa.SA_ERR_UNSUPPORTED),
+    (dict(d=desc(abi_version=3)), fa.SA_ERR_ABI),
+])
+def test_kv_append_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_append(lib, d, **case) == code
+
+
 def call_decode(lib, d, q=A, hq=32, idx=A, width=2048, splits=4, ws=A, ws_bytes=1 << 30, out=A, lse=None,
                 scale=0.1):
     return lib.sparse_attn_fwd_decode(ctypes.byref(d), q, hq, idx, width, scale, splits, ws, ws_bytes,

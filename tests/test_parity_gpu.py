@@ -140,6 +140,48 @@ def test_masked_prefill_irregular_lists():
     assert_close((float(e.max()), float(e.mean()), float(np.concatenate(lse_errs).max())))
 
 
+@pytest.mark.parametrize("n_new,shared_idx,hole", [(1, False, False), (70, False, True),
+                                                   (1, True, True), (130, True, False)])
+def test_kv_append_matches_oracle(n_new, shared_idx, hole):
+    """New tokens written through the page table: every pool element equals the oracle's
+    append (bit-exact), tokens of a page missing from the table are skipped, and a decode step
+    over the updated cache matches the oracle."""
+    w = W(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, seq_len=300, q_len=1, top_k=40,
+          idx_dim=64, prefix_len=2)
+    _banner(f"kv append n_new={n_new} shared_idx={shared_idx} hole={hole}")
+    lens = [300, 200, 177]
+    inp = make_inputs(w, seed=31, device="cpu", seq_lens=lens, spare_pages=3,
+                      num_idx_heads=1 if shared_idx else None)
+    if hole:  # the page of sequence 1's last token is missing
+        inp.page_table[1, (lens[1] - 1) // w.page_size] = -1
+    g = torch.Generator().manual_seed(32)
+    Hi = inp.num_idx_heads
+    k_new = torch.randn((w.batch, n_new, w.num_kv_heads, w.head_dim), generator=g).to(torch.bfloat16)
+    v_new = torch.randn((w.batch, n_new, w.num_kv_heads, w.head_dim), generator=g).to(torch.bfloat16)
+    i_new = torch.randint(-127, 128, (w.batch, n_new, Hi, w.idx_dim), generator=g).to(torch.int8)
+    # oracle: the same rows written into host copies of the pools
+    kp, vp, ip = bits(inp.k_pool), bits(inp.v_pool), inp.kidx_pool.numpy().copy()
+    table = inp.page_table.numpy()
+    for b in range(w.batch):
+        t = np.arange(lens[b] - n_new, lens[b])
+        for h in range(w.num_kv_heads):
+            oracle.append_rows(kp, table[b], w.page_size, h, t, bits(k_new[b, :, h]))
+            oracle.append_rows(vp, table[b], w.page_size, h, t, bits(v_new[b, :, h]))
+        for h in range(Hi):
+            oracle.append_rows(ip, table[b], w.page_size, h, t, i_new[b, :, h].numpy())
+    inp = inp.to(DEV)
+    kv = make_kv(inp)
+    fa.kv_append(kv, k_new.to(DEV), v_new.to(DEV), i_new.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(inp.k_pool), kp)
+    assert np.array_equal(bits(inp.v_pool), vp)
+    assert np.array_equal(inp.kidx_pool.cpu().numpy(), ip)
+    if not hole:
+        gpu = run_gpu(inp, fused=True)
+        torch.cuda.synchronize()
+        assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
+
+
 DECODE = {
     "decode_ragged_prefix": (W(batch=4, num_q_heads=16, num_kv_heads=2, head_dim=64, idx_dim=128,
                                seq_len=1000, q_len=1, top_k=100, prefix_len=13),
