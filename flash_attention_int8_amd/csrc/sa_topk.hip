@@ -186,18 +186,63 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const voi
   // stream the row into the per-wave lists
   uint32_t* lk = l_key + wv * kStrCap;
   int cnt = 0;
-  stream([&](int j0, const uint32_t (&k)[kStrLd]) {
+  if constexpr (COARSE) {
+    // Lane-major: each lane takes 8 consecutive 16-bit keys (one 16-byte load) per step, so a
+    // step covers 512 consecutive keys with lane order = token order; one wave prefix sum of
+    // the per-lane counts places a lane's kept keys, and it loops over those only.
+    if (j_begin < j_end) {  // uniform
+      const int r_begin = P + j_begin, r_end = P + j_end;  // row indices of this wave's range
+      const int a0 = r_begin & ~7;
+      const int a_last = (r_end - 1) & ~7;  // last 8-key block holding range keys (in bounds)
+      auto ld = [&](int a) {
+        return *reinterpret_cast<const uint4*>(crow + min(a + lane * 8, a_last));
+      };
+      auto put = [&](int a, const uint4 v) {
+        const int r0 = a + lane * 8;  // row index of this lane's first key (before clamping)
+        const uint64_t lo = ((uint64_t)v.y << 32) | v.x, hi = ((uint64_t)v.w << 32) | v.z;
+        uint32_t bits = 0;
 #pragma unroll
-    for (int u = 0; u < kStrLd; ++u) {
-      const int j = j0 + u * 64 + lane;
-      const uint32_t key = key_of(k[u]);
-      const bool keep = j < j_end && key >= T;
-      const uint64_t km = __ballot(keep);
-      const int o = cnt + __popcll(km & lt_mask);
-      if (keep && o < kStrCap) lk[o] = (min(key - T, 65535u) << 16) | (uint32_t)j;
-      cnt += __popcll(km);
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t key = (uint32_t)(((u < 4 ? lo : hi) >> ((u & 3) * 16)) & 0xffffu);
+          const bool in = (unsigned)(r0 + u - r_begin) < (unsigned)(r_end - r_begin);
+          bits |= (uint32_t)(in && key >= T) << u;
+        }
+        const int c = __popc(bits);
+        const int incl = wave_incl_sum(c);
+        int o = cnt + incl - c;
+        cnt += __builtin_amdgcn_readlane(incl, 63);
+        while (bits != 0u) {
+          const int u = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          const uint32_t key = (uint32_t)(((u < 4 ? lo : hi) >> ((u & 3) * 16)) & 0xffffu);
+          if (o < kStrCap) lk[o] = ((key - T) << 16) | (uint32_t)(r0 + u - P);
+          ++o;
+        }
+      };
+      uint4 va = ld(a0), vb;
+      for (int a = a0; a <= a_last; a += 1024) {
+        const int a1 = a + 512;
+        if (a1 <= a_last) vb = ld(a1);
+        put(a, va);
+        if (a1 > a_last) break;
+        if (a1 + 512 <= a_last) va = ld(a1 + 512);
+        put(a1, vb);
+      }
     }
-  });
+  } else {
+    stream([&](int j0, const uint32_t (&k)[kStrLd]) {
+#pragma unroll
+      for (int u = 0; u < kStrLd; ++u) {
+        const int j = j0 + u * 64 + lane;
+        const uint32_t key = key_of(k[u]);
+        const bool keep = j < j_end && key >= T;
+        const uint64_t km = __ballot(keep);
+        const int o = cnt + __popcll(km & lt_mask);
+        if (keep && o < kStrCap) lk[o] = (min(key - T, 65535u) << 16) | (uint32_t)j;
+        cnt += __popcll(km);
+      }
+    });
+  }
   if (lane == 0) s_cnt[wv] = cnt;
   __syncthreads();
   int m = 0;
