@@ -462,6 +462,31 @@ def test_decode_matches_last_prefill_row():
         assert np.abs(d).max() <= 1e-2
 
 
+def test_top_k_covering_context_equals_dense():
+    """K >= every row's candidate count: each list is 0..pos, and the gathered, masked-dense and
+    dense causal kernels give the same attention (each within the bar of the oracle)."""
+    w = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=300, q_len=300, top_k=400, prefix_len=3)
+    _banner("top-K covering the context vs dense")
+    inp = make_inputs(w, seed=23, device="cpu", seq_lens=[300, 300], spare_pages=2).to(DEV)
+    gat = run_gpu(inp, q_chunk=128)
+    msk = run_gpu(inp, q_chunk=128, masked=True, fused=True)
+    kv = make_kv(inp)
+    den_out, den_lse = fa.prefill(kv, inp.q, q_tail=w.q_len)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        for i in (0, 1, 63, 64, 150, 299):
+            want = np.full(w.index_width, -1, dtype=np.int32)
+            want[: i + 1] = np.arange(i + 1)
+            for g in range(w.num_kv_heads):
+                assert np.array_equal(gat.indices[b, i, g].cpu().numpy(), want)
+                assert np.array_equal(msk.indices[b, i, g].cpu().numpy(), want)
+    ref = f64(den_out)
+    for got in (gat.out, msk.out):
+        d = np.abs(f64(got) - ref)
+        assert d.max() <= 1e-2 and d.mean() <= 1e-3, (d.max(), d.mean())
+    assert_close(compare_rows(gat, OracleView(inp), all_rows(inp)[::7]))
+
+
 def test_lse_matches_definition_dense():
     """Dense LSE equals log-sum-exp of the scaled logits computed by the oracle."""
     w = SMALL["dense_contiguous_g4"][0]
