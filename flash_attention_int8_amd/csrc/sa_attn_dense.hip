@@ -28,6 +28,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -41,8 +42,8 @@ constexpr int kDenseThreads = 64 * kDenseWaves;  // MI355X: 8 accelerator dies, 
 // same stale maximum.
 constexpr float kRescaleLog2 = 8.f;
 constexpr int KPAD = 8;   // bf16 padding of a K row in LDS
-constexpr int VPAD = 4;   // bf16 padding of a V^T row in LDS (row stride 136 B: 16 consecutive rows
-                          // hit 16 distinct 8-byte bank pairs)
+constexpr int VPAD = 32;  // bf16 padding of a V row in LDS (row stride 2D + 64 B: the 4-row groups of
+                          // a transposed read land on distinct banks)
 
 // max(x[l], x[l ^ 32]) in every lane l: a self-swap of the two 32-lane halves gives both
 // values whichever half moves.
@@ -54,7 +55,7 @@ __device__ __forceinline__ float halves_max(float x) {
 template <int D>
 struct DenseShared {
   uint16_t k[2][BN][D + KPAD];
-  uint16_t vt[2][D][BN + VPAD];
+  uint16_t v[2][BN][D + VPAD];  // row-major V tiles, read transposed
 };
 
 union Frag8 {
@@ -158,8 +159,6 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   const int ltid = tid & (kDenseThreads / 2 - 1);
   const int ld_c = ltid % CPR;
   const int ld_kq = ltid / CPR;
-  const int lv_kq = (ltid / 4) % KQ;
-  const int lv_c = (ltid / (4 * KQ)) * 4 + ltid % 4;
   const int64_t head_stride = (int64_t)kv.page_size * D;
   const int64_t page_stride = head_stride * kv.num_kv_heads;
 
@@ -169,7 +168,6 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   // when the tile is stored to LDS, so the loads stay in flight until then. The tile base is
   // wave-uniform; each lane adds one 32-bit offset (its first row and dims chunk).
   const uint32_t k_off = (uint32_t)(ld_kq * KPT * D + ld_c * 8);
-  const uint32_t v_off = (uint32_t)(lv_kq * KPT * D + lv_c * 8);
   auto load_rows = [&](const uint16_t* pool, int tile, int64_t ph, uint32_t lane_off, uint4 (&dst)[KPT]) {
     const int t0 = tile * BN;
     const uint16_t* tp = pool + ((ph < 0 ? 0 : ph) * page_stride + g * head_stride +
@@ -200,25 +198,10 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     for (int r = 0; r < KPT; ++r)
       *reinterpret_cast<uint4*>(&sh.k[buf][ld_kq * KPT + r][ld_c * 8]) = src[r];
   };
-  auto store_v = [&](int buf, const uint4 (&src)[KPT]) {  // transpose: KPT-key runs per dim
-    const uint32_t* w[KPT];
+  auto store_v = [&](int buf, const uint4 (&src)[KPT]) {  // row-major, like K
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) w[r] = reinterpret_cast<const uint32_t*>(&src[r]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t vals[KPT];
-#pragma unroll
-      for (int r = 0; r < KPT; ++r) vals[r] = (uint16_t)((w[r][e >> 1] >> ((e & 1) * 16)) & 0xffff);
-      uint16_t* dst = &sh.vt[buf][lv_c * 8 + e][lv_kq * KPT];
-      if constexpr (KPT == 4) {
-        uint2 pkd;
-        pkd.x = (uint32_t)vals[0] | ((uint32_t)vals[1] << 16);
-        pkd.y = (uint32_t)vals[2] | ((uint32_t)vals[3] << 16);
-        *reinterpret_cast<uint2*>(dst) = pkd;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)vals[0] | ((uint32_t)vals[1] << 16);
-      }
-    }
+    for (int r = 0; r < KPT; ++r)
+      *reinterpret_cast<uint4*>(&sh.v[buf][ld_kq * KPT + r][ld_c * 8]) = src[r];
   };
 
   // S^T = K Q^T for the K tile in buffer buf. s[mb][j*4+i] is key mb*32 + j*8 + hi*4 + i of the
@@ -358,10 +341,16 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     auto vfrag = [&](int i) {  // i = st * DB + db; st outer: step st needs the first 8(st+1) exps
       const int st = i / DB, db = i % DB;
       const int kb = (st >> 1) * 32 + (st & 1) * 16 + hi * 4;
-      const uint16_t* vrow = &sh.vt[buf][db * 32 + l32][0];
+      // transposed reads: in each 16-lane group, lane c supplies key row kb + c/4, dims
+      // db*32 + 16*(group & 1) + 4*(c % 4) .. +4, and receives its own dim (db*32 + l32) of the
+      // four rows; the second read takes keys kb + 8 .. kb + 11
+      const int c = lane & 15;
+      const uint16_t* vp = &sh.v[buf][kb + (c >> 2)][db * 32 + 16 * ((lane >> 4) & 1) + 4 * (c & 3)];
       Frag8 a;
-      a.h[0] = *reinterpret_cast<const uint2*>(vrow + kb);
-      a.h[1] = *reinterpret_cast<const uint2*>(vrow + kb + 8);
+      a.h[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                             (__attribute__((address_space(3))) v4s*)(vp)));
+      a.h[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                             (__attribute__((address_space(3))) v4s*)(vp + 8 * (D + VPAD))));
       return a;
     };
     // V^T fragments are read kVPre steps ahead into a rolling buffer; a scheduling barrier
@@ -402,9 +391,9 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     raw_next = raw_page(2);
   } else {
     const int64_t ph = phys_page(kv, b, 0);
-    load_rows(kv.v_pool, 0, ph, v_off, st);
+    load_rows(kv.v_pool, 0, ph, k_off, st);
     const int lim = valid_rows(0, ph);
-    if (lim < BN) mask_rows(st, lv_kq * KPT, lim);
+    if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
     store_v(0, st);
     raw_next = raw_page(1);
   }
@@ -431,7 +420,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     const int lt = more ? ltile : n_tiles - 1;
     const int64_t ph = more ? checked_page(ltile, raw_next) : 0;
     raw_next = raw_page(ltile + 1);
-    load_rows(k_loader ? kv.k_pool : kv.v_pool, lt, ph, k_loader ? k_off : v_off, st);
+    load_rows(k_loader ? kv.k_pool : kv.v_pool, lt, ph, k_off, st);
     const int lim = valid_rows(lt, ph);
     float mx = -INFINITY;
     if (j <= last_w) {
@@ -454,7 +443,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
       pv(j & 1, pf, sn, mx, j + 1 <= last_w);
     }
     if (more) {
-      if (lim < BN) mask_rows(st, k_loader ? ld_kq * KPT : lv_kq * KPT, lim);
+      if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
       if (k_loader) store_k(j & 1, st);
       else store_v((j + 1) & 1, st);
     }
