@@ -14,10 +14,11 @@
 //                   The accumulator layout gives each lane 32 of the 64 scores of ONE query
 //                   (the other 32 sit in lane ^ 32), so the softmax row max is a local max
 //                   plus one cross-half exchange, and row sums stay per lane until the end.
-//   O^T += V^T * P^T  (A = V^T from LDS, B = P^T taken straight from the S^T accumulators:
-//                   the 8 scores a lane holds for one 16-key step become its B operand, and
-//                   the V^T reads use the same key permutation, so no shuffle is needed).
-// V is transposed into LDS on the way in. Softmax is base 2 with sm_scale*log2(e) applied to
+//   O^T += V^T * P^T  (A = V^T fragments read from the row-major V tile with ds_read_b64_tr_b16,
+//                   B = P^T taken straight from the S^T accumulators: the 8 scores a lane holds
+//                   for one 16-key step become its B operand, and the transposed reads fetch
+//                   the same key permutation, so no shuffle is needed).
+// K and V tiles are copied into LDS as they are. Softmax is base 2 with sm_scale*log2(e) applied to
 // the fp32 scores; Q, K and V stay exact bf16, accumulation is fp32, P is rounded to bf16 and
 // the row sum adds the rounded P. Workgroups are ordered for L2 reuse across the 8 XCDs.
 #include "sa_common.h"
