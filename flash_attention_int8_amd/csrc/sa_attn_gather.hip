@@ -294,11 +294,28 @@ __global__ __launch_bounds__(256) void k_merge_splits(const float* __restrict__ 
                                                       int num_splits, int num_q_heads,
                                                       int num_kv_heads, uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
-  __shared__ float s_w[kMaxSplits][G];  // exp2(m_s - M)
+  __shared__ float s_w[kMaxSplits][G];  // m_s, then exp2(m_s - M)
+  __shared__ float s_l[kMaxSplits][G];
   __shared__ float s_M[G], s_L[G];
+  constexpr int NPER = (G * D + 255) / 256;  // output columns per thread
+  constexpr int kPre = 8;                    // splits whose columns are loaded at entry
   const int64_t unit = blockIdx.x;
   const float* ml = ws + units * num_splits * G * D + unit * num_splits * G * 2;
-  for (int x = threadIdx.x; x < num_splits * G; x += 256) s_w[x / G][x % G] = ml[x * 2];
+  const float* acc = ws + unit * num_splits * G * D;
+  // Every load is issued before the first wait: the (max, sum) pairs into LDS and, for the
+  // first kPre splits, this thread's accumulator columns into registers (split index clamped,
+  // so the loads are unconditional; the extra ones get weight 0).
+  float pre[NPER][kPre];
+#pragma unroll
+  for (int k = 0; k < NPER; ++k) {
+    const int x = min((int)threadIdx.x + k * 256, G * D - 1);
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) pre[k][u] = acc[(int64_t)min(u, num_splits - 1) * G * D + x];
+  }
+  for (int x = threadIdx.x; x < num_splits * G; x += 256) {
+    s_w[x / G][x % G] = ml[x * 2];
+    s_l[x / G][x % G] = ml[x * 2 + 1];
+  }
   __syncthreads();
   if (threadIdx.x < G) {
     const int h = threadIdx.x;
@@ -307,7 +324,7 @@ __global__ __launch_bounds__(256) void k_merge_splits(const float* __restrict__ 
     float L = 0.f;
     for (int s = 0; s < num_splits; ++s) {
       const float w = safe_scale(s_w[s][h], M);
-      L += ml[(s * G + h) * 2 + 1] * w;
+      L += s_l[s][h] * w;
       s_w[s][h] = w;
     }
     s_M[h] = M;
@@ -316,19 +333,16 @@ __global__ __launch_bounds__(256) void k_merge_splits(const float* __restrict__ 
   __syncthreads();
   const int g = (int)(unit % num_kv_heads);
   const int64_t bi = unit / num_kv_heads;
-  const float* acc = ws + unit * num_splits * G * D;
-  for (int x = threadIdx.x; x < G * D; x += 256) {
+#pragma unroll
+  for (int k = 0; k < NPER; ++k) {
+    const int x = threadIdx.x + k * 256;
+    if (x >= G * D) break;
     const int h = x / D;
     float aa = 0.f;
-    int s = 0;
-    for (; s + 8 <= num_splits; s += 8) {
-      float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = acc[(int64_t)(s + u) * G * D + x];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) aa += v[u] * s_w[s + u][h];
-    }
-    for (; s < num_splits; ++s) aa += acc[(int64_t)s * G * D + x] * s_w[s][h];
+    for (int u = 0; u < kPre; ++u)
+      if (u < num_splits) aa += pre[k][u] * s_w[u][h];
+    for (int s = kPre; s < num_splits; ++s) aa += acc[(int64_t)s * G * D + x] * s_w[s][h];
     const float L = s_L[h];
     const int64_t qh = bi * num_q_heads + (int64_t)g * G + h;
     out[qh * D + (x - h * D)] = (uint16_t)f32_to_bf16((L > 0.f) ? aa / L : 0.f);
