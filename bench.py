@@ -264,22 +264,27 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048):
             "attention_mfma_tflops": causal_flop / (stage[1] * 1e-3) / 1e12,
             "select_two_step_ms": two_sel,
             "attention_gathered_ms": gather_ms,
+            # every selected (query, group, key) reads a 256-byte K row and a 256-byte V row
+            "gathered_rows_gbps_through_caches": sel * Hkv * 512 / (gather_ms * 1e-3) / 1e9,
             "q_chunk": q_chunk}
 
 
-def bench_decode_1m(fa, steps, warmup):
+def bench_decode_1m(fa, steps, warmup, workload="sparse_decode_1m_prefix", seed=5,
+                    num_idx_heads=None):
     """One decode step at 1M context with a 196-token forced prefix (B=4, 32/8 heads, d=128,
-    d_idx=64, top-K=2048): fused indexer + top-K, then split-K attention and merge."""
+    d_idx=64, top-K=2048): fused indexer + top-K, then split-K attention and merge. The same
+    measurement serves the 128K decode with one indexer key shared by the KV groups."""
     import torch
 
     from synthetic import CONFIGS, make_inputs
-    w = CONFIGS["sparse_decode_1m_prefix"]
-    inp = make_inputs(w, seed=5, device="cuda")
+    w = CONFIGS[workload]
+    inp = make_inputs(w, seed=seed, device="cuda", num_idx_heads=num_idx_heads)
     kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
                     page_table=inp.page_table, seq_lens=inp.seq_lens, max_seq_len=w.seq_len,
                     prefix_len=w.prefix_len)
     B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
-    idx = torch.empty((B, 1, Hkv, w.index_width), dtype=torch.int32, device="cuda")
+    Hi = inp.num_idx_heads
+    idx = torch.empty((B, 1, Hi, w.index_width), dtype=torch.int32, device="cuda")
     q = inp.q[:, 0].contiguous()
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
@@ -302,11 +307,11 @@ def bench_decode_1m(fa, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    kidx_bytes = B * Hkv * w.seq_len * w.idx_dim
+    kidx_bytes = B * Hi * w.seq_len * w.idx_dim
     gather = B * Hkv * (w.prefix_len + w.top_k) * 2 * w.head_dim * 2
     del inp, idx, q, out, lse, fu, dec
     torch.cuda.empty_cache()
-    return {"workload": w.name, "ms": ms, "tokens_per_s": B / (ms * 1e-3),
+    return {"workload": w.name, "idx_heads": Hi, "ms": ms, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbps": (kidx_bytes + gather) / (ms * 1e-3) / 1e9, "cache": "warm (back-to-back steps)"}
 
 
@@ -384,7 +389,10 @@ def main():
         evs[k][1].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_step = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    step_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    ms_step = sum(step_ms) / args.steps
+    pct = {f"p{q}": step_ms[min(len(step_ms) - 1, int(round(q / 100 * (len(step_ms) - 1))))]
+           for q in (10, 50, 90)}
     # breakdown: a separate pass with an event between every entry point (the extra
     # event records add a few microseconds that the headline does not carry)
     bev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -417,6 +425,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_percentiles": pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -451,6 +460,9 @@ def main():
         torch.cuda.empty_cache()
         result["sparse_prefill"] = bench_sparse_prefill(fa, reps=2)
         result["decode_1m_prefix"] = bench_decode_1m(fa, steps=10, warmup=3)
+        # the 128K step with one indexer key shared by all KV groups (a stride-0 indexer head)
+        result["decode_128k_shared_indexer"] = bench_decode_1m(
+            fa, steps=20, warmup=5, workload="sparse_decode_128k", seed=args.seed, num_idx_heads=1)
     print(json.dumps(result), flush=True)
 
 
