@@ -64,9 +64,10 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const voi
   constexpr int NT = kStrNT;
   constexpr int NW = NT / 64;
   constexpr int kBatch = 64 * kStrLd;
-  static_assert(NW * kStrCap >= kBins, "the list space holds a 4096-bin histogram");
+  constexpr int kCap = kStrCap;
+  static_assert(NW * kCap >= kBins, "the list space holds a 4096-bin histogram");
   // per-wave lists, entry = min(key - T, 65535) << 16 | candidate index (or a histogram)
-  __shared__ __align__(16) uint32_t l_key[NW * kStrCap];
+  __shared__ __align__(16) uint32_t l_key[NW * kCap];
   __shared__ __align__(16) uint32_t s_hist[512];          // fine (256) and sub (256) bins
   __shared__ int32_t s_cnt[NW], s_cnt2[NW], s_seg[NW];
   const int tid = threadIdx.x;
@@ -184,12 +185,13 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const voi
   __syncthreads();  // the sample histogram is no longer read
 
   // stream the row into the per-wave lists
-  uint32_t* lk = l_key + wv * kStrCap;
+  uint32_t* lk = l_key + wv * kCap;
   int cnt = 0;
   if constexpr (COARSE) {
     // Lane-major: each lane takes 8 consecutive 16-bit keys (one 16-byte load) per step, so a
     // step covers 512 consecutive keys with lane order = token order; one wave prefix sum of
-    // the per-lane counts places a lane's kept keys, and it loops over those only.
+    // the per-lane counts places a lane's kept keys, and it loops over those only. Four steps
+    // of loads are kept in flight.
     if (j_begin < j_end) {  // uniform
       const int r_begin = P + j_begin, r_end = P + j_end;  // row indices of this wave's range
       const int a0 = r_begin & ~7;
@@ -215,18 +217,25 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const voi
           const int u = __builtin_ctz(bits);
           bits &= bits - 1u;
           const uint32_t key = (uint32_t)(((u < 4 ? lo : hi) >> ((u & 3) * 16)) & 0xffffu);
-          if (o < kStrCap) lk[o] = ((key - T) << 16) | (uint32_t)(r0 + u - P);
+          if (o < kCap) lk[o] = ((key - T) << 16) | (uint32_t)(r0 + u - P);
           ++o;
         }
       };
-      uint4 va = ld(a0), vb;
-      for (int a = a0; a <= a_last; a += 1024) {
-        const int a1 = a + 512;
-        if (a1 <= a_last) vb = ld(a1);
-        put(a, va);
-        if (a1 > a_last) break;
-        if (a1 + 512 <= a_last) va = ld(a1 + 512);
-        put(a1, vb);
+      // kAhead steps of loads in flight per wave (a step is one 1 KiB load instruction; with
+      // one step ahead the stream waited a round trip per step)
+      constexpr int kAhead = 4;
+      uint4 ring[kAhead];
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k) ring[k] = ld(a0 + k * 512);  // clamped: in bounds
+      for (int a = a0; a <= a_last; a += 512 * kAhead) {
+#pragma unroll
+        for (int k = 0; k < kAhead; ++k) {
+          const int ak = a + k * 512;
+          if (ak > a_last) break;  // uniform
+          const uint4 v = ring[k];
+          ring[k] = ld(ak + kAhead * 512);
+          put(ak, v);
+        }
       }
     }
   } else {
@@ -238,7 +247,7 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const voi
         const bool keep = j < j_end && key >= T;
         const uint64_t km = __ballot(keep);
         const int o = cnt + __popcll(km & lt_mask);
-        if (keep && o < kStrCap) lk[o] = (min(key - T, 65535u) << 16) | (uint32_t)j;
+        if (keep && o < kCap) lk[o] = (min(key - T, 65535u) << 16) | (uint32_t)j;
         cnt += __popcll(km);
       }
     });
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const voi
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     m += s_cnt[w];
-    over = over || s_cnt[w] > kStrCap;
+    over = over || s_cnt[w] > kCap;
   }
   if (m >= top_k && !over) {
     for (int c = lane; c < cnt; c += 64) atomicAdd(&s_hist[lk[c] >> 24], 1u);
