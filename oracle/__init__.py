@@ -31,6 +31,7 @@ from .dsa import (  # noqa: F401
     index_scores,
     topk_select,
     index_list,
+    hybrid_index_list,
     attend,
     dsa_query,
     dense_query,

@@ -4,6 +4,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring): only tests, the smoke chec
 the benchmark's CPU-baseline leg may use it.
 
 [DSA-page] = "国产AI芯片完成前沿大模型Day-0适配:稀疏注意力与混合精度推理全解析" (ruibaoantu.com).
+[MTT-page] = "…在摩尔线程MTT S5000上的原生推理优化实践" (blog.csdn.net): §2.3 describes a hybrid of
+global sparse and local sliding-window attention.
 
 Readings taken where the page leaves a step open (each is also listed with its reason in
 the design notes):
@@ -24,8 +26,9 @@ invariants; index_list against the prefix rule and a hand-worked golden case; at
 against closed forms (single key, constant V, identical keys, one-hot V rows giving the
 probabilities), scipy's logsumexp, and a full-matrix masked softmax for the dense case;
 page_rows against an unpaged copy under a random page permutation; append_rows against
-page_rows (round trip) and an unpaged array write, untouched rows kept. No function is
-"parity unpinned".
+page_rows (round trip) and an unpaged array write, untouched rows kept; hybrid_index_list
+against a brute-force full sort with the window and prefix marked, index_list at window 0, and
+every key at window >= pos + 1. No function is "parity unpinned".
 """
 import numpy as np
 
@@ -126,6 +129,26 @@ def index_list(pos: int, prefix_len: int, top_k: int, width: int, score_fn) -> n
     """
     f = forced_keys(pos, prefix_len)
     c = candidate_keys(pos, prefix_len)
+    sel = topk_select(score_fn(c), c, top_k) if c.size else c
+    keys = np.sort(np.concatenate([f, sel]))
+    out = np.full(width, -1, dtype=np.int64)
+    out[:keys.size] = keys
+    return out
+
+
+def hybrid_index_list(pos: int, prefix_len: int, window: int, top_k: int, width: int,
+                      score_fn) -> np.ndarray:
+    """[MTT-page] §2.3: hybrid attention = global sparse attention plus local sliding-window
+    attention. Read here as one key list per (query, KV-head group): the last `window` keys up
+    to the query (pos - window + 1 .. pos) are always attended, like the forced prefix of
+    [DSA-page] §2.4, and are not screened; the top-K is taken over the remaining causal keys
+    outside the prefix. Ascending, padded with -1 to `width` (= prefix_len + top_k + window).
+    window = 0 gives index_list.
+    """
+    pos = int(pos)
+    lo = max(0, pos - int(window) + 1)  # first window key (window empty when lo > pos)
+    f = np.union1d(forced_keys(pos, prefix_len), np.arange(lo, pos + 1, dtype=np.int64))
+    c = np.arange(int(prefix_len), lo, dtype=np.int64)  # screened: outside prefix and window
     sel = topk_select(score_fn(c), c, top_k) if c.size else c
     keys = np.sort(np.concatenate([f, sel]))
     out = np.full(width, -1, dtype=np.int64)

@@ -156,6 +156,44 @@ def test_index_list_ignores_prefix_scores():
 
 # ---------------------------------------------------------------- paging
 
+@pytest.mark.parametrize("seed", range(12))
+def test_hybrid_list_matches_brute_force(seed):
+    """Window + prefix forced, the top-K of the rest by (score desc, token asc): checked
+    against a full sort of every key with the forced ones marked, on tied small scores."""
+    rng = np.random.default_rng(100 + seed)
+    pos = int(rng.integers(0, 90))
+    P, W, K = int(rng.integers(0, 6)), int(rng.integers(0, 40)), int(rng.integers(1, 30))
+    scores = rng.integers(-3, 4, size=pos + 1)
+    got = oracle.hybrid_index_list(pos, P, W, K, P + K + W, lambda t: scores[t])
+    forced = [t for t in range(pos + 1) if t < P or t > pos - W]
+    rest = sorted((t for t in range(pos + 1) if t not in forced), key=lambda t: (-scores[t], t))
+    want = sorted(forced + rest[:K])
+    assert list(got[:len(want)]) == want
+    assert np.all(got[len(want):] == -1) and len(got) == P + K + W
+
+
+def test_hybrid_list_special_cases():
+    rng = np.random.default_rng(7)
+    scores = rng.integers(-50, 50, size=400)
+    fn = lambda t: scores[t]
+    for pos in (0, 5, 63, 200, 399):
+        for P in (0, 3):
+            # no window: the plain selection
+            assert np.array_equal(oracle.hybrid_index_list(pos, P, 0, 20, P + 20, fn),
+                                  oracle.index_list(pos, P, 20, P + 20, fn))
+            # a window reaching the first key: every key, nothing screened
+            got = oracle.hybrid_index_list(pos, P, pos + 1, 20, P + 20 + pos + 1, fn)
+            assert np.array_equal(got[:pos + 1], np.arange(pos + 1))
+            assert np.all(got[pos + 1:] == -1)
+    # maximal scores inside the window take no place of the top-K
+    s2 = scores.copy()
+    s2[380:] = 10 ** 6
+    got = oracle.hybrid_index_list(399, 2, 20, 10, 32, lambda t: s2[t])
+    assert np.array_equal(got[-20:], np.arange(380, 400))
+    top = got[(got >= 2) & (got < 380)]
+    assert len(top) == 10 and np.array_equal(top, np.sort(oracle.topk_select(s2[2:380], np.arange(2, 380), 10)))
+
+
 def test_page_rows_follow_the_page_table():
     rng = np.random.default_rng(3)
     T, ps, H, D = 200, 16, 3, 5
