@@ -26,6 +26,7 @@ SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_H
 EXPORTS = ["sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_index",
            "sparse_attn_topk_workspace_size", "sparse_attn_topk",
            "sparse_attn_index_topk_workspace_size", "sparse_attn_index_topk",
+           "sparse_attn_index_topk_window_workspace_size", "sparse_attn_index_topk_window",
            "sparse_attn_fwd_prefill", "sparse_attn_prefill_masked_workspace_size",
            "sparse_attn_fwd_prefill_masked", "sparse_attn_kv_append",
            "sparse_attn_decode_workspace_size", "sparse_attn_fwd_decode"]
@@ -82,6 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sparse_attn_topk": (I32, [KV, P, I64, I32, I32, I32, P, P, SZ, P]),
         "sparse_attn_index_topk_workspace_size": (SZ, [KV, I32, I32]),
         "sparse_attn_index_topk": (I32, [KV, P, I32, I32, I32, P, P, SZ, P]),
+        "sparse_attn_index_topk_window_workspace_size": (SZ, [KV, I32, I32, I32]),
+        "sparse_attn_index_topk_window": (I32, [KV, P, I32, I32, I32, I32, P, P, SZ, P]),
         "sparse_attn_fwd_prefill": (I32, [KV, P, I32, I32, I32, P, I32, F32, P, P, P]),
         "sparse_attn_prefill_masked_workspace_size": (SZ, [KV, I32]),
         "sparse_attn_fwd_prefill_masked": (I32, [KV, P, I32, I32, I32, P, I32, F32, P, SZ, P, P, P]),
@@ -192,6 +195,19 @@ def sparse_attn_index_topk(kv: PagedKV, q_idx, q_len, q_tail, top_k, indices, wo
         _stream(stream)))
 
 
+def sparse_attn_index_topk_window_workspace_size(kv: PagedKV, q_len, top_k, window) -> int:
+    return int(load().sparse_attn_index_topk_window_workspace_size(kv.ref, q_len, top_k, window))
+
+
+def sparse_attn_index_topk_window(kv: PagedKV, q_idx, q_len, q_tail, top_k, window, indices,
+                                  workspace, workspace_bytes, stream=None):
+    lib = load()
+    _check("sparse_attn_index_topk_window", lib.sparse_attn_index_topk_window(
+        kv.ref, _ptr(q_idx, torch.int8, "q_idx"), q_len, q_tail, top_k, window,
+        _ptr(indices, torch.int32, "indices"), _ptr(workspace, None, "workspace"), workspace_bytes,
+        _stream(stream)))
+
+
 def sparse_attn_fwd_prefill(kv: PagedKV, q, num_q_heads, q_len, q_tail, indices, index_width,
                             sm_scale, out, lse=None, stream=None):
     lib = load()
@@ -289,6 +305,22 @@ def index_topk(kv: PagedKV, q_idx, q_len, q_tail, top_k, indices=None, workspace
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_idx.device)
     sparse_attn_index_topk(kv, q_idx, q_len, q_tail, top_k, indices, workspace,
                            workspace.numel() * workspace.element_size(), stream)
+    return indices
+
+
+def index_topk_window(kv: PagedKV, q_idx, q_len, q_tail, top_k, window, indices=None,
+                      workspace=None, stream=None):
+    """Hybrid lists: prefix + window forced, top-K over the rest; width P + top_k + window."""
+    d = kv.desc
+    width = d.prefix_len + top_k + window
+    if indices is None:
+        indices = torch.empty((d.batch, q_len, d.num_idx_heads, width), dtype=torch.int32,
+                              device=q_idx.device)
+    need = sparse_attn_index_topk_window_workspace_size(kv, q_len, top_k, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_idx.device)
+    sparse_attn_index_topk_window(kv, q_idx, q_len, q_tail, top_k, window, indices, workspace,
+                                  workspace.numel() * workspace.element_size(), stream)
     return indices
 
 

@@ -136,29 +136,18 @@ size_t composite_bytes(const sa::KvView& v, int32_t q_len, int32_t top_k) {
 
 }  // namespace
 
-size_t sparse_attn_index_topk_workspace_size(const sa_paged_kv* kv, int32_t q_len, int32_t top_k) {
-  sa::KvView v;
-  if (check_kv(kv, NEED_IDX, &v) != SA_OK || q_len < 1 || top_k < 1) return 0;
+namespace {
+
+size_t index_topk_bytes(const sa::KvView& v, int32_t q_len, int32_t top_k) {
   if (sa::fused_applies(v, q_len)) return sa::fused_workspace_bytes(v);
   return composite_bytes(v, q_len, top_k);
 }
 
-int32_t sparse_attn_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
-                               int32_t q_tail, int32_t top_k, int32_t* indices, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-  sa::KvView v;
-  int32_t st = check_kv(kv, NEED_IDX, &v);
-  if (st != SA_OK) return st;
-  if ((st = check_block(v, q_len, q_tail)) != SA_OK) return st;
-  if (q_idx == nullptr || indices == nullptr) return SA_ERR_NULL;
-  if (!aligned16(q_idx) || !aligned16(indices)) return SA_ERR_ALIGN;
-  if (top_k < 1 || (int64_t)top_k + v.prefix_len > (1 << 30)) return SA_ERR_SHAPE;
-  const bool fused = sa::fused_applies(v, q_len);
-  const size_t need = fused ? sa::fused_workspace_bytes(v) : composite_bytes(v, q_len, top_k);
-  if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return SA_ERR_ALIGN;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (fused) return hip_status(sa::launch_index_topk_fused(v, q_idx, q_tail, top_k, indices, workspace, s));
+// The selection of sparse_attn_index_topk on a validated descriptor and workspace.
+int32_t index_topk_run(const sa::KvView& v, const int8_t* q_idx, int32_t q_len, int32_t q_tail,
+                       int32_t top_k, int32_t* indices, void* workspace, hipStream_t s) {
+  if (sa::fused_applies(v, q_len))
+    return hip_status(sa::launch_index_topk_fused(v, q_idx, q_tail, top_k, indices, workspace, s));
   if (sa::topk_coarse_applies(v, q_len)) {
     // many-query blocks of rows up to 32K: 16-bit keys (half the traffic of int32 scores) in the
     // score space of the workspace, row stride a multiple of 8 keys
@@ -176,6 +165,84 @@ int32_t sparse_attn_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32
   if (e != hipSuccess) return SA_ERR_HIP;
   return hip_status(sa::launch_topk(v, scores, stride, q_len, q_tail, top_k, indices, tk_ws,
                                     sa::topk_workspace_bytes(v, q_len, top_k), s));
+}
+
+// Checks shared by the selection entry points; on success *need is the workspace size.
+int32_t check_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len, int32_t q_tail,
+                         int32_t top_k, int64_t extra_width, const int32_t* indices, sa::KvView* v) {
+  int32_t st = check_kv(kv, NEED_IDX, v);
+  if (st != SA_OK) return st;
+  if ((st = check_block(*v, q_len, q_tail)) != SA_OK) return st;
+  if (q_idx == nullptr || indices == nullptr) return SA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(indices)) return SA_ERR_ALIGN;
+  if (top_k < 1 || (int64_t)top_k + v->prefix_len + extra_width > (1 << 30)) return SA_ERR_SHAPE;
+  return SA_OK;
+}
+
+}  // namespace
+
+size_t sparse_attn_index_topk_workspace_size(const sa_paged_kv* kv, int32_t q_len, int32_t top_k) {
+  sa::KvView v;
+  if (check_kv(kv, NEED_IDX, &v) != SA_OK || q_len < 1 || top_k < 1) return 0;
+  return index_topk_bytes(v, q_len, top_k);
+}
+
+int32_t sparse_attn_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
+                               int32_t q_tail, int32_t top_k, int32_t* indices, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  sa::KvView v;
+  int32_t st = check_index_topk(kv, q_idx, q_len, q_tail, top_k, 0, indices, &v);
+  if (st != SA_OK) return st;
+  const size_t need = index_topk_bytes(v, q_len, top_k);
+  if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SA_ERR_ALIGN;
+  return index_topk_run(v, q_idx, q_len, q_tail, top_k, indices, workspace,
+                        static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+// Workspace of the hybrid selection: shortened lengths, the shortened lists, the selection's own.
+size_t window_bytes(const sa::KvView& v, int32_t q_len, int32_t top_k) {
+  const size_t rows = (size_t)v.batch * q_len * v.num_idx_heads;
+  return align256((size_t)v.batch * sizeof(int32_t)) +
+         align256(rows * ((size_t)v.prefix_len + top_k) * sizeof(int32_t)) +
+         index_topk_bytes(v, q_len, top_k);
+}
+
+}  // namespace
+
+size_t sparse_attn_index_topk_window_workspace_size(const sa_paged_kv* kv, int32_t q_len,
+                                                    int32_t top_k, int32_t window) {
+  sa::KvView v;
+  if (check_kv(kv, NEED_IDX, &v) != SA_OK || q_len < 1 || top_k < 1 || window < 0) return 0;
+  return window_bytes(v, q_len, top_k);
+}
+
+int32_t sparse_attn_index_topk_window(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
+                                      int32_t q_tail, int32_t top_k, int32_t window,
+                                      int32_t* indices, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  sa::KvView v;
+  if (window < 0) return SA_ERR_SHAPE;
+  int32_t st = check_index_topk(kv, q_idx, q_len, q_tail, top_k, window, indices, &v);
+  if (st != SA_OK) return st;
+  const size_t need = window_bytes(v, q_len, top_k);
+  if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SA_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t rows = (size_t)v.batch * q_len * v.num_idx_heads;
+  char* base = static_cast<char*>(workspace);
+  int32_t* short_lens = reinterpret_cast<int32_t*>(base);
+  int32_t* lists = reinterpret_cast<int32_t*>(base + align256((size_t)v.batch * sizeof(int32_t)));
+  void* inner = base + align256((size_t)v.batch * sizeof(int32_t)) +
+                align256(rows * ((size_t)v.prefix_len + top_k) * sizeof(int32_t));
+  if (sa::launch_window_lens(v, window, short_lens, s) != hipSuccess) return SA_ERR_HIP;
+  sa::KvView vs = v;
+  vs.seq_lens = short_lens;
+  if ((st = index_topk_run(vs, q_idx, q_len, q_tail, top_k, lists, inner, s)) != SA_OK) return st;
+  return hip_status(sa::launch_window_finish(v, short_lens, q_len, q_tail, top_k, window, lists,
+                                             indices, s));
 }
 
 int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_t num_q_heads,

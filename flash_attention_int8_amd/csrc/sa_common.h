@@ -152,6 +152,11 @@ bool topk_coarse_applies(const KvView& kv, int q_len);
 hipError_t launch_topk_coarse(const KvView& kv, const uint16_t* keys, int64_t row_stride, int q_len,
                               int q_tail, int top_k, const int8_t* q_idx, int32_t* indices,
                               hipStream_t stream);
+// Hybrid index lists (local window + global top-K): shortened lengths, then the window appended.
+hipError_t launch_window_lens(const KvView& kv, int window, int32_t* short_lens, hipStream_t stream);
+hipError_t launch_window_finish(const KvView& kv, const int32_t* short_lens, int q_len, int q_tail,
+                                int top_k, int window, const int32_t* lists, int32_t* indices,
+                                hipStream_t stream);
 // KV-cache append: new tokens' rows written into the paged pools.
 hipError_t launch_kv_append(const KvView& kv, const uint16_t* k_new, const uint16_t* v_new,
                             const int8_t* kidx_new, int n_new, hipStream_t stream);

@@ -167,6 +167,27 @@ int32_t sparse_attn_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32
                                size_t workspace_bytes, void* stream);
 
 /*
+ * Hybrid index lists: the selection of sparse_attn_index_topk plus a local window. Global sparse
+ * attention next to local sliding-window attention is the hybrid described on the page
+ * "…在摩尔线程MTT S5000上的原生推理优化实践" (blog.csdn.net) §2.3; the window is read here as a
+ * second forced set like the prefix of [DSA-page] §2.4. For a query at pos the forced keys are
+ * the prefix (t < min(P, pos + 1)) and the window (max(0, pos - window + 1) <= t <= pos); the
+ * top-K runs over the remaining causal keys, ties to the lower token. The list holds all of
+ * them ascending, -1 padded:
+ *   indices  int32 [batch][q_len][num_idx_heads][prefix_len + top_k + window]
+ * window = 0 gives sparse_attn_index_topk's lists. The attention entry points take these lists
+ * with index_width = prefix_len + top_k + window.
+ * workspace: sparse_attn_index_topk_window_workspace_size(kv, q_len, top_k, window) bytes of
+ * device memory; its contents on entry do not matter. window >= 0.
+ */
+size_t sparse_attn_index_topk_window_workspace_size(const sa_paged_kv* kv, int32_t q_len,
+                                                    int32_t top_k, int32_t window);
+int32_t sparse_attn_index_topk_window(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
+                                      int32_t q_tail, int32_t top_k, int32_t window,
+                                      int32_t* indices, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * Prefill attention ([DSA-page] §2.3, prefill): online-softmax attention of a block of
  * queries over their index lists, or dense causal attention when indices == NULL.
  *

@@ -131,6 +131,37 @@ def test_prefill_masked_workspace_size(lib):
     assert lib.sparse_attn_prefill_masked_workspace_size(ctypes.byref(d1), 256) == 2 * 8 * 16 * 256
 
 
+def call_window(lib, d, q_idx=A, q_len=1, q_tail=1, k=64, window=16, idx=A, ws=A, ws_bytes=1 << 30):
+    return lib.sparse_attn_index_topk_window(ctypes.byref(d), q_idx, q_len, q_tail, k, window, idx,
+                                             ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(window=-1), fa.SA_ERR_SHAPE),
+    (dict(k=0), fa.SA_ERR_SHAPE),
+    (dict(window=1 << 30), fa.SA_ERR_SHAPE),
+    (dict(q_idx=None), fa.SA_ERR_NULL),
+    (dict(idx=None), fa.SA_ERR_NULL),
+    (dict(ws=None), fa.SA_ERR_WORKSPACE),
+    (dict(ws_bytes=64), fa.SA_ERR_WORKSPACE),
+    (dict(ws=A + 4), fa.SA_ERR_ALIGN),
+    (dict(d=desc(kidx_pool=None)), fa.SA_ERR_NULL),
+    (dict(q_len=2, q_tail=1), fa.SA_ERR_SHAPE),
+])
+def test_index_topk_window_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_window(lib, d, **case) == code
+
+
+def test_index_topk_window_workspace_grows_with_the_lists(lib):
+    d = desc()
+    plain = lib.sparse_attn_index_topk_workspace_size(ctypes.byref(d), 1, 64)
+    w = lib.sparse_attn_index_topk_window_workspace_size(ctypes.byref(d), 1, 64, 16)
+    assert w >= plain + 2 * 8 * 64 * 4  # the shortened lists (B=2, H_idx=8, P+K=64)
+    assert lib.sparse_attn_index_topk_window_workspace_size(ctypes.byref(d), 1, 64, -1) == 0
+
+
 def call_append(lib, d, k=A, v=A + 0x100, ki=A + 0x200, n=4):
     return lib.sparse_attn_kv_append(ctypes.byref(d), k, v, ki, n, None)
 

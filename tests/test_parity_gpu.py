@@ -182,6 +182,73 @@ def test_kv_append_matches_oracle(n_new, shared_idx, hole):
         assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
 
 
+WINDOW_CASES = {
+    # (workload, inputs, window)
+    "decode_window_ragged": (W(batch=4, num_q_heads=16, num_kv_heads=2, head_dim=64, idx_dim=128,
+                               seq_len=3000, q_len=1, top_k=100, prefix_len=13),
+                             dict(seq_lens=[3000, 64, 777, 10], spare_pages=5), 200),
+    "decode_window_long": (W(batch=2, seq_len=40000, q_len=1, top_k=2048, prefix_len=5),
+                           dict(seq_lens=[40000, 20000]), 512),
+    "prefill_window_ragged": (W(batch=2, seq_len=300, q_len=250, top_k=40, prefix_len=5),
+                              dict(seq_lens=[300, 250], spare_pages=3), 64),
+    "prefill_window_ties_shared": (W(seq_len=320, q_len=320, top_k=50, prefix_len=7),
+                                   dict(idx_values=(-1, 0, 1), num_idx_heads=1), 33),
+}
+
+
+@pytest.mark.parametrize("name", list(WINDOW_CASES))
+def test_index_topk_window_matches_oracle(name):
+    """Hybrid lists (the last `window` keys and the prefix forced, the top-K over the rest):
+    bit-exact against the oracle, and attention over them (gathered, masked dense, decode)
+    within the bar."""
+    w, kw, win = WINDOW_CASES[name]
+    _banner(f"hybrid lists {name} window={win}")
+    inp = make_inputs(w, seed=41, device="cpu", **kw).to(DEV)
+    kv = make_kv(inp)
+    B, S, G, Hi = w.batch, w.q_len, w.group, inp.num_idx_heads
+    width = w.prefix_len + w.top_k + win
+    lists = torch.empty((B, S, Hi, width), dtype=torch.int32, device=DEV)
+    chunk = 96 if S > 200 else S
+    for q0 in range(0, S, chunk):
+        c = min(chunk, S - q0)
+        lists[:, q0:q0 + c] = fa.index_topk_window(kv, inp.q_idx[:, q0:q0 + c].contiguous(), c, S - q0,
+                                                   w.top_k, win)
+    outs = []
+    if S == 1:
+        o, l = fa.decode(kv, inp.q[:, 0].contiguous(), lists[:, 0].contiguous())
+        outs.append((o.unsqueeze(1), l.unsqueeze(1)))
+    else:
+        outs.append(fa.prefill(kv, inp.q, q_tail=S, indices=lists))
+        outs.append(fa.prefill_masked(kv, inp.q, q_tail=S, indices=lists))
+    torch.cuda.synchronize()
+    ov = OracleView(inp)
+    got_lists = lists.cpu().numpy()
+    rows = all_rows(inp)
+    if len(rows) > 300:
+        rows = rows[:: len(rows) // 300]
+    scale = 1.0 / math.sqrt(w.head_dim)
+    errs = [[] for _ in outs]
+    lerrs = [[] for _ in outs]
+    for (b, i, g) in rows:
+        gi = 0 if Hi == 1 else g
+        pos = oracle.query_position(inp.seq_lens_host[b], S, i)
+        qi = inp.q_idx[b, i, gi].cpu().numpy()
+        fn = lambda t: oracle.index_scores(qi, oracle.page_rows(ov.kidx, ov.table[b], w.page_size, gi, t))
+        want = oracle.hybrid_index_list(pos, w.prefix_len, win, w.top_k, width, fn)
+        assert np.array_equal(got_lists[b, i, gi], want), (name, b, i, g)
+        keys = want[want >= 0]
+        kr = oracle.bf16_to_f64(oracle.page_rows(ov.k_pool, ov.table[b], w.page_size, g, keys))
+        vr = oracle.bf16_to_f64(oracle.page_rows(ov.v_pool, ov.table[b], w.page_size, g, keys))
+        qb = oracle.bf16_to_f64(bits(inp.q[b, i, g * G:(g + 1) * G]))
+        o_ref, l_ref = oracle.attend(qb, kr, vr, scale)
+        for k, (o, l) in enumerate(outs):
+            errs[k].append(np.abs(f64(o[b, i, g * G:(g + 1) * G]) - o_ref).ravel())
+            lerrs[k].append(np.abs(l[b, i, g * G:(g + 1) * G].double().cpu().numpy() - l_ref))
+    for e, le in zip(errs, lerrs):
+        e = np.concatenate(e)
+        assert_close((float(e.max()), float(e.mean()), float(np.concatenate(le).max())))
+
+
 DECODE = {
     "decode_ragged_prefix": (W(batch=4, num_q_heads=16, num_kv_heads=2, head_dim=64, idx_dim=128,
                                seq_len=1000, q_len=1, top_k=100, prefix_len=13),
