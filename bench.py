@@ -270,7 +270,7 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048):
 
 
 def bench_decode_1m(fa, steps, warmup, workload="sparse_decode_1m_prefix", seed=5,
-                    num_idx_heads=None):
+                    num_idx_heads=None, window=0):
     """One decode step at 1M context with a 196-token forced prefix (B=4, 32/8 heads, d=128,
     d_idx=64, top-K=2048): fused indexer + top-K, then split-K attention and merge. The same
     measurement serves the 128K decode with one indexer key shared by the KV groups."""
@@ -284,19 +284,24 @@ def bench_decode_1m(fa, steps, warmup, workload="sparse_decode_1m_prefix", seed=
                     prefix_len=w.prefix_len)
     B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
     Hi = inp.num_idx_heads
-    idx = torch.empty((B, 1, Hi, w.index_width), dtype=torch.int32, device="cuda")
+    width = w.index_width + window
+    idx = torch.empty((B, 1, Hi, width), dtype=torch.int32, device="cuda")
     q = inp.q[:, 0].contiguous()
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    fu_n = fa.sparse_attn_index_topk_workspace_size(kv, 1, w.top_k)
+    fu_n = (fa.sparse_attn_index_topk_window_workspace_size(kv, 1, w.top_k, window) if window
+            else fa.sparse_attn_index_topk_workspace_size(kv, 1, w.top_k))
     fu = torch.empty(max(fu_n, 16), dtype=torch.uint8, device="cuda")
-    dec_n = fa.sparse_attn_decode_workspace_size(kv, Hq, w.index_width, 0)
+    dec_n = fa.sparse_attn_decode_workspace_size(kv, Hq, width, 0)
     dec = torch.empty(max(dec_n, 16), dtype=torch.uint8, device="cuda")
     scale = 1 / math.sqrt(w.head_dim)
 
     def step():
-        fa.sparse_attn_index_topk(kv, inp.q_idx, 1, 1, w.top_k, idx, fu, fu_n)
-        fa.sparse_attn_fwd_decode(kv, q, Hq, idx[:, 0], w.index_width, scale, 0, dec, dec_n, out, lse)
+        if window:
+            fa.sparse_attn_index_topk_window(kv, inp.q_idx, 1, 1, w.top_k, window, idx, fu, fu_n)
+        else:
+            fa.sparse_attn_index_topk(kv, inp.q_idx, 1, 1, w.top_k, idx, fu, fu_n)
+        fa.sparse_attn_fwd_decode(kv, q, Hq, idx[:, 0], width, scale, 0, dec, dec_n, out, lse)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -308,10 +313,10 @@ def bench_decode_1m(fa, steps, warmup, workload="sparse_decode_1m_prefix", seed=
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     kidx_bytes = B * Hi * w.seq_len * w.idx_dim
-    gather = B * Hkv * (w.prefix_len + w.top_k) * 2 * w.head_dim * 2
+    gather = B * Hkv * width * 2 * w.head_dim * 2
     del inp, idx, q, out, lse, fu, dec
     torch.cuda.empty_cache()
-    return {"workload": w.name, "idx_heads": Hi, "ms": ms, "tokens_per_s": B / (ms * 1e-3),
+    return {"workload": w.name, "idx_heads": Hi, "window": window, "ms": ms, "tokens_per_s": B / (ms * 1e-3),
             "hbm_gbps": (kidx_bytes + gather) / (ms * 1e-3) / 1e9, "cache": "warm (back-to-back steps)"}
 
 
@@ -463,6 +468,9 @@ def main():
         # the 128K step with one indexer key shared by all KV groups (a stride-0 indexer head)
         result["decode_128k_shared_indexer"] = bench_decode_1m(
             fa, steps=20, warmup=5, workload="sparse_decode_128k", seed=args.seed, num_idx_heads=1)
+        # the 128K step with hybrid lists: the last 512 keys forced beside the top-2048
+        result["decode_128k_window_512"] = bench_decode_1m(
+            fa, steps=20, warmup=5, workload="sparse_decode_128k", seed=args.seed, window=512)
     print(json.dumps(result), flush=True)
 
 
