@@ -9,7 +9,7 @@
 //
 // Two launches over rows r = (sequence, indexer head):
 //   main    per (row, 8192-token chunk): scores every key of the chunk; the histogram of key >> 12
-//           over the chunk's first 1024 keys sets the chunk's threshold bin theta_c (the highest
+//           over the chunk's first 4096 keys sets the chunk's threshold bin theta_c (the highest
 //           bin whose tail holds well over those keys' share of K), and the keys in bins >=
 //           theta_c are compacted, in token order, into the chunk's candidate slots.
 //   final   one workgroup per row: the histogram of the candidates gives b1, the bin of the
@@ -30,6 +30,7 @@ using namespace sel;
 
 constexpr int kFChunk = 8192;             // tokens per main-pass workgroup
 constexpr int kFBlocks = kFChunk / 64;    // 64-token blocks per chunk
+constexpr int kSampleSlabs = 4;           // 1024-token slabs whose histogram sets the chunk threshold
 constexpr int kFinalNT = 1024;
 
 struct FusedWs {
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
   constexpr int NW = NT / 64;
   constexpr int U = 4;  // blocks per wave per slab; a slab is NW * U = 16 blocks (1024 tokens)
   __shared__ TopkShared<NT> sh;
+  __shared__ uint4 s_sample[kSampleSlabs][NT];
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
@@ -180,6 +182,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
     }
   };
   constexpr int kSlabs = kFBlocks / (NW * U);
+  static_assert(kSampleSlabs >= 1 && kSampleSlabs < kSlabs, "the sample is a proper prefix of the chunk");
   uint32_t key[U];
   bool in[U], keep[U], ok[U];
   int tok[U];
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
   slab_pages(1, raw_nxt);
   issue_slab(0, raw_cur, kd, ok);
   // After a slab is scored its registers take the next slab's loads, which stay in flight
-  // while the slab is compacted (and, for the first slab, while the threshold is found).
+  // while the slab is compacted (and, for the sample slabs, while the threshold is found).
   auto next_slab = [&](int slab) {
     if (slab + 1 < kSlabs) {
 #pragma unroll
@@ -198,14 +201,25 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
       issue_slab(slab + 1, raw_cur, kd, ok);
     }
   };
-  // The chunk's threshold from its first slab: the highest bin whose tail holds well over the
-  // slab's share of K (twice the expected count plus three standard deviations plus 8). Any
-  // value is safe: the final pass checks it and rescores the row if it was too high.
-  score_slab(0, kd, ok, key, in, tok);
-  next_slab(0);
+  // The chunk's threshold from its first kSampleSlabs slabs, whose keys stay in registers: the
+  // highest bin whose tail holds well over the sample's share of K (twice the expected count
+  // plus three standard deviations plus 8). Any value is safe: the final pass checks it and
+  // rescores the row if it was too high. A larger sample gives a threshold closer to the
+  // sample's share, so fewer candidates reach the final pass.
+  // The sample keys wait in LDS (each lane reads back only its own), kNotIn marking the
+  // tokens that are not candidates; keys are at most 24 bits, so the mark is unambiguous.
+  static_assert(U == 4, "one 16-byte LDS entry per lane and slab");
+  constexpr uint32_t kNotIn = 0xffffffffu;
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (in[u]) atomicAdd(&sh.hist[key[u] >> 12], 1u);
+  for (int sl = 0; sl < kSampleSlabs; ++sl) {
+    score_slab(sl, kd, ok, key, in, tok);
+    next_slab(sl);
+    s_sample[sl][tid] = make_uint4(in[0] ? key[0] : kNotIn, in[1] ? key[1] : kNotIn,
+                                   in[2] ? key[2] : kNotIn, in[3] ? key[3] : kNotIn);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (in[u]) atomicAdd(&sh.hist[key[u] >> 12], 1u);
+  }
   __syncthreads();
   uint32_t th = 0;
   {
@@ -215,15 +229,25 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
     block_incl_scan<NT>(cnt, sh.wave_tot, &n_s);
     const float expect = (float)top_k * (float)n_s / (float)r.n;
     const int target = (int)(2.f * expect + 3.f * sqrtf(expect) + 8.f);
-    if (n_s >= 256 && target < n_s) {  // short first slabs (row edges) keep everything
+    if (n_s >= 256 && target < n_s) {  // short samples (row edges) keep everything
       find_bin<NT>(sh, target);
       th = (uint32_t)sh.found_bin;
     }
   }
+  int fill = 0;
 #pragma unroll
-  for (int u = 0; u < U; ++u) keep[u] = in[u] && (key[u] >> 12) >= th;
-  int fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, 0);
-  for (int slab = 1; slab < kSlabs; ++slab) {
+  for (int sl = 0; sl < kSampleSlabs; ++sl) {
+    const int blk0 = c * kFBlocks + sl * NW * U + wave * U;
+    const uint4 pk = s_sample[sl][tid];
+    key[0] = pk.x; key[1] = pk.y; key[2] = pk.z; key[3] = pk.w;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      tok[u] = ((blk0 + u) << 6) + lane;
+      keep[u] = key[u] != kNotIn && (key[u] >> 12) >= th;
+    }
+    fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, fill);
+  }
+  for (int slab = kSampleSlabs; slab < kSlabs; ++slab) {
     score_slab(slab, kd, ok, key, in, tok);
     next_slab(slab);
 #pragma unroll
@@ -314,18 +338,24 @@ __device__ __forceinline__ bool select_row_registers(TopkShared<NT>& sh, const F
   }
   if (over) return false;
   const int kfirst = spec ? kRegSpec : 0;
+  // Wave-local candidate j = k * 64 + lane belongs to the last chunk whose offset is <= j.
+  // The offsets rise with the chunk number, so a wave-uniform cursor walks forward with k and
+  // only the chunk boundaries that fall inside the current 64 candidates are compared per lane.
+  const int nchu = __builtin_amdgcn_readfirstlane(nch);
+  int cur = 0;
 #pragma unroll
   for (int k = 0; k < kRegPer; ++k) {
     if (k * 64 >= wtot) break;
+    if (k < kfirst) continue;
+    while (cur + 1 < nchu && __builtin_amdgcn_readlane(ex, cur + 1) <= k * 64) ++cur;
     const int j = k * 64 + lane;
-    if (k >= kfirst && j < wtot) {
-      int ci = 0, off = 0;
-      for (int t = 1; t < nch; ++t) {  // chunk of wave-local candidate j
-        const int o = __builtin_amdgcn_readlane(ex, t);
-        if (j >= o) { ci = t; off = o; }
-      }
-      e[k] = cw[ci * (int64_t)kFChunk + (j - off)];
+    int ci = cur, off = __builtin_amdgcn_readlane(ex, cur);
+    for (int t = cur + 1; t < nchu; ++t) {
+      const int o = __builtin_amdgcn_readlane(ex, t);
+      if (o > k * 64 + 63) break;
+      if (j >= o) { ci = t; off = o; }
     }
+    if (j < wtot) e[k] = cw[ci * (int64_t)kFChunk + (j - off)];
   }
   const uint32_t base = thmax << 12;
 #pragma unroll

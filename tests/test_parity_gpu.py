@@ -384,9 +384,9 @@ def test_fused_index_topk_many_chunks_ragged():
 
 def test_fused_index_topk_top_far_above_thresholds():
     """The top of each row lies far above every chunk's threshold (blocks of maximal keys
-    outside the chunks' first 1024 tokens, hundreds of coarse bins above the bulk), so the
-    K-th largest falls beyond the final pass's fine histogram; 2560 tied maximal keys also
-    make the tie order decide which 2048 are kept."""
+    outside the chunks' first 4096 tokens, the sample that sets a chunk's threshold, hundreds
+    of coarse bins above the bulk), so the K-th largest falls beyond the final pass's fine
+    histogram; 2560 tied maximal keys also make the tie order decide which 2048 are kept."""
     w = W(batch=2, seq_len=131072, q_len=1, top_k=2048)
     _banner("fused index+topk, top far above the chunk thresholds")
     inp = make_inputs(w, seed=13, device="cpu")
@@ -395,9 +395,9 @@ def test_fused_index_topk_top_far_above_thresholds():
     k.copy_(torch.randint(-127, 128, k.shape, generator=torch.Generator().manual_seed(3)).to(torch.int8))
     table = inp.page_table
     for b in range(w.batch):
-        for c in range(8):              # 5 blocks in each of chunks 2, 4, .., 16, past the first slab
+        for c in range(8):              # 5 blocks in each of chunks 2, 4, .., 16, past the sample
             for j in range(5):
-                k[table[b, 128 * (2 * c + 1) + 20 + 17 * j]] = 127
+                k[table[b, 128 * (2 * c + 1) + 64 + 13 * j]] = 127
     inp = inp.to(DEV)
     fused = run_gpu(inp, fused=True)
     two = run_gpu(inp)
