@@ -14,7 +14,8 @@ What it computes follows the page "å›½äº§AIèŠ¯ç‰‡å®Œæˆå‰æ²¿å¤§æ¨¡å‹Day-0é€‚é…
   Â§2.3  prefill and decode run the same selection + gather + attention, with different
         parallel shapes;
   Â§2.4  vision tokens form a sequence prefix that is always attended in full and never
-        enters the sparse screening.
+        enters the sparse screening; a KV dynamic allocator hands out and takes back cache
+        blocks with an independent block map per layer and head.
 Dense causal attention is the special case where every causal key is selected.
 
 Everything is numpy in float64 (integers in int64). Parity status of each function is
@@ -28,6 +29,8 @@ from .dsa import (  # noqa: F401
     forced_keys,
     page_rows,
     append_rows,
+    allocate_blocks,
+    release_blocks,
     index_scores,
     topk_select,
     index_list,

@@ -6,6 +6,8 @@ the benchmark's CPU-baseline leg may use it.
 [DSA-page] = "国产AI芯片完成前沿大模型Day-0适配:稀疏注意力与混合精度推理全解析" (ruibaoantu.com).
 [MTT-page] = "…在摩尔线程MTT S5000上的原生推理优化实践" (blog.csdn.net): §2.3 describes a hybrid of
 global sparse and local sliding-window attention.
+[DSA-page] §2.4 also describes the KV dynamic allocator (per-layer, per-head block maps),
+modelled by allocate_blocks / release_blocks.
 
 Readings taken where the page leaves a step open (each is also listed with its reason in
 the design notes):
@@ -28,7 +30,9 @@ probabilities), scipy's logsumexp, and a full-matrix masked softmax for the dens
 page_rows against an unpaged copy under a random page permutation; append_rows against
 page_rows (round trip) and an unpaged array write, untouched rows kept; hybrid_index_list
 against a brute-force full sort with the window and prefix marked, index_list at window 0, and
-every key at window >= pos + 1. No function is "parity unpinned".
+every key at window >= pos + 1; allocate_blocks against a one-block-at-a-time first-fit
+scan, the shortfall and bad-length cases leaving the map unchanged, and release_blocks
+restoring the map after an allocation. No function is "parity unpinned".
 """
 import numpy as np
 
@@ -84,6 +88,58 @@ def append_rows(pool, page_table_row, page_size: int, head: int, t, rows) -> Non
     phys = table[t // page_size]
     ok = phys >= 0
     pool[phys[ok], head, (t % page_size)[ok]] = np.asarray(rows)[ok]
+
+
+def allocate_blocks(in_use, table, old_lens, new_lens, page_size: int):
+    """[DSA-page] §2.4: a KV dynamic allocator hands out and takes back cache blocks, with an
+    independent block map per layer and head so that heads never write into each other's
+    blocks. This is one such map: `in_use` (bool [num_pages]) marks the blocks taken and
+    `table` (int [batch][max_pages]) is the block table of the sequences that use the map.
+
+    A sequence growing from old_lens[b] to new_lens[b] tokens needs its logical blocks
+    ceil(old / page_size) .. ceil(new / page_size) - 1. Reading taken where the page leaves
+    the order open: the needs are served in (sequence, logical block) order by the free
+    blocks in ascending block number (first fit). All or nothing: when fewer blocks are
+    free than needed, nothing changes and the status is the shortfall; a negative length or
+    a need beyond max_pages also changes nothing (status -1). Returns (in_use, table,
+    status) as new arrays; status 0 on success.
+    """
+    in_use = np.array(in_use, dtype=bool)
+    table = np.array(table, dtype=np.int64)
+    max_pages = table.shape[1]
+    needs = []
+    for b, (old, new) in enumerate(zip(old_lens, new_lens)):
+        old, new = int(old), int(new)
+        last = -(-new // page_size)
+        if old < 0 or new < 0 or last > max_pages:
+            return in_use, table, -1
+        needs += [(b, lp) for lp in range(-(-old // page_size), last)]
+    free = np.flatnonzero(~in_use)
+    if free.size < len(needs):
+        return in_use, table, len(needs) - int(free.size)
+    for (b, lp), page in zip(needs, free):
+        table[b, lp] = page
+        in_use[page] = True
+    return in_use, table, 0
+
+
+def release_blocks(in_use, table, seq_lens, release, page_size: int):
+    """[DSA-page] §2.4, the other half of the allocator: the blocks of every sequence b with
+    release[b] != 0 (its logical blocks 0 .. ceil(seq_lens[b] / page_size) - 1, at most
+    max_pages) go back to the map and their table entries become -1. An entry outside
+    [0, num_pages) frees nothing. Returns (in_use, table) as new arrays."""
+    in_use = np.array(in_use, dtype=bool)
+    table = np.array(table, dtype=np.int64)
+    max_pages = table.shape[1]
+    for b, (n, rel) in enumerate(zip(seq_lens, release)):
+        if not rel:
+            continue
+        for lp in range(min(max(-(-int(n) // page_size), 0), max_pages)):
+            page = table[b, lp]
+            if 0 <= page < in_use.size:
+                in_use[page] = False
+            table[b, lp] = -1
+    return in_use, table
 
 
 def index_scores(q_idx_vec, k_rows) -> np.ndarray:

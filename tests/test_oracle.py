@@ -339,3 +339,94 @@ def test_golden_hand_example():
         assert abs(o[0, 0] - eval(case["o0"], env)) < 1e-12, case["pos"]
         assert abs(o[0, 1] - eval(case["o1"], env)) < 1e-12, case["pos"]
         assert abs(lse[0] - eval(case["lse"], env)) < 1e-12, case["pos"]
+
+
+# ----------------------------------------------------------------- KV block allocator pins
+
+def _first_fit_one_at_a_time(in_use, table, old_lens, new_lens, page_size):
+    """Independent restatement: walk the sequences, and for each missing logical block scan
+    the map from block 0 for the first free block (no precomputed free list)."""
+    in_use = [bool(x) for x in in_use]
+    table = [list(map(int, row)) for row in table]
+    max_pages = len(table[0])
+    wanted = []
+    for b in range(len(old_lens)):
+        if old_lens[b] < 0 or new_lens[b] < 0 or (new_lens[b] + page_size - 1) // page_size > max_pages:
+            return in_use, table, -1
+        lo = (old_lens[b] + page_size - 1) // page_size
+        hi = (new_lens[b] + page_size - 1) // page_size
+        wanted += [(b, lp) for lp in range(lo, hi)]
+    if sum(not x for x in in_use) < len(wanted):
+        return in_use, table, len(wanted) - sum(not x for x in in_use)
+    for b, lp in wanted:
+        page = 0
+        while in_use[page]:
+            page += 1
+        in_use[page] = True
+        table[b][lp] = page
+    return in_use, table, 0
+
+
+def test_allocate_blocks_hand_example():
+    """[DSA-page] §2.4 allocator, worked by hand: blocks 0, 2, 5 taken, 4-token blocks.
+    Sequence 0 grows 3 -> 9 tokens (needs logical blocks 1, 2), sequence 1 grows 0 -> 5
+    (blocks 0, 1); the free blocks 1, 3, 4, 6 go to them in that order."""
+    in_use = np.array([1, 0, 1, 0, 0, 1, 0, 0], dtype=bool)
+    table = np.full((2, 4), -1)
+    table[0, 0] = 0
+    u, t, st = oracle.allocate_blocks(in_use, table, [3, 0], [9, 5], 4)
+    assert st == 0
+    assert t.tolist() == [[0, 1, 3, -1], [4, 6, -1, -1]]
+    assert u.tolist() == [True] * 7 + [False]
+    # one block short: nothing changes, the status is the shortfall
+    u2, t2, st2 = oracle.allocate_blocks(np.array([1, 0, 1, 1, 0, 1, 1, 0], bool), table, [3, 0], [9, 5], 4)
+    assert st2 == 1 and t2.tolist() == table.tolist() and u2.sum() == 5
+    # a length beyond the table, or a negative one: status -1, nothing changes
+    for old, new in (([3, 0], [9, 17]), ([-1, 0], [9, 5]), ([3, 0], [9, -2])):
+        u3, t3, st3 = oracle.allocate_blocks(in_use, table, old, new, 4)
+        assert st3 == -1 and t3.tolist() == table.tolist() and u3.tolist() == in_use.tolist()
+    # a shrinking or unchanged sequence needs nothing
+    u4, t4, st4 = oracle.allocate_blocks(in_use, table, [9, 5], [4, 5], 4)
+    assert st4 == 0 and t4.tolist() == table.tolist() and u4.tolist() == in_use.tolist()
+
+
+def test_allocate_blocks_matches_one_at_a_time_first_fit():
+    rng = np.random.default_rng(21)
+    for trial in range(200):
+        n_pages = int(rng.integers(1, 90))
+        in_use = rng.random(n_pages) < rng.random()
+        B = int(rng.integers(1, 6))
+        ps = int(rng.choice([1, 2, 4, 8]))
+        max_pages = int(rng.integers(1, 8))
+        table = rng.integers(-1, n_pages, (B, max_pages))
+        old = rng.integers(-1 if trial % 17 == 0 else 0, max_pages * ps + 1, B)
+        new = old + rng.integers(-2, 2 * ps + 3, B)
+        got = oracle.allocate_blocks(in_use, table, old, new, ps)
+        want = _first_fit_one_at_a_time(in_use, table, old.tolist(), new.tolist(), ps)
+        assert got[2] == want[2]
+        assert got[0].tolist() == want[0] and got[1].tolist() == want[1]
+
+
+def test_release_blocks_undoes_allocation():
+    rng = np.random.default_rng(22)
+    for trial in range(50):
+        n_pages, B, ps, max_pages = 200, 4, 8, 6
+        in_use = rng.random(n_pages) < 0.5
+        table = np.full((B, max_pages), -1)
+        new = rng.integers(0, max_pages * ps + 1, B)
+        u, t, st = oracle.allocate_blocks(in_use, table, np.zeros(B, int), new, ps)
+        assert st == 0
+        taken = t[t >= 0]
+        assert len(set(taken.tolist())) == taken.size          # distinct blocks
+        assert not in_use[taken].any()                          # all were free before
+        assert u.sum() == in_use.sum() + taken.size
+        rel = rng.integers(0, 2, B)
+        u2, t2 = oracle.release_blocks(u, t, new, rel, ps)
+        for b in range(B):
+            n = -(-int(new[b]) // ps)
+            if rel[b]:
+                assert (t2[b] == -1).all() and not u2[t[b, :n]].any()
+            else:
+                assert t2[b].tolist() == t[b].tolist() and u2[t[b, :n]].all()
+        u3, t3 = oracle.release_blocks(u, t, new, np.ones(B, int), ps)
+        assert u3.tolist() == in_use.tolist() and (t3 == -1).all()
