@@ -28,8 +28,8 @@ EXPORTS = ["sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_
            "sparse_attn_index_topk_workspace_size", "sparse_attn_index_topk",
            "sparse_attn_index_topk_window_workspace_size", "sparse_attn_index_topk_window",
            "sparse_attn_fwd_prefill", "sparse_attn_prefill_masked_workspace_size",
-           "sparse_attn_fwd_prefill_masked", "sparse_attn_kv_append",
-           "sparse_attn_decode_workspace_size", "sparse_attn_fwd_decode"]
+           "sparse_attn_fwd_prefill_masked", "sparse_attn_kv_append", "sparse_attn_kv_alloc",
+           "sparse_attn_kv_release", "sparse_attn_decode_workspace_size", "sparse_attn_fwd_decode"]
 
 
 class SparseAttnError(RuntimeError):
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sparse_attn_prefill_masked_workspace_size": (SZ, [KV, I32]),
         "sparse_attn_fwd_prefill_masked": (I32, [KV, P, I32, I32, I32, P, I32, F32, P, SZ, P, P, P]),
         "sparse_attn_kv_append": (I32, [KV, P, P, P, I32, P]),
+        "sparse_attn_kv_alloc": (I32, [I32, I32, P, I32, I32, I32, P, P, P, P, P]),
+        "sparse_attn_kv_release": (I32, [I32, I32, P, I32, I32, I32, P, P, P, P]),
         "sparse_attn_decode_workspace_size": (SZ, [KV, I32, I32, I32]),
         "sparse_attn_fwd_decode": (I32, [KV, P, I32, P, I32, F32, I32, P, SZ, P, P, P]),
     }
@@ -246,6 +248,44 @@ def kv_append(kv: PagedKV, k_new=None, v_new=None, kidx_new=None, stream=None):
     sparse_attn_kv_append(kv, None if k_new is None else k_new.contiguous(),
                           None if v_new is None else v_new.contiguous(),
                           None if kidx_new is None else kidx_new.contiguous(), n_new, stream)
+
+
+def sparse_attn_kv_alloc(num_maps, num_pages, block_maps, batch, page_size, max_pages_per_seq,
+                         old_lens, new_lens, page_tables, status, stream=None):
+    lib = load()
+    _check("sparse_attn_kv_alloc", lib.sparse_attn_kv_alloc(
+        num_maps, num_pages, _ptr(block_maps, torch.int32, "block_maps"), batch, page_size,
+        max_pages_per_seq, _ptr(old_lens, torch.int32, "old_lens"),
+        _ptr(new_lens, torch.int32, "new_lens"), _ptr(page_tables, torch.int32, "page_tables"),
+        _ptr(status, torch.int32, "status"), _stream(stream)))
+
+
+def sparse_attn_kv_release(num_maps, num_pages, block_maps, batch, page_size, max_pages_per_seq,
+                           seq_lens, release, page_tables, stream=None):
+    lib = load()
+    _check("sparse_attn_kv_release", lib.sparse_attn_kv_release(
+        num_maps, num_pages, _ptr(block_maps, torch.int32, "block_maps"), batch, page_size,
+        max_pages_per_seq, _ptr(seq_lens, torch.int32, "seq_lens"),
+        _ptr(release, torch.int32, "release"), _ptr(page_tables, torch.int32, "page_tables"),
+        _stream(stream)))
+
+
+def kv_alloc(block_maps, page_tables, old_lens, new_lens, page_size, num_pages, stream=None):
+    """Grow the caches of every (layer, head) map: block_maps int32 [M][ceil(num_pages/32)]
+    (the uint32 bit words, held as int32), page_tables int32 [M][B][max_pages], lengths int32
+    [B]. Returns the int32 [M] status (0, the shortfall, or -1; see sparse_attn_kv_alloc)."""
+    M, B, max_pages = page_tables.shape
+    status = torch.empty(M, dtype=torch.int32, device=page_tables.device)
+    sparse_attn_kv_alloc(M, num_pages, block_maps, B, page_size, max_pages, old_lens, new_lens,
+                         page_tables, status, stream)
+    return status
+
+
+def kv_release(block_maps, page_tables, seq_lens, release, page_size, num_pages, stream=None):
+    """Return the blocks of the sequences flagged in release (int32 [B]) to every map."""
+    M, B, max_pages = page_tables.shape
+    sparse_attn_kv_release(M, num_pages, block_maps, B, page_size, max_pages, seq_lens, release,
+                           page_tables, stream)
 
 
 def sparse_attn_decode_workspace_size(kv: PagedKV, num_q_heads, index_width, num_splits=0) -> int:

@@ -313,6 +313,49 @@ int32_t sparse_attn_kv_append(const sa_paged_kv* kv, const uint16_t* k_new, cons
                                          static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+int32_t check_block_maps(int32_t num_maps, int32_t num_pages, int32_t batch, int32_t page_size,
+                         int32_t max_pages_per_seq) {
+  if (num_maps < 1 || num_maps > 65535 || num_pages < 1 || batch < 1 ||
+      batch > sa::kAllocMaxBatch || page_size < 1 || max_pages_per_seq < 1)
+    return SA_ERR_SHAPE;
+  if ((int64_t)batch * max_pages_per_seq > INT32_MAX) return SA_ERR_SHAPE;
+  return SA_OK;
+}
+
+}  // namespace
+
+int32_t sparse_attn_kv_alloc(int32_t num_maps, int32_t num_pages, uint32_t* block_maps,
+                             int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                             const int32_t* old_lens, const int32_t* new_lens,
+                             int32_t* page_tables, int32_t* status, void* stream) {
+  if (!block_maps || !old_lens || !new_lens || !page_tables || !status) return SA_ERR_NULL;
+  const int32_t st = check_block_maps(num_maps, num_pages, batch, page_size, max_pages_per_seq);
+  if (st != SA_OK) return st;
+  if (!aligned16(block_maps) || !aligned16(old_lens) || !aligned16(new_lens) ||
+      !aligned16(page_tables) || !aligned16(status))
+    return SA_ERR_ALIGN;
+  return hip_status(sa::launch_kv_alloc(num_maps, num_pages, block_maps, batch, page_size,
+                                        max_pages_per_seq, old_lens, new_lens, page_tables, status,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int32_t sparse_attn_kv_release(int32_t num_maps, int32_t num_pages, uint32_t* block_maps,
+                               int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                               const int32_t* seq_lens, const int32_t* release,
+                               int32_t* page_tables, void* stream) {
+  if (!block_maps || !seq_lens || !release || !page_tables) return SA_ERR_NULL;
+  const int32_t st = check_block_maps(num_maps, num_pages, batch, page_size, max_pages_per_seq);
+  if (st != SA_OK) return st;
+  if (!aligned16(block_maps) || !aligned16(seq_lens) || !aligned16(release) ||
+      !aligned16(page_tables))
+    return SA_ERR_ALIGN;
+  return hip_status(sa::launch_kv_release(num_maps, num_pages, block_maps, batch, page_size,
+                                          max_pages_per_seq, seq_lens, release, page_tables,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 size_t sparse_attn_decode_workspace_size(const sa_paged_kv* kv, int32_t num_q_heads,
                                          int32_t index_width, int32_t num_splits) {
   sa::KvView v;

@@ -160,6 +160,15 @@ hipError_t launch_window_finish(const KvView& kv, const int32_t* short_lens, int
 // KV-cache append: new tokens' rows written into the paged pools.
 hipError_t launch_kv_append(const KvView& kv, const uint16_t* k_new, const uint16_t* v_new,
                             const int8_t* kidx_new, int n_new, hipStream_t stream);
+// KV-cache block allocator: per-(layer, head) block maps, allocation and release.
+constexpr int kAllocMaxBatch = 8192;  // sequences per allocation call (offsets held in LDS)
+int map_words(int num_pages);
+hipError_t launch_kv_alloc(int num_maps, int num_pages, uint32_t* maps, int batch, int page_size,
+                           int max_pages, const int32_t* old_lens, const int32_t* new_lens,
+                           int32_t* tables, int32_t* status, hipStream_t stream);
+hipError_t launch_kv_release(int num_maps, int num_pages, uint32_t* maps, int batch, int page_size,
+                             int max_pages, const int32_t* seq_lens, const int32_t* release,
+                             int32_t* tables, hipStream_t stream);
 // Masked-dense sparse prefill: selection masks built from index lists in the workspace, then
 // the dense kernel with every unselected score set to -inf.
 int sel_query_blocks(int q_len);

@@ -249,6 +249,43 @@ int32_t sparse_attn_kv_append(const sa_paged_kv* kv, const uint16_t* k_new, cons
                               const int8_t* kidx_new, int32_t n_new, void* stream);
 
 /*
+ * KV-cache block allocator ([DSA-page] §2.4: a KV dynamic allocator hands out and takes back
+ * cache blocks; in sparse mode it tracks layer and head and keeps an independent block map
+ * per head, so that heads never write into each other's blocks). One call serves num_maps
+ * independent maps, e.g. one per (layer, KV head), or one per layer when the heads of a
+ * layer share pages as in sa_paged_kv.
+ *   block_maps   uint32 [num_maps][ceil(num_pages / 32)]: bit p % 32 of word p / 32 set means
+ *                block p of that map is taken; bits at or past num_pages are never touched
+ *   page_tables  int32 [num_maps][batch][max_pages_per_seq]: each map's block tables
+ *
+ * sparse_attn_kv_alloc grows sequence b from old_lens[b] to new_lens[b] tokens: it needs the
+ * logical blocks ceil(old / page_size) .. ceil(new / page_size) - 1 (none when new <= old).
+ * Per map, the needs are served in (sequence, logical block) order by the free blocks in
+ * ascending block number (first fit, so the result is deterministic); the blocks are marked
+ * taken and written into the table. All or nothing per map: status[m] (int32 [num_maps]) is
+ * 0 on success, the number of blocks missing when too few are free, or -1 when a length is
+ * negative or needs more than max_pages_per_seq blocks; in the last two cases the map and
+ * its table are left unchanged. Table entries other than the allocated ones are not written.
+ *
+ * sparse_attn_kv_release returns the blocks of every sequence b with release[b] != 0 (int32
+ * [batch]): its logical blocks 0 .. ceil(seq_lens[b] / page_size) - 1 (at most
+ * max_pages_per_seq) are cleared in the map and their table entries set to -1; an entry
+ * outside [0, num_pages) clears nothing. A block must belong to one sequence only.
+ *
+ * 1 <= num_maps <= 65535, 1 <= batch <= 8192, page_size >= 1, max_pages_per_seq >= 1 and
+ * batch * max_pages_per_seq < 2^31 (SA_ERR_SHAPE otherwise). Lengths and flags are device
+ * arrays; maps and tables are updated in place on the stream.
+ */
+int32_t sparse_attn_kv_alloc(int32_t num_maps, int32_t num_pages, uint32_t* block_maps,
+                             int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                             const int32_t* old_lens, const int32_t* new_lens,
+                             int32_t* page_tables, int32_t* status, void* stream);
+int32_t sparse_attn_kv_release(int32_t num_maps, int32_t num_pages, uint32_t* block_maps,
+                               int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                               const int32_t* seq_lens, const int32_t* release,
+                               int32_t* page_tables, void* stream);
+
+/*
  * Decode attention ([DSA-page] §2.3, decode): one query token per sequence (pos =
  * seq_lens[b] - 1) attends to its index list. Each (b, KV group) list is cut into
  * num_splits chunks processed in parallel; partial softmax states (max, sum, weighted V in

@@ -186,6 +186,53 @@ def test_kv_append_validation(lib, case, code):
     assert call_append(lib, d, **case) == code
 
 
+def call_alloc(lib, maps=8, pages=1000, bm=A, batch=4, ps=64, mp=16, old=A + 0x100, new=A + 0x200,
+               tab=A + 0x300, st=A + 0x400):
+    return lib.sparse_attn_kv_alloc(maps, pages, bm, batch, ps, mp, old, new, tab, st, None)
+
+
+def call_release(lib, maps=8, pages=1000, bm=A, batch=4, ps=64, mp=16, lens=A + 0x100, rel=A + 0x200,
+                 tab=A + 0x300):
+    return lib.sparse_attn_kv_release(maps, pages, bm, batch, ps, mp, lens, rel, tab, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(bm=None), fa.SA_ERR_NULL),
+    (dict(old=None), fa.SA_ERR_NULL),
+    (dict(new=None), fa.SA_ERR_NULL),
+    (dict(tab=None), fa.SA_ERR_NULL),
+    (dict(st=None), fa.SA_ERR_NULL),
+    (dict(maps=0), fa.SA_ERR_SHAPE),
+    (dict(maps=65536), fa.SA_ERR_SHAPE),
+    (dict(pages=0), fa.SA_ERR_SHAPE),
+    (dict(batch=0), fa.SA_ERR_SHAPE),
+    (dict(batch=8193), fa.SA_ERR_SHAPE),
+    (dict(ps=0), fa.SA_ERR_SHAPE),
+    (dict(mp=0), fa.SA_ERR_SHAPE),
+    (dict(batch=8192, mp=1 << 18), fa.SA_ERR_SHAPE),     # batch * max_pages reaches 2^31
+    (dict(bm=A + 4), fa.SA_ERR_ALIGN),
+    (dict(tab=A + 0x308), fa.SA_ERR_ALIGN),
+    (dict(st=A + 0x404), fa.SA_ERR_ALIGN),
+])
+def test_kv_alloc_validation(lib, case, code):
+    assert call_alloc(lib, **case) == code
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(bm=None), fa.SA_ERR_NULL),
+    (dict(lens=None), fa.SA_ERR_NULL),
+    (dict(rel=None), fa.SA_ERR_NULL),
+    (dict(tab=None), fa.SA_ERR_NULL),
+    (dict(maps=0), fa.SA_ERR_SHAPE),
+    (dict(pages=-5), fa.SA_ERR_SHAPE),
+    (dict(batch=9000), fa.SA_ERR_SHAPE),
+    (dict(mp=-1), fa.SA_ERR_SHAPE),
+    (dict(rel=A + 0x204), fa.SA_ERR_ALIGN),
+])
+def test_kv_release_validation(lib, case, code):
+    assert call_release(lib, **case) == code
+
+
 def call_decode(lib, d, q=A, hq=32, idx=A, width=2048, splits=4, ws=A, ws_bytes=1 << 30, out=A, lse=None,
                 scale=0.1):
     return lib.sparse_attn_fwd_decode(ctypes.byref(d), q, hq, idx, width, scale, splits, ws, ws_bytes,
