@@ -179,6 +179,53 @@ def bench_prefill(fa, reps):
             "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS, "flop": flops}
 
 
+def bench_tiny(fa, reps=50, warmup=10):
+    """The tiny sparse prefill (B=1, 4/1 heads, S=T=512, d=64, d_idx=32, top-K=64, causal):
+    latency per call of the selection (sparse_attn_index_topk) and of the attention over the
+    lists, on gathered rows (sparse_attn_fwd_prefill) and on masked dense tiles
+    (sparse_attn_fwd_prefill_masked); median, p10 and p90 over reps, events around each call."""
+    import torch
+
+    from synthetic import CONFIGS, make_inputs
+    w = CONFIGS["tiny_sparse_prefill"]
+    inp = make_inputs(w, seed=1, device="cuda")
+    kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
+                    page_table=inp.page_table, seq_lens=inp.seq_lens, max_seq_len=w.seq_len,
+                    prefix_len=w.prefix_len)
+    S, Hkv, Hq = w.q_len, w.num_kv_heads, w.num_q_heads
+    idx = torch.empty((1, S, Hkv, w.index_width), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(inp.q)
+    lse = torch.empty((1, S, Hq), dtype=torch.float32, device="cuda")
+    fu_n = fa.sparse_attn_index_topk_workspace_size(kv, S, w.top_k)
+    fu_ws = torch.empty(max(fu_n, 16), dtype=torch.uint8, device="cuda")
+    mk_n = fa.sparse_attn_prefill_masked_workspace_size(kv, S)
+    mk_ws = torch.empty(max(mk_n, 16), dtype=torch.uint8, device="cuda")
+    scale = 1 / math.sqrt(w.head_dim)
+    calls = {
+        "select": lambda: fa.sparse_attn_index_topk(kv, inp.q_idx, S, S, w.top_k, idx, fu_ws, fu_n),
+        "attention_gathered": lambda: fa.sparse_attn_fwd_prefill(
+            kv, inp.q, Hq, S, S, idx, w.index_width, scale, out, lse),
+        "attention_masked": lambda: fa.sparse_attn_fwd_prefill_masked(
+            kv, inp.q, Hq, S, S, idx, w.index_width, scale, mk_ws, mk_n, out, lse),
+    }
+    res = {"workload": w.name, "unit": "us per call"}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        res[name] = {"p10": t[int(0.1 * (reps - 1))], "p50": t[(reps - 1) // 2], "p90": t[int(0.9 * (reps - 1))]}
+    del inp, kv, idx, out, lse, fu_ws, mk_ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_sparse_prefill(fa, reps, q_chunk=2048):
     """Whole sparse prefill of 32K tokens (B=1, 32/8 heads, d=128, d_idx=64, top-K=2048): per
     chunk of q_chunk queries, the fused selection (sparse_attn_index_topk: indexer keys ->
@@ -464,6 +511,7 @@ def main():
         del inp, evict_buf
         torch.cuda.empty_cache()
         result["sparse_prefill"] = bench_sparse_prefill(fa, reps=2)
+        result["tiny_sparse_prefill"] = bench_tiny(fa)
         result["decode_1m_prefix"] = bench_decode_1m(fa, steps=10, warmup=3)
         # the 128K step with one indexer key shared by all KV groups (a stride-0 indexer head)
         result["decode_128k_shared_indexer"] = bench_decode_1m(
