@@ -267,6 +267,10 @@ DECODE = {
                          dict(idx_values=(-1, 0, 1))),
     "decode_long_shared_indexer": (W(batch=2, num_q_heads=8, seq_len=24576, q_len=1, top_k=2048,
                                      idx_dim=32), dict(num_idx_heads=1)),
+    # the fused selection at d_idx = 128 (two waves per SIMD in its main pass), ragged rows
+    "decode_long_didx128": (W(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, idx_dim=128,
+                              seq_len=45000, q_len=1, top_k=1000, prefix_len=5),
+                            dict(seq_lens=[45000, 17000, 30001])),
 }
 
 
@@ -282,7 +286,8 @@ def test_decode_every_row(name, splits):
 
 
 @pytest.mark.parametrize("name", ["decode_long_ragged_prefix", "decode_long_ties",
-                                  "decode_long_shared_indexer", "decode_ragged_prefix"])
+                                  "decode_long_shared_indexer", "decode_long_didx128",
+                                  "decode_ragged_prefix"])
 def test_fused_index_topk_matches(name):
     """The fused indexer + top-K gives the oracle's lists, identical to the two-step path."""
     w, kw = DECODE[name]
