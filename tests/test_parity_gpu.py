@@ -645,3 +645,39 @@ def test_full_sparse_decode_1m_prefix():
     # every list starts with the forced prefix 0..195
     idx = gpu.indices[:, 0].cpu().numpy()
     assert np.all(idx[..., :196] == np.arange(196))
+
+
+def test_full_sparse_decode_128k_window():
+    """The 128K decode step with hybrid lists as the benchmark runs it (the last 512 keys forced
+    beside the top-2048; fused selection at window-shortened positions, then split-K decode):
+    sampled rows' lists bit-exact against the oracle, their attention within the bar."""
+    w = CONFIGS["sparse_decode_128k"]
+    win = 512
+    _banner(f"full {w.name}, hybrid lists window={win}")
+    inp = make_inputs(w, seed=3, device=DEV)
+    kv = make_kv(inp)
+    width = w.prefix_len + w.top_k + win
+    lists = fa.index_topk_window(kv, inp.q_idx, 1, 1, w.top_k, win)
+    o, lse = fa.decode(kv, inp.q[:, 0].contiguous(), lists[:, 0].contiguous())
+    torch.cuda.synchronize()
+    ov = OracleView(inp, host_copy=False)
+    got = lists.cpu().numpy()
+    G, scale = w.group, 1.0 / math.sqrt(w.head_dim)
+    errs, lerrs = [], []
+    for b in range(w.batch):
+        for g in ((b % 8), (b + 5) % 8):
+            pos = oracle.query_position(inp.seq_lens_host[b], 1, 0)
+            qi = inp.q_idx[b, 0, g].cpu().numpy()
+            fn = lambda t: oracle.index_scores(qi, oracle.page_rows(ov.kidx, ov.table[b], w.page_size, g, t))
+            want = oracle.hybrid_index_list(pos, w.prefix_len, win, w.top_k, width, fn)
+            assert np.array_equal(got[b, 0, g], want), (b, g)
+            keys = want[want >= 0]
+            assert keys.size == w.top_k + win and keys[-1] == pos
+            kr = oracle.bf16_to_f64(oracle.page_rows(ov.k_pool, ov.table[b], w.page_size, g, keys))
+            vr = oracle.bf16_to_f64(oracle.page_rows(ov.v_pool, ov.table[b], w.page_size, g, keys))
+            qb = oracle.bf16_to_f64(bits(inp.q[b, 0, g * G:(g + 1) * G]))
+            o_ref, l_ref = oracle.attend(qb, kr, vr, scale)
+            errs.append(np.abs(f64(o[b, g * G:(g + 1) * G]) - o_ref).ravel())
+            lerrs.append(np.abs(lse[b, g * G:(g + 1) * G].double().cpu().numpy() - l_ref))
+    e = np.concatenate(errs)
+    assert_close((float(e.max()), float(e.mean()), float(np.concatenate(lerrs).max())))
