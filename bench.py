@@ -226,6 +226,79 @@ def bench_tiny(fa, reps=50, warmup=10):
     return res
 
 
+def bench_cache_maintenance(fa, reps=50, warmup=5):
+    """Cache upkeep on the 128K decode layout (B=8, 8 KV heads, d=128, d_idx=64, 64-token pages;
+    8K tokens cached, which does not change the cost): sparse_attn_kv_append of one decode
+    token per sequence and of 2048 tokens per sequence (K, V and indexer rows), and
+    sparse_attn_kv_alloc / sparse_attn_kv_release over 64 (layer, head) block maps of 300000
+    blocks each. Median, p10 and p90 per call over reps; events around each call."""
+    import numpy as np
+    import torch
+
+    from synthetic import CONFIGS, make_inputs
+    w = CONFIGS["sparse_decode_128k"].with_(seq_len=8192)
+    inp = make_inputs(w, seed=6, device="cuda", with_q=False)
+    kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
+                    page_table=inp.page_table, seq_lens=inp.seq_lens, max_seq_len=w.seq_len)
+    B, H, d, Hi, di = w.batch, w.num_kv_heads, w.head_dim, inp.num_idx_heads, w.idx_dim
+    g = torch.Generator(device="cuda").manual_seed(6)
+
+    def rows(n):
+        k = torch.randn((B, n, H, d), generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn((B, n, H, d), generator=g, device="cuda").to(torch.bfloat16)
+        ki = torch.randint(-127, 128, (B, n, Hi, di), generator=g, device="cuda").to(torch.int8)
+        return k, v, ki
+
+    def timed(fn, setup=None):
+        for _ in range(warmup):
+            if setup:
+                setup()
+            fn()
+        evs = []
+        for _ in range(reps):
+            if setup:
+                setup()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        t = sorted(x.elapsed_time(y) * 1e3 for x, y in evs)
+        return {"p10": t[int(0.1 * (reps - 1))], "p50": t[(reps - 1) // 2], "p90": t[int(0.9 * (reps - 1))]}
+
+    res = {"workload": "cache upkeep on the 128K decode layout", "unit": "us per call"}
+    k1, v1, i1 = rows(1)
+    res["append_1_token"] = timed(lambda: fa.sparse_attn_kv_append(kv, k1, v1, i1, 1))
+    n = 2048
+    kn, vn, inn = rows(n)
+    t = timed(lambda: fa.sparse_attn_kv_append(kv, kn, vn, inn, n))
+    moved = 2 * B * n * (H * 2 * d * 2 + Hi * di)  # rows read and written
+    res["append_2048_tokens"] = dict(t, hbm_gbps=moved / (t["p50"] * 1e-6) / 1e9, bytes=moved)
+    del inp, kv, kn, vn, inn
+    torch.cuda.empty_cache()
+
+    M, pages, mp = 64, 300000, 2048
+    words = -(-pages // 32)
+    rng = np.random.default_rng(6)
+    maps0 = torch.from_numpy(rng.integers(0, 2 ** 31, (M, words)).astype(np.int32)).cuda()
+    maps = torch.empty_like(maps0)
+    tables = torch.full((M, B, mp), -1, dtype=torch.int32, device="cuda")
+    status = torch.empty(M, dtype=torch.int32, device="cuda")
+    old = torch.full((B,), 64 * 1000, dtype=torch.int32, device="cuda")  # each crosses a block
+    new = old + 1
+    rel = torch.ones(B, dtype=torch.int32, device="cuda")
+    reset = lambda: maps.copy_(maps0)
+    res["alloc_64_maps_decode"] = timed(
+        lambda: fa.sparse_attn_kv_alloc(M, pages, maps, B, 64, mp, old, new, tables, status), reset)
+    res["release_64_maps"] = timed(
+        lambda: fa.sparse_attn_kv_release(M, pages, maps, B, 64, mp, new, rel, tables), reset)
+    torch.cuda.synchronize()
+    del maps0, maps, tables
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_sparse_prefill(fa, reps, q_chunk=2048):
     """Whole sparse prefill of 32K tokens (B=1, 32/8 heads, d=128, d_idx=64, top-K=2048): per
     chunk of q_chunk queries, the fused selection (sparse_attn_index_topk: indexer keys ->
@@ -512,6 +585,7 @@ def main():
         torch.cuda.empty_cache()
         result["sparse_prefill"] = bench_sparse_prefill(fa, reps=2)
         result["tiny_sparse_prefill"] = bench_tiny(fa)
+        result["cache_maintenance"] = bench_cache_maintenance(fa)
         result["decode_1m_prefix"] = bench_decode_1m(fa, steps=10, warmup=3)
         # the 128K step with one indexer key shared by all KV groups (a stride-0 indexer head)
         result["decode_128k_shared_indexer"] = bench_decode_1m(
