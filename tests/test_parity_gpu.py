@@ -267,6 +267,11 @@ DECODE = {
                          dict(idx_values=(-1, 0, 1))),
     "decode_long_shared_indexer": (W(batch=2, num_q_heads=8, seq_len=24576, q_len=1, top_k=2048,
                                      idx_dim=32), dict(num_idx_heads=1)),
+    # the first tokens of sequences (1 and 2 cached tokens, a page boundary at 64 / 65) beside a
+    # row long enough for the fused selection; the prefix covers the short rows entirely
+    "decode_first_tokens": (W(batch=5, num_q_heads=8, num_kv_heads=2, seq_len=20000, q_len=1,
+                              top_k=64, prefix_len=3),
+                            dict(seq_lens=[20000, 1, 2, 64, 65])),
     # the fused selection at d_idx = 128 (two waves per SIMD in its main pass), ragged rows
     "decode_long_didx128": (W(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, idx_dim=128,
                               seq_len=45000, q_len=1, top_k=1000, prefix_len=5),
@@ -287,6 +292,7 @@ def test_decode_every_row(name, splits):
 
 @pytest.mark.parametrize("name", ["decode_long_ragged_prefix", "decode_long_ties",
                                   "decode_long_shared_indexer", "decode_long_didx128",
+                                  "decode_first_tokens",
                                   "decode_ragged_prefix"])
 def test_fused_index_topk_matches(name):
     """The fused indexer + top-K gives the oracle's lists, identical to the two-step path."""
