@@ -272,6 +272,10 @@ DECODE = {
     "decode_first_tokens": (W(batch=5, num_q_heads=8, num_kv_heads=2, seq_len=20000, q_len=1,
                               top_k=64, prefix_len=3),
                             dict(seq_lens=[20000, 1, 2, 64, 65])),
+    # a large K: the fused final pass holds more candidates than its registers (general path),
+    # and a row with barely more candidates than K
+    "decode_large_k": (W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=40000, q_len=1,
+                         top_k=12000, prefix_len=1), dict(seq_lens=[40000, 12100])),
     # the fused selection at d_idx = 128 (two waves per SIMD in its main pass), ragged rows
     "decode_long_didx128": (W(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, idx_dim=128,
                               seq_len=45000, q_len=1, top_k=1000, prefix_len=5),
@@ -292,7 +296,7 @@ def test_decode_every_row(name, splits):
 
 @pytest.mark.parametrize("name", ["decode_long_ragged_prefix", "decode_long_ties",
                                   "decode_long_shared_indexer", "decode_long_didx128",
-                                  "decode_first_tokens",
+                                  "decode_first_tokens", "decode_large_k",
                                   "decode_ragged_prefix"])
 def test_fused_index_topk_matches(name):
     """The fused indexer + top-K gives the oracle's lists, identical to the two-step path."""
@@ -314,6 +318,9 @@ FUSED_PREFILL = {
                           dict(idx_values=(-1, 0, 1))),
     "prefill_long_random": (W(batch=2, seq_len=20000, q_len=40, top_k=1000, prefix_len=5),
                             dict(seq_lens=[20000, 9000])),
+    # K near the row length (more places than one wave's list holds, rows of 4000-6000
+    # candidates) and rows shorter than K at the block's start
+    "prefill_large_k": (W(seq_len=6000, q_len=3000, top_k=3000, prefix_len=4), {}),
 }
 
 
