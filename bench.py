@@ -46,6 +46,9 @@ def parse():
                     help="select with sparse_attn_index then sparse_attn_topk (score rows in HBM) "
                          "instead of the fused sparse_attn_index_topk")
     ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--sparse-prefill-only", action="store_true",
+                    help="run only the 32K sparse prefill measurement once and print its JSON "
+                         "(a short program for counter collection)")
     return ap.parse_args()
 
 
@@ -455,6 +458,9 @@ def main():
 
     fa.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sparse_prefill_only:
+        print(json.dumps({"sparse_prefill": bench_sparse_prefill(fa, reps=1)}), flush=True)
+        return
     w = CONFIGS["sparse_decode_128k"]
     inp = make_inputs(w, seed=args.seed, device="cuda")
     kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
