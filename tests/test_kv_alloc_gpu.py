@@ -129,3 +129,86 @@ def test_kv_alloc_then_release_decode_loop():
     lens2 = np.where(rel != 0, rng.integers(0, 300, B), lens1)
     old2 = np.where(rel != 0, 0, lens1)
     check_against_oracle(u3, t3, old2.tolist(), lens2.tolist(), ps)
+
+
+def _bf16(rng, shape):
+    t = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16)
+    return t, t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_decode_loop_allocate_append_select_attend():
+    """A decode loop over the cache upkeep and the hot path together ([DSA-page] §2.2-§2.4):
+    blocks allocated from a partly taken map, the prompt's rows appended, then three steps of
+    (allocate, append the new token, select, attend). Expected values come only from the
+    oracle: its allocation of the same requests, pools filled by its append from the host-side
+    token arrays, and its selection and attention over them."""
+    _banner("decode loop: alloc, append, select, attend")
+    rng = np.random.default_rng(31)
+    B, H, G, d, di, ps, mp, npages, P, K = 3, 2, 4, 64, 32, 64, 12, 40, 2, 64
+    Hq, steps = H * G, 3
+    lens = np.array([300, 130, 1])
+    tmax = int(lens.max()) + steps
+    k_tok, k_bits = _bf16(rng, (B, tmax, H, d))
+    v_tok, v_bits = _bf16(rng, (B, tmax, H, d))
+    i_tok = rng.integers(-127, 128, (B, tmax, H, di)).astype(np.int8)
+    q_step, q_bits = _bf16(rng, (steps, B, Hq, d))
+    qi_step = rng.integers(-127, 128, (steps, B, H, di)).astype(np.int8)
+
+    in_use = rng.random(npages) < 0.3
+    bm = torch.from_numpy(pack(in_use[None])).to(DEV)
+    tab = torch.full((1, B, mp), -1, dtype=torch.int32, device=DEV)
+    o_use, o_tab = in_use.copy(), np.full((B, mp), -1)
+    k_pool = torch.zeros((npages, H, ps, d), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.zeros_like(k_pool)
+    i_pool = torch.zeros((npages, H, ps, di), dtype=torch.int8, device=DEV)
+    ok_pool = np.zeros((npages, H, ps, d), np.uint16)
+    ov_pool = np.zeros_like(ok_pool)
+    oi_pool = np.zeros((npages, H, ps, di), np.int8)
+    seq_lens = torch.zeros(B, dtype=torch.int32, device=DEV)
+    kv = fa.PagedKV(k_pool=k_pool, v_pool=v_pool, kidx_pool=i_pool, page_table=tab[0],
+                    seq_lens=seq_lens, max_seq_len=mp * ps, prefix_len=P)
+
+    def grow(old, new):
+        st = fa.kv_alloc(bm, tab, torch.tensor(old, dtype=torch.int32, device=DEV),
+                         torch.tensor(new, dtype=torch.int32, device=DEV), ps, npages)
+        nonlocal o_use, o_tab
+        o_use, o_tab, o_st = oracle.allocate_blocks(o_use, o_tab, old, new, ps)
+        torch.cuda.synchronize()
+        assert int(st[0]) == o_st == 0
+        assert np.array_equal(tab[0].cpu().numpy(), o_tab)
+        seq_lens.copy_(torch.tensor(new, dtype=torch.int32))
+        # append tokens old .. new - 1 of every sequence (n = the largest growth; positions
+        # before a sequence's own new tokens are rewritten with their existing values)
+        n = int(max(np.asarray(new) - np.asarray(old)))
+        idx = np.asarray(new)[:, None] - n + np.arange(n)[None, :]
+        src = np.clip(idx, 0, tmax - 1)
+        take = lambda a: torch.from_numpy(np.take_along_axis(a, src[:, :, None, None], axis=1)) if isinstance(a, np.ndarray) \
+            else torch.stack([a[b, src[b]] for b in range(B)])
+        fa.kv_append(kv, take(k_tok).to(DEV), take(v_tok).to(DEV), take(i_tok).to(DEV))
+        for b in range(B):
+            t = np.arange(old[b], new[b])
+            for h in range(H):
+                oracle.append_rows(ok_pool, o_tab[b], ps, h, t, k_bits[b, t, h])
+                oracle.append_rows(ov_pool, o_tab[b], ps, h, t, v_bits[b, t, h])
+                oracle.append_rows(oi_pool, o_tab[b], ps, h, t, i_tok[b, t, h])
+
+    grow([0] * B, lens.tolist())
+    errs, lerrs = [], []
+    for s in range(steps):
+        grow(lens.tolist(), (lens + 1).tolist())
+        lens = lens + 1
+        lists = fa.index_topk(kv, torch.from_numpy(qi_step[s][:, None]).to(DEV), 1, 1, K)
+        out, lse = fa.decode(kv, q_step[s].to(DEV), lists[:, 0].contiguous())
+        torch.cuda.synchronize()
+        got = lists[:, 0].cpu().numpy()
+        for b in range(B):
+            for g in range(H):
+                idx, o_ref, l_ref = oracle.dsa_query(
+                    q_bits=q_bits[s, b, g * G:(g + 1) * G], q_idx_vec=qi_step[s, b, g], kidx_pool=oi_pool,
+                    k_pool=ok_pool, v_pool=ov_pool, page_table_row=o_tab[b], page_size=ps, kv_head=g,
+                    idx_head=g, pos=int(lens[b]) - 1, prefix_len=P, top_k=K, sm_scale=d ** -0.5)
+                assert np.array_equal(got[b, g], idx), (s, b, g)
+                errs.append(np.abs(out[b, g * G:(g + 1) * G].float().cpu().numpy() - o_ref).ravel())
+                lerrs.append(np.abs(lse[b, g * G:(g + 1) * G].double().cpu().numpy() - l_ref))
+    e = np.concatenate(errs)
+    assert e.max() <= 2e-2 and e.mean() <= 2e-3 and np.concatenate(lerrs).max() <= 4e-3
