@@ -203,11 +203,19 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const voi
         const int r0 = a + lane * 8;  // row index of this lane's first key (before clamping)
         const uint64_t lo = ((uint64_t)v.y << 32) | v.x, hi = ((uint64_t)v.w << 32) | v.z;
         uint32_t bits = 0;
+        if (a >= r_begin && a + 512 <= r_end) {  // uniform: every key of the step is in range
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t key = (uint32_t)(((u < 4 ? lo : hi) >> ((u & 3) * 16)) & 0xffffu);
-          const bool in = (unsigned)(r0 + u - r_begin) < (unsigned)(r_end - r_begin);
-          bits |= (uint32_t)(in && key >= T) << u;
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t key = (uint32_t)(((u < 4 ? lo : hi) >> ((u & 3) * 16)) & 0xffffu);
+            bits |= (uint32_t)(key >= T) << u;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t key = (uint32_t)(((u < 4 ? lo : hi) >> ((u & 3) * 16)) & 0xffffu);
+            const bool in = (unsigned)(r0 + u - r_begin) < (unsigned)(r_end - r_begin);
+            bits |= (uint32_t)(in && key >= T) << u;
+          }
         }
         const int c = __popc(bits);
         const int incl = wave_incl_sum(c);
