@@ -221,12 +221,21 @@ __global__ __launch_bounds__(kStrNT) void k_topk_row_stream(KvView kv, const voi
         const int incl = wave_incl_sum(c);
         int o = cnt + incl - c;
         cnt += __builtin_amdgcn_readlane(incl, 63);
-        while (bits != 0u) {
-          const int u = __builtin_ctz(bits);
-          bits &= bits - 1u;
-          const uint32_t key = (uint32_t)(((u < 4 ? lo : hi) >> ((u & 3) * 16)) & 0xffffu);
-          if (o < kCap) lk[o] = ((key - T) << 16) | (uint32_t)(r0 + u - P);
-          ++o;
+        if (cnt <= kCap) {  // uniform: the whole step fits in the list
+          while (bits != 0u) {
+            const int u = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const uint32_t key = (uint32_t)(((u < 4 ? lo : hi) >> ((u & 3) * 16)) & 0xffffu);
+            lk[o++] = ((key - T) << 16) | (uint32_t)(r0 + u - P);
+          }
+        } else {
+          while (bits != 0u) {
+            const int u = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const uint32_t key = (uint32_t)(((u < 4 ? lo : hi) >> ((u & 3) * 16)) & 0xffffu);
+            if (o < kCap) lk[o] = ((key - T) << 16) | (uint32_t)(r0 + u - P);
+            ++o;
+          }
         }
       };
       // kAhead steps of loads in flight per wave (a step is one 1 KiB load instruction; with
