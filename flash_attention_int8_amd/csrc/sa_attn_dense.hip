@@ -166,7 +166,8 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   // Global -> registers for one tile of K or V. The loads are unconditional and always in
   // bounds: a tile never crosses a page, and a page missing from the table reads page 0. Rows
   // that must not be attended (past the end of the sequence, or of a missing page) are zeroed
-  // when the tile is stored to LDS, so the loads stay in flight until then. The tile base is
+  // when the tile is stored to LDS, so the loads stay in flight until then; the scores of a
+  // missing page's keys are masked like those of keys past the query. The tile base is
   // wave-uniform; each lane adds one 32-bit offset (its first row and dims chunk).
   const uint32_t k_off = (uint32_t)(ld_kq * KPT * D + ld_c * 8);
   auto load_rows = [&](const uint16_t* pool, int tile, int64_t ph, uint32_t lane_off, uint4 (&dst)[KPT]) {
@@ -228,24 +229,28 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   // is positive, so it is applied in the exponent).
   // Masked mode: every key outside the query's selection (a subset of 0..pos) gets -inf, one
   // v_cndmask per score with the tile record's lane masks (scalar loads) as the condition.
-  auto apply_sel = [&](const uint64_t (&mw)[32], f32x16 (&s)[2]) {
+  // A tile on a page missing from the table (page_ok false, wave-uniform) is masked whole, as
+  // the gathered kernels skip such keys: its masks are cleared (scalar work) or its causal
+  // limit is put below the tile.
+  auto apply_sel = [&](const uint64_t (&mw)[32], f32x16 (&s)[2], bool page_ok) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        s[mb][r] = __builtin_amdgcn_inverse_ballot_w64(mw[mb * 16 + r]) ? s[mb][r] : -INFINITY;
+        s[mb][r] = __builtin_amdgcn_inverse_ballot_w64(page_ok ? mw[mb * 16 + r] : 0ull) ? s[mb][r]
+                                                                                          : -INFINITY;
   };
-  auto mask_tile = [&](int tile, f32x16 (&s)[2]) {
+  auto mask_tile = [&](int tile, f32x16 (&s)[2], bool page_ok) {
     if constexpr (MASKED) {  // the prologue's tile; the loop uses apply_sel
       uint64_t mw[32];
 #pragma unroll
       for (int k = 0; k < 32; ++k) mw[k] = selw[(int64_t)tile * 32 + k];
-      apply_sel(mw, s);
+      apply_sel(mw, s, page_ok);
       return;
     }
     const int t0 = tile * BN;
-    if (t0 + BN - 1 > pos0 + i_w) {
-      const int lim = my_pos - t0 - hi * 4;  // key offsets above lim are masked
+    if (!page_ok || t0 + BN - 1 > pos0 + i_w) {
+      const int lim = page_ok ? my_pos - t0 - hi * 4 : -BN;  // key offsets above lim are masked
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -376,14 +381,19 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   // Each loader role looks its page up one iteration ahead of the load that needs it.
   uint4 st[KPT];
   int32_t raw_next;  // page-table entry of the next tile this wave loads
+  // Whether the page of the tile whose scores the wave masks next is in the table: V loaders
+  // look up tile j+1 in iteration j (the tile masked there), K loaders one iteration earlier.
+  bool ok_tile0, ok_ahead = true;
   if (k_loader) {
     int64_t ph = phys_page(kv, b, 0);
+    ok_tile0 = ph >= 0;
     load_rows(kv.k_pool, 0, ph, k_off, st);
     int lim = valid_rows(0, ph);
     if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
     store_k(0, st);
     if (n_tiles > 1) {
       ph = phys_page(kv, b, BN);
+      ok_ahead = ph >= 0;
       load_rows(kv.k_pool, 1, ph, k_off, st);
       lim = valid_rows(1, ph);
       if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
@@ -392,6 +402,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     raw_next = raw_page(2);
   } else {
     const int64_t ph = phys_page(kv, b, 0);
+    ok_tile0 = ph >= 0;
     load_rows(kv.v_pool, 0, ph, k_off, st);
     const int lim = valid_rows(0, ph);
     if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
@@ -402,7 +413,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   f32x16 sa[2], sb[2];
   if (last_w >= 0) {
     qk(0, sa);
-    mask_tile(0, sa);
+    mask_tile(0, sa, ok_tile0);
     float mx0 = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 32; ++e) mx0 = fmaxf(mx0, sa[e >> 4][e & 15]);
@@ -421,6 +432,13 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     const int lt = more ? ltile : n_tiles - 1;
     const int64_t ph = more ? checked_page(ltile, raw_next) : 0;
     raw_next = raw_page(ltile + 1);
+    bool ok_next;  // page status of tile j+1, whose scores this iteration masks
+    if (k_loader) {
+      ok_next = ok_ahead;
+      ok_ahead = ph >= 0;
+    } else {
+      ok_next = ph >= 0;
+    }
     load_rows(k_loader ? kv.k_pool : kv.v_pool, lt, ph, k_off, st);
     const int lim = valid_rows(lt, ph);
     float mx = -INFINITY;
@@ -439,8 +457,8 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
       qk_softmax((j + 1) & 1, sn, sc, pf);
       // (masked mode applies the record unconditionally: S(j+1) is not used past last_w, and
       // a conditional use would let the compiler sink the loads to it)
-      if constexpr (MASKED) apply_sel(mw, sn);
-      else if (j + 1 <= last_w) mask_tile(j + 1, sn);
+      if constexpr (MASKED) apply_sel(mw, sn, ok_next);
+      else if (j + 1 <= last_w) mask_tile(j + 1, sn, ok_next);
       pv(j & 1, pf, sn, mx, j + 1 <= last_w);
     }
     if (more) {

@@ -32,10 +32,12 @@ from .dsa import (  # noqa: F401
     allocate_blocks,
     release_blocks,
     index_scores,
+    index_scores_many,
     topk_select,
     index_list,
     hybrid_index_list,
     attend,
+    attend_causal_many,
     dsa_query,
     dense_query,
 )

@@ -23,7 +23,10 @@ the design notes):
   * query head h reads KV head h // (H_q / H_kv).
 
 Parity pins (tests/test_oracle.py): index_scores against a pure-Python integer loop and
-the int8 extreme closed form; topk_select against a brute-force full sort and the order
+the int8 extreme closed form; index_scores_many against the same loop and extremes (the
+-128 corner included) and row by row against index_scores; attend_causal_many against
+closed forms (constant V, a query at position 0 seeing only key 0) and per token against
+dense_query; topk_select against a brute-force full sort and the order
 invariants; index_list against the prefix rule and a hand-worked golden case; attend
 against closed forms (single key, constant V, identical keys, one-hot V rows giving the
 probabilities), scipy's logsumexp, and a full-matrix masked softmax for the dense case;
@@ -152,6 +155,19 @@ def index_scores(q_idx_vec, k_rows) -> np.ndarray:
     return k @ q
 
 
+def index_scores_many(q_idx_rows, k_rows) -> np.ndarray:
+    """[DSA-page] §2.1 for many indexer queries at once: sigma[n, t] = sum_j q[n, j] * k[t, j].
+
+    Every product of two int8 values is an integer of magnitude at most 2^14, so each partial
+    sum of a row is an integer far below 2^53 and a float64 matrix product is exact in any
+    summation order (this is what lets BLAS do the work). Returned as int64 [n][T].
+    """
+    q = np.asarray(q_idx_rows, dtype=np.float64)
+    k = np.asarray(k_rows, dtype=np.float64)
+    assert q.shape[-1] == k.shape[-1] and q.shape[-1] <= (1 << 30)
+    return (q @ k.T).astype(np.int64)
+
+
 def topk_select(scores, t, k: int) -> np.ndarray:
     """[DSA-page] §2.1: keep the K best-scoring candidates.
 
@@ -227,6 +243,36 @@ def attend(q_heads, k_rows, v_rows, sm_scale: float):
     s = e.sum(axis=1)
     o = (e @ v) / s[:, None]
     return o, m + np.log(s)
+
+
+def attend_causal_many(q_rows, k_rows, v_rows, positions, sm_scale: float, chunk: int = 64):
+    """Dense causal attention of many query tokens of one KV group, in float64.
+
+    q_rows [n][G][d] are the group's query heads of n tokens; k_rows, v_rows [T][d] the
+    group's keys and values in token order; token n attends to keys 0..positions[n]. The
+    logits form one full matrix with every non-causal entry at -inf; softmax per row, times V
+    (the same definition as `attend` over keys 0..pos). Rows are processed `chunk` tokens at
+    a time to bound memory. Returns (O [n][G][d], LSE [n][G]).
+    """
+    q = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k_rows, dtype=np.float64)
+    v = np.asarray(v_rows, dtype=np.float64)
+    pos = np.asarray(positions, dtype=np.int64)
+    n, G, d = q.shape
+    o = np.empty((n, G, v.shape[1]), dtype=np.float64)
+    lse = np.empty((n, G), dtype=np.float64)
+    t = np.arange(k.shape[0], dtype=np.int64)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        z = float(sm_scale) * (q[s:e].reshape(-1, d) @ k.T)            # [(e-s)*G][T]
+        causal = t[None, :] <= np.repeat(pos[s:e], G)[:, None]
+        z = np.where(causal, z, -np.inf)
+        m = z.max(axis=1)
+        w = np.exp(z - m[:, None])
+        tot = w.sum(axis=1)
+        o[s:e] = ((w @ v) / tot[:, None]).reshape(e - s, G, -1)
+        lse[s:e] = (m + np.log(tot)).reshape(e - s, G)
+    return o, lse
 
 
 def dsa_query(*, q_bits, q_idx_vec, kidx_pool, k_pool, v_pool, page_table_row, page_size,

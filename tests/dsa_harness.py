@@ -192,3 +192,73 @@ def assert_close(stats):
     assert mx <= MAX_ABS, f"max abs error {mx}"
     assert mean <= MEAN_ABS, f"mean abs error {mean}"
     assert lse <= LSE_ABS, f"lse error {lse}"
+
+
+def sampled_positions(S: int, n_random: int, edge: int = 64, seed: int = 0) -> list:
+    """The first and last `edge` query rows of a block of S plus `n_random` seeded others."""
+    ends = set(range(min(S, edge))) | set(range(max(0, S - edge), S))
+    mid = np.array([i for i in range(S) if i not in ends], dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(mid.size, size=min(n_random, mid.size), replace=False) if mid.size else []
+    return sorted(ends | set(int(mid[j]) for j in pick))
+
+
+def oracle_block(ov: OracleView, b: int, rows, g: int):
+    """Oracle results of query tokens `rows` of sequence b, KV group g, from host copies of
+    the pools: (index lists [n][P+K] or None for dense, O [n][G][d], LSE [n][G]). Scores of
+    all rows come from one exact float64 product (oracle.index_scores_many), dense rows from
+    oracle.attend_causal_many."""
+    w, inp = ov.w, ov.inp
+    T = inp.seq_lens_host[b]
+    G = w.group
+    rows = [int(i) for i in rows]
+    pos = np.array([oracle.query_position(T, w.q_len, i) for i in rows], dtype=np.int64)
+    t = np.arange(T, dtype=np.int64)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    sel = torch.as_tensor(rows, device=inp.q.device, dtype=torch.long)
+    qd = oracle.bf16_to_f64(bits(inp.q[b].index_select(0, sel)[:, g * G:(g + 1) * G]))
+    kd = oracle.bf16_to_f64(oracle.page_rows(ov.k_pool, ov.table[b], w.page_size, g, t))
+    vd = oracle.bf16_to_f64(oracle.page_rows(ov.v_pool, ov.table[b], w.page_size, g, t))
+    if w.dense:
+        o, lse = oracle.attend_causal_many(qd, kd, vd, pos, scale)
+        return None, o, lse
+    gi = 0 if inp.num_idx_heads == 1 else g
+    kidx = oracle.page_rows(ov.kidx, ov.table[b], w.page_size, gi, t)
+    qi = inp.q_idx[b].index_select(0, sel)[:, gi].cpu().numpy()
+    sc = oracle.index_scores_many(qi, kidx)
+    width = w.prefix_len + w.top_k
+    lists = np.empty((len(rows), width), dtype=np.int64)
+    o = np.empty((len(rows), G, w.head_dim))
+    lse = np.empty((len(rows), G))
+    for n, p in enumerate(pos):
+        lists[n] = oracle.index_list(int(p), w.prefix_len, w.top_k, width, lambda c, n=n: sc[n, c])
+        keys = lists[n][lists[n] >= 0]
+        o[n], lse[n] = oracle.attend(qd[n], kd[keys], vd[keys], scale)
+    return lists, o, lse
+
+
+def compare_block(gpu: GpuRun, ov: OracleView, b: int, rows, g: int, want=None):
+    """compare_rows for many rows of one (sequence, group) through oracle_block (or a
+    precomputed result `want`); returns (max_abs, mean_abs, max_lse, oracle result)."""
+    w = ov.w
+    G = w.group
+    want = want if want is not None else oracle_block(ov, b, rows, g)
+    lists, o, lse = want
+    sel = torch.as_tensor([int(i) for i in rows], device=gpu.out.device, dtype=torch.long)
+    if lists is not None:
+        gi = 0 if ov.inp.num_idx_heads == 1 else g
+        got = gpu.indices[b].index_select(0, sel)[:, gi].cpu().numpy()
+        bad = np.nonzero(np.any(got != lists, axis=1))[0]
+        assert bad.size == 0, (b, g, [int(rows[k]) for k in bad[:8]], got[bad[0]][:16], lists[bad[0]][:16])
+    og = f64(gpu.out[b].index_select(0, sel)[:, g * G:(g + 1) * G])
+    e = np.abs(og - o)
+    le = 0.0
+    if gpu.lse is not None:
+        lg = gpu.lse[b].index_select(0, sel)[:, g * G:(g + 1) * G].double().cpu().numpy()
+        le = float(np.abs(lg - lse).max())
+    return float(e.max()), float(e.mean()), le, want
+
+
+def merge_stats(stats):
+    """Worst max-abs, mean of mean-abs (equal row counts per item), worst LSE error."""
+    return (max(s[0] for s in stats), float(np.mean([s[1] for s in stats])), max(s[2] for s in stats))

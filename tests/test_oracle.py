@@ -71,6 +71,39 @@ def test_index_scores_int8_extremes():
     assert list(oracle.index_scores(q2, np.full((1, 128), -128, np.int8))) == [2 ** 21]
 
 
+@pytest.mark.parametrize("d_idx", [1, 32, 64, 128])
+def test_index_scores_many_brute_force(d_idx):
+    """The batched scores (a float64 matrix product) equal pure-Python integer loops, with
+    the int8 minimum -128 mixed in, and equal index_scores row by row."""
+    rng = np.random.default_rng(100 + d_idx)
+    q = rng.integers(-128, 128, size=(5, d_idx)).astype(np.int8)
+    k = rng.integers(-128, 128, size=(29, d_idx)).astype(np.int8)
+    q[0] = -128
+    k[3] = -128
+    k[4] = 127
+    got = oracle.index_scores_many(q, k)
+    assert got.dtype == np.int64 and got.shape == (5, 29)
+    want = [[sum(int(q[n, j]) * int(k[t, j]) for j in range(d_idx)) for t in range(29)] for n in range(5)]
+    assert got.tolist() == want
+    assert got[0, 3] == d_idx * 2 ** 14 and got[0, 4] == -d_idx * 128 * 127
+    for n in range(5):
+        assert np.array_equal(got[n], oracle.index_scores(q[n], k))
+
+
+def test_index_scores_many_extremes_exact():
+    """At the largest magnitudes (+-2^21 at d_idx = 128, one unit apart from neighbours) the
+    float64 product is still exact."""
+    q = np.full((2, 128), -128, dtype=np.int8)
+    q[1, 0] = -127
+    k = np.full((3, 128), -128, dtype=np.int8)
+    k[1, :] = 127
+    k[2, 5] = 127
+    got = oracle.index_scores_many(q, k)
+    assert got.tolist() == [[2 ** 21, -128 * 128 * 127, 2 ** 21 - 128 * 128 - 128 * 127],
+                            [2 ** 21 - 128, -127 * 127 - 127 * 128 * 127,
+                             2 ** 21 - 128 - 128 * 128 - 128 * 127]]
+
+
 # ---------------------------------------------------------------- top-K
 
 def _brute_topk(scores, t, k):
@@ -310,6 +343,55 @@ def test_dense_is_top_k_of_everything_and_masked_softmax():
                                       page_size=ps, kv_head=0, pos=i, sm_scale=scale)
         assert np.allclose(od, want[i], rtol=0, atol=1e-12)
         assert np.allclose(lsed, lse, rtol=0, atol=1e-12)
+
+
+def test_attend_causal_many_matches_masked_softmax_and_dense_query():
+    """Many tokens at once: equals one full masked softmax(QK^T)V built with scipy, and
+    dense_query token by token through a shuffled page table."""
+    rng = np.random.default_rng(9)
+    T, d, ps, G = 90, 16, 16, 4
+    pages = -(-T // ps)
+    q = rng.standard_normal((T, G, d)) * 2
+    kf = rng.standard_normal((pages * ps, d)).astype(np.float32)
+    vf = rng.standard_normal((pages * ps, d)).astype(np.float32)
+    kb = (kf.view(np.uint32) >> 16).astype(np.uint16)
+    vb = (vf.view(np.uint32) >> 16).astype(np.uint16)
+    kd, vd = oracle.bf16_to_f64(kb[:T]), oracle.bf16_to_f64(vb[:T])
+    scale = 1 / math.sqrt(d)
+    pos = np.array([0, 1, 5, 15, 16, 17, 44, 63, 64, 89])
+    o, lse = oracle.attend_causal_many(q[pos], kd, vd, pos, scale, chunk=3)
+    z = scale * np.einsum("igd,td->igt", q[pos], kd)
+    z = np.where(np.arange(T)[None, None, :] <= pos[:, None, None], z, -np.inf)
+    want = np.einsum("igt,td->igd", scipy.special.softmax(z, axis=2), vd)
+    assert np.allclose(o, want, rtol=0, atol=1e-12)
+    assert np.allclose(lse, scipy.special.logsumexp(z, axis=2), rtol=0, atol=1e-12)
+    perm = rng.permutation(pages)
+    k_pool = np.zeros((pages, 1, ps, d), np.uint16)
+    v_pool = np.zeros((pages, 1, ps, d), np.uint16)
+    k_pool[perm, 0] = kb.reshape(pages, ps, d)
+    v_pool[perm, 0] = vb.reshape(pages, ps, d)
+    q_bits = (q.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    o2, lse2 = oracle.attend_causal_many(oracle.bf16_to_f64(q_bits[pos]), kd, vd, pos, scale)
+    for n, p in enumerate(pos):
+        od, ld = oracle.dense_query(q_bits=q_bits[p], k_pool=k_pool, v_pool=v_pool, page_table_row=perm,
+                                    page_size=ps, kv_head=0, pos=int(p), sm_scale=scale)
+        assert np.allclose(o2[n], od, rtol=0, atol=1e-12)
+        assert np.allclose(lse2[n], ld, rtol=0, atol=1e-12)
+
+
+def test_attend_causal_many_closed_forms():
+    """Position 0 sees only key 0 (O = V[0], LSE = its logit); constant V gives V."""
+    rng = np.random.default_rng(10)
+    T, d, G = 20, 8, 2
+    q = rng.standard_normal((3, G, d))
+    k = rng.standard_normal((T, d))
+    v = rng.standard_normal((T, d))
+    o, lse = oracle.attend_causal_many(q, k, v, [0, 0, 0], 0.5)
+    assert np.allclose(o, np.broadcast_to(v[0], o.shape), rtol=0, atol=1e-15)
+    assert np.allclose(lse, 0.5 * (q @ k[0]), rtol=0, atol=1e-14)
+    vc = np.tile(v[7], (T, 1))
+    o, _ = oracle.attend_causal_many(q, k, vc, [3, 11, 19], 0.5)
+    assert np.allclose(o, np.broadcast_to(v[7], o.shape), rtol=0, atol=1e-14)
 
 
 # ---------------------------------------------------------------- hand-worked golden case

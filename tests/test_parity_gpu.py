@@ -15,7 +15,8 @@ import torch
 import flash_attention_int8_amd as fa
 import oracle
 from synthetic import CONFIGS, Workload, make_inputs
-from dsa_harness import (OracleView, assert_close, bits, compare_rows, make_kv, run_gpu, f64)
+from dsa_harness import (OracleView, assert_close, bits, compare_block, compare_rows, make_kv,
+                         merge_stats, run_gpu, f64, sampled_positions)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -582,26 +583,147 @@ def test_lse_matches_definition_dense():
     assert_close(compare_rows(gpu, OracleView(inp), rows))
 
 
+# ------------------------------------------------------------------ int8 minimum, missing pages
+
+def _saturate(inp, rng, q_frac, key_frac):
+    """Writes -128 into every entry of a fraction of the indexer queries and keys: such a
+    query scores such a key at d_idx * 2^14, the largest score int8 values can make (the
+    value at which the 16-bit prefill keys saturate at 65535). A few keys get one entry -127
+    (one step below) and a few all +127 (the most negative scores)."""
+    q, k = inp.q_idx, inp.kidx_pool
+    nq = q.shape[0] * q.shape[1] * q.shape[2]
+    qf = q.view(nq, -1)
+    qf[torch.from_numpy(rng.random(nq) < q_frac)] = -128
+    nk = k.shape[0] * k.shape[1] * k.shape[2]
+    kf = k.view(nk, -1)
+    r = rng.random(nk)
+    kf[torch.from_numpy(r < key_frac)] = -128
+    near = torch.from_numpy((r >= key_frac) & (r < key_frac * 1.5))
+    kf[near] = -128
+    kf[near, 0] = -127
+    kf[torch.from_numpy((r >= key_frac * 1.5) & (r < key_frac * 1.8))] = 127
+
+
+@pytest.mark.parametrize("d_idx", [32, 64, 128])
+def test_int8_minimum_ties_at_largest_score(d_idx):
+    """Queries and keys of all -128 reach the largest score (d_idx * 2^14) on more keys than K
+    takes, so the lower-index rule decides among them. The two-step path, the fused 16-bit
+    prefill selection and the fused decode selection all give the oracle's lists bit for bit;
+    attention through both prefill kernels and the decode within the bar."""
+    rng = np.random.default_rng(d_idx)
+    # prefill block (q_len >= 16, rows <= 32K: the 16-bit key path)
+    w = W(batch=1, num_q_heads=8, num_kv_heads=2, seq_len=1100, q_len=300, idx_dim=d_idx, top_k=48,
+          prefix_len=2)
+    _banner(f"int8 minimum, prefill, d_idx={d_idx}")
+    inp = make_inputs(w, seed=31, device="cpu")
+    _saturate(inp, rng, q_frac=0.5, key_frac=0.15)
+    inp = inp.to(DEV)
+    two = run_gpu(inp)
+    fused = run_gpu(inp, fused=True, masked=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.indices, two.indices)
+    ov = OracleView(inp)
+    assert_close(compare_rows(two, ov, all_rows(inp)))
+    assert_close(compare_rows(fused, ov, all_rows(inp)))
+    # decode rows of >= 16384 candidates (the fused decode path), ties at the top spread over
+    # every chunk
+    wd = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=20000, q_len=1, idx_dim=d_idx, top_k=256)
+    _banner(f"int8 minimum, decode, d_idx={d_idx}")
+    inp = make_inputs(wd, seed=32, device="cpu")
+    _saturate(inp, rng, q_frac=0.75, key_frac=0.03)
+    inp = inp.to(DEV)
+    two = run_gpu(inp)
+    fused = run_gpu(inp, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.indices, two.indices)
+    assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
+
+
+def test_missing_page_keys_are_left_out():
+    """A page missing from the table (entry -1): its keys take no part in the softmax of the
+    dense kernel, the masked-dense kernel and the gathered kernel alike (lists of every
+    causal key), matching the oracle over the present keys."""
+    w = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=330, q_len=300, idx_dim=64, top_k=330)
+    _banner("missing page: dense, masked and gathered prefill")
+    inp = make_inputs(w, seed=33, device="cpu", seq_lens=[330, 300], spare_pages=1)
+    inp.page_table[0, 2] = -1       # tokens 128..191 of sequence 0
+    inp.page_table[1, 0] = -1       # tokens 0..63 of sequence 1: its first queries see nothing
+    inp = inp.to(DEV)
+    kv = make_kv(inp)
+    S, H, width = w.q_len, w.num_kv_heads, 330
+    lists = torch.full((w.batch, S, H, width), -1, dtype=torch.int32)
+    for b in range(w.batch):
+        for i in range(S):
+            pos = oracle.query_position(inp.seq_lens_host[b], S, i)
+            if pos >= 0:
+                lists[b, i, :, :pos + 1] = torch.arange(pos + 1, dtype=torch.int32)
+    lists = lists.to(DEV)
+    out_d, lse_d = fa.prefill(kv, inp.q, q_tail=S)
+    out_m, lse_m = fa.prefill_masked(kv, inp.q, q_tail=S, indices=lists)
+    out_g, lse_g = fa.prefill(kv, inp.q, q_tail=S, indices=lists)
+    torch.cuda.synchronize()
+    ov = OracleView(inp)
+    G, scale = w.group, 1.0 / math.sqrt(w.head_dim)
+    errs, lerrs = [], []
+    for b in range(w.batch):
+        T = inp.seq_lens_host[b]
+        for i in range(S):
+            pos = oracle.query_position(T, S, i)
+            keys = np.array([t for t in range(pos + 1) if ov.table[b][t // w.page_size] >= 0])
+            for g in range(H):
+                sl = slice(g * G, (g + 1) * G)
+                outs = [(out_d, lse_d), (out_m, lse_m), (out_g, lse_g)]
+                if keys.size == 0:      # nothing to attend: out 0, lse -inf (all three kernels)
+                    for o, l in outs:
+                        assert torch.all(o[b, i, sl] == 0) and torch.all(torch.isneginf(l[b, i, sl]))
+                    continue
+                qb = oracle.bf16_to_f64(bits(inp.q[b, i, sl]))
+                kr = oracle.bf16_to_f64(oracle.page_rows(ov.k_pool, ov.table[b], w.page_size, g, keys))
+                vr = oracle.bf16_to_f64(oracle.page_rows(ov.v_pool, ov.table[b], w.page_size, g, keys))
+                o_ref, l_ref = oracle.attend(qb, kr, vr, scale)
+                for o, l in outs:
+                    errs.append(np.abs(f64(o[b, i, sl]) - o_ref).ravel())
+                    lerrs.append(np.abs(l[b, i, sl].double().cpu().numpy() - l_ref))
+    e = np.concatenate(errs)
+    assert_close((float(e.max()), float(e.mean()), float(np.concatenate(lerrs).max())))
+
+
 # ------------------------------------------------------------------ full-size workloads
 
-def _sample_queries(S, n, seed):
-    rng = np.random.default_rng(seed)
-    head = list(range(min(S, 4)))
-    tail = list(range(max(0, S - 4), S))
-    mid = sorted(rng.choice(S, size=min(S, n), replace=False).tolist())
-    return sorted(set(head + tail + mid))
+# Oracle results of the full-size prefill blocks, shared by the tests that run the same seeded
+# inputs through different GPU paths (the inputs are a pure function of workload and seed).
+_ORACLE_CACHE = {}
+
+
+def _check_full_prefill(name, seed, gpu, inp, rows_of_b):
+    """Every KV group of the sampled rows of every sequence against the oracle (index lists
+    bit-exact, outputs within the bar); returns the number of (row, group) pairs checked."""
+    w = inp.workload
+    ov = OracleView(inp, host_copy=True)
+    stats, n = [], 0
+    for b in range(w.batch):
+        rows = rows_of_b(b)
+        for g in range(w.num_kv_heads):
+            key = (name, seed, b, g)
+            mx, mean, le, want = compare_block(gpu, ov, b, rows, g, _ORACLE_CACHE.get(key))
+            _ORACLE_CACHE[key] = want
+            stats.append((mx, mean, le))
+            n += len(rows)
+    assert_close(merge_stats(stats))
+    return n
 
 
 def test_full_dense_prefill_8k():
+    """Dense causal 8K, B=4: per sequence the first and last 64 queries and 256 seeded others
+    (1024 random rows in all), every KV group (all 32 query heads)."""
     w = CONFIGS["dense_prefill_8k"]
     _banner(f"full {w.name}")
     inp = make_inputs(w, seed=2, device=DEV)
     gpu = run_gpu(inp)
     torch.cuda.synchronize()
-    ov = OracleView(inp, host_copy=False)
-    rows = [(b, i, g) for b in range(w.batch) for i in _sample_queries(w.q_len, 6, b)
-            for g in (0, 3, 7)]
-    assert_close(compare_rows(gpu, ov, rows))
+    n = _check_full_prefill(w.name, 2, gpu, inp,
+                            lambda b: sampled_positions(w.q_len, 256, edge=64, seed=20 + b))
+    assert n == 4 * 384 * 8
 
 
 def test_full_sparse_decode_128k():
@@ -616,20 +738,33 @@ def test_full_sparse_decode_128k():
     assert_close(compare_rows(gpu, ov, all_rows(inp)))
 
 
+_ROWS_32K = None
+
+
+def _rows_32k():
+    global _ROWS_32K
+    if _ROWS_32K is None:
+        _ROWS_32K = sampled_positions(CONFIGS["sparse_prefill_32k"].q_len, 1024, edge=64, seed=40)
+    return _ROWS_32K
+
+
 def test_full_sparse_prefill_32k():
+    """Two-step selection and gathered-row attention over the 32K prefill in 2048-query
+    blocks: the first and last 64 queries and 1024 seeded others, all 8 KV groups, lists
+    bit-exact and outputs within the bar."""
     w = CONFIGS["sparse_prefill_32k"]
     _banner(f"full {w.name}")
     inp = make_inputs(w, seed=4, device=DEV)
     gpu = run_gpu(inp, q_chunk=2048)
     torch.cuda.synchronize()
-    ov = OracleView(inp, host_copy=False)
-    rows = [(0, i, g) for i in _sample_queries(w.q_len, 10, 4) for g in (0, 5)]
-    assert_close(compare_rows(gpu, ov, rows))
+    n = _check_full_prefill(w.name, 4, gpu, inp, lambda b: _rows_32k())
+    assert n == 1152 * 8
 
 
 def test_full_sparse_prefill_32k_masked():
     """The 32K sparse prefill as the benchmark runs it: fused selection (16-bit keys) and the
-    attention on masked dense tiles, in 2048-query blocks; lists equal the two-step path's."""
+    attention on masked dense tiles, in 2048-query blocks; lists equal the two-step path's on
+    every row, and the sampled rows (as above) match the oracle."""
     w = CONFIGS["sparse_prefill_32k"]
     _banner(f"full {w.name}, fused selection, masked dense tiles")
     inp = make_inputs(w, seed=4, device=DEV)
@@ -639,9 +774,8 @@ def test_full_sparse_prefill_32k_masked():
     assert torch.equal(gpu.indices, two.indices)
     del two
     torch.cuda.synchronize()
-    ov = OracleView(inp, host_copy=False)
-    rows = [(0, i, g) for i in _sample_queries(w.q_len, 10, 4) for g in (1, 6)]
-    assert_close(compare_rows(gpu, ov, rows))
+    n = _check_full_prefill(w.name, 4, gpu, inp, lambda b: _rows_32k())
+    assert n == 1152 * 8
 
 
 def test_full_sparse_decode_1m_prefix():
@@ -653,8 +787,7 @@ def test_full_sparse_decode_1m_prefix():
     torch.cuda.synchronize()
     assert torch.equal(gpu.indices, two.indices)
     ov = OracleView(inp, host_copy=False)
-    rows = [(b, 0, g) for b in range(w.batch) for g in (0, 3, 7)]
-    assert_close(compare_rows(gpu, ov, rows))
+    assert_close(compare_rows(gpu, ov, all_rows(inp)))   # all 32 (sequence, group) rows
     # every list starts with the forced prefix 0..195
     idx = gpu.indices[:, 0].cpu().numpy()
     assert np.all(idx[..., :196] == np.arange(196))
