@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
 SA_ABI_VERSION = 1
 
 STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_UNSUPPORTED",
-          4: "SA_ERR_WORKSPACE", 5: "SA_ERR_HIP", 6: "SA_ERR_ABI", 7: "SA_ERR_ALIGN"}
+          4: "SA_ERR_WORKSPACE", 5: "SA_ERR_HIP", 6: "SA_ERR_ABI", 7: "SA_ERR_ALIGN",
+          8: "SA_ERR_SCRATCH"}
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_ABI, \
-    SA_ERR_ALIGN = range(8)
+    SA_ERR_ALIGN, SA_ERR_SCRATCH = range(9)
 
 EXPORTS = ["sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_index",
            "sparse_attn_topk_workspace_size", "sparse_attn_topk",
@@ -29,7 +30,8 @@ EXPORTS = ["sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_
            "sparse_attn_index_topk_window_workspace_size", "sparse_attn_index_topk_window",
            "sparse_attn_fwd_prefill", "sparse_attn_prefill_masked_workspace_size",
            "sparse_attn_fwd_prefill_masked", "sparse_attn_kv_append", "sparse_attn_kv_alloc",
-           "sparse_attn_kv_release", "sparse_attn_decode_workspace_size", "sparse_attn_fwd_decode"]
+           "sparse_attn_kv_release", "sparse_attn_decode_workspace_size", "sparse_attn_fwd_decode",
+           "sparse_attn_decode_noalloc_max_bytes", "sparse_attn_fwd_decode_noalloc"]
 
 
 class SparseAttnError(RuntimeError):
@@ -93,6 +95,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sparse_attn_kv_release": (I32, [I32, I32, P, I32, I32, I32, P, P, P, P]),
         "sparse_attn_decode_workspace_size": (SZ, [KV, I32, I32, I32]),
         "sparse_attn_fwd_decode": (I32, [KV, P, I32, P, I32, F32, I32, P, SZ, P, P, P]),
+        "sparse_attn_decode_noalloc_max_bytes": (SZ, []),
+        "sparse_attn_fwd_decode_noalloc": (I32, [KV, P, I32, P, I32, F32, I32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -299,6 +303,19 @@ def sparse_attn_fwd_decode(kv: PagedKV, q, num_q_heads, indices, index_width, sm
         kv.ref, _ptr(q, torch.bfloat16, "q"), num_q_heads, _ptr(indices, torch.int32, "indices"),
         index_width, float(sm_scale), num_splits, _ptr(workspace, None, "workspace"), workspace_bytes,
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def sparse_attn_decode_noalloc_max_bytes() -> int:
+    return int(load().sparse_attn_decode_noalloc_max_bytes())
+
+
+def sparse_attn_fwd_decode_noalloc(kv: PagedKV, q, num_q_heads, indices, index_width, sm_scale,
+                                   num_splits, out, lse=None, stream=None):
+    lib = load()
+    _check("sparse_attn_fwd_decode_noalloc", lib.sparse_attn_fwd_decode_noalloc(
+        kv.ref, _ptr(q, torch.bfloat16, "q"), num_q_heads, _ptr(indices, torch.int32, "indices"),
+        index_width, float(sm_scale), num_splits, _ptr(out, torch.bfloat16, "out"),
+        _ptr(lse, torch.float32, "lse"), _stream(stream)))
 
 
 # ------------------------------------------------------------------ allocating helpers

@@ -80,6 +80,7 @@ const char* sparse_attn_status_string(int32_t status) {
     case SA_ERR_HIP: return "HIP runtime rejected a launch";
     case SA_ERR_ABI: return "descriptor ABI version mismatch";
     case SA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SA_ERR_SCRATCH: return "call needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -369,31 +370,70 @@ size_t sparse_attn_decode_workspace_size(const sa_paged_kv* kv, int32_t num_q_he
   return sa::gather_workspace_bytes(units, num_q_heads / v.num_kv_heads, v.head_dim, splits);
 }
 
+namespace {
+
+// Checks shared by the decode entry points; on success *splits and *need are the split count
+// and the partials' size in bytes.
+int32_t check_decode(const sa_paged_kv* kv, const uint16_t* q, int32_t num_q_heads,
+                     const int32_t* indices, int32_t index_width, float sm_scale,
+                     int32_t num_splits, const uint16_t* out, const float* lse, sa::KvView* v,
+                     int* splits, size_t* need) {
+  int32_t st = check_kv(kv, NEED_KV, v);
+  if (st != SA_OK) return st;
+  if (q == nullptr || out == nullptr || indices == nullptr) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(indices) || (lse != nullptr && !aligned16(lse)))
+    return SA_ERR_ALIGN;
+  if (num_q_heads < 1 || num_q_heads % v->num_kv_heads != 0) return SA_ERR_SHAPE;
+  const int group = num_q_heads / v->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return SA_ERR_UNSUPPORTED;
+  if (index_width < 1 || num_splits < 0 || num_splits > 256) return SA_ERR_SHAPE;
+  if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return SA_ERR_SHAPE;
+  const int64_t units = (int64_t)v->batch * v->num_kv_heads;
+  int sp = num_splits > 0 ? num_splits : sa::auto_splits(units, index_width, v->head_dim, group);
+  if (sp > index_width) sp = index_width;
+  *splits = sp;
+  *need = sa::gather_workspace_bytes(units, group, v->head_dim, sp);
+  return SA_OK;
+}
+
+}  // namespace
+
 int32_t sparse_attn_fwd_decode(const sa_paged_kv* kv, const uint16_t* q, int32_t num_q_heads,
                                const int32_t* indices, int32_t index_width, float sm_scale,
                                int32_t num_splits, void* workspace, size_t workspace_bytes,
                                uint16_t* out, float* lse, void* stream) {
   sa::KvView v;
-  int32_t st = check_kv(kv, NEED_KV, &v);
+  int splits = 0;
+  size_t need = 0;
+  int32_t st = check_decode(kv, q, num_q_heads, indices, index_width, sm_scale, num_splits, out,
+                            lse, &v, &splits, &need);
   if (st != SA_OK) return st;
-  if (q == nullptr || out == nullptr || indices == nullptr) return SA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(indices) || (lse != nullptr && !aligned16(lse)))
-    return SA_ERR_ALIGN;
-  if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0) return SA_ERR_SHAPE;
-  const int group = num_q_heads / v.num_kv_heads;
-  if (group != 1 && group != 2 && group != 4 && group != 8) return SA_ERR_UNSUPPORTED;
-  if (index_width < 1 || num_splits < 0 || num_splits > 256) return SA_ERR_SHAPE;
-  if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return SA_ERR_SHAPE;
-  const int64_t units = (int64_t)v.batch * v.num_kv_heads;
-  int splits = num_splits > 0 ? num_splits : sa::auto_splits(units, index_width, v.head_dim, group);
-  if (splits > index_width) splits = index_width;
-  const size_t need = sa::gather_workspace_bytes(units, group, v.head_dim, splits);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SA_ERR_ALIGN;
   }
   return hip_status(sa::launch_attn_gather(v, q, num_q_heads, 1, 1, indices, index_width, sm_scale,
                                            splits, static_cast<float*>(workspace), out, lse,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t sparse_attn_decode_noalloc_max_bytes(void) { return sa::kDecodeScratchBytes; }
+
+int32_t sparse_attn_fwd_decode_noalloc(const sa_paged_kv* kv, const uint16_t* q,
+                                       int32_t num_q_heads, const int32_t* indices,
+                                       int32_t index_width, float sm_scale, int32_t num_splits,
+                                       uint16_t* out, float* lse, void* stream) {
+  sa::KvView v;
+  int splits = 0;
+  size_t need = 0;
+  int32_t st = check_decode(kv, q, num_q_heads, indices, index_width, sm_scale, num_splits, out,
+                            lse, &v, &splits, &need);
+  if (st != SA_OK) return st;
+  if (need > sa::kDecodeScratchBytes) return SA_ERR_SCRATCH;
+  float* scratch = nullptr;
+  if (need > 0 && sa::decode_scratch(&scratch) != hipSuccess) return SA_ERR_HIP;
+  return hip_status(sa::launch_attn_gather(v, q, num_q_heads, 1, 1, indices, index_width, sm_scale,
+                                           splits, scratch, out, lse,
                                            static_cast<hipStream_t>(stream)));
 }
 

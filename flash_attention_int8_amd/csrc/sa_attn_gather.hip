@@ -18,6 +18,8 @@
 // are merged across lane groups and waves at the end, then either normalised and stored
 // (one split) or written as partials for k_merge_splits (several splits). All merges run in
 // a fixed order, so results are deterministic.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "sa_common.h"
@@ -394,6 +396,39 @@ int auto_splits(int64_t units, int index_width, int head_dim, int group) {
   int s = (index_width + 2 * batch - 1) / (2 * batch);
   if (units * s < 256) s = (index_width + batch - 1) / batch;
   return s < 1 ? 1 : (s > 256 ? 256 : s);
+}
+
+// Split partials of the decode entry point that allocates nothing: a file-scope device array
+// (each GPU holds its own copy for the life of the process). Host code never passes the
+// array's name to a kernel; it looks up each device's address once and passes that.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+}  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (addr == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<float*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_attn_gather(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,

@@ -134,6 +134,10 @@ hipError_t launch_attn_gather(const KvView& kv, const uint16_t* q, int num_q_hea
                               hipStream_t stream);
 size_t gather_workspace_bytes(int64_t units, int group, int head_dim, int num_splits);
 int auto_splits(int64_t units, int index_width, int head_dim, int group);
+// Static split-partials buffer of sparse_attn_fwd_decode_noalloc: its size, and its device
+// address on the current device (looked up once per device, no allocation).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(float** ptr);
 bool fused_applies(const KvView& kv, int q_len);
 size_t fused_workspace_bytes(const KvView& kv);
 hipError_t launch_index_topk_fused(const KvView& kv, const int8_t* q_idx, int q_tail, int top_k,

@@ -21,7 +21,8 @@
  *  Ownership   The caller owns every buffer. All array pointers are DEVICE pointers, except
  *              the descriptor itself, which is read on the host during the call and may be
  *              freed as soon as the call returns. The library keeps no state between calls
- *              and allocates no memory.
+ *              and allocates no memory (sparse_attn_fwd_decode_noalloc alone uses a static
+ *              device buffer of the library, described there).
  *  Streams     `stream` is a hipStream_t (NULL = the default stream). Every call only
  *              enqueues work on it and returns; nothing synchronises.
  *  Errors      Each call returns SA_OK (0) or an SA_ERR_* code. All argument checks run on
@@ -68,7 +69,8 @@ enum sa_status {
   SA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the *_workspace_size value */
   SA_ERR_HIP = 5,          /* the HIP runtime rejected a launch */
   SA_ERR_ABI = 6,          /* descriptor abi_version differs from SA_ABI_VERSION */
-  SA_ERR_ALIGN = 7         /* a pointer is not 16-byte aligned */
+  SA_ERR_ALIGN = 7,        /* a pointer is not 16-byte aligned */
+  SA_ERR_SCRATCH = 8       /* the call needs more than the static scratch buffer holds (noalloc) */
 };
 
 /*
@@ -304,6 +306,29 @@ int32_t sparse_attn_fwd_decode(const sa_paged_kv* kv, const uint16_t* q, int32_t
                                const int32_t* indices, int32_t index_width, float sm_scale,
                                int32_t num_splits, void* workspace, size_t workspace_bytes,
                                uint16_t* out, float* lse, void* stream);
+
+/*
+ * Decode attention that allocates nothing, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Computes exactly what sparse_attn_fwd_decode computes, with the same kernels and split
+ * choice, but the split partials live in a static device buffer of the library instead of a
+ * caller workspace: sparse_attn_decode_noalloc_max_bytes() bytes (16 MiB) on each GPU the
+ * library runs on, held until the process ends. A call whose partials need more
+ * (sparse_attn_decode_workspace_size(...) larger than that) returns SA_ERR_SCRATCH and
+ * launches nothing. No hipMalloc/hipFree or other allocating routine is called; the first
+ * call on a device looks up that device's copy of the buffer (hipGetSymbolAddress), so the
+ * current device must be the one that owns `stream` and the pointers.
+ * Every call on one GPU shares that GPU's buffer and it keeps the last call's contents (each
+ * call rewrites every partial it reads, so nothing needs clearing): calls that overlap on one
+ * GPU (different streams, or threads without ordering) race and give undefined results.
+ * Arguments, layouts and the other status codes as for sparse_attn_fwd_decode.
+ */
+size_t sparse_attn_decode_noalloc_max_bytes(void);
+int32_t sparse_attn_fwd_decode_noalloc(const sa_paged_kv* kv, const uint16_t* q,
+                                       int32_t num_q_heads, const int32_t* indices,
+                                       int32_t index_width, float sm_scale, int32_t num_splits,
+                                       uint16_t* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -41,8 +41,8 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.sparse_attn_abi_version() == fa.SA_ABI_VERSION == 1
-    for code in range(8):
-        assert lib.sparse_attn_status_string(code)
+    for code in range(9):
+        assert lib.sparse_attn_status_string(code) != b"unknown status"
     assert lib.sparse_attn_status_string(0) == b"ok"
     assert lib.sparse_attn_status_string(99) == b"unknown status"
 
@@ -333,6 +333,41 @@ def test_decode_workspace_size(lib):
     auto = lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 32, 2048, 0)
     assert auto > 0 and auto % (2 * 8 * 4 * 130 * 4) == 0
     assert lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 30, 2048, 0) == 0
+
+
+def call_decode_noalloc(lib, d, q=A, hq=32, idx=A, width=2048, splits=4, out=A, lse=None, scale=0.1):
+    return lib.sparse_attn_fwd_decode_noalloc(None if d is None else ctypes.byref(d), q, hq, idx, width,
+                                              scale, splits, out, lse, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(d=None), fa.SA_ERR_NULL),
+    (dict(d=desc(abi_version=2)), fa.SA_ERR_ABI),
+    (dict(splits=-1), fa.SA_ERR_SHAPE),
+    (dict(splits=257), fa.SA_ERR_SHAPE),
+    (dict(idx=None), fa.SA_ERR_NULL),
+    (dict(out=A + 8), fa.SA_ERR_ALIGN),
+    (dict(hq=24), fa.SA_ERR_UNSUPPORTED),
+    (dict(width=0), fa.SA_ERR_SHAPE),
+    (dict(scale=float("nan")), fa.SA_ERR_SHAPE),
+    # partials beyond the 16 MiB static buffer: 32 units x 256 splits x 4 heads x 130 floats
+    (dict(d=desc(batch=4), splits=256), fa.SA_ERR_SCRATCH),
+    (dict(d=desc(batch=64), width=4096, splits=64), fa.SA_ERR_SCRATCH),
+])
+def test_decode_noalloc_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_decode_noalloc(lib, d, **case) == code
+
+
+def test_decode_noalloc_buffer_size(lib):
+    cap = lib.sparse_attn_decode_noalloc_max_bytes()
+    assert cap == 16 << 20
+    d = desc(batch=4)
+    need = lib.sparse_attn_decode_workspace_size(ctypes.byref(d), 32, 2048, 256)
+    assert need > cap   # the SA_ERR_SCRATCH cases above really are over the limit
+    d64 = desc(batch=64)
+    assert lib.sparse_attn_decode_workspace_size(ctypes.byref(d64), 32, 4096, 64) > cap
 
 
 def call_index_topk(lib, d, q_idx=A, q_len=1, q_tail=1, k=64, idx=A, ws=A, ws_bytes=1 << 34):
