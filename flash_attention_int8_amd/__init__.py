@@ -31,7 +31,10 @@ EXPORTS = ["sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_
            "sparse_attn_fwd_prefill", "sparse_attn_prefill_masked_workspace_size",
            "sparse_attn_fwd_prefill_masked", "sparse_attn_kv_append", "sparse_attn_kv_alloc",
            "sparse_attn_kv_release", "sparse_attn_decode_workspace_size", "sparse_attn_fwd_decode",
-           "sparse_attn_decode_noalloc_max_bytes", "sparse_attn_fwd_decode_noalloc"]
+           "sparse_attn_decode_noalloc_max_bytes", "sparse_attn_fwd_decode_noalloc",
+           "sparse_attn_select_thresholds", "sparse_attn_prefill_fused_workspace_size",
+           "sparse_attn_prefill_fused_choice", "sparse_attn_prefill_fused"]
+SA_PREFILL_AUTO, SA_PREFILL_GATHER, SA_PREFILL_MASKED = 0, 1, 2
 
 
 class SparseAttnError(RuntimeError):
@@ -97,6 +100,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sparse_attn_fwd_decode": (I32, [KV, P, I32, P, I32, F32, I32, P, SZ, P, P, P]),
         "sparse_attn_decode_noalloc_max_bytes": (SZ, []),
         "sparse_attn_fwd_decode_noalloc": (I32, [KV, P, I32, P, I32, F32, I32, P, P, P]),
+        "sparse_attn_select_thresholds": (I32, [KV, P, I32, I32, I32, P, P]),
+        "sparse_attn_prefill_fused_workspace_size": (SZ, [KV, I32, I32, I32, I32, I32]),
+        "sparse_attn_prefill_fused_choice": (I32, [KV, I32, I32, I32, I32]),
+        "sparse_attn_prefill_fused": (I32, [KV, P, P, I32, I32, I32, I32, F32, I32, P, SZ, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -318,6 +325,32 @@ def sparse_attn_fwd_decode_noalloc(kv: PagedKV, q, num_q_heads, indices, index_w
         _ptr(lse, torch.float32, "lse"), _stream(stream)))
 
 
+def sparse_attn_select_thresholds(kv: PagedKV, q_idx, q_len, q_tail, top_k, thresholds, stream=None):
+    lib = load()
+    _check("sparse_attn_select_thresholds", lib.sparse_attn_select_thresholds(
+        kv.ref, _ptr(q_idx, torch.int8, "q_idx"), q_len, q_tail, top_k,
+        _ptr(thresholds, torch.int32, "thresholds"), _stream(stream)))
+
+
+def sparse_attn_prefill_fused_workspace_size(kv: PagedKV, num_q_heads, q_len, q_tail, top_k,
+                                             path=SA_PREFILL_AUTO) -> int:
+    return int(load().sparse_attn_prefill_fused_workspace_size(kv.ref, num_q_heads, q_len, q_tail,
+                                                               top_k, path))
+
+
+def sparse_attn_prefill_fused_choice(kv: PagedKV, num_q_heads, q_len, q_tail, top_k) -> int:
+    return int(load().sparse_attn_prefill_fused_choice(kv.ref, num_q_heads, q_len, q_tail, top_k))
+
+
+def sparse_attn_prefill_fused(kv: PagedKV, q, q_idx, num_q_heads, q_len, q_tail, top_k, sm_scale,
+                              path, workspace, workspace_bytes, out, lse=None, stream=None):
+    lib = load()
+    _check("sparse_attn_prefill_fused", lib.sparse_attn_prefill_fused(
+        kv.ref, _ptr(q, torch.bfloat16, "q"), _ptr(q_idx, torch.int8, "q_idx"), num_q_heads, q_len,
+        q_tail, top_k, float(sm_scale), path, _ptr(workspace, None, "workspace"), workspace_bytes,
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
 # ------------------------------------------------------------------ allocating helpers
 
 def _row_stride(max_seq_len: int) -> int:
@@ -393,6 +426,34 @@ def prefill(kv: PagedKV, q, q_tail, indices=None, sm_scale=None, out=None, lse=N
         lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
     width = 0 if indices is None else int(indices.shape[-1])
     sparse_attn_fwd_prefill(kv, q, Hq, q_len, q_tail, indices, width, sm_scale, out, lse, stream)
+    return out, lse
+
+
+def select_thresholds(kv: PagedKV, q_idx, q_len, q_tail, top_k, thresholds=None, stream=None):
+    """Per-row (tau, t_cut): int32 [B][q_len][H_idx][2]."""
+    d = kv.desc
+    if thresholds is None:
+        thresholds = torch.empty((d.batch, q_len, d.num_idx_heads, 2), dtype=torch.int32,
+                                 device=q_idx.device)
+    sparse_attn_select_thresholds(kv, q_idx, q_len, q_tail, top_k, thresholds, stream)
+    return thresholds
+
+
+def prefill_fused(kv: PagedKV, q, q_idx, q_tail, top_k, sm_scale=None, path=SA_PREFILL_AUTO,
+                  out=None, lse=None, workspace=None, want_lse=True, stream=None):
+    """Indexer + top-K + attention of a prefill block in one call -> (out, lse)."""
+    B, q_len, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+    need = sparse_attn_prefill_fused_workspace_size(kv, Hq, q_len, q_tail, top_k, path)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    sparse_attn_prefill_fused(kv, q, q_idx, Hq, q_len, q_tail, top_k, sm_scale, path, workspace,
+                              workspace.numel() * workspace.element_size(), out, lse, stream)
     return out, lse
 
 

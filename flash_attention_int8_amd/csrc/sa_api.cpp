@@ -269,6 +269,109 @@ int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_
                                                 index_width, sm_scale, out, lse, s));
 }
 
+int32_t sparse_attn_select_thresholds(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
+                                      int32_t q_tail, int32_t top_k, int32_t* thresholds,
+                                      void* stream) {
+  sa::KvView v;
+  int32_t st = check_index_topk(kv, q_idx, q_len, q_tail, top_k, 0, thresholds, &v);
+  if (st != SA_OK) return st;
+  if (!sa::sel_thresh_applies(v)) return SA_ERR_UNSUPPORTED;
+  return hip_status(sa::launch_sel_thresh(v, q_idx, q_len, q_tail, top_k, thresholds, nullptr,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+// Average number of candidate keys of a query of the block, from the host-side length bound.
+double mean_candidates(const sa::KvView& v, int32_t q_len, int32_t q_tail) {
+  const double first = (double)v.max_seq_len - q_tail;  // position of the block's first query
+  return first + (q_len - 1) * 0.5 + 1.0 - v.prefix_len;
+}
+
+// Path of sparse_attn_prefill_fused: masked-dense tiles when the lists select a large enough
+// share of the causal keys (the dense tiles cost per causal key what a gathered row costs per
+// selected key divided by kMaskedGatherRatio, measured on MI355X), else gathered rows.
+constexpr double kMaskedGatherRatio = 16.0;
+
+int32_t fused_path(const sa::KvView& v, int32_t num_q_heads, int32_t q_len, int32_t q_tail,
+                   int32_t top_k, int32_t path) {
+  const int group = num_q_heads / v.num_kv_heads;
+  const bool gather_ok = group == 1 || group == 2 || group == 4 || group == 8;
+  const bool masked_ok = sa::sel_thresh_applies(v);
+  if (path == SA_PREFILL_GATHER) return gather_ok ? SA_PREFILL_GATHER : -1;
+  if (path == SA_PREFILL_MASKED) return masked_ok ? SA_PREFILL_MASKED : -1;
+  if (!masked_ok) return gather_ok ? SA_PREFILL_GATHER : -1;
+  if (!gather_ok) return SA_PREFILL_MASKED;
+  const bool dense_enough = (double)top_k * kMaskedGatherRatio >= mean_candidates(v, q_len, q_tail);
+  return (dense_enough && q_len >= 64) ? SA_PREFILL_MASKED : SA_PREFILL_GATHER;
+}
+
+size_t fused_bytes(const sa::KvView& v, int32_t q_len, int32_t top_k, int32_t chosen) {
+  const size_t rows = (size_t)v.batch * q_len * v.num_idx_heads;
+  if (chosen == SA_PREFILL_MASKED) return align256(rows * 2 * sizeof(int32_t)) + sa::sel_workspace_bytes(v, q_len);
+  return align256(rows * ((size_t)v.prefix_len + top_k) * sizeof(int32_t)) + index_topk_bytes(v, q_len, top_k);
+}
+
+}  // namespace
+
+size_t sparse_attn_prefill_fused_workspace_size(const sa_paged_kv* kv, int32_t num_q_heads,
+                                                int32_t q_len, int32_t q_tail, int32_t top_k,
+                                                int32_t path) {
+  sa::KvView v;
+  if (check_kv(kv, NEED_KV | NEED_IDX, &v) != SA_OK || q_len < 1 || top_k < 1) return 0;
+  if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0 || q_tail < q_len) return 0;
+  if (path != SA_PREFILL_AUTO && path != SA_PREFILL_GATHER && path != SA_PREFILL_MASKED) return 0;
+  const int32_t chosen = fused_path(v, num_q_heads, q_len, q_tail, top_k, path);
+  return chosen < 0 ? 0 : fused_bytes(v, q_len, top_k, chosen);
+}
+
+int32_t sparse_attn_prefill_fused_choice(const sa_paged_kv* kv, int32_t num_q_heads, int32_t q_len,
+                                         int32_t q_tail, int32_t top_k) {
+  sa::KvView v;
+  if (check_kv(kv, NEED_KV | NEED_IDX, &v) != SA_OK || q_len < 1 || top_k < 1) return -1;
+  if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0 || q_tail < q_len) return -1;
+  return fused_path(v, num_q_heads, q_len, q_tail, top_k, SA_PREFILL_AUTO);
+}
+
+int32_t sparse_attn_prefill_fused(const sa_paged_kv* kv, const uint16_t* q, const int8_t* q_idx,
+                                  int32_t num_q_heads, int32_t q_len, int32_t q_tail,
+                                  int32_t top_k, float sm_scale, int32_t path, void* workspace,
+                                  size_t workspace_bytes, uint16_t* out, float* lse, void* stream) {
+  sa::KvView v;
+  int32_t st = check_kv(kv, NEED_KV | NEED_IDX, &v);
+  if (st != SA_OK) return st;
+  if ((st = check_block(v, q_len, q_tail)) != SA_OK) return st;
+  if (q == nullptr || q_idx == nullptr || out == nullptr) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(q_idx) || !aligned16(out) || (lse != nullptr && !aligned16(lse)))
+    return SA_ERR_ALIGN;
+  if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0) return SA_ERR_SHAPE;
+  if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return SA_ERR_SHAPE;
+  if (top_k < 1 || (int64_t)top_k + v.prefix_len > (1 << 30)) return SA_ERR_SHAPE;
+  if (path != SA_PREFILL_AUTO && path != SA_PREFILL_GATHER && path != SA_PREFILL_MASKED)
+    return SA_ERR_SHAPE;
+  const int32_t chosen = fused_path(v, num_q_heads, q_len, q_tail, top_k, path);
+  if (chosen < 0) return SA_ERR_UNSUPPORTED;
+  const size_t need = fused_bytes(v, q_len, top_k, chosen);
+  if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SA_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  const size_t rows = (size_t)v.batch * q_len * v.num_idx_heads;
+  if (chosen == SA_PREFILL_MASKED) {
+    int32_t* thr = reinterpret_cast<int32_t*>(base);
+    uint64_t* sel = reinterpret_cast<uint64_t*>(base + align256(rows * 2 * sizeof(int32_t)));
+    if (sa::launch_sel_thresh(v, q_idx, q_len, q_tail, top_k, thr, sel, s) != hipSuccess) return SA_ERR_HIP;
+    return hip_status(sa::launch_attn_masked_records(v, q, num_q_heads, q_len, q_tail, sm_scale, sel,
+                                                     out, lse, s));
+  }
+  const int32_t width = v.prefix_len + top_k;
+  int32_t* lists = reinterpret_cast<int32_t*>(base);
+  void* inner = base + align256(rows * (size_t)width * sizeof(int32_t));
+  if ((st = index_topk_run(v, q_idx, q_len, q_tail, top_k, lists, inner, s)) != SA_OK) return st;
+  return hip_status(sa::launch_attn_sparse_mfma(v, q, num_q_heads, q_len, q_tail, lists, width,
+                                                sm_scale, out, lse, s));
+}
+
 size_t sparse_attn_prefill_masked_workspace_size(const sa_paged_kv* kv, int32_t q_len) {
   sa::KvView v;
   if (check_kv(kv, 0, &v) != SA_OK || q_len < 1) return 0;

@@ -616,4 +616,14 @@ hipError_t launch_attn_masked(const KvView& kv, const uint16_t* q, int num_q_hea
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_attn_masked_records(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
+                                      int q_tail, float sm_scale, const uint64_t* sel, uint16_t* out,
+                                      float* lse, hipStream_t stream) {
+  if (kv.head_dim == 128)
+    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, stream);
+  if (kv.head_dim == 64)
+    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace sa

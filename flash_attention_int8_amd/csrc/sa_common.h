@@ -181,4 +181,13 @@ size_t sel_workspace_bytes(const KvView& kv, int q_len);
 hipError_t launch_attn_masked(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                               int q_tail, const int32_t* indices, int index_width, float sm_scale,
                               void* ws, uint16_t* out, float* lse, hipStream_t stream);
+// The masked-dense attention on selection masks already in `sel` (sel_workspace_bytes).
+hipError_t launch_attn_masked_records(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
+                                      int q_tail, float sm_scale, const uint64_t* sel, uint16_t* out,
+                                      float* lse, hipStream_t stream);
+// Per-row selection thresholds (tau, t_cut) from recomputed indexer scores, and optionally the
+// masked-dense attention's selection masks written from them (sel: sel_workspace_bytes or NULL).
+bool sel_thresh_applies(const KvView& kv);
+hipError_t launch_sel_thresh(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail, int top_k,
+                             int32_t* thresholds, uint64_t* sel, hipStream_t stream);
 }  // namespace sa

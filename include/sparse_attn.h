@@ -211,6 +211,55 @@ int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_
                                 void* stream);
 
 /*
+ * Per-row selection thresholds ([DSA-page] §2.1): the top-K of every (b, i, gi) row as two
+ * numbers instead of an index list. With C the row's candidates (see Selection above), tau
+ * the K-th largest indexer score among them and t_cut the largest token scoring tau that the
+ * lower-index rule still takes, a key t of C is selected exactly when
+ *     s(t) > tau   or   (s(t) == tau and t <= t_cut).
+ * Rows with at most top_k candidates take all of them (tau = INT32_MIN, t_cut = INT32_MAX);
+ * t_cut = INT32_MAX also when every candidate scoring tau is taken.
+ *   q_idx       int8  [batch][q_len][num_idx_heads][idx_dim]
+ *   thresholds  int32 [batch][q_len][num_idx_heads][2]   (tau, t_cut)
+ * Keys on pages missing from the table are not candidates. Requires max_seq_len <= 131072
+ * (SA_ERR_UNSUPPORTED otherwise). No workspace.
+ */
+int32_t sparse_attn_select_thresholds(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_len,
+                                      int32_t q_tail, int32_t top_k, int32_t* thresholds,
+                                      void* stream);
+
+/*
+ * Sparse prefill in one call ([DSA-page] §2.3: prefill fuses index selection, the gather of the
+ * selected keys and attention): indexer, top-K selection and attention of a block of queries,
+ * the result of sparse_attn_index_topk followed by sparse_attn_fwd_prefill on its lists.
+ *   q, out, lse  as for sparse_attn_fwd_prefill;  q_idx as for sparse_attn_index_topk
+ * Two ways to compute it, chosen by `path`:
+ *   SA_PREFILL_MASKED  no index lists: sparse_attn_select_thresholds' (tau, t_cut) per row, the
+ *                      dense kernel's selection masks written from indexer scores recomputed
+ *                      on the matrix units, then attention over every causal key with the
+ *                      unselected ones masked. Cost follows the causal length.
+ *   SA_PREFILL_GATHER  index lists (sparse_attn_index_topk) and attention over gathered rows.
+ *                      Cost follows top_k.
+ *   SA_PREFILL_AUTO    masked when top_k is at least 1/16 of the block's mean candidate count
+ *                      (the measured ratio of a gathered row's cost to a dense key's) and
+ *                      q_len >= 64; gathered otherwise. sparse_attn_prefill_fused_choice tells
+ *                      which path AUTO takes (or -1 if none applies).
+ * The masked path needs max_seq_len <= 131072; the gathered one a group size H_q/H_kv in
+ * {1, 2, 4, 8}; a forced path that does not apply returns SA_ERR_UNSUPPORTED.
+ * workspace: sparse_attn_prefill_fused_workspace_size(kv, num_q_heads, q_len, q_tail, top_k,
+ * path) bytes of device memory (0 when no path applies); its contents on entry do not matter.
+ */
+enum sa_prefill_path { SA_PREFILL_AUTO = 0, SA_PREFILL_GATHER = 1, SA_PREFILL_MASKED = 2 };
+size_t sparse_attn_prefill_fused_workspace_size(const sa_paged_kv* kv, int32_t num_q_heads,
+                                                int32_t q_len, int32_t q_tail, int32_t top_k,
+                                                int32_t path);
+int32_t sparse_attn_prefill_fused_choice(const sa_paged_kv* kv, int32_t num_q_heads, int32_t q_len,
+                                         int32_t q_tail, int32_t top_k);
+int32_t sparse_attn_prefill_fused(const sa_paged_kv* kv, const uint16_t* q, const int8_t* q_idx,
+                                  int32_t num_q_heads, int32_t q_len, int32_t q_tail,
+                                  int32_t top_k, float sm_scale, int32_t path, void* workspace,
+                                  size_t workspace_bytes, uint16_t* out, float* lse, void* stream);
+
+/*
  * Sparse prefill on dense matrix tiles ([DSA-page] §2.3, prefill): the result of
  * sparse_attn_fwd_prefill with the same index lists, computed by the dense causal kernel
  * over every key 0..pos with each key that is not in the query's list masked out of the

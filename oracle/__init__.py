@@ -34,6 +34,9 @@ from .dsa import (  # noqa: F401
     index_scores,
     index_scores_many,
     topk_select,
+    selection_thresholds,
+    INT32_MIN,
+    INT32_MAX,
     index_list,
     hybrid_index_list,
     attend,

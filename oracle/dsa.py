@@ -26,7 +26,8 @@ Parity pins (tests/test_oracle.py): index_scores against a pure-Python integer l
 the int8 extreme closed form; index_scores_many against the same loop and extremes (the
 -128 corner included) and row by row against index_scores; attend_causal_many against
 closed forms (constant V, a query at position 0 seeing only key 0) and per token against
-dense_query; topk_select against a brute-force full sort and the order
+dense_query; selection_thresholds by rebuilding the kept set from (tau, t_cut) and comparing it
+with a brute-force full sort, and a hand-worked case; topk_select against a brute-force full sort and the order
 invariants; index_list against the prefix rule and a hand-worked golden case; attend
 against closed forms (single key, constant V, identical keys, one-hot V rows giving the
 probabilities), scipy's logsumexp, and a full-matrix masked softmax for the dense case;
@@ -191,6 +192,27 @@ def topk_select(scores, t, k: int) -> np.ndarray:
     keep[above] = True
     keep[at_tau] = True
     return t[keep]
+
+
+INT32_MIN, INT32_MAX = -(1 << 31), (1 << 31) - 1
+
+
+def selection_thresholds(scores, t, k: int):
+    """The selection of topk_select written as two numbers (tau, t_cut): tau is the smallest
+    kept score (the K-th largest) and t_cut the largest kept token scoring tau, so that a
+    candidate is kept exactly when its score exceeds tau, or equals tau at a token <= t_cut.
+    With K or fewer candidates every one is kept: (INT32_MIN, INT32_MAX). t_cut is INT32_MAX
+    as well when every candidate scoring tau is kept."""
+    scores = np.asarray(scores, dtype=np.int64)
+    t = np.asarray(t, dtype=np.int64)
+    if scores.shape[0] <= k:
+        return INT32_MIN, INT32_MAX
+    kept = np.isin(t, topk_select(scores, t, k))
+    tau = int(scores[kept].min())
+    at_tau = scores == tau
+    if np.all(kept[at_tau]):
+        return tau, INT32_MAX
+    return tau, int(t[kept & at_tau].max())
 
 
 def index_list(pos: int, prefix_len: int, top_k: int, width: int, score_fn) -> np.ndarray:

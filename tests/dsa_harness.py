@@ -58,15 +58,19 @@ class GpuRun:
     def __init__(self):
         self.scores = []       # list of (q0, scores chunk)
         self.indices = None
+        self.thresholds = None
         self.out = None
         self.lse = None
 
 
 def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
-            keep_scores: bool = False, fused: bool = False, masked: bool = False) -> GpuRun:
+            keep_scores: bool = False, fused: bool = False, masked: bool = False,
+            prefill_path: Optional[int] = None, thresholds: bool = False) -> GpuRun:
     """The whole path on the device: index -> top-K -> attention (or dense attention).
     fused=True selects with sparse_attn_index_topk instead of index then topk; masked=True
-    runs the prefill attention on masked dense tiles (sparse_attn_fwd_prefill_masked)."""
+    runs the prefill attention on masked dense tiles (sparse_attn_fwd_prefill_masked);
+    prefill_path runs each prefill block through sparse_attn_prefill_fused on that path (no
+    lists come back); thresholds=True also keeps sparse_attn_select_thresholds' (tau, t_cut)."""
     w = inp.workload
     kv = make_kv(inp)
     r = GpuRun()
@@ -90,13 +94,25 @@ def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
         return r
     q_chunk = q_chunk or S
     T = max(inp.seq_lens_host)
-    r.indices = torch.empty((B, S, inp.num_idx_heads, w.index_width), dtype=torch.int32, device=inp.q.device)
+    if prefill_path is None:
+        r.indices = torch.empty((B, S, inp.num_idx_heads, w.index_width), dtype=torch.int32,
+                                device=inp.q.device)
+    if thresholds:
+        r.thresholds = torch.empty((B, S, inp.num_idx_heads, 2), dtype=torch.int32, device=inp.q.device)
     r.out = torch.empty_like(inp.q)
     r.lse = torch.empty((B, S, w.num_q_heads), dtype=torch.float32, device=inp.q.device)
     for q0 in range(0, S, q_chunk):
         c = min(q_chunk, S - q0)
         tail = S - q0
         qi = inp.q_idx[:, q0:q0 + c].contiguous()
+        if thresholds:
+            r.thresholds[:, q0:q0 + c] = fa.select_thresholds(kv, qi, c, tail, w.top_k)
+        if prefill_path is not None:
+            qc = inp.q[:, q0:q0 + c].contiguous()
+            out, lse = fa.prefill_fused(kv, qc, qi, tail, w.top_k, path=prefill_path)
+            r.out[:, q0:q0 + c] = out
+            r.lse[:, q0:q0 + c] = lse
+            continue
         if fused:
             idx = fa.index_topk(kv, qi, c, tail, w.top_k)
         else:
@@ -153,6 +169,11 @@ class OracleView:
                                 page_size=w.page_size, kv_head=g, idx_head=gi, pos=pos,
                                 prefix_len=w.prefix_len, top_k=w.top_k, sm_scale=scale)
 
+    def thresholds(self, b: int, i: int, gi: int):
+        """Oracle (tau, t_cut) of the selection of (b, i, gi)."""
+        c, sc = self.scores_row(b, i, gi)
+        return oracle.selection_thresholds(sc, c, self.w.top_k)
+
     def scores_row(self, b: int, i: int, gi: int) -> np.ndarray:
         """Oracle indexer scores of every candidate key of (b, i, gi), with their tokens."""
         w = self.w
@@ -173,10 +194,15 @@ def compare_rows(gpu: GpuRun, ov: OracleView, rows, check_lse: bool = True):
     errs, lse_errs = [], []
     for (b, i, g) in rows:
         idx, o, lse = ov.query(b, i, g)
-        if idx is not None:
+        if idx is not None and gpu.indices is not None:
             gi = 0 if ov.inp.num_idx_heads == 1 else g
             got = gpu.indices[b, i, gi].cpu().numpy()
             assert np.array_equal(got, idx), (b, i, g, got[:16], idx[:16])
+        if idx is not None and gpu.thresholds is not None:
+            gi = 0 if ov.inp.num_idx_heads == 1 else g
+            want = ov.thresholds(b, i, gi)
+            got = tuple(int(x) for x in gpu.thresholds[b, i, gi].cpu())
+            assert got == want, (b, i, g, got, want)
         og = f64(gpu.out[b, i, g * G:(g + 1) * G])
         errs.append(np.abs(og - o).ravel())
         if check_lse and gpu.lse is not None:
@@ -228,13 +254,16 @@ def oracle_block(ov: OracleView, b: int, rows, g: int):
     sc = oracle.index_scores_many(qi, kidx)
     width = w.prefix_len + w.top_k
     lists = np.empty((len(rows), width), dtype=np.int64)
+    thr = np.empty((len(rows), 2), dtype=np.int64)
     o = np.empty((len(rows), G, w.head_dim))
     lse = np.empty((len(rows), G))
     for n, p in enumerate(pos):
         lists[n] = oracle.index_list(int(p), w.prefix_len, w.top_k, width, lambda c, n=n: sc[n, c])
+        c = oracle.candidate_keys(int(p), w.prefix_len)
+        thr[n] = oracle.selection_thresholds(sc[n, c], c, w.top_k)
         keys = lists[n][lists[n] >= 0]
         o[n], lse[n] = oracle.attend(qd[n], kd[keys], vd[keys], scale)
-    return lists, o, lse
+    return (lists, thr), o, lse
 
 
 def compare_block(gpu: GpuRun, ov: OracleView, b: int, rows, g: int, want=None):
@@ -243,13 +272,19 @@ def compare_block(gpu: GpuRun, ov: OracleView, b: int, rows, g: int, want=None):
     w = ov.w
     G = w.group
     want = want if want is not None else oracle_block(ov, b, rows, g)
-    lists, o, lse = want
+    sel_ref, o, lse = want
     sel = torch.as_tensor([int(i) for i in rows], device=gpu.out.device, dtype=torch.long)
-    if lists is not None:
-        gi = 0 if ov.inp.num_idx_heads == 1 else g
+    gi = 0 if ov.inp.num_idx_heads == 1 else g
+    if sel_ref is not None and gpu.indices is not None:
+        lists = sel_ref[0]
         got = gpu.indices[b].index_select(0, sel)[:, gi].cpu().numpy()
         bad = np.nonzero(np.any(got != lists, axis=1))[0]
         assert bad.size == 0, (b, g, [int(rows[k]) for k in bad[:8]], got[bad[0]][:16], lists[bad[0]][:16])
+    if sel_ref is not None and gpu.thresholds is not None:
+        thr = sel_ref[1]
+        got = gpu.thresholds[b].index_select(0, sel)[:, gi].cpu().numpy().astype(np.int64)
+        bad = np.nonzero(np.any(got != thr, axis=1))[0]
+        assert bad.size == 0, (b, g, [int(rows[k]) for k in bad[:8]], got[bad[:4]], thr[bad[:4]])
     og = f64(gpu.out[b].index_select(0, sel)[:, g * G:(g + 1) * G])
     e = np.abs(og - o)
     le = 0.0

@@ -370,6 +370,84 @@ def test_decode_noalloc_buffer_size(lib):
     assert lib.sparse_attn_decode_workspace_size(ctypes.byref(d64), 32, 4096, 64) > cap
 
 
+def call_thresholds(lib, d, q_idx=A, q_len=16, q_tail=16, k=64, thr=A):
+    return lib.sparse_attn_select_thresholds(None if d is None else ctypes.byref(d), q_idx, q_len, q_tail,
+                                             k, thr, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(d=None), fa.SA_ERR_NULL),
+    (dict(d=desc(kidx_pool=None)), fa.SA_ERR_NULL),
+    (dict(q_idx=None), fa.SA_ERR_NULL),
+    (dict(thr=None), fa.SA_ERR_NULL),
+    (dict(thr=A + 4), fa.SA_ERR_ALIGN),
+    (dict(k=0), fa.SA_ERR_SHAPE),
+    (dict(q_len=17, q_tail=16), fa.SA_ERR_SHAPE),
+    (dict(d=desc(idx_dim=48)), fa.SA_ERR_UNSUPPORTED),
+    # more than 131072 tokens: the per-tile tie counts would not fit the workgroup's LDS
+    (dict(d=desc(max_pages_per_seq=4096, max_seq_len=131073, num_pages=8192)), fa.SA_ERR_UNSUPPORTED),
+])
+def test_select_thresholds_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_thresholds(lib, d, **case) == code
+
+
+def call_fused(lib, d, q=A, q_idx=A + 0x100, hq=32, q_len=16, q_tail=16, k=64, scale=0.1, path=0,
+               ws=A, ws_bytes=1 << 34, out=A, lse=None):
+    return lib.sparse_attn_prefill_fused(None if d is None else ctypes.byref(d), q, q_idx, hq, q_len,
+                                         q_tail, k, scale, path, ws, ws_bytes, out, lse, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(d=None), fa.SA_ERR_NULL),
+    (dict(d=desc(k_pool=None)), fa.SA_ERR_NULL),
+    (dict(d=desc(kidx_pool=None)), fa.SA_ERR_NULL),
+    (dict(q=None), fa.SA_ERR_NULL),
+    (dict(q_idx=None), fa.SA_ERR_NULL),
+    (dict(out=None), fa.SA_ERR_NULL),
+    (dict(q=A + 2), fa.SA_ERR_ALIGN),
+    (dict(hq=30), fa.SA_ERR_SHAPE),
+    (dict(k=0), fa.SA_ERR_SHAPE),
+    (dict(scale=0.0), fa.SA_ERR_SHAPE),
+    (dict(path=3), fa.SA_ERR_SHAPE),
+    (dict(ws=None), fa.SA_ERR_WORKSPACE),
+    (dict(ws_bytes=64), fa.SA_ERR_WORKSPACE),
+    (dict(ws=A + 8), fa.SA_ERR_ALIGN),
+    (dict(hq=24, path=fa.SA_PREFILL_GATHER), fa.SA_ERR_UNSUPPORTED),    # group of 3: no gathered kernel
+    (dict(d=desc(max_pages_per_seq=4096, max_seq_len=131073, num_pages=8192), path=fa.SA_PREFILL_MASKED),
+     fa.SA_ERR_UNSUPPORTED),
+])
+def test_prefill_fused_validation(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_fused(lib, d, **case) == code
+
+
+def test_prefill_fused_dispatch_and_workspace(lib):
+    d = desc(max_pages_per_seq=512, max_seq_len=32768, num_pages=1024)
+    ch = lambda q_len, q_tail, k, hq=32: lib.sparse_attn_prefill_fused_choice(ctypes.byref(d), hq, q_len, q_tail, k)
+    # a 2048-query block of a 32K prefill with top-2048: masked tiles at the start and the end
+    assert ch(2048, 32768, 2048) == fa.SA_PREFILL_MASKED
+    assert ch(2048, 2048, 2048) == fa.SA_PREFILL_MASKED
+    # a small top-K far into a long context, or a short block: gathered rows
+    assert ch(2048, 2048, 256) == fa.SA_PREFILL_GATHER
+    assert ch(16, 16, 2048) == fa.SA_PREFILL_GATHER
+    # a group of 3 has no gathered kernel: masked whatever the density
+    assert ch(16, 16, 64, hq=24) == fa.SA_PREFILL_MASKED
+    # more than 131072 tokens: no masked path
+    dl = desc(max_pages_per_seq=4096, max_seq_len=200000, num_pages=8192)
+    assert lib.sparse_attn_prefill_fused_choice(ctypes.byref(dl), 32, 2048, 2048, 2048) == fa.SA_PREFILL_GATHER
+    ws = lambda q_len, q_tail, k, path: lib.sparse_attn_prefill_fused_workspace_size(ctypes.byref(d), 32, q_len,
+                                                                                     q_tail, k, path)
+    rows = 2 * 2048 * 8
+    masked = ws(2048, 2048, 2048, fa.SA_PREFILL_MASKED)
+    assert masked >= rows * 8 + lib.sparse_attn_prefill_masked_workspace_size(ctypes.byref(d), 2048)
+    assert ws(2048, 2048, 2048, fa.SA_PREFILL_GATHER) >= rows * 2048 * 4
+    assert ws(2048, 2048, 2048, fa.SA_PREFILL_AUTO) == masked
+    assert ws(2048, 2048, 2048, 9) == 0   # not a path
+
+
 def call_index_topk(lib, d, q_idx=A, q_len=1, q_tail=1, k=64, idx=A, ws=A, ws_bytes=1 << 34):
     return lib.sparse_attn_index_topk(ctypes.byref(d), q_idx, q_len, q_tail, k, idx, ws, ws_bytes, None)
 

@@ -138,6 +138,36 @@ def test_topk_invariants_large():
     assert t[eq & chosen].max() < t[eq & ~chosen].min()
 
 
+def _kept_by_thresholds(scores, t, tau, t_cut):
+    scores, t = np.asarray(scores), np.asarray(t)
+    return t[(scores > tau) | ((scores == tau) & (t <= t_cut))]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_selection_thresholds_rebuild_the_brute_force_top_k(seed):
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 60))
+    t = np.sort(rng.choice(1000, size=n, replace=False))
+    scores = rng.integers(-3, 4, size=n) * int(rng.choice([1, 1000]))   # heavy ties
+    k = int(rng.integers(1, 70))
+    tau, t_cut = oracle.selection_thresholds(scores, t, k)
+    assert list(_kept_by_thresholds(scores, t, tau, t_cut)) == list(_brute_topk(scores, t, k))
+
+
+def test_selection_thresholds_hand_worked():
+    t = np.array([3, 5, 8, 9, 12, 20])
+    s = np.array([7, 4, 4, 9, 4, 1])
+    # K = 3: 9 (t9), 7 (t3), then the lowest token of the three 4s (t5): tau 4, cut at 5
+    assert oracle.selection_thresholds(s, t, 3) == (4, 5)
+    # K = 5: all three 4s are kept: no cut
+    assert oracle.selection_thresholds(s, t, 5) == (4, oracle.INT32_MAX)
+    # K = 4: two of the three 4s, cut at 8
+    assert oracle.selection_thresholds(s, t, 4) == (4, 8)
+    # K >= candidates: everything
+    assert oracle.selection_thresholds(s, t, 6) == (oracle.INT32_MIN, oracle.INT32_MAX)
+    assert oracle.selection_thresholds(s[:0], t[:0], 1) == (oracle.INT32_MIN, oracle.INT32_MAX)
+
+
 def test_topk_all_equal_takes_lowest_indices():
     t = np.arange(5, 105)
     assert list(oracle.topk_select(np.zeros(100, np.int64), t, 7)) == list(range(5, 12))

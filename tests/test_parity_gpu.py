@@ -583,6 +583,82 @@ def test_lse_matches_definition_dense():
     assert_close(compare_rows(gpu, OracleView(inp), rows))
 
 
+# ------------------------------------------------------------------ fused prefill (thresholds, dispatch)
+
+SPARSE_SMALL = [n for n, (w, _) in SMALL.items() if not w.dense]
+
+
+@pytest.mark.parametrize("name", SPARSE_SMALL)
+def test_thresholds_and_fused_masked_every_row(name):
+    """sparse_attn_select_thresholds equals the oracle's (tau, t_cut) on every row, bit for bit,
+    and sparse_attn_prefill_fused on the masked path (no lists: masks from recomputed scores)
+    matches the oracle on every row."""
+    w, kw = SMALL[name]
+    _banner(f"thresholds + fused masked prefill {name}: {w}")
+    inp = make_inputs(w, seed=11, device="cpu", **kw).to(DEV)
+    chunk = 96 if w.q_len > 200 else None
+    gpu = run_gpu(inp, q_chunk=chunk, prefill_path=fa.SA_PREFILL_MASKED, thresholds=True)
+    torch.cuda.synchronize()
+    assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
+
+
+@pytest.mark.parametrize("path", [fa.SA_PREFILL_GATHER, fa.SA_PREFILL_AUTO])
+@pytest.mark.parametrize("name", SPARSE_SMALL)
+def test_fused_prefill_other_paths_every_row(name, path):
+    w, kw = SMALL[name]
+    _banner(f"fused prefill path={path} {name}")
+    inp = make_inputs(w, seed=11, device="cpu", **kw).to(DEV)
+    gpu = run_gpu(inp, q_chunk=96 if w.q_len > 200 else None, prefill_path=path)
+    torch.cuda.synchronize()
+    assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
+
+
+@pytest.mark.parametrize("top_k,want", [(64, fa.SA_PREFILL_GATHER), (1024, fa.SA_PREFILL_MASKED)])
+def test_fused_prefill_dispatch_both_sides(top_k, want):
+    """A 256-query block at the end of an 8192-token sequence (mean ~8064 candidates): top-64
+    is a small share of the causal keys (gathered rows), top-1024 a large one (masked dense
+    tiles). AUTO takes the expected path, and both paths match the oracle on sampled rows
+    and every KV group; thresholds bit-exact."""
+    w = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=8192, q_len=256, top_k=top_k, prefix_len=4)
+    _banner(f"fused prefill dispatch top_k={top_k}")
+    inp = make_inputs(w, seed=41, device=DEV, seq_lens=[8192, 7000])
+    kv = make_kv(inp)
+    assert fa.sparse_attn_prefill_fused_choice(kv, w.num_q_heads, w.q_len, w.q_len, top_k) == want
+    rows = [(b, i, g) for b in range(2) for i in (0, 1, 77, 128, 200, 254, 255) for g in range(2)]
+    ov = OracleView(inp)
+    for path in (fa.SA_PREFILL_AUTO, fa.SA_PREFILL_GATHER, fa.SA_PREFILL_MASKED):
+        gpu = run_gpu(inp, prefill_path=path, thresholds=True)
+        torch.cuda.synchronize()
+        assert_close(compare_rows(gpu, ov, rows))
+
+
+@pytest.mark.parametrize("values,seq_len", [((0,), 1500), ((-1, 1), 1500), ((-2, 0, 3), 700)])
+def test_thresholds_many_equal_scores(values, seq_len):
+    """Indexer values from tiny sets: every score equal (all keys of a row share one histogram
+    bin, more than the selection's LDS lists hold, so it takes its histogram passes), or a few
+    distinct scores with long runs of ties. Thresholds bit-exact and the masked fused prefill
+    within the bar on every row."""
+    w = W(batch=1, num_q_heads=8, num_kv_heads=2, seq_len=seq_len, q_len=96, top_k=100, prefix_len=3)
+    _banner(f"thresholds, indexer values {values}, T={seq_len}")
+    inp = make_inputs(w, seed=43, device="cpu", idx_values=values).to(DEV)
+    gpu = run_gpu(inp, prefill_path=fa.SA_PREFILL_MASKED, thresholds=True)
+    torch.cuda.synchronize()
+    assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
+
+
+def test_fused_prefill_middle_blocks_ragged():
+    """Blocks of 160 queries in the middle of sequences of different lengths, with a prefix and
+    spare pages: every block through the masked path and the gathered path, every row."""
+    w = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=900, q_len=800, top_k=96, prefix_len=9)
+    _banner("fused prefill, middle blocks")
+    inp = make_inputs(w, seed=42, device="cpu", seq_lens=[900, 820], spare_pages=4).to(DEV)
+    ov = OracleView(inp)
+    for path in (fa.SA_PREFILL_MASKED, fa.SA_PREFILL_GATHER):
+        gpu = run_gpu(inp, q_chunk=160, prefill_path=path, thresholds=True)
+        torch.cuda.synchronize()
+        assert_close(compare_rows(gpu, ov, all_rows(inp)))
+
+
 # ------------------------------------------------------------------ int8 minimum, missing pages
 
 def _saturate(inp, rng, q_frac, key_frac):
@@ -620,11 +696,13 @@ def test_int8_minimum_ties_at_largest_score(d_idx):
     inp = inp.to(DEV)
     two = run_gpu(inp)
     fused = run_gpu(inp, fused=True, masked=True)
+    thr = run_gpu(inp, prefill_path=fa.SA_PREFILL_MASKED, thresholds=True)
     torch.cuda.synchronize()
     assert torch.equal(fused.indices, two.indices)
     ov = OracleView(inp)
     assert_close(compare_rows(two, ov, all_rows(inp)))
     assert_close(compare_rows(fused, ov, all_rows(inp)))
+    assert_close(compare_rows(thr, ov, all_rows(inp)))
     # decode rows of >= 16384 candidates (the fused decode path), ties at the top spread over
     # every chunk
     wd = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=20000, q_len=1, idx_dim=d_idx, top_k=256)
@@ -773,6 +851,23 @@ def test_full_sparse_prefill_32k_masked():
     torch.cuda.synchronize()
     assert torch.equal(gpu.indices, two.indices)
     del two
+    torch.cuda.synchronize()
+    n = _check_full_prefill(w.name, 4, gpu, inp, lambda b: _rows_32k())
+    assert n == 1152 * 8
+
+
+def test_full_sparse_prefill_32k_fused():
+    """The 32K sparse prefill through sparse_attn_prefill_fused (AUTO: every 2048-query block
+    takes the masked path, no lists), with the thresholds of every block: sampled rows as above,
+    (tau, t_cut) bit-exact and outputs within the bar."""
+    w = CONFIGS["sparse_prefill_32k"]
+    _banner(f"full {w.name}, fused prefill (thresholds, masks from recomputed scores)")
+    inp = make_inputs(w, seed=4, device=DEV)
+    kv = make_kv(inp)
+    for q0 in range(0, w.q_len, 2048):
+        assert fa.sparse_attn_prefill_fused_choice(kv, w.num_q_heads, 2048, w.q_len - q0,
+                                                   w.top_k) == fa.SA_PREFILL_MASKED
+    gpu = run_gpu(inp, q_chunk=2048, prefill_path=fa.SA_PREFILL_AUTO, thresholds=True)
     torch.cuda.synchronize()
     n = _check_full_prefill(w.name, 4, gpu, inp, lambda b: _rows_32k())
     assert n == 1152 * 8
