@@ -46,6 +46,9 @@ def parse():
                     help="select with sparse_attn_index then sparse_attn_topk (score rows in HBM) "
                          "instead of the fused sparse_attn_index_topk")
     ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only the roofline micro-benchmarks (measured ceilings)")
+    ap.add_argument("--no-calibrate", action="store_true")
     ap.add_argument("--sparse-prefill-only", action="store_true",
                     help="run only the 32K sparse prefill measurement once and print its JSON "
                          "(a short program for counter collection)")
@@ -110,49 +113,165 @@ def traffic_for(key: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, w, budget_s=12.0):
-    """The oracle, untuned, on host copies of whole sequences of the decode workload."""
+def _pct(ms):
+    ms = sorted(ms)
+    return {f"p{q}": ms[min(len(ms) - 1, int(round(q / 100 * (len(ms) - 1))))] for q in (10, 50, 90)}
+
+
+def calibrate(fa):
+    """Measured ceilings from the library's micro-benchmarks (sparse_attn_calib_*): a streaming
+    read of 4 GiB, random 256-byte row gathers from a 128 MiB pool (the 32K prefill's K+V pool
+    size; it stays in the Infinity Cache between passes) and from a 4 GiB pool (mostly HBM), and
+    back-to-back bf16 and int8 MFMA. Median of 5 timed runs after a warmup run. The row gathers
+    from the 2 MiB pool bound rows that are reused across queries (they hit in L2), those from
+    the larger pools rows read once."""
+    import torch
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+    big = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+    read_ms = timed(lambda: fa.sparse_attn_calib_read(big, sink, 2048))
+    n_rows = 1 << 21
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    pools = {"2mib": 2 * MIB, "128mib": 128 * MIB, "4gib": 4 << 30}
+    gather = {}
+    for name, size in pools.items():
+        rows = torch.randint(0, size // 256, (n_rows,), generator=g, dtype=torch.int32, device="cuda")
+        gather[name] = n_rows * 256 / (timed(lambda: fa.sparse_attn_calib_gather(big[:size], rows, sink, 4096))
+                                       * 1e-3) / 1e9
+        del rows
+    del big
+    torch.cuda.empty_cache()
+    wgs, iters = 512, 20000
+    bf_ms = timed(lambda: fa.sparse_attn_calib_mfma(0, iters, wgs, sink), reps=3)
+    i8_ms = timed(lambda: fa.sparse_attn_calib_mfma(1, iters, wgs, sink), reps=3)
+    n_mfma = wgs * 4 * iters * 4
+    return {"hbm_read_gbps": (4 << 30) / (read_ms * 1e-3) / 1e9,
+            "row_gather_2mib_gbps": gather["2mib"],
+            "row_gather_128mib_gbps": gather["128mib"],
+            "row_gather_4gib_gbps": gather["4gib"],
+            "mfma_bf16_tflops": n_mfma * 32768 / (bf_ms * 1e-3) / 1e12,
+            "mfma_i8_tops": n_mfma * 65536 / (i8_ms * 1e-3) / 1e12,
+            "how": "sparse_attn_calib_read (4 GiB), sparse_attn_calib_gather (2^21 random 256-byte rows; "
+                   "a 2 MiB pool that every L2 holds, a 128 MiB pool warm in the Infinity Cache, a 4 GiB "
+                   "pool), sparse_attn_calib_mfma "
+                   "(512 workgroups x 4 waves x 80000 back-to-back 32x32 MFMAs); median of 5 (MFMA: 3)"}
+
+
+def _host_cores():
+    from threadpoolctl import threadpool_info
+    cores = len(os.sched_getaffinity(0))
+    blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return cores, blas
+
+
+def cpu_baselines(fa, budget_s=4.0):
+    """The oracle, untuned, on this host for every workload: numpy float64 with BLAS on all the
+    host's cores (the batched oracle functions: exact float64 products for the int8 scores,
+    masked-softmax attention for dense rows). Each workload runs on a bounded sample of its rows
+    (about budget_s of CPU time) and is scaled to its unit; the sample is stated."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_limits
 
     import oracle
+    from synthetic import CONFIGS, make_inputs
+    cores, blas = _host_cores()
+    out = {}
 
-    B, Hkv, G = w.batch, w.num_kv_heads, w.group
-    table = inp.page_table.cpu().numpy()
-    q_bits = inp.q.view(torch.int16).cpu().numpy().view(np.uint16)
-    q_idx = inp.q_idx.cpu().numpy()
-    done, t_total = 0, 0.0
-    host = {}
-    for n in range(64 * B):  # whole sequences, repeated until the time budget is used
-        b = n % B
-        if b not in host:  # host copies of the sequence's pages, in logical order
-            pages = torch.as_tensor(table[b], dtype=torch.long, device=inp.k_pool.device)
-            host[b] = (inp.k_pool[pages].view(torch.int16).cpu().numpy().view(np.uint16),
-                       inp.v_pool[pages].view(torch.int16).cpu().numpy().view(np.uint16),
-                       inp.kidx_pool[pages].cpu().numpy())
-        kp, vp, ip = host[b]
-        local = np.arange(kp.shape[0])
-        pos = w.seq_len - 1
-        with threadpool_limits(limits=1):
-            t0 = time.perf_counter()
-            for g in range(Hkv):
-                oracle.dsa_query(q_bits=q_bits[b, 0, g * G:(g + 1) * G], q_idx_vec=q_idx[b, 0, g],
-                                 kidx_pool=ip, k_pool=kp, v_pool=vp, page_table_row=local,
-                                 page_size=w.page_size, kv_head=g, idx_head=g, pos=pos,
-                                 prefix_len=w.prefix_len, top_k=w.top_k,
-                                 sm_scale=1 / math.sqrt(w.head_dim))
-            t_total += time.perf_counter() - t0
-        done += 1
-        if t_total >= budget_s:
-            break
-    return {"value": done / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} sequence-steps (the {B} sequences of the 128K decode step, cycled) "
-                      f"with all {Hkv} KV groups each: scores over {w.seq_len} keys, top-{w.top_k}, "
-                      f"attention; fp64 numpy on one thread, {t_total:.1f} s"}
+    def host(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def logical(pool, table_row, ps, head, T):
+        t = torch.arange(T, device=pool.device)
+        pages = torch.as_tensor(table_row, device=pool.device).long()[t // ps]
+        return pool[pages, head, t % ps]
+
+    def run_rows(w, inp, b, g, rows, T):
+        """Oracle time for query rows of (b, g): index lists (sparse) and attention. The rows of
+        the sequence are copied to host memory (bf16 bits, int8) before the clock starts."""
+        G = w.group
+        scale = 1 / math.sqrt(w.head_dim)
+        table = inp.page_table[b].cpu().numpy()
+        kb = host(logical(inp.k_pool, table, w.page_size, g, T))
+        vb = host(logical(inp.v_pool, table, w.page_size, g, T))
+        qb = host(inp.q[b, rows][:, g * G:(g + 1) * G])
+        pos = np.array([oracle.query_position(T, w.q_len, i) for i in rows])
+        ki = None if w.dense else logical(inp.kidx_pool, table, w.page_size, g, T).cpu().numpy()
+        qi = None if w.dense else inp.q_idx[b, rows, g].cpu().numpy()
+        t0 = time.perf_counter()
+        qd = oracle.bf16_to_f64(qb)
+        if w.dense:
+            oracle.attend_causal_many(qd, oracle.bf16_to_f64(kb), oracle.bf16_to_f64(vb), pos, scale)
+        else:
+            sc = oracle.index_scores_many(qi, ki)
+            width = w.prefix_len + w.top_k
+            for n, p in enumerate(pos):
+                lst = oracle.index_list(int(p), w.prefix_len, w.top_k, width, lambda c, n=n: sc[n, c])
+                keys = lst[lst >= 0]
+                oracle.attend(qd[n], oracle.bf16_to_f64(kb[keys]), oracle.bf16_to_f64(vb[keys]), scale)
+        return time.perf_counter() - t0
+
+    def sample(name, seed, rows_fn, unit_fn, desc, max_visits=4096):
+        """(sequence, group) pairs visited in turn, again and again, until budget_s is spent."""
+        w = CONFIGS[name]
+        inp = make_inputs(w, seed=seed, device="cuda")
+        spent, units, n = 0.0, 0.0, 0
+        pairs = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+        while spent < budget_s and n < max_visits:
+            b, g = pairs[n % len(pairs)]
+            rows = rows_fn(w, n)
+            spent += run_rows(w, inp, b, g, rows, inp.seq_lens_host[b])
+            units += unit_fn(w, rows)
+            n += 1
+        del inp
+        torch.cuda.empty_cache()
+        return units / spent, spent, n, desc
+    rng = np.random.default_rng(0)
+    # decode: one (sequence, group) row is 1/H_kv of a token
+    dec_rows = lambda w, n: [0]
+    dec_unit = lambda w, rows: 1.0 / w.num_kv_heads
+    for name, seed, key in (("sparse_decode_128k", 3, "sparse_decode_128k"),
+                            ("sparse_decode_1m_prefix", 5, "sparse_decode_1m_prefix")):
+        v, spent, n, _ = sample(name, seed, dec_rows, dec_unit, "")
+        out[key] = {"value": v, "unit": "tokens/s", "cores": cores, "blas_threads": blas, "kind": "oracle",
+                    "sample": f"{n} (sequence, KV group) rows: scores over the whole context, top-K, "
+                              f"attention; {spent:.1f} s"}
+    # prefill: TFLOP/s of the attention it computes (dense: every causal pair; sparse: the
+    # selected keys), on 32 seeded query rows per (sequence, group) visited
+    def pf_rows(w, n):
+        return sorted(rng.choice(w.q_len, size=32, replace=False).tolist())
+
+    def pf_flop(w, rows):
+        G, d = w.group, w.head_dim
+        sel = [i + 1 if w.dense else max(0, min(w.top_k, i + 1 - w.prefix_len)) + min(w.prefix_len, i + 1)
+               for i in rows]
+        return 4.0 * G * d * sum(sel) / 1e12
+    for name, seed in (("dense_prefill_8k", 2), ("sparse_prefill_32k", 4), ("tiny_sparse_prefill", 1)):
+        v, spent, n, _ = sample(name, seed, pf_rows, pf_flop, "")
+        w = CONFIGS[name]
+        out[name] = {"value": v, "unit": "TFLOP/s", "cores": cores, "blas_threads": blas, "kind": "oracle",
+                     "tokens_per_s": n * 32 / spent / w.num_kv_heads,
+                     "sample": f"{n} (sequence, KV group) pairs x 32 seeded query rows "
+                               f"({'dense causal attention' if name == 'dense_prefill_8k' else 'scores, top-K, attention'}); "
+                               f"{spent:.1f} s"}
+    return out
 
 
 def bench_prefill(fa, reps):
+    """Dense causal prefill (B=4, 32/8 heads, S=8192, d=128): reps calls after a warmup call,
+    events around each call; the mean and p10/p50/p90."""
     import torch
 
     from synthetic import CONFIGS, make_inputs
@@ -168,18 +287,19 @@ def bench_prefill(fa, reps):
         fa.sparse_attn_fwd_prefill(kv, inp.q, w.num_q_heads, w.q_len, w.q_len, None, 0, scale, out, lse)
     run()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
         run()
-    e1.record()
+        b.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    t = [a.elapsed_time(b) for a, b in evs]
+    ms = sum(t) / reps
     flops = 4.0 * w.batch * w.num_q_heads * w.head_dim * w.q_len * (w.q_len + 1) / 2
     del inp, out, lse
     torch.cuda.empty_cache()
-    return {"workload": w.name, "ms": ms, "tflops": flops / ms / 1e9,
-            "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS, "flop": flops}
+    return {"workload": w.name, "ms": ms, "ms_percentiles": _pct(t), "reps": reps,
+            "tflops": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS, "flop": flops}
 
 
 def bench_tiny(fa, reps=50, warmup=10):
@@ -302,12 +422,13 @@ def bench_cache_maintenance(fa, reps=50, warmup=5):
     return res
 
 
-def bench_sparse_prefill(fa, reps, q_chunk=2048):
-    """Whole sparse prefill of 32K tokens (B=1, 32/8 heads, d=128, d_idx=64, top-K=2048): per
-    chunk of q_chunk queries, the fused selection (sparse_attn_index_topk: indexer keys ->
-    exact top-K lists) then attention on masked dense tiles (sparse_attn_fwd_prefill_masked).
-    Separate passes time the two-step selection (sparse_attn_index, then sparse_attn_topk on
-    int32 score rows) and the gathered-row attention (sparse_attn_fwd_prefill with the lists)."""
+def bench_sparse_prefill(fa, reps, q_chunk=2048, calib=None):
+    """Whole sparse prefill of 32K tokens (B=1, 32/8 heads, d=128, d_idx=64, top-K=2048) in
+    blocks of q_chunk queries through sparse_attn_prefill_fused (the automatic path: every block
+    takes the masked dense tiles, selection by per-row thresholds, no index lists): reps whole
+    prefills after a warmup one, events around each, mean and p10/p50/p90. Separate passes time
+    the selection alone (sparse_attn_select_thresholds), the gathered-row path of the same call,
+    and the path through index lists (sparse_attn_index_topk, then the masked attention)."""
     import torch
 
     from synthetic import CONFIGS, make_inputs
@@ -317,86 +438,95 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048):
                     page_table=inp.page_table, seq_lens=inp.seq_lens, max_seq_len=w.seq_len,
                     prefix_len=w.prefix_len)
     S, Hkv, Hq, d = w.q_len, w.num_kv_heads, w.num_q_heads, w.head_dim
-    stride = (w.seq_len + 3) & ~3
-    idx = torch.empty((1, q_chunk, Hkv, w.index_width), dtype=torch.int32, device="cuda")
+    blocks = [(q0, min(q_chunk, S - q0), S - q0) for q0 in range(0, S, q_chunk)]
+    q_idx = [inp.q_idx[:, q0:q0 + n].contiguous() for q0, n, _ in blocks]
     out = torch.empty_like(inp.q)
     lse = torch.empty((1, S, Hq), dtype=torch.float32, device="cuda")
-    q_idx = [inp.q_idx[:, q0:q0 + q_chunk].contiguous() for q0 in range(0, S, q_chunk)]
+    paths = [fa.sparse_attn_prefill_fused_choice(kv, Hq, n, tail, w.top_k) for _, n, tail in blocks]
+    ws_n = max(fa.sparse_attn_prefill_fused_workspace_size(kv, Hq, n, tail, w.top_k, p)
+               for (_, n, tail) in blocks for p in (fa.SA_PREFILL_AUTO, fa.SA_PREFILL_GATHER))
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    thr = torch.empty((1, q_chunk, Hkv, 2), dtype=torch.int32, device="cuda")
+    idx = torch.empty((1, q_chunk, Hkv, w.index_width), dtype=torch.int32, device="cuda")
     fu_n = fa.sparse_attn_index_topk_workspace_size(kv, q_chunk, w.top_k)
-    fu_ws = torch.empty(max(fu_n, 16), dtype=torch.uint8, device="cuda")
-    tk_n = fa.sparse_attn_topk_workspace_size(kv, q_chunk, w.top_k)
-    tk_ws = torch.empty(max(tk_n, 16), dtype=torch.uint8, device="cuda")
     mk_n = fa.sparse_attn_prefill_masked_workspace_size(kv, q_chunk)
-    mk_ws = torch.empty(max(mk_n, 16), dtype=torch.uint8, device="cuda")
     scale = 1 / math.sqrt(d)
-    # the two-step pass keeps its int32 score rows in the fused call's workspace
-    scores = fu_ws[: q_chunk * Hkv * stride * 4].view(torch.int32).view(1, q_chunk, Hkv, stride)
 
-    def run(evs=None, gather=False, two_step=False):
-        for c, q0 in enumerate(range(0, S, q_chunk)):
-            n, tail = min(q_chunk, S - q0), S - q0
-            if evs:
-                evs[c][0].record()
-            if two_step:
-                fa.sparse_attn_index(kv, q_idx[c], n, tail, scores, stride)
-                fa.sparse_attn_topk(kv, scores, stride, n, tail, w.top_k, idx, tk_ws, tk_n)
-            else:
-                fa.sparse_attn_index_topk(kv, q_idx[c], n, tail, w.top_k, idx, fu_ws, fu_n)
-            if evs:
-                evs[c][1].record()
-            if gather:
-                fa.sparse_attn_fwd_prefill(kv, inp.q[:, q0:q0 + n], Hq, n, tail, idx, w.index_width,
-                                           scale, out[:, q0:q0 + n], lse[:, q0:q0 + n])
-            else:
-                fa.sparse_attn_fwd_prefill_masked(kv, inp.q[:, q0:q0 + n], Hq, n, tail, idx,
-                                                  w.index_width, scale, mk_ws, mk_n,
-                                                  out[:, q0:q0 + n], lse[:, q0:q0 + n])
-            if evs:
-                evs[c][2].record()
-    run()
-    torch.cuda.synchronize()
-    chunks = (S + q_chunk - 1) // q_chunk
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    def run(path=fa.SA_PREFILL_AUTO):
+        for c, (q0, n, tail) in enumerate(blocks):
+            fa.sparse_attn_prefill_fused(kv, inp.q[:, q0:q0 + n], q_idx[c], Hq, n, tail, w.top_k, scale,
+                                         path, ws, ws_n, out[:, q0:q0 + n], lse[:, q0:q0 + n])
 
-    def staged(**kw):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(chunks)]
-        run(evs, **kw)
+    def run_thresholds():
+        for c, (q0, n, tail) in enumerate(blocks):
+            fa.sparse_attn_select_thresholds(kv, q_idx[c], n, tail, w.top_k, thr[:, :n])
+
+    def run_lists(fu_ws, mk_ws):
+        for c, (q0, n, tail) in enumerate(blocks):
+            fa.sparse_attn_index_topk(kv, q_idx[c], n, tail, w.top_k, idx[:, :n], fu_ws, fu_n)
+            fa.sparse_attn_fwd_prefill_masked(kv, inp.q[:, q0:q0 + n], Hq, n, tail, idx[:, :n], w.index_width,
+                                              scale, mk_ws, mk_n, out[:, q0:q0 + n], lse[:, q0:q0 + n])
+
+    def timed(fn, n):
+        fn()
         torch.cuda.synchronize()
-        return [sum(evs[c][k].elapsed_time(evs[c][k + 1]) for c in range(chunks)) for k in range(2)]
-    stage = staged()
-    two_sel = staged(two_step=True)[0]
-    gather_ms = staged(gather=True)[1]
-    # algorithmic attention flops: 4 heads x (QK + PV) per selected key per (query, group)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+    t = timed(run, reps)
+    ms = sum(t) / reps
+    thr_ms = sorted(timed(run_thresholds, 3))[1]
+    gather_ms = sorted(timed(lambda: run(fa.SA_PREFILL_GATHER), 3))[1]
+    fu_ws = torch.empty(fu_n, dtype=torch.uint8, device="cuda")
+    mk_ws = torch.empty(mk_n, dtype=torch.uint8, device="cuda")
+    lists_ms = sorted(timed(lambda: run_lists(fu_ws, mk_ws), 3))[1]
+    del fu_ws, mk_ws
+    # algorithmic attention flops: G heads x (QK + PV) per selected key per (query, group)
     sel = sum(min(w.top_k, i + 1) for i in range(S))
     attn_flop = 4.0 * d * Hq * sel
-    # the masked dense tiles compute every causal (query, key) pair
-    causal_flop = 4.0 * d * Hq * S * (S + 1) / 2
-    del inp, scores, idx, out, lse, q_idx, tk_ws, mk_ws, fu_ws
+    causal_flop = 4.0 * d * Hq * S * (S + 1) / 2   # what the masked dense tiles compute
+    # the gathered path reads a 256-byte K row and a 256-byte V row per selected (query, group, key)
+    gather_gbps = sel * Hkv * 512 / (gather_ms * 1e-3) / 1e9
+    del inp, out, lse, q_idx, ws, thr, idx
     torch.cuda.empty_cache()
-    return {"workload": w.name, "ms": ms, "tokens_per_s": S / (ms * 1e-3),
-            "stage_ms": {"select": stage[0], "attention": stage[1]},
-            "select": "sparse_attn_index_topk (16-bit indexer keys, exact ties)",
-            "attention": "masked dense tiles (sparse_attn_fwd_prefill_masked)",
-            "attention_tflops": attn_flop / (stage[1] * 1e-3) / 1e12,
-            "attention_mfma_tflops": causal_flop / (stage[1] * 1e-3) / 1e12,
-            "select_two_step_ms": two_sel,
-            "attention_gathered_ms": gather_ms,
-            # every selected (query, group, key) reads a 256-byte K row and a 256-byte V row
-            "gathered_rows_gbps_through_caches": sel * Hkv * 512 / (gather_ms * 1e-3) / 1e9,
-            "q_chunk": q_chunk}
+    res = {"workload": w.name, "ms": ms, "ms_percentiles": _pct(t), "reps": reps,
+           "tokens_per_s": S / (ms * 1e-3), "q_chunk": q_chunk,
+           "path": "sparse_attn_prefill_fused, automatic path: " + ", ".join(
+               sorted({"masked dense tiles (thresholds, no lists)" if p == fa.SA_PREFILL_MASKED
+                       else "gathered rows (index lists)" for p in paths})),
+           "select_thresholds_ms": thr_ms,
+           "gathered_path_ms": gather_ms,
+           "list_path_ms": lists_ms,
+           "mfma": {"bound": "mfma", "achieved": attn_flop / (ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": attn_flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    "flop": attn_flop, "dense_equivalent_tflops": causal_flop / (ms * 1e-3) / 1e12,
+                    "note": "algorithmic flops of the selected keys over the whole call; the masked "
+                            "tiles compute every causal pair (dense_equivalent)"},
+           "gather": {"bound": "row gather", "achieved": gather_gbps, "unit": "GB/s",
+                      "note": "gathered-row path: 512 B of K and V rows per selected key"}}
+    if calib:
+        # a block's queries select overlapping keys, so most of its rows hit in L2: the ceiling
+        # is the gather of random rows that L2 holds (the 2 MiB pool); rows read once would be
+        # bounded by the 128 MiB pool's figure instead
+        res["gather"]["measured_peak"] = calib["row_gather_2mib_gbps"]
+        res["gather"]["frac_of_measured"] = gather_gbps / calib["row_gather_2mib_gbps"]
+        res["gather"]["frac_of_128mib_pool_gather"] = gather_gbps / calib["row_gather_128mib_gbps"]
+        res["mfma"]["measured_peak"] = calib["mfma_bf16_tflops"]
+        res["mfma"]["frac_of_measured"] = res["mfma"]["achieved"] / calib["mfma_bf16_tflops"]
+    return res
 
 
 def bench_decode_1m(fa, steps, warmup, workload="sparse_decode_1m_prefix", seed=5,
-                    num_idx_heads=None, window=0):
+                    num_idx_heads=None, window=0, evict=None):
     """One decode step at 1M context with a 196-token forced prefix (B=4, 32/8 heads, d=128,
-    d_idx=64, top-K=2048): fused indexer + top-K, then split-K attention and merge. The same
-    measurement serves the 128K decode with one indexer key shared by the KV groups."""
+    d_idx=64, top-K=2048): fused indexer + top-K, then split-K attention and merge. With
+    `evict` (a callable run before each step, outside its events) caches are cold; otherwise
+    steps run back to back. The same measurement serves the 128K decode variants (one indexer
+    key shared by the KV groups, hybrid lists with a local window)."""
     import torch
 
     from synthetic import CONFIGS, make_inputs
@@ -419,28 +549,49 @@ def bench_decode_1m(fa, steps, warmup, workload="sparse_decode_1m_prefix", seed=
     dec = torch.empty(max(dec_n, 16), dtype=torch.uint8, device="cuda")
     scale = 1 / math.sqrt(w.head_dim)
 
-    def step():
+    def select():
         if window:
             fa.sparse_attn_index_topk_window(kv, inp.q_idx, 1, 1, w.top_k, window, idx, fu, fu_n)
         else:
             fa.sparse_attn_index_topk(kv, inp.q_idx, 1, 1, w.top_k, idx, fu, fu_n)
+
+    def step():
+        select()
         fa.sparse_attn_fwd_decode(kv, q, Hq, idx[:, 0], width, scale, 0, dec, dec_n, out, lse)
+
+    def timed(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            if evict:
+                evict()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    t = timed(step)
+    ms = sum(t) / steps
+    sel_ms = sum(timed(select)) / steps
     kidx_bytes = B * Hi * w.seq_len * w.idx_dim
+    pt_bytes = B * (w.seq_len // w.page_size) * 4
     gather = B * Hkv * width * 2 * w.head_dim * 2
+    sel_bytes = kidx_bytes + pt_bytes + B * Hi * w.idx_dim
     del inp, idx, q, out, lse, fu, dec
     torch.cuda.empty_cache()
-    return {"workload": w.name, "idx_heads": Hi, "window": window, "ms": ms, "tokens_per_s": B / (ms * 1e-3),
-            "hbm_gbps": (kidx_bytes + gather) / (ms * 1e-3) / 1e9, "cache": "warm (back-to-back steps)"}
+    res = {"workload": w.name, "idx_heads": Hi, "window": window, "ms": ms, "ms_percentiles": _pct(t),
+           "steps": steps, "tokens_per_s": B / (ms * 1e-3),
+           "hbm_gbps": (kidx_bytes + gather) / (ms * 1e-3) / 1e9,
+           "hbm_frac": (kidx_bytes + gather) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "cache": "evicted by a 1 GiB read before each step" if evict else "warm (back-to-back steps)"}
+    if evict:
+        ach = sel_bytes / (sel_ms * 1e-3) / 1e9
+        res["roofline"] = {"kernel": "sparse_attn_index_topk (k_fused_main + k_fused_final)", "bound": "hbm",
+                           "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                           "bytes_per_launch": sel_bytes, "ms": sel_ms}
+    return res
 
 
 def main():
@@ -458,9 +609,13 @@ def main():
 
     fa.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.sparse_prefill_only:
-        print(json.dumps({"sparse_prefill": bench_sparse_prefill(fa, reps=1)}), flush=True)
+    if args.calibrate:
+        print(json.dumps({"calibration": calibrate(fa)}), flush=True)
         return
+    if args.sparse_prefill_only:
+        print(json.dumps({"sparse_prefill": bench_sparse_prefill(fa, reps=3)}), flush=True)
+        return
+    calib = None if args.no_calibrate else calibrate(fa)
     w = CONFIGS["sparse_decode_128k"]
     inp = make_inputs(w, seed=args.seed, device="cuda")
     kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
@@ -578,27 +733,43 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_for("k_index_stream<64>" if args.two_step else "fused_select")},
     }
+    if calib:
+        result["calibration"] = calib
+        result["roofline"]["measured_peak"] = calib["hbm_read_gbps"]
+        result["roofline"]["frac_of_measured"] = achieved / calib["hbm_read_gbps"]
     if not args.no_prefill:
         del scores
         torch.cuda.empty_cache()
         pf = bench_prefill(fa, args.prefill_reps)
+        pf["roofline"] = {"kernel": "k_attn_dense<128, false>", "bound": "mfma", "achieved": pf["tflops"],
+                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": pf["mfma_frac"]}
+        if calib:
+            pf["roofline"]["measured_peak"] = calib["mfma_bf16_tflops"]
+            pf["roofline"]["frac_of_measured"] = pf["tflops"] / calib["mfma_bf16_tflops"]
         result["prefill_tflops"] = pf["tflops"]
         result["prefill"] = pf
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, w)
     if not args.no_extra:
-        del inp, evict_buf
+        del inp
         torch.cuda.empty_cache()
-        result["sparse_prefill"] = bench_sparse_prefill(fa, reps=2)
+        result["sparse_prefill"] = bench_sparse_prefill(fa, reps=10, calib=calib)
+        result["decode_1m_prefix"] = bench_decode_1m(fa, steps=10, warmup=3,
+                                                     evict=None if args.warm_cache else evict)
+        del evict_buf
+        torch.cuda.empty_cache()
         result["tiny_sparse_prefill"] = bench_tiny(fa)
         result["cache_maintenance"] = bench_cache_maintenance(fa)
-        result["decode_1m_prefix"] = bench_decode_1m(fa, steps=10, warmup=3)
         # the 128K step with one indexer key shared by all KV groups (a stride-0 indexer head)
         result["decode_128k_shared_indexer"] = bench_decode_1m(
             fa, steps=20, warmup=5, workload="sparse_decode_128k", seed=args.seed, num_idx_heads=1)
         # the 128K step with hybrid lists: the last 512 keys forced beside the top-2048
         result["decode_128k_window_512"] = bench_decode_1m(
             fa, steps=20, warmup=5, workload="sparse_decode_128k", seed=args.seed, window=512)
+    if not args.no_cpu_baseline:
+        torch.cuda.empty_cache()
+        cb = cpu_baselines(fa)
+        result["cpu_baseline"] = dict(cb["sparse_decode_128k"])
+        result["cpu_baseline"]["sample"] += " (128K decode workload)"
+        result["cpu_baselines"] = cb
     print(json.dumps(result), flush=True)
 
 

@@ -33,7 +33,8 @@ EXPORTS = ["sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_
            "sparse_attn_kv_release", "sparse_attn_decode_workspace_size", "sparse_attn_fwd_decode",
            "sparse_attn_decode_noalloc_max_bytes", "sparse_attn_fwd_decode_noalloc",
            "sparse_attn_select_thresholds", "sparse_attn_prefill_fused_workspace_size",
-           "sparse_attn_prefill_fused_choice", "sparse_attn_prefill_fused"]
+           "sparse_attn_prefill_fused_choice", "sparse_attn_prefill_fused",
+           "sparse_attn_calib_read", "sparse_attn_calib_gather", "sparse_attn_calib_mfma"]
 SA_PREFILL_AUTO, SA_PREFILL_GATHER, SA_PREFILL_MASKED = 0, 1, 2
 
 
@@ -104,6 +105,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sparse_attn_prefill_fused_workspace_size": (SZ, [KV, I32, I32, I32, I32, I32]),
         "sparse_attn_prefill_fused_choice": (I32, [KV, I32, I32, I32, I32]),
         "sparse_attn_prefill_fused": (I32, [KV, P, P, I32, I32, I32, I32, F32, I32, P, SZ, P, P, P]),
+        "sparse_attn_calib_read": (I32, [P, SZ, P, I32, P]),
+        "sparse_attn_calib_gather": (I32, [P, SZ, P, I64, P, I32, P]),
+        "sparse_attn_calib_mfma": (I32, [I32, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -349,6 +353,23 @@ def sparse_attn_prefill_fused(kv: PagedKV, q, q_idx, num_q_heads, q_len, q_tail,
         kv.ref, _ptr(q, torch.bfloat16, "q"), _ptr(q_idx, torch.int8, "q_idx"), num_q_heads, q_len,
         q_tail, top_k, float(sm_scale), path, _ptr(workspace, None, "workspace"), workspace_bytes,
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def sparse_attn_calib_read(buf, sink, workgroups, stream=None):
+    _check("sparse_attn_calib_read", load().sparse_attn_calib_read(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink, torch.int32, "sink"), workgroups,
+        _stream(stream)))
+
+
+def sparse_attn_calib_gather(pool, rows, sink, workgroups, stream=None):
+    _check("sparse_attn_calib_gather", load().sparse_attn_calib_gather(
+        _ptr(pool), pool.numel() * pool.element_size(), _ptr(rows, torch.int32, "rows"), rows.numel(),
+        _ptr(sink, torch.int32, "sink"), workgroups, _stream(stream)))
+
+
+def sparse_attn_calib_mfma(kind, iters, workgroups, sink, stream=None):
+    _check("sparse_attn_calib_mfma", load().sparse_attn_calib_mfma(
+        kind, iters, workgroups, _ptr(sink, torch.int32, "sink"), _stream(stream)))
 
 
 # ------------------------------------------------------------------ allocating helpers

@@ -540,4 +540,28 @@ int32_t sparse_attn_fwd_decode_noalloc(const sa_paged_kv* kv, const uint16_t* q,
                                            static_cast<hipStream_t>(stream)));
 }
 
+int32_t sparse_attn_calib_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups,
+                               void* stream) {
+  if (buf == nullptr || sink == nullptr) return SA_ERR_NULL;
+  if (!aligned16(buf) || (bytes & 15) != 0) return SA_ERR_ALIGN;
+  if (bytes < 16 || workgroups < 1 || workgroups > 65536) return SA_ERR_SHAPE;
+  return hip_status(sa::launch_calib_read(buf, bytes, sink, workgroups, static_cast<hipStream_t>(stream)));
+}
+
+int32_t sparse_attn_calib_gather(const void* pool, size_t pool_bytes, const int32_t* rows,
+                                 int64_t n_rows, uint32_t* sink, int32_t workgroups, void* stream) {
+  if (pool == nullptr || rows == nullptr || sink == nullptr) return SA_ERR_NULL;
+  if (!aligned16(pool) || !aligned16(rows) || (pool_bytes & 255) != 0) return SA_ERR_ALIGN;
+  if (pool_bytes < 256 || n_rows < 1 || workgroups < 1 || workgroups > 65536) return SA_ERR_SHAPE;
+  return hip_status(sa::launch_calib_gather(pool, pool_bytes, rows, n_rows, sink, workgroups,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int32_t sparse_attn_calib_mfma(int32_t kind, int32_t iters, int32_t workgroups, uint32_t* sink,
+                               void* stream) {
+  if (sink == nullptr) return SA_ERR_NULL;
+  if ((kind != 0 && kind != 1) || iters < 1 || workgroups < 1 || workgroups > 65536) return SA_ERR_SHAPE;
+  return hip_status(sa::launch_calib_mfma(kind, iters, workgroups, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

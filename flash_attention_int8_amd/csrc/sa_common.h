@@ -190,4 +190,10 @@ hipError_t launch_attn_masked_records(const KvView& kv, const uint16_t* q, int n
 bool sel_thresh_applies(const KvView& kv);
 hipError_t launch_sel_thresh(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail, int top_k,
                              int32_t* thresholds, uint64_t* sel, hipStream_t stream);
+// Roofline micro-benchmarks (streaming read, random 256-byte row gather, MFMA loops).
+hipError_t launch_calib_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups,
+                             hipStream_t stream);
+hipError_t launch_calib_gather(const void* pool, size_t pool_bytes, const int32_t* rows, int64_t n_rows,
+                               uint32_t* sink, int workgroups, hipStream_t stream);
+hipError_t launch_calib_mfma(int kind, int iters, int workgroups, uint32_t* sink, hipStream_t stream);
 }  // namespace sa

@@ -379,6 +379,28 @@ int32_t sparse_attn_fwd_decode_noalloc(const sa_paged_kv* kv, const uint16_t* q,
                                        int32_t index_width, float sm_scale, int32_t num_splits,
                                        uint16_t* out, float* lse, void* stream);
 
+/*
+ * Roofline micro-benchmarks. They measure what the device reaches on the operations the path is
+ * bound by, with the instructions the kernels use, so that roofline fractions can be given
+ * against measured ceilings as well as vendor peaks. The caller times them (e.g. with events on
+ * `stream`); each workgroup writes at most one word of `sink` (uint32 [workgroups]).
+ *   sparse_attn_calib_read    streams `bytes` (a multiple of 16, >= 16) of `buf` with 16-byte
+ *                             loads: bytes / time is the streaming read bandwidth.
+ *   sparse_attn_calib_gather  loads n_rows random 256-byte rows of `pool` (pool_bytes a multiple
+ *                             of 256), rows[k] = row number (int32; a number outside the pool
+ *                             reads row 0): 256 * n_rows / time is the row-gather bandwidth.
+ *   sparse_attn_calib_mfma    `iters` x 4 back-to-back matrix instructions per wave, 4 waves per
+ *                             workgroup: kind 0 = v_mfma_f32_32x32x16_bf16 (32768 flop each),
+ *                             kind 1 = v_mfma_i32_32x32x32_i8 (65536 op each).
+ * 1 <= workgroups <= 65536. Pointers are device pointers, 16-byte aligned.
+ */
+int32_t sparse_attn_calib_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups,
+                               void* stream);
+int32_t sparse_attn_calib_gather(const void* pool, size_t pool_bytes, const int32_t* rows,
+                                 int64_t n_rows, uint32_t* sink, int32_t workgroups, void* stream);
+int32_t sparse_attn_calib_mfma(int32_t kind, int32_t iters, int32_t workgroups, uint32_t* sink,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif
