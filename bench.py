@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--calibrate", action="store_true",
                     help="only the roofline micro-benchmarks (measured ceilings)")
     ap.add_argument("--no-calibrate", action="store_true")
+    ap.add_argument("--dispatch-sweep", action="store_true",
+                    help="only the crossover sweep of the fused sparse prefill's two paths")
     ap.add_argument("--sparse-prefill-only", action="store_true",
                     help="run only the 32K sparse prefill measurement once and print its JSON "
                          "(a short program for counter collection)")
@@ -520,6 +522,51 @@ def bench_sparse_prefill(fa, reps, q_chunk=2048, calib=None):
     return res
 
 
+def dispatch_sweep(fa):
+    """Crossover of sparse_attn_prefill_fused's two paths on the 32K sparse prefill inputs:
+    blocks of 128, 512 and 2048 queries at five positions, top-K 32..2048; the median of 3
+    timed calls of each forced path, and the path AUTO takes. One JSON line per point."""
+    import torch
+
+    from synthetic import CONFIGS, make_inputs
+    w = CONFIGS["sparse_prefill_32k"]
+    inp = make_inputs(w, seed=4, device="cuda")
+    kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
+                    page_table=inp.page_table, seq_lens=inp.seq_lens, max_seq_len=w.seq_len,
+                    prefix_len=w.prefix_len)
+    S, Hq = w.q_len, w.num_q_heads
+
+    def timed(qc, qi, tail, k, path):
+        out = torch.empty_like(qc)
+        lse = torch.empty((1, qc.shape[1], Hq), dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.sparse_attn_prefill_fused_workspace_size(kv, Hq, qc.shape[1], tail, k, path),
+                         dtype=torch.uint8, device="cuda")
+        ts = []
+        for r in range(4):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fa.prefill_fused(kv, qc, qi, tail, k, path=path, out=out, lse=lse, workspace=ws)
+            b.record()
+            torch.cuda.synchronize()
+            if r:
+                ts.append(a.elapsed_time(b))
+        return sorted(ts)[1]
+    for q_len in (2048, 512, 128):
+        for q0 in (0, 2048, 8192, 16384, S - q_len):
+            tail = S - q0
+            qc = inp.q[:, q0:q0 + q_len].contiguous()
+            qi = inp.q_idx[:, q0:q0 + q_len].contiguous()
+            for k in (32, 128, 512, 2048):
+                if k > q0 + q_len:
+                    continue
+                print(json.dumps({"q_len": q_len, "q0": q0, "top_k": k,
+                                  "mean_candidates": q0 + (q_len - 1) / 2 + 1,
+                                  "masked_ms": timed(qc, qi, tail, k, fa.SA_PREFILL_MASKED),
+                                  "gather_ms": timed(qc, qi, tail, k, fa.SA_PREFILL_GATHER),
+                                  "auto": fa.sparse_attn_prefill_fused_choice(kv, Hq, q_len, tail, k)}),
+                      flush=True)
+
+
 def bench_decode_1m(fa, steps, warmup, workload="sparse_decode_1m_prefix", seed=5,
                     num_idx_heads=None, window=0, evict=None):
     """One decode step at 1M context with a 196-token forced prefix (B=4, 32/8 heads, d=128,
@@ -611,6 +658,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate:
         print(json.dumps({"calibration": calibrate(fa)}), flush=True)
+        return
+    if args.dispatch_sweep:
+        dispatch_sweep(fa)
         return
     if args.sparse_prefill_only:
         print(json.dumps({"sparse_prefill": bench_sparse_prefill(fa, reps=3)}), flush=True)

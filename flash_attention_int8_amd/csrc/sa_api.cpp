@@ -2,6 +2,8 @@
 // Every check runs before anything is enqueued, so an error return launches nothing.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "../../include/sparse_attn.h"
 #include "sa_common.h"
 
@@ -288,10 +290,14 @@ double mean_candidates(const sa::KvView& v, int32_t q_len, int32_t q_tail) {
   return first + (q_len - 1) * 0.5 + 1.0 - v.prefix_len;
 }
 
-// Path of sparse_attn_prefill_fused: masked-dense tiles when the lists select a large enough
-// share of the causal keys (the dense tiles cost per causal key what a gathered row costs per
-// selected key divided by kMaskedGatherRatio, measured on MI355X), else gathered rows.
-constexpr double kMaskedGatherRatio = 16.0;
+// Path of sparse_attn_prefill_fused: masked-dense tiles when top_k is a large enough share of
+// the block's mean candidate count, else gathered rows. Measured on MI355X (32K context, blocks
+// of 128, 512 and 2048 queries at five positions, top-K 32..2048): for 2048-query blocks the
+// two paths cost the same at a share of about 1/16; shorter blocks need a larger share (about
+// 0.18 at 512 queries, 0.25-0.5 at 128), since the selection then runs few workgroups and the
+// dense tiles of a 256-query workgroup are partly empty. max(1/16, 64/q_len) follows both.
+constexpr double kMaskedMinShare = 1.0 / 16.0;
+constexpr double kMaskedShareQueries = 64.0;
 
 int32_t fused_path(const sa::KvView& v, int32_t num_q_heads, int32_t q_len, int32_t q_tail,
                    int32_t top_k, int32_t path) {
@@ -302,7 +308,8 @@ int32_t fused_path(const sa::KvView& v, int32_t num_q_heads, int32_t q_len, int3
   if (path == SA_PREFILL_MASKED) return masked_ok ? SA_PREFILL_MASKED : -1;
   if (!masked_ok) return gather_ok ? SA_PREFILL_GATHER : -1;
   if (!gather_ok) return SA_PREFILL_MASKED;
-  const bool dense_enough = (double)top_k * kMaskedGatherRatio >= mean_candidates(v, q_len, q_tail);
+  const double share = fmax(kMaskedMinShare, kMaskedShareQueries / q_len);
+  const bool dense_enough = (double)top_k >= share * mean_candidates(v, q_len, q_tail);
   return (dense_enough && q_len >= 64) ? SA_PREFILL_MASKED : SA_PREFILL_GATHER;
 }
 

@@ -239,10 +239,11 @@ int32_t sparse_attn_select_thresholds(const sa_paged_kv* kv, const int8_t* q_idx
  *                      unselected ones masked. Cost follows the causal length.
  *   SA_PREFILL_GATHER  index lists (sparse_attn_index_topk) and attention over gathered rows.
  *                      Cost follows top_k.
- *   SA_PREFILL_AUTO    masked when top_k is at least 1/16 of the block's mean candidate count
- *                      (the measured ratio of a gathered row's cost to a dense key's) and
- *                      q_len >= 64; gathered otherwise. sparse_attn_prefill_fused_choice tells
- *                      which path AUTO takes (or -1 if none applies).
+ *   SA_PREFILL_AUTO    masked when q_len >= 64 and top_k is at least max(1/16, 64/q_len) of
+ *                      the block's mean candidate count (the crossover measured on MI355X for
+ *                      blocks of 128 to 2048 queries); gathered otherwise.
+ *                      sparse_attn_prefill_fused_choice tells which path AUTO takes (or -1 if
+ *                      none applies).
  * The masked path needs max_seq_len <= 131072; the gathered one a group size H_q/H_kv in
  * {1, 2, 4, 8}; a forced path that does not apply returns SA_ERR_UNSUPPORTED.
  * workspace: sparse_attn_prefill_fused_workspace_size(kv, num_q_heads, q_len, q_tail, top_k,

@@ -613,12 +613,13 @@ def test_fused_prefill_other_paths_every_row(name, path):
     assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
 
 
-@pytest.mark.parametrize("top_k,want", [(64, fa.SA_PREFILL_GATHER), (1024, fa.SA_PREFILL_MASKED)])
+@pytest.mark.parametrize("top_k,want", [(64, fa.SA_PREFILL_GATHER), (1024, fa.SA_PREFILL_GATHER),
+                                         (2048, fa.SA_PREFILL_MASKED)])
 def test_fused_prefill_dispatch_both_sides(top_k, want):
     """A 256-query block at the end of an 8192-token sequence (mean ~8064 candidates): top-64
-    is a small share of the causal keys (gathered rows), top-1024 a large one (masked dense
-    tiles). AUTO takes the expected path, and both paths match the oracle on sampled rows
-    and every KV group; thresholds bit-exact."""
+    and top-1024 are below the share a 256-query block needs for dense tiles (64/256 of the
+    candidates), top-2048 above it. AUTO takes the expected path, and both paths match the
+    oracle on sampled rows and every KV group; thresholds bit-exact."""
     w = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=8192, q_len=256, top_k=top_k, prefix_len=4)
     _banner(f"fused prefill dispatch top_k={top_k}")
     inp = make_inputs(w, seed=41, device=DEV, seq_lens=[8192, 7000])

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import flash_attention_int8_amd as fa
-from dsa_harness import OracleView, assert_close, compare_rows, make_kv
+from dsa_harness import GpuRun, OracleView, assert_close, compare_rows, make_kv
 from synthetic import Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +54,7 @@ def test_noalloc_decode_matches_workspace_entry(num_splits):
         assert torch.equal(o_na, o_ws)
         assert torch.equal(l_na, l_ws)
         ov = OracleView(inp)
-        g = type("R", (), {})()
+        g = GpuRun()
         g.indices = idx.unsqueeze(1)
         g.out = o_na.unsqueeze(1)
         g.lse = l_na.unsqueeze(1)
