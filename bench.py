@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--calibrate", action="store_true",
                     help="only the roofline micro-benchmarks (measured ceilings)")
     ap.add_argument("--no-calibrate", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the dense 8K prefill (for counter runs)")
     ap.add_argument("--dispatch-sweep", action="store_true",
                     help="only the crossover sweep of the fused sparse prefill's two paths")
     ap.add_argument("--sparse-prefill-only", action="store_true",
@@ -661,6 +663,9 @@ def main():
         return
     if args.dispatch_sweep:
         dispatch_sweep(fa)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill(fa, args.prefill_reps)}), flush=True)
         return
     if args.sparse_prefill_only:
         print(json.dumps({"sparse_prefill": bench_sparse_prefill(fa, reps=3)}), flush=True)

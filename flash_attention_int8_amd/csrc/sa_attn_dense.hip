@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   };
   // O^T += V^T P^T. Step st = (mb, kk) covers keys mb*32 + kk*16 + {hi*4 + 0..3, 8 + hi*4 + 0..3},
   // the key permutation of the P^T fragments.
-  auto pv = [&](int buf, const Frag8 (&pf)[4], const f32x16 (&sm)[2], float& mx, bool do_max) {
+  auto pv = [&](int buf, const Frag8 (&pf)[4], const f32x16 (&sm)[2], float& mx) {
     auto vfrag = [&](int i) {  // i = st * DB + db; st outer: step st needs the first 8(st+1) exps
       const int st = i / DB, db = i % DB;
       const int kb = (st >> 1) * 32 + (st & 1) * 16 + hi * 4;
@@ -369,10 +369,10 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     for (int i = 0; i < 4 * DB; ++i) {
       o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % kVPre].v, pf[i / DB].v, o[i % DB], 0, 0, 0);
       if (i + kVPre < 4 * DB) va[i % kVPre] = vfrag(i + kVPre);
-      if (do_max) {
+      // (taken on every tile: the maximum of the one extra tile past the wave's end is never
+      // used, and a conditional maximum costs a select per step)
 #pragma unroll
-        for (int e = i * (32 / (4 * DB)); e < (i + 1) * (32 / (4 * DB)); ++e) mx = fmaxf(mx, sm[e >> 4][e & 15]);
-      }
+      for (int e = i * (32 / (4 * DB)); e < (i + 1) * (32 / (4 * DB)); ++e) mx = fmaxf(mx, sm[e >> 4][e & 15]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
       ok_next = ph >= 0;
     }
     load_rows(k_loader ? kv.k_pool : kv.v_pool, lt, ph, k_off, st);
-    const int lim = valid_rows(lt, ph);
+    const int lim = __builtin_amdgcn_readfirstlane(valid_rows(lt, ph));
     float mx = -INFINITY;
     if (j <= last_w) {
       // S(j+1) is computed unconditionally (one extra tile at the wave's end, never used) so
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
       // a conditional use would let the compiler sink the loads to it)
       if constexpr (MASKED) apply_sel(mw, sn, ok_next);
       else if (j + 1 <= last_w) mask_tile(j + 1, sn, ok_next);
-      pv(j & 1, pf, sn, mx, j + 1 <= last_w);
+      pv(j & 1, pf, sn, mx);
     }
     if (more) {
       if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
