@@ -34,7 +34,10 @@ EXPORTS = ["sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_
            "sparse_attn_decode_noalloc_max_bytes", "sparse_attn_fwd_decode_noalloc",
            "sparse_attn_select_thresholds", "sparse_attn_prefill_fused_workspace_size",
            "sparse_attn_prefill_fused_choice", "sparse_attn_prefill_fused",
-           "sparse_attn_calib_read", "sparse_attn_calib_gather", "sparse_attn_calib_mfma"]
+           "sparse_attn_calib_read", "sparse_attn_calib_gather", "sparse_attn_calib_mfma",
+           "sparse_attn_validate", "sparse_attn_check_report", "sparse_attn_workspace_size"]
+SA_OP_TOPK, SA_OP_INDEX_TOPK, SA_OP_INDEX_TOPK_WINDOW, SA_OP_PREFILL_MASKED, SA_OP_PREFILL_FUSED, \
+    SA_OP_DECODE = range(1, 7)
 SA_PREFILL_AUTO, SA_PREFILL_GATHER, SA_PREFILL_MASKED = 0, 1, 2
 
 
@@ -108,6 +111,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sparse_attn_calib_read": (I32, [P, SZ, P, I32, P]),
         "sparse_attn_calib_gather": (I32, [P, SZ, P, I64, P, I32, P]),
         "sparse_attn_calib_mfma": (I32, [I32, I32, I32, P, P]),
+        "sparse_attn_validate": (I32, [KV, P, I32, I32, I32, P, P]),
+        "sparse_attn_check_report": (I32, [P, P]),
+        "sparse_attn_workspace_size": (SZ, [I32, KV, I32, I32, I32, I32, I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -353,6 +359,17 @@ def sparse_attn_prefill_fused(kv: PagedKV, q, q_idx, num_q_heads, q_len, q_tail,
         kv.ref, _ptr(q, torch.bfloat16, "q"), _ptr(q_idx, torch.int8, "q_idx"), num_q_heads, q_len,
         q_tail, top_k, float(sm_scale), path, _ptr(workspace, None, "workspace"), workspace_bytes,
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def sparse_attn_validate(kv: PagedKV, indices, index_width, q_len, q_tail, report, stream=None):
+    _check("sparse_attn_validate", load().sparse_attn_validate(
+        kv.ref, _ptr(indices, torch.int32, "indices"), index_width, q_len, q_tail,
+        _ptr(report, torch.int32, "report"), _stream(stream)))
+
+
+def sparse_attn_check_report(report, stream=None):
+    _check("sparse_attn_check_report", load().sparse_attn_check_report(
+        _ptr(report, torch.int32, "report"), _stream(stream)))
 
 
 def sparse_attn_calib_read(buf, sink, workgroups, stream=None):

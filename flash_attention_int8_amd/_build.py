@@ -12,7 +12,8 @@ LIB_NAME = "libsparse_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["sa_api.cpp", "sa_index.hip", "sa_topk.hip", "sa_index_topk.hip", "sa_attn_gather.hip",
            "sa_attn_sparse_mfma.hip", "sa_attn_dense.hip", "sa_kv_append.hip", "sa_kv_alloc.hip", "sa_window.hip",
-           "sa_prefill_select.hip", "sa_calibrate.hip"]
+           "sa_prefill_select.hip", "sa_calibrate.hip",
+           "sa_check.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

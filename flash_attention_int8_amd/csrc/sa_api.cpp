@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 
 #include "../../include/sparse_attn.h"
 #include "sa_common.h"
@@ -66,6 +67,22 @@ int32_t check_block(const sa::KvView& v, int32_t q_len, int32_t q_tail) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
 
+// SPARSE_ATTN_CHECK=1 in the environment: every call first validates the device data it reads
+// (sequence lengths, page-table entries, the index lists it takes) into the library's report,
+// read back with sparse_attn_check_report.
+bool check_mode() {
+  const char* e = std::getenv("SPARSE_ATTN_CHECK");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
+int32_t checked(const sa::KvView& v, const int32_t* lists, int width, int q_len, int q_tail,
+                hipStream_t s) {
+  if (!check_mode()) return SA_OK;
+  int32_t* report = nullptr;
+  if (sa::check_report_ptr(&report, s) != hipSuccess) return SA_ERR_HIP;
+  return hip_status(sa::launch_check(v, lists, width, q_len, q_tail, report, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,6 +114,7 @@ int32_t sparse_attn_index(const sa_paged_kv* kv, const int8_t* q_idx, int32_t q_
   if (q_idx == nullptr || scores == nullptr) return SA_ERR_NULL;
   if (!aligned16(q_idx) || !aligned16(scores)) return SA_ERR_ALIGN;
   if (score_row_stride < v.max_seq_len || (score_row_stride & 3) != 0) return SA_ERR_SHAPE;
+  if ((st = checked(v, nullptr, 0, q_len, q_tail, static_cast<hipStream_t>(stream))) != SA_OK) return st;
   return hip_status(sa::launch_index(v, q_idx, q_len, q_tail, scores, score_row_stride,
                                      static_cast<hipStream_t>(stream)));
 }
@@ -121,6 +139,7 @@ int32_t sparse_attn_topk(const sa_paged_kv* kv, const int32_t* scores, int64_t s
   const size_t need = sa::topk_workspace_bytes(v, q_len, top_k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return SA_ERR_ALIGN;
+  if ((st = checked(v, nullptr, 0, q_len, q_tail, static_cast<hipStream_t>(stream))) != SA_OK) return st;
   return hip_status(sa::launch_topk(v, scores, score_row_stride, q_len, q_tail, top_k, indices,
                                     workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
@@ -199,6 +218,7 @@ int32_t sparse_attn_index_topk(const sa_paged_kv* kv, const int8_t* q_idx, int32
   const size_t need = index_topk_bytes(v, q_len, top_k);
   if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SA_ERR_ALIGN;
+  if ((st = checked(v, nullptr, 0, q_len, q_tail, static_cast<hipStream_t>(stream))) != SA_OK) return st;
   return index_topk_run(v, q_idx, q_len, q_tail, top_k, indices, workspace,
                         static_cast<hipStream_t>(stream));
 }
@@ -234,6 +254,7 @@ int32_t sparse_attn_index_topk_window(const sa_paged_kv* kv, const int8_t* q_idx
   if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SA_ERR_ALIGN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = checked(v, nullptr, 0, q_len, q_tail, s)) != SA_OK) return st;
   const size_t rows = (size_t)v.batch * q_len * v.num_idx_heads;
   char* base = static_cast<char*>(workspace);
   int32_t* short_lens = reinterpret_cast<int32_t*>(base);
@@ -261,12 +282,15 @@ int32_t sparse_attn_fwd_prefill(const sa_paged_kv* kv, const uint16_t* q, int32_
   if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0) return SA_ERR_SHAPE;
   if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return SA_ERR_SHAPE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (indices == nullptr)
+  if (indices == nullptr) {
+    if ((st = checked(v, nullptr, 0, q_len, q_tail, s)) != SA_OK) return st;
     return hip_status(sa::launch_attn_dense(v, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, s));
+  }
   const int group = num_q_heads / v.num_kv_heads;
   if (group != 1 && group != 2 && group != 4 && group != 8) return SA_ERR_UNSUPPORTED;
   if (index_width < 1) return SA_ERR_SHAPE;
   if (!aligned16(indices)) return SA_ERR_ALIGN;
+  if ((st = checked(v, indices, index_width, q_len, q_tail, s)) != SA_OK) return st;
   return hip_status(sa::launch_attn_sparse_mfma(v, q, num_q_heads, q_len, q_tail, indices,
                                                 index_width, sm_scale, out, lse, s));
 }
@@ -278,6 +302,7 @@ int32_t sparse_attn_select_thresholds(const sa_paged_kv* kv, const int8_t* q_idx
   int32_t st = check_index_topk(kv, q_idx, q_len, q_tail, top_k, 0, thresholds, &v);
   if (st != SA_OK) return st;
   if (!sa::sel_thresh_applies(v)) return SA_ERR_UNSUPPORTED;
+  if ((st = checked(v, nullptr, 0, q_len, q_tail, static_cast<hipStream_t>(stream))) != SA_OK) return st;
   return hip_status(sa::launch_sel_thresh(v, q_idx, q_len, q_tail, top_k, thresholds, nullptr,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -362,6 +387,7 @@ int32_t sparse_attn_prefill_fused(const sa_paged_kv* kv, const uint16_t* q, cons
   if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SA_ERR_ALIGN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = checked(v, nullptr, 0, q_len, q_tail, s)) != SA_OK) return st;
   char* base = static_cast<char*>(workspace);
   const size_t rows = (size_t)v.batch * q_len * v.num_idx_heads;
   if (chosen == SA_PREFILL_MASKED) {
@@ -403,6 +429,8 @@ int32_t sparse_attn_fwd_prefill_masked(const sa_paged_kv* kv, const uint16_t* q,
   const size_t need = sa::sel_workspace_bytes(v, q_len);
   if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SA_ERR_ALIGN;
+  if ((st = checked(v, indices, index_width, q_len, q_tail, static_cast<hipStream_t>(stream))) != SA_OK)
+    return st;
   return hip_status(sa::launch_attn_masked(v, q, num_q_heads, q_len, q_tail, indices, index_width,
                                            sm_scale, workspace, out, lse,
                                            static_cast<hipStream_t>(stream)));
@@ -420,6 +448,7 @@ int32_t sparse_attn_kv_append(const sa_paged_kv* kv, const uint16_t* k_new, cons
   if ((k_new != nullptr && (!aligned16(k_new) || !aligned16(v_new))) ||
       (kidx_new != nullptr && !aligned16(kidx_new)))
     return SA_ERR_ALIGN;
+  if ((st = checked(v, nullptr, 0, 1, 1, static_cast<hipStream_t>(stream))) != SA_OK) return st;
   return hip_status(sa::launch_kv_append(v, k_new, v_new, kidx_new, n_new,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -522,6 +551,7 @@ int32_t sparse_attn_fwd_decode(const sa_paged_kv* kv, const uint16_t* q, int32_t
     if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SA_ERR_ALIGN;
   }
+  if ((st = checked(v, indices, index_width, 1, 1, static_cast<hipStream_t>(stream))) != SA_OK) return st;
   return hip_status(sa::launch_attn_gather(v, q, num_q_heads, 1, 1, indices, index_width, sm_scale,
                                            splits, static_cast<float*>(workspace), out, lse,
                                            static_cast<hipStream_t>(stream)));
@@ -542,9 +572,51 @@ int32_t sparse_attn_fwd_decode_noalloc(const sa_paged_kv* kv, const uint16_t* q,
   if (need > sa::kDecodeScratchBytes) return SA_ERR_SCRATCH;
   float* scratch = nullptr;
   if (need > 0 && sa::decode_scratch(&scratch) != hipSuccess) return SA_ERR_HIP;
+  if ((st = checked(v, indices, index_width, 1, 1, static_cast<hipStream_t>(stream))) != SA_OK) return st;
   return hip_status(sa::launch_attn_gather(v, q, num_q_heads, 1, 1, indices, index_width, sm_scale,
                                            splits, scratch, out, lse,
                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t sparse_attn_workspace_size(int32_t op, const sa_paged_kv* kv, int32_t q_len, int32_t q_tail,
+                                  int32_t top_k, int32_t num_q_heads, int32_t extra) {
+  switch (op) {
+    case SA_OP_TOPK: return sparse_attn_topk_workspace_size(kv, q_len, top_k);
+    case SA_OP_INDEX_TOPK: return sparse_attn_index_topk_workspace_size(kv, q_len, top_k);
+    case SA_OP_INDEX_TOPK_WINDOW: return sparse_attn_index_topk_window_workspace_size(kv, q_len, top_k, extra);
+    case SA_OP_PREFILL_MASKED: return sparse_attn_prefill_masked_workspace_size(kv, q_len);
+    case SA_OP_PREFILL_FUSED:
+      return sparse_attn_prefill_fused_workspace_size(kv, num_q_heads, q_len, q_tail, top_k, extra);
+    case SA_OP_DECODE: return sparse_attn_decode_workspace_size(kv, num_q_heads, top_k, extra);
+    default: return 0;
+  }
+}
+
+int32_t sparse_attn_validate(const sa_paged_kv* kv, const int32_t* indices, int32_t index_width,
+                             int32_t q_len, int32_t q_tail, int32_t* report, void* stream) {
+  sa::KvView v;
+  int32_t st = check_kv(kv, 0, &v);
+  if (st != SA_OK) return st;
+  if (report == nullptr) return SA_ERR_NULL;
+  if (!aligned16(report)) return SA_ERR_ALIGN;
+  if (indices != nullptr) {
+    if ((st = check_block(v, q_len, q_tail)) != SA_OK) return st;
+    if (index_width < 1) return SA_ERR_SHAPE;
+    if (!aligned16(indices)) return SA_ERR_ALIGN;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sa::launch_check_reset(report, s) != hipSuccess) return SA_ERR_HIP;
+  return hip_status(sa::launch_check(v, indices, indices != nullptr ? index_width : 0, q_len, q_tail,
+                                     report, s));
+}
+
+int32_t sparse_attn_check_report(int32_t* report, void* stream) {
+  if (report == nullptr) return SA_ERR_NULL;
+  if (!aligned16(report)) return SA_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* lib_report = nullptr;
+  if (sa::check_report_ptr(&lib_report, s) != hipSuccess) return SA_ERR_HIP;
+  return hip_status(sa::launch_check_copy_reset(lib_report, report, s));
 }
 
 int32_t sparse_attn_calib_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups,

@@ -190,6 +190,14 @@ hipError_t launch_attn_masked_records(const KvView& kv, const uint16_t* q, int n
 bool sel_thresh_applies(const KvView& kv);
 hipError_t launch_sel_thresh(const KvView& kv, const int8_t* q_idx, int q_len, int q_tail, int top_k,
                              int32_t* thresholds, uint64_t* sel, hipStream_t stream);
+// Validation of device-side contents (sequence lengths, page-table entries, index lists) into
+// an int32 [kReportWords] report; the SPARSE_ATTN_CHECK mode adds to a report of the library.
+constexpr int kReportWords = 8;
+hipError_t launch_check(const KvView& kv, const int32_t* indices, int index_width, int q_len, int q_tail,
+                        int32_t* report, hipStream_t stream);
+hipError_t launch_check_reset(int32_t* report, hipStream_t stream);
+hipError_t launch_check_copy_reset(int32_t* report, int32_t* out, hipStream_t stream);
+hipError_t check_report_ptr(int32_t** ptr, hipStream_t stream);
 // Roofline micro-benchmarks (streaming read, random 256-byte row gather, MFMA loops).
 hipError_t launch_calib_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups,
                              hipStream_t stream);

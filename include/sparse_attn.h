@@ -33,6 +33,9 @@
  *              caller's contract and are not validated. Kernels still never read or write
  *              out of bounds: a page id outside [0, num_pages) or an index outside the
  *              query's causal range is skipped, which makes the result unspecified but safe.
+ *              sparse_attn_validate reports such contents; with SPARSE_ATTN_CHECK=1 in the
+ *              environment every call validates the device data it reads first, into a report
+ *              of the library that sparse_attn_check_report reads back.
  *  Alignment   Every array pointer must be 16-byte aligned (SA_ERR_ALIGN otherwise).
  *  Threads     Calls are re-entrant; concurrent calls on different streams are safe as long
  *              as their output and workspace buffers do not overlap.
@@ -379,6 +382,48 @@ int32_t sparse_attn_fwd_decode_noalloc(const sa_paged_kv* kv, const uint16_t* q,
                                        int32_t num_q_heads, const int32_t* indices,
                                        int32_t index_width, float sm_scale, int32_t num_splits,
                                        uint16_t* out, float* lse, void* stream);
+
+/*
+ * Workspace of any call in one function: the bytes the call `op` needs for these sizes
+ * (0 when it needs none, or when the sizes are invalid for it). `extra` is the call's own
+ * parameter: the local window (SA_OP_INDEX_TOPK_WINDOW), the path (SA_OP_PREFILL_FUSED) or
+ * num_splits (SA_OP_DECODE, where top_k is the index width); it is ignored otherwise. q_tail
+ * matters only for SA_OP_PREFILL_FUSED, num_q_heads for it and SA_OP_DECODE. Equal to the
+ * per-call *_workspace_size functions.
+ */
+enum sa_op {
+  SA_OP_TOPK = 1,
+  SA_OP_INDEX_TOPK = 2,
+  SA_OP_INDEX_TOPK_WINDOW = 3,
+  SA_OP_PREFILL_MASKED = 4,
+  SA_OP_PREFILL_FUSED = 5,
+  SA_OP_DECODE = 6
+};
+size_t sparse_attn_workspace_size(int32_t op, const sa_paged_kv* kv, int32_t q_len, int32_t q_tail,
+                                  int32_t top_k, int32_t num_q_heads, int32_t extra);
+
+/*
+ * Validation of device data (the checks SPARSE_ATTN_CHECK=1 runs before every call).
+ * Report: int32 [8] of device memory, written on the stream:
+ *   [0] sequence lengths outside [1, max_seq_len]
+ *   [1] page-table entries outside [0, num_pages), among the pages each sequence's tokens use
+ *   [2] index-list entries that are neither -1 nor a token in [0, pos] of their query
+ *   [3] index-list entries that do not follow the list's ascending order (-1 only at the end)
+ *   [4] flat position (b * max_pages_per_seq + p) of the first bad page-table entry, else INT32_MAX
+ *   [5] flat position of the first bad list entry (row * index_width + k), else INT32_MAX
+ *   [6] calls checked, [7] 0
+ * sparse_attn_validate clears `report`, then checks the descriptor's sequence lengths and page
+ * table and, when indices is not NULL, the lists indices [batch][q_len][num_idx_heads]
+ * [index_width] of a block of q_len queries at q_tail (positions as for the other calls).
+ * With SPARSE_ATTN_CHECK=1 in the environment, every entry point taking a descriptor (except
+ * the block allocator's) runs the same checks on what it reads before its own launches, adding
+ * to a report of the library (a static device array per GPU, so no allocation);
+ * sparse_attn_check_report copies it into `report` on the stream and clears it. Calls that
+ * overlap on one GPU add to the same report.
+ */
+int32_t sparse_attn_validate(const sa_paged_kv* kv, const int32_t* indices, int32_t index_width,
+                             int32_t q_len, int32_t q_tail, int32_t* report, void* stream);
+int32_t sparse_attn_check_report(int32_t* report, void* stream);
 
 /*
  * Roofline micro-benchmarks. They measure what the device reaches on the operations the path is

@@ -448,6 +448,50 @@ def test_prefill_fused_dispatch_and_workspace(lib):
     assert ws(2048, 2048, 2048, 9) == 0   # not a path
 
 
+def call_validate(lib, d, idx=A, width=64, q_len=1, q_tail=1, report=A + 0x500):
+    return lib.sparse_attn_validate(None if d is None else ctypes.byref(d), idx, width, q_len, q_tail,
+                                    report, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(d=None), fa.SA_ERR_NULL),
+    (dict(d=desc(abi_version=3)), fa.SA_ERR_ABI),
+    (dict(d=desc(page_table=None)), fa.SA_ERR_NULL),
+    (dict(report=None), fa.SA_ERR_NULL),
+    (dict(report=A + 4), fa.SA_ERR_ALIGN),
+    (dict(idx=A + 4), fa.SA_ERR_ALIGN),
+    (dict(width=0), fa.SA_ERR_SHAPE),
+    (dict(q_len=3, q_tail=2), fa.SA_ERR_SHAPE),
+    (dict(q_tail=1025), fa.SA_ERR_SHAPE),
+])
+def test_validate_arguments(lib, case, code):
+    case = dict(case)
+    d = case.pop("d", desc())
+    assert call_validate(lib, d, **case) == code
+
+
+def test_check_report_arguments(lib):
+    assert lib.sparse_attn_check_report(None, None) == fa.SA_ERR_NULL
+    assert lib.sparse_attn_check_report(A + 4, None) == fa.SA_ERR_ALIGN
+
+
+def test_workspace_size_by_op_equals_the_per_call_functions(lib):
+    d = desc(max_pages_per_seq=512, max_seq_len=32768, num_pages=1024)
+    r = ctypes.byref(d)
+    ws = lambda op, q_len, q_tail, k, hq, extra: lib.sparse_attn_workspace_size(op, r, q_len, q_tail, k, hq, extra)
+    assert ws(fa.SA_OP_TOPK, 1, 1, 2048, 32, 0) == lib.sparse_attn_topk_workspace_size(r, 1, 2048)
+    assert ws(fa.SA_OP_INDEX_TOPK, 2048, 2048, 2048, 32, 0) == lib.sparse_attn_index_topk_workspace_size(r, 2048, 2048)
+    assert ws(fa.SA_OP_INDEX_TOPK_WINDOW, 1, 1, 2048, 32, 512) == \
+        lib.sparse_attn_index_topk_window_workspace_size(r, 1, 2048, 512)
+    assert ws(fa.SA_OP_PREFILL_MASKED, 2048, 2048, 0, 32, 0) == lib.sparse_attn_prefill_masked_workspace_size(r, 2048)
+    for path in (0, 1, 2):
+        assert ws(fa.SA_OP_PREFILL_FUSED, 2048, 4096, 2048, 32, path) == \
+            lib.sparse_attn_prefill_fused_workspace_size(r, 32, 2048, 4096, 2048, path)
+    assert ws(fa.SA_OP_DECODE, 1, 1, 2048, 32, 8) == lib.sparse_attn_decode_workspace_size(r, 32, 2048, 8)
+    assert ws(fa.SA_OP_DECODE, 1, 1, 2048, 32, 8) > 0
+    assert ws(99, 1, 1, 2048, 32, 0) == 0
+
+
 def call_index_topk(lib, d, q_idx=A, q_len=1, q_tail=1, k=64, idx=A, ws=A, ws_bytes=1 << 34):
     return lib.sparse_attn_index_topk(ctypes.byref(d), q_idx, q_len, q_tail, k, idx, ws, ws_bytes, None)
 
