@@ -643,6 +643,74 @@ def bench_decode_1m(fa, steps, warmup, workload="sparse_decode_1m_prefix", seed=
     return res
 
 
+def bench_decode_concentrated(fa, evict, steps=20):
+    """The 128K decode selection (sparse_attn_index_topk) on score layouts far from i.i.d.,
+    each against the same call on the i.i.d. inputs of the headline step (cold-cache medians):
+      concentrated  i.i.d. scores, except that in every row one 8192-token chunk holds most of
+                    the top-K: its first 1024 tokens score highest, its next 1536 lower but
+                    still above every other key, so that chunk's sampled threshold lies above
+                    the row's K-th largest key and the selection must rescore it
+      narrow        the same chunk layout over small keys (values in [-20, 20], every query
+                    element 2), whose scores all fall into one or two histogram bins
+      all_equal     every indexer key zero: every score ties, the top-K is the first K tokens"""
+    import torch
+
+    from synthetic import CONFIGS, make_inputs
+    w = CONFIGS["sparse_decode_128k"]
+
+    def timed_select(inp):
+        kv = fa.PagedKV(k_pool=inp.k_pool, v_pool=inp.v_pool, kidx_pool=inp.kidx_pool,
+                        page_table=inp.page_table, seq_lens=inp.seq_lens, max_seq_len=w.seq_len,
+                        prefix_len=w.prefix_len)
+        idx = torch.empty((w.batch, 1, inp.num_idx_heads, w.top_k), dtype=torch.int32, device="cuda")
+        n = fa.sparse_attn_index_topk_workspace_size(kv, 1, w.top_k)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            fa.sparse_attn_index_topk(kv, inp.q_idx, 1, 1, w.top_k, idx, ws, n)
+        ts = []
+        for _ in range(steps):
+            evict()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fa.sparse_attn_index_topk(kv, inp.q_idx, 1, 1, w.top_k, idx, ws, n)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    inp = make_inputs(w, seed=3, device="cuda")
+    kidx0 = inp.kidx_pool.clone()
+    q0 = inp.q_idx.clone()
+    out = {"workload": w.name, "cache": "evicted by a 1 GiB read before each call",
+           "select_ms_iid": timed_select(inp)}
+    table = inp.page_table.long()
+    first, second = table[:, 256:272], table[:, 272:296]  # tokens 16384..17407, 17408..18943
+
+    def plant(hi, lo):
+        for b in range(w.batch):
+            sgn = torch.sign(inp.q_idx[b, 0].to(torch.int16)).to(torch.int8)  # [H_idx][d_idx]
+            inp.kidx_pool[first[b]] = (sgn * hi)[None, :, None, :]
+            inp.kidx_pool[second[b]] = (sgn * lo)[None, :, None, :]
+
+    plant(127, 64)
+    out["select_ms_concentrated"] = timed_select(inp)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    inp.q_idx.fill_(2)
+    inp.kidx_pool.copy_(torch.randint(-20, 21, inp.kidx_pool.shape, generator=g, device="cuda",
+                                      dtype=torch.int16).to(torch.int8))
+    plant(127, 64)
+    out["select_ms_narrow"] = timed_select(inp)
+    inp.kidx_pool.zero_()
+    inp.q_idx.copy_(q0)
+    out["select_ms_all_equal"] = timed_select(inp)
+    for k in ("concentrated", "narrow", "all_equal"):
+        out["ratio_" + k] = out["select_ms_" + k] / out["select_ms_iid"]
+    del inp, kidx0, q0
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -809,6 +877,7 @@ def main():
         result["sparse_prefill"] = bench_sparse_prefill(fa, reps=10, calib=calib)
         result["decode_1m_prefix"] = bench_decode_1m(fa, steps=10, warmup=3,
                                                      evict=None if args.warm_cache else evict)
+        result["decode_128k_concentrated_top"] = bench_decode_concentrated(fa, evict)
         del evict_buf
         torch.cuda.empty_cache()
         result["tiny_sparse_prefill"] = bench_tiny(fa)

@@ -9,16 +9,22 @@
 //
 // Two launches over rows r = (sequence, indexer head):
 //   main    per (row, 8192-token chunk): scores every key of the chunk; the histogram of key >> 12
-//           over the chunk's first 4096 keys sets the chunk's threshold bin theta_c (the highest
-//           bin whose tail holds well over those keys' share of K), and the keys in bins >=
-//           theta_c are compacted, in token order, into the chunk's candidate slots.
-//   final   one workgroup per row: the histogram of the candidates gives b1, the bin of the
-//           K-th largest candidate. If b1 >= theta_c for every chunk, every key of the row in
-//           a bin >= b1 is a candidate, so the K-th largest key of the row is in bin b1 and the
-//           exact selection runs on the candidates (a few thousand per row). Otherwise (a chunk
-//           holds far more than its share of the top) the workgroup rescores the row: an exact
-//           histogram first, then every key in bins >= the exact b1 is collected, so the
-//           result stays exact whatever the score distribution.
+//           over the chunk's first 4096 keys sets the chunk's threshold theta_c: the lower edge
+//           of the highest bin whose tail holds well over those keys' share of K, refined to a
+//           single key by a histogram of that bin's low digits when the bin alone holds many
+//           more (scores packed into a few bins). The keys >= theta_c are compacted, in token
+//           order, into the chunk's candidate slots, except that keys equal to theta_c stop
+//           being kept once the chunk holds K candidates: each later one has K keys of its own
+//           chunk ranked above it (larger, or equal and earlier), so it is not in the top K.
+//           With every score equal this keeps about K keys per chunk instead of all of them.
+//   final   one workgroup per row: tau_c, the K-th largest candidate key. If tau_c >= theta_c
+//           for every chunk, every key of the row >= tau_c is a candidate, so tau_c is the
+//           row's K-th largest key and the exact selection runs on the candidates (a few
+//           thousand per row). Otherwise (a chunk holds far more than its share of the top)
+//           the workgroup rescores the chunks whose threshold lies above tau_c: an exact
+//           histogram (their keys plus the other chunks' candidates) first, then every key of
+//           theirs in bins >= the exact b1 is collected, so the result stays exact whatever the
+//           score distribution.
 #include "sa_index_dev.h"
 #include "sa_select_dev.h"
 
@@ -217,11 +223,10 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
     s_sample[sl][tid] = make_uint4(in[0] ? key[0] : kNotIn, in[1] ? key[1] : kNotIn,
                                    in[2] ? key[2] : kNotIn, in[3] ? key[3] : kNotIn);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (in[u]) atomicAdd(&sh.hist[key[u] >> 12], 1u);
+    for (int u = 0; u < U; ++u) hist_add_wave(sh.hist, key[u] >> 12, in[u]);
   }
   __syncthreads();
-  uint32_t th = 0;
+  uint32_t th = 0;  // the chunk keeps its keys >= th
   {
     int cnt = 0;
     for (int j = tid; j < kBins; j += NT) cnt += sh.hist[j];
@@ -231,7 +236,29 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
     const int target = (int)(2.f * expect + 3.f * sqrtf(expect) + 8.f);
     if (n_s >= 256 && target < n_s) {  // short samples (row edges) keep everything
       find_bin<NT>(sh, target);
-      th = (uint32_t)sh.found_bin;
+      const uint32_t tb = (uint32_t)sh.found_bin;
+      const int above = sh.found_above;
+      const int tail = above + (int)sh.hist[tb];
+      th = tb << 12;
+      if (tail > 2 * target) {
+        // The bin is crowded (scores packed into few bins): refine the threshold to one key
+        // with a histogram of the sample's keys in that bin.
+        __syncthreads();
+        for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
+        if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
+        __syncthreads();
+#pragma unroll
+        for (int sl = 0; sl < kSampleSlabs; ++sl) {
+          const uint4 pk = s_sample[sl][tid];
+          const uint32_t kk[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            hist_add_wave(sh.hist, kk[u] & 0xfffu, kk[u] != kNotIn && (kk[u] >> 12) == tb);
+        }
+        __syncthreads();
+        find_bin<NT>(sh, target - above);
+        th |= (uint32_t)sh.found_bin;
+      }
     }
   }
   int fill = 0;
@@ -243,7 +270,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       tok[u] = ((blk0 + u) << 6) + lane;
-      keep[u] = key[u] != kNotIn && (key[u] >> 12) >= th;
+      keep[u] = key[u] != kNotIn && (key[u] > th || (key[u] == th && fill < top_k));
     }
     fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, fill);
   }
@@ -251,7 +278,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
     score_slab(slab, kd, ok, key, in, tok);
     next_slab(slab);
 #pragma unroll
-    for (int u = 0; u < U; ++u) keep[u] = in[u] && (key[u] >> 12) >= th;
+    for (int u = 0; u < U; ++u) keep[u] = in[u] && (key[u] > th || (key[u] == th && fill < top_k));
     fill = compact_slab<NW, U>(key, keep, tok, sh.wave_tot2, dst, fill);
   }
   if (tid == 0) {
@@ -268,9 +295,9 @@ constexpr int kFineShift = 8;  // fine bins are 256 key units; 1024 of them span
 
 // Exact selection for one row from the candidates held in registers. Wave w owns chunks
 // [w*cpw, (w+1)*cpw) and their candidates, in token order, as e[k] for index k*64 + lane.
-// Every key of the row in a coarse bin (key >> 12) at or above theta_max, the highest chunk
-// threshold, is a candidate; so if at least K candidates lie at or above theta_max << 12, the
-// K largest keys of the row are the K largest of those candidates. A 1024-bin histogram of
+// Every key of the row at or above theta_max, the highest chunk threshold, is a candidate; so
+// if at least K candidates lie at or above theta_max, the K largest keys of the row are the K
+// largest of those candidates. A 1024-bin histogram of
 // 256-unit fine bins above that base locates the K-th largest to one fine bin and a 256-entry
 // histogram of that bin gives it exactly. Returns false (uniformly, nothing written) when a
 // wave holds more candidates than its registers, when fewer than K candidates lie above the
@@ -357,13 +384,13 @@ __device__ __forceinline__ bool select_row_registers(TopkShared<NT>& sh, const F
     }
     if (j < wtot) e[k] = cw[ci * (int64_t)kFChunk + (j - off)];
   }
-  const uint32_t base = thmax << 12;
+  const uint32_t base = thmax;
 #pragma unroll
   for (int k = 0; k < kRegPer; ++k) {
     if (k * 64 >= wtot) break;
     const uint32_t key = (uint32_t)e[k].x;
-    if (k * 64 + lane < wtot && key >= base)
-      atomicAdd(&sh.hist[min((key - base) >> kFineShift, (uint32_t)kFineBins - 1)], 1u);
+    hist_add_wave(sh.hist, min((key - base) >> kFineShift, (uint32_t)kFineBins - 1),
+                  k * 64 + lane < wtot && key >= base);
   }
   __syncthreads();
   static_assert(kFineBins == NW * 64, "one 64-bin segment per wave");
@@ -376,8 +403,9 @@ __device__ __forceinline__ bool select_row_registers(TopkShared<NT>& sh, const F
   for (int k = 0; k < kRegPer; ++k) {
     if (k * 64 >= wtot) break;
     const uint32_t key = (uint32_t)e[k].x;
-    if (k * 64 + lane < wtot && key >= fb_lo && key < fb_lo + (1u << kFineShift))
-      atomicAdd(&sh.hist[kFineBins + (key & 255u)], 1u);
+    // fb_lo need not be 256-aligned: the sub-bin is the offset from it
+    hist_add_wave(sh.hist + kFineBins, key - fb_lo,
+                  k * 64 + lane < wtot && key >= fb_lo && key < fb_lo + (1u << kFineShift));
   }
   __syncthreads();
   int above_sb;
@@ -458,29 +486,52 @@ __global__ __launch_bounds__(kFinalNT) void k_fused_final(KvView kv, const int8_
   __syncthreads();
   if (tid < chunks) atomicMax(&s_thmax, cth[tid]);  // the highest chunk threshold
   __syncthreads();
-  // b1 from the candidates, valid when no chunk threshold lies above it
+  // the selection from the candidates, valid when their K-th largest key is >= every chunk's
+  // threshold
+  uint32_t lb = 0;
   if (!select_candidates<NT>(sh, s_off, cand, cc, chunks, kFChunk, 0u, 0, top_k, out + r.nf,
-                             s_thmax)) {
-    // Some chunk kept only bins above b1: the candidates may miss part of the top. Rescore
-    // the row: the exact histogram first, then every key in bins >= the exact b1.
+                             s_thmax, &lb)) {
+    // Some chunk's threshold lies above lb = tau_c, the candidates' K-th largest key: such a
+    // chunk may miss part of the top, and only those chunks are rescored. Every other chunk's
+    // threshold is <= tau_c, and it kept all its keys >= that threshold but ties dropped past
+    // K candidates, which are never in the top K. Adding keys only raises the K-th largest, so
+    // tau_c <= tau, the row's K-th largest key, and those chunks hold every key > tau and
+    // enough ties at tau, in token order, for the top K. A histogram of their candidates plus
+    // every key of the rescored chunks then counts every bin above tau's exactly and reaches K
+    // at tau's bin b1, which gives the row's b1 and the count above it; the rescored chunks'
+    // candidates are rewritten with every key in bins >= b1, and the final selection sees
+    // every key of the top K.
+    __syncthreads();
     const v4i qf = *reinterpret_cast<const v4i*>(q_idx + (row * (int64_t)D) + lane_part<D>(lane) * 16);
     for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
     if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
     __syncthreads();
-    for (int blk = r.blk_first + wave; blk <= r.blk_last; blk += NW) {
-      const int64_t base = block_base<D>(kv, r.b, r.gi, blk);
-      if (base < 0) continue;  // wave-uniform
-      v4i kd[Blk<D>::R];
-      load_block<D>(kv.kidx_pool + base, lane, kd);
-      const int s = to_token_order<D>(score_block<D>(qf, kd, lane), lane);
-      const int tok = (blk << 6) + lane;
-      if (tok >= r.P && tok <= r.pos) atomicAdd(&sh.hist[score_key(s) >> 12], 1u);
+    auto offending = [&](int ch) { return (uint32_t)cth[ch] > lb; };
+    for (int ch = 0; ch < chunks; ++ch) {
+      if (offending(ch)) {
+        if (ch * kFChunk > r.pos) continue;
+        const int blk0 = max(r.blk_first, ch * kFBlocks), blk1 = min(r.blk_last, ch * kFBlocks + kFBlocks - 1);
+        for (int blk = blk0 + wave; blk <= blk1; blk += NW) {
+          const int64_t base = block_base<D>(kv, r.b, r.gi, blk);
+          if (base < 0) continue;  // wave-uniform
+          v4i kd[Blk<D>::R];
+          load_block<D>(kv.kidx_pool + base, lane, kd);
+          const int s = to_token_order<D>(score_block<D>(qf, kd, lane), lane);
+          const int tok = (blk << 6) + lane;
+          if (tok >= r.P && tok <= r.pos) atomicAdd(&sh.hist[score_key(s) >> 12], 1u);
+        }
+      } else {
+        const int2* cch = cand + (int64_t)ch * kFChunk;
+        const int n = cc[ch];
+        for (int j = tid; j < n; j += NT) atomicAdd(&sh.hist[(uint32_t)cch[j].x >> 12], 1u);
+      }
     }
     __syncthreads();
     find_bin<NT>(sh, top_k);
     const uint32_t b1 = (uint32_t)sh.found_bin;
     const int above1 = sh.found_above;
     for (int ch = 0; ch < chunks; ++ch) {
+      if (!offending(ch)) continue;  // uniform: every thread reads the same threshold
       int2* dst = w.cand + (row * chunks + ch) * (int64_t)kFChunk;
       int fill = 0;
       if (ch * kFChunk <= r.pos) {

@@ -156,6 +156,19 @@ __device__ __forceinline__ int block_incl_scan(int v, int32_t* wave_tot, int* to
   return v + before;
 }
 
+// Adds one to hist[bin] for every active lane of the wave. The lanes whose bin equals the
+// first active lane's add together with one atomic, so a wave whose keys share a bin (packed
+// or tied scores) costs one LDS atomic instead of 64 serialised on one address.
+__device__ __forceinline__ void hist_add_wave(uint32_t* hist, uint32_t bin, bool active) {
+  const uint64_t act = __ballot(active);
+  if (act == 0) return;
+  const int first = __builtin_ctzll(act);
+  const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
+  const uint64_t same = __ballot(active && bin == b0);
+  if (active && bin != b0) atomicAdd(&hist[bin], 1u);
+  if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[b0], (uint32_t)__popcll(same));
+}
+
 // Largest bin b with sum(hist[b..]) >= k; stores b and sum(hist[b+1..]) in shared memory.
 template <int NT>
 __device__ __forceinline__ void find_bin(TopkShared<NT>& sh, int k) {
@@ -201,17 +214,18 @@ __device__ __forceinline__ int block_excl_scan(int v, int32_t* wave_tot, int* to
 // and each wave then writes its taken keys in order. Two barriers instead of two
 // workgroup scans per 1024 candidates.
 //
-// With check_bin >= 0, b1 and above1 are not given: they are taken from the candidates' own
-// histogram, which equals the row's for every bin >= check_bin. If b1 < check_bin that is not
-// enough to know the row's K-th largest key: nothing is written and the call returns false
-// (uniformly). Otherwise, and always with check_bin < 0, it returns true.
+// With check_key >= 0, b1 and above1 are not given: they are taken from the candidates' own
+// histogram, and the candidates must hold every key of the row >= check_key. If the K-th
+// largest candidate key tau is below check_key, that is not enough to know the row's K-th
+// largest key: nothing is written, *tau_lb receives tau and the call returns false
+// (uniformly). Otherwise, and always with check_key < 0, it returns true.
 template <int NT>
 __device__ __forceinline__ bool select_candidates(TopkShared<NT>& sh, int32_t* s_off,
                                                   const int2* __restrict__ cand,
                                                   const int32_t* __restrict__ ccount, int chunks,
                                                   int chunk_cap, uint32_t b1, int above1,
                                                   int top_k, int32_t* __restrict__ out,
-                                                  int check_bin = -1) {
+                                                  int check_key = -1, uint32_t* tau_lb = nullptr) {
   constexpr int NW = NT / 64;
   constexpr int kPer = 8;  // candidates per lane loaded together
   const int tid = threadIdx.x;
@@ -248,26 +262,29 @@ __device__ __forceinline__ bool select_candidates(TopkShared<NT>& sh, int32_t* s
       const int j = seg_begin + k * 64 + lane;
       e[k] = (j < total) ? fetch(j) : make_int2(0, 0);
     }
-    if (check_bin >= 0) {  // b1 from the candidates' high digits
+    if (check_key >= 0) {  // b1 from the candidates' high digits
 #pragma unroll
       for (int k = 0; k < kPer; ++k)
-        if (seg_begin + k * 64 + lane < total) atomicAdd(&sh.hist[(uint32_t)e[k].x >> 12], 1u);
+        hist_add_wave(sh.hist, (uint32_t)e[k].x >> 12, seg_begin + k * 64 + lane < total);
       __syncthreads();
       find_bin<NT>(sh, top_k);
       b1 = (uint32_t)sh.found_bin;
       above1 = sh.found_above;
-      if ((int)b1 < check_bin) return false;
       for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
       if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
       __syncthreads();
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
-      if (seg_begin + k * 64 + lane < total && ((uint32_t)e[k].x >> 12) == b1)
-        atomicAdd(&sh.hist[(uint32_t)e[k].x & 0xfff], 1u);
+      hist_add_wave(sh.hist, (uint32_t)e[k].x & 0xfff,
+                    seg_begin + k * 64 + lane < total && ((uint32_t)e[k].x >> 12) == b1);
     __syncthreads();
     find_bin<NT>(sh, top_k - above1);
     const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
+    if (check_key >= 0 && (int)tau < check_key) {
+      *tau_lb = tau;
+      return false;
+    }
     const int need = top_k - above1 - sh.found_above;
     int gt_w = 0, eq_w = 0;
 #pragma unroll
@@ -305,7 +322,7 @@ __device__ __forceinline__ bool select_candidates(TopkShared<NT>& sh, int32_t* s
     return true;
   }
   // General path (more candidates than the workgroup holds at once): streamed passes.
-  if (check_bin >= 0) {  // b1 from the candidates' high digits
+  if (check_key >= 0) {  // b1 from the candidates' high digits
     for (int base = 0; base < total; base += NT * kPer) {
       int2 e[kPer];
 #pragma unroll
@@ -315,13 +332,12 @@ __device__ __forceinline__ bool select_candidates(TopkShared<NT>& sh, int32_t* s
       }
 #pragma unroll
       for (int k = 0; k < kPer; ++k)
-        if (base + k * NT + tid < total) atomicAdd(&sh.hist[(uint32_t)e[k].x >> 12], 1u);
+        hist_add_wave(sh.hist, (uint32_t)e[k].x >> 12, base + k * NT + tid < total);
     }
     __syncthreads();
     find_bin<NT>(sh, top_k);
     b1 = (uint32_t)sh.found_bin;
     above1 = sh.found_above;
-    if ((int)b1 < check_bin) return false;
     for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0u;
     if (tid == 0) { sh.found_bin = 0; sh.found_above = 0; }
     __syncthreads();
@@ -336,12 +352,16 @@ __device__ __forceinline__ bool select_candidates(TopkShared<NT>& sh, int32_t* s
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
-      if (base + k * NT + tid < total && ((uint32_t)e[k].x >> 12) == b1)
-        atomicAdd(&sh.hist[(uint32_t)e[k].x & 0xfff], 1u);
+      hist_add_wave(sh.hist, (uint32_t)e[k].x & 0xfff,
+                    base + k * NT + tid < total && ((uint32_t)e[k].x >> 12) == b1);
   }
   __syncthreads();
   find_bin<NT>(sh, top_k - above1);
   const uint32_t tau = (b1 << 12) | (uint32_t)sh.found_bin;
+  if (check_key >= 0 && (int)tau < check_key) {
+    *tau_lb = tau;
+    return false;
+  }
   const int need = top_k - above1 - sh.found_above;
 
   // wave segments of whole 64-entry steps

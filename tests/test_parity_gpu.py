@@ -368,6 +368,37 @@ def test_fused_index_topk_concentrated_chunk_rescore():
     assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
 
 
+@pytest.mark.parametrize("case", ["all_equal", "equal_with_some_higher", "narrow"])
+def test_fused_index_topk_packed_scores(case):
+    """Scores packed into one or two histogram bins, where a chunk's threshold is refined to a
+    single key and keys equal to it stop being kept once the chunk holds K candidates:
+      all_equal               every indexer key zero, so the top-K is the first K tokens
+      equal_with_some_higher  zero keys except scattered blocks of small positive keys, so the
+                              top holds those blocks plus the earliest ties
+      narrow                  small random keys (values in [-20, 20]) under a constant query"""
+    w = W(batch=2, seq_len=65536, q_len=1, top_k=2048, prefix_len=3)
+    _banner(f"fused index+topk, packed scores: {case}")
+    inp = make_inputs(w, seed=21, device="cpu", seq_lens=[65536, 40001])
+    k = inp.kidx_pool
+    if case == "narrow":
+        inp.q_idx.fill_(2)
+        k.copy_(torch.randint(-20, 21, k.shape, generator=torch.Generator().manual_seed(5)).to(torch.int8))
+    else:
+        inp.q_idx.fill_(1)
+        k.zero_()
+        if case == "equal_with_some_higher":
+            table = inp.page_table
+            for b in range(w.batch):
+                for j in range(9):       # 9 blocks of 64 keys spread over the first 40000 tokens
+                    k[table[b, 3 + 67 * j]] = 1 + j % 3
+    inp = inp.to(DEV)
+    fused = run_gpu(inp, fused=True)
+    two = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.indices, two.indices)
+    assert_close(compare_rows(fused, OracleView(inp), all_rows(inp)))
+
+
 def test_fused_index_topk_spread_maximal_blocks():
     """24 blocks of maximal keys spread over the row (every 4th block pattern) among small
     random keys: the lists must still equal the two-step path and the oracle."""
