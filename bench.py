@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--calibrate", action="store_true",
                     help="only the roofline micro-benchmarks (measured ceilings)")
     ap.add_argument("--no-calibrate", action="store_true")
+    ap.add_argument("--no-layouts", action="store_true",
+                    help="skip the 128K selection on adversarial score layouts (kernel traces "
+                         "attribute dispatches by kernel and grid, which those runs share)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the dense 8K prefill (for counter runs)")
     ap.add_argument("--dispatch-sweep", action="store_true",
@@ -643,7 +646,7 @@ def bench_decode_1m(fa, steps, warmup, workload="sparse_decode_1m_prefix", seed=
     return res
 
 
-def bench_decode_concentrated(fa, evict, steps=20):
+def bench_decode_adversarial(fa, evict, steps=20):
     """The 128K decode selection (sparse_attn_index_topk) on score layouts far from i.i.d.,
     each against the same call on the i.i.d. inputs of the headline step (cold-cache medians):
       concentrated  i.i.d. scores, except that in every row one 8192-token chunk holds most of
@@ -877,7 +880,8 @@ def main():
         result["sparse_prefill"] = bench_sparse_prefill(fa, reps=10, calib=calib)
         result["decode_1m_prefix"] = bench_decode_1m(fa, steps=10, warmup=3,
                                                      evict=None if args.warm_cache else evict)
-        result["decode_128k_concentrated_top"] = bench_decode_concentrated(fa, evict)
+        if not args.no_layouts:
+            result["decode_128k_adversarial_layouts"] = bench_decode_adversarial(fa, evict)
         del evict_buf
         torch.cuda.empty_cache()
         result["tiny_sparse_prefill"] = bench_tiny(fa)
