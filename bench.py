@@ -184,11 +184,12 @@ def _host_cores():
     return cores, blas
 
 
-def cpu_baselines(fa, budget_s=4.0):
+def cpu_baselines(fa, budget_s=4.0, headline_budget_s=12.0):
     """The oracle, untuned, on this host for every workload: numpy float64 with BLAS on all the
     host's cores (the batched oracle functions: exact float64 products for the int8 scores,
     masked-softmax attention for dense rows). Each workload runs on a bounded sample of its rows
-    (about budget_s of CPU time) and is scaled to its unit; the sample is stated."""
+    (about budget_s of CPU time, headline_budget_s for the 128K decode step) and is scaled to its
+    unit; the sample is stated."""
     import numpy as np
     import torch
 
@@ -231,12 +232,13 @@ def cpu_baselines(fa, budget_s=4.0):
         return time.perf_counter() - t0
 
     def sample(name, seed, rows_fn, unit_fn, desc, max_visits=4096):
-        """(sequence, group) pairs visited in turn, again and again, until budget_s is spent."""
+        """(sequence, group) pairs visited in turn, again and again, until the budget is spent."""
         w = CONFIGS[name]
+        budget = headline_budget_s if name == "sparse_decode_128k" else budget_s
         inp = make_inputs(w, seed=seed, device="cuda")
         spent, units, n = 0.0, 0.0, 0
         pairs = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
-        while spent < budget_s and n < max_visits:
+        while spent < budget and n < max_visits:
             b, g = pairs[n % len(pairs)]
             rows = rows_fn(w, n)
             spent += run_rows(w, inp, b, g, rows, inp.seq_lens_host[b])
