@@ -272,6 +272,24 @@ __global__ __launch_bounds__(kThNT, 1) void k_sel_thresh(KvView kv, const int8_t
     const int t = t0 + key_off(mb, r, hi);
     return t >= P && t <= my_pos;
   };
+  // body(mb, r) on the elements of tile t0 that are candidates of this lane's query. A tile
+  // past the prefix and at or below the block's first position is wholly candidate for every
+  // query (the common case: it needs no per-element position test, which would cost as much
+  // as the rest of a pass); only the tiles at the prefix edge and on the diagonal test each.
+  auto for_cands = [&](int t0, auto&& body) {
+    if (t0 >= P && t0 + kTile - 1 <= pos_first) {  // wave-uniform
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) body(mb, r);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (is_cand(t0, mb, r)) body(mb, r);
+    }
+  };
   uint32_t* hq = hist + l32 * kHStride;
 
   const int j_cand0 = P / kTile;                       // first tile holding a candidate
@@ -284,19 +302,7 @@ __global__ __launch_bounds__(kThNT, 1) void k_sel_thresh(KvView kv, const int8_t
     __syncthreads();
     for_tiles(j_cand0, j_cand1, [&](int j, bool ok, const i32x16 (&acc)[2]) {
       if (!ok) return;
-      const int t0 = j * kTile;
-      if (t0 >= P && t0 + kTile - 1 <= pos_first) {  // every pair of the tile is a candidate
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) atomicAdd(&hq[acc[mb][r] >> R::kShift1], 1u);
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (is_cand(t0, mb, r)) atomicAdd(&hq[acc[mb][r] >> R::kShift1], 1u);
-      }
+      for_cands(j * kTile, [&](int mb, int r) { atomicAdd(&hq[acc[mb][r] >> R::kShift1], 1u); });
     });
     __syncthreads();
     // per query: the coarse bin of the K-th largest, the keys above it and the keys in it
@@ -343,16 +349,12 @@ __global__ __launch_bounds__(kThNT, 1) void k_sel_thresh(KvView kv, const int8_t
         if (!ok) return;
         const int t0 = j * kTile;
         const int tb = kTokMask - t0 - hi * 4;  // 131071 - token of element (mb, r) = tb - offset
-        const bool full = t0 >= P && t0 + kTile - 1 <= pos_first;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int a = acc[mb][r];
-            if ((a >> R::kShift1) == my_bin && (full || is_cand(t0, mb, r)))
-              list[my_off + atomicAdd(fill, 1)] = ((uint32_t)(a & fmask) << kTokBits) |
-                                                  (uint32_t)(tb - (mb * 32 + (r >> 2) * 8 + (r & 3)));
-          }
+        for_cands(t0, [&](int mb, int r) {
+          const int a = acc[mb][r];
+          if ((a >> R::kShift1) == my_bin)
+            list[my_off + atomicAdd(fill, 1)] = ((uint32_t)(a & fmask) << kTokBits) |
+                                                (uint32_t)(tb - (mb * 32 + (r >> 2) * 8 + (r & 3)));
+        });
       });
       __syncthreads();
       // per query: the need-th largest list key, 8 bits at a time (histograms per wave)
@@ -408,17 +410,13 @@ __global__ __launch_bounds__(kThNT, 1) void k_sel_thresh(KvView kv, const int8_t
         const int fmask = (1 << dg) - 1;
         for_tiles(j_cand0, j_cand1, [&](int j, bool ok, const i32x16 (&acc)[2]) {
           if (!ok) return;
-          const int t0 = j * kTile;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int a = acc[mb][r];
-              if ((a >> bits) == my_prefix && is_cand(t0, mb, r)) {
-                const int f = (a >> lo) & fmask;
-                atomicAdd(&hq[f >> 1], 1u << ((f & 1) << 4));
-              }
+          for_cands(j * kTile, [&](int mb, int r) {
+            const int a = acc[mb][r];
+            if ((a >> bits) == my_prefix) {
+              const int f = (a >> lo) & fmask;
+              atomicAdd(&hq[f >> 1], 1u << ((f & 1) << 4));
             }
+          });
         });
         __syncthreads();
         for (int qq = wave; qq < kQB; qq += kThWaves) {
@@ -451,12 +449,8 @@ __global__ __launch_bounds__(kThNT, 1) void k_sel_thresh(KvView kv, const int8_t
         const int my_tau = my_tie ? st_prefix[l32] : -1;
         for_tiles(j_cand0, j_cand1, [&](int j, bool ok, const i32x16 (&acc)[2]) {
           if (!ok) return;
-          const int t0 = j * kTile;
           int c = 0;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) c += (acc[mb][r] == my_tau && is_cand(t0, mb, r)) ? 1 : 0;
+          for_cands(j * kTile, [&](int mb, int r) { c += acc[mb][r] == my_tau ? 1 : 0; });
           c += __shfl_xor(c, 32, 64);
           if (hi == 0 && c != 0) cnt[l32 * nt + j] = (uint16_t)c;
         });

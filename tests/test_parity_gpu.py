@@ -678,6 +678,24 @@ def test_thresholds_many_equal_scores(values, seq_len):
     assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
 
 
+@pytest.mark.parametrize("tiles,top_k", [((0, 8), 40), ((3, 11, 19), 150), ((5,), 70)])
+def test_thresholds_boundary_keys_in_one_wave(tiles, top_k):
+    """The keys of the boundary bin all lie in 64-key tiles that one wave of the selection
+    takes (tiles 8 apart), tied at the top score: that wave's list segments overflow and the
+    selection falls back to its histogram passes. Thresholds bit-exact, outputs within the bar."""
+    w = W(batch=1, num_q_heads=8, num_kv_heads=2, seq_len=2048, q_len=64, top_k=top_k)
+    _banner(f"thresholds, boundary keys in tiles {tiles}, K={top_k}")
+    inp = make_inputs(w, seed=44, device="cpu", idx_values=(-1, 0))
+    inp.q_idx.fill_(1)
+    table = inp.page_table
+    for t in tiles:  # 64-token pages: tile t is page t
+        inp.kidx_pool[table[0, t]] = 1
+    inp = inp.to(DEV)
+    gpu = run_gpu(inp, prefill_path=fa.SA_PREFILL_MASKED, thresholds=True)
+    torch.cuda.synchronize()
+    assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
+
+
 def test_fused_prefill_middle_blocks_ragged():
     """Blocks of 160 queries in the middle of sequences of different lengths, with a prefix and
     spare pages: every block through the masked path and the gathered path, every row."""
