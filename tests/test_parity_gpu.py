@@ -681,8 +681,8 @@ def test_thresholds_many_equal_scores(values, seq_len):
 @pytest.mark.parametrize("tiles,top_k", [((0, 8), 40), ((3, 11, 19), 150), ((5,), 70)])
 def test_thresholds_boundary_keys_in_one_wave(tiles, top_k):
     """The keys of the boundary bin all lie in 64-key tiles that one wave of the selection
-    takes (tiles 8 apart), tied at the top score: that wave's list segments overflow and the
-    selection falls back to its histogram passes. Thresholds bit-exact, outputs within the bar."""
+    takes (tiles 8 apart), tied at the top score, so one wave feeds every query's list and the
+    last tie taken decides t_cut. Thresholds bit-exact, outputs within the bar."""
     w = W(batch=1, num_q_heads=8, num_kv_heads=2, seq_len=2048, q_len=64, top_k=top_k)
     _banner(f"thresholds, boundary keys in tiles {tiles}, K={top_k}")
     inp = make_inputs(w, seed=44, device="cpu", idx_values=(-1, 0))
