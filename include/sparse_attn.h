@@ -156,9 +156,11 @@ int32_t sparse_attn_topk(const sa_paged_kv* kv, const int32_t* scores, int64_t s
  *   q_idx    int8  [batch][q_len][num_idx_heads][idx_dim]
  *   indices  int32 [batch][q_len][num_idx_heads][prefix_len + top_k]
  * For decode-shaped calls (q_len == 1, rows of >= 16384 candidates) it scores every key once
- * and writes only the keys above a per-chunk provisional threshold (taken from the chunk's
- * first 4096 keys); the selection checks that no threshold could have dropped a selected key
- * and rescores the row exactly if one could, so the result never depends on the thresholds.
+ * and writes only the keys at or above a per-chunk provisional threshold (taken from the
+ * chunk's first 4096 keys); the selection checks that no threshold could have dropped a
+ * selected key and rescores exactly the chunks whose threshold could have, so the result never
+ * depends on the thresholds (on scores packed into few values or tied, the call takes up to
+ * about twice its time on spread scores).
  * Many-query blocks (q_len >= 16) of rows up to 32768 candidates hold 16-bit order-preserving
  * keys of the scores in the workspace instead (half the traffic) and settle the keys that tie
  * at the K-th largest by recomputing their exact int8 scores. Other shapes run the two-step
