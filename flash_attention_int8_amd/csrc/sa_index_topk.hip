@@ -389,8 +389,8 @@ __device__ __forceinline__ bool select_row_registers(TopkShared<NT>& sh, const F
   for (int k = 0; k < kRegPer; ++k) {
     if (k * 64 >= wtot) break;
     const uint32_t key = (uint32_t)e[k].x;
-    hist_add_wave(sh.hist, min((key - base) >> kFineShift, (uint32_t)kFineBins - 1),
-                  k * 64 + lane < wtot && key >= base);
+    if (k * 64 + lane < wtot && key >= base)
+      atomicAdd(&sh.hist[min((key - base) >> kFineShift, (uint32_t)kFineBins - 1)], 1u);
   }
   __syncthreads();
   static_assert(kFineBins == NW * 64, "one 64-bin segment per wave");
@@ -404,8 +404,8 @@ __device__ __forceinline__ bool select_row_registers(TopkShared<NT>& sh, const F
     if (k * 64 >= wtot) break;
     const uint32_t key = (uint32_t)e[k].x;
     // fb_lo need not be 256-aligned: the sub-bin is the offset from it
-    hist_add_wave(sh.hist + kFineBins, key - fb_lo,
-                  k * 64 + lane < wtot && key >= fb_lo && key < fb_lo + (1u << kFineShift));
+    if (k * 64 + lane < wtot && key >= fb_lo && key < fb_lo + (1u << kFineShift))
+      atomicAdd(&sh.hist[kFineBins + (key - fb_lo)], 1u);
   }
   __syncthreads();
   int above_sb;
