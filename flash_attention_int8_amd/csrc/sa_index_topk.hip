@@ -207,11 +207,12 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 4) void k_fused_main(KvView kv,
       issue_slab(slab + 1, raw_cur, kd, ok);
     }
   };
-  // The chunk's threshold from its first kSampleSlabs slabs, whose keys stay in registers: the
-  // highest bin whose tail holds well over the sample's share of K (twice the expected count
-  // plus three standard deviations plus 8). Any value is safe: the final pass checks it and
-  // rescores the row if it was too high. A larger sample gives a threshold closer to the
-  // sample's share, so fewer candidates reach the final pass.
+  // The chunk's threshold from its first kSampleSlabs slabs: the lower edge of the highest bin
+  // whose tail holds well over the sample's share of K (twice the expected count plus three
+  // standard deviations plus 8), refined to a single key when that bin holds most of the tail.
+  // Any value is safe: the final pass checks it and rescores the chunks whose threshold was too
+  // high. A larger sample gives a threshold closer to the sample's share, so fewer candidates
+  // reach the final pass.
   // The sample keys wait in LDS (each lane reads back only its own), kNotIn marking the
   // tokens that are not candidates; keys are at most 24 bits, so the mark is unambiguous.
   static_assert(U == 4, "one 16-byte LDS entry per lane and slab");
