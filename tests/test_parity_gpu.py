@@ -696,6 +696,19 @@ def test_thresholds_boundary_keys_in_one_wave(tiles, top_k):
     assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
 
 
+@pytest.mark.parametrize("seq_len,q_len", [(70000, 40), (65600, 100)])
+def test_thresholds_rows_over_65535_candidates(seq_len, q_len):
+    """Rows of more than 65535 candidates through the threshold pass (counts past 16 bits);
+    the second case's block straddles that count. Thresholds bit-exact and outputs within the
+    bar."""
+    w = W(batch=1, num_q_heads=8, num_kv_heads=2, seq_len=seq_len, q_len=q_len, top_k=700, prefix_len=5)
+    _banner(f"thresholds, rows of {seq_len} tokens")
+    inp = make_inputs(w, seed=45, device="cpu").to(DEV)
+    gpu = run_gpu(inp, prefill_path=fa.SA_PREFILL_MASKED, thresholds=True)
+    torch.cuda.synchronize()
+    assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
+
+
 def test_fused_prefill_middle_blocks_ragged():
     """Blocks of 160 queries in the middle of sequences of different lengths, with a prefix and
     spare pages: every block through the masked path and the gathered path, every row."""
