@@ -19,8 +19,10 @@
 // Passes over the candidate tiles (64 keys each; every wave takes every 8th tile):
 //   1. histogram of the top 10 bits of acc = s + d_idx * 2^14 (in [0, 2^RB]: 1025 bins of
 //      32-bit counters per query), then per query the bin holding the K-th largest;
-//   2. histograms of the next <= 11 bits among the keys of that bin (16-bit counters, two per
-//      word), repeated until the K-th largest is known exactly;
+//   2. the keys of that bin collected into per-query lists in LDS as (low bits, token) keys,
+//      then per query an 8-bit radix select over its list gives tau and t_cut; when the lists
+//      do not fit, histograms of the next <= 11 bits among the bin's keys (16-bit counters, two
+//      per word) instead, repeated until the K-th largest is known exactly, and then
 //   3. only when some query has more keys equal to tau than it takes: ties counted per 64-key
 //      tile, the tile holding the last tie taken found by a prefix sum, and that tile rescored
 //      key by key to find t_cut;
