@@ -709,6 +709,59 @@ def test_thresholds_rows_over_65535_candidates(seq_len, q_len):
     assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
 
 
+def _random_case(seed):
+    """A small random workload and its input options, drawn from `seed`: batch 1-3, 1-2 KV
+    heads, group 1/2/4/8, d 64/128, d_idx 32/64/128, pages of 64-256 tokens, ragged lengths,
+    a forced prefix, a shared indexer head or tied indexer values now and then."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 4))
+    hkv = int(rng.integers(1, 3))
+    group = int(rng.choice([1, 2, 4, 8]))
+    decode = rng.random() < 0.3
+    q_len = 1 if decode else int(rng.integers(1, 300))
+    t_max = int(rng.integers(max(q_len, 2), 1500))
+    lens = [int(rng.integers(q_len, t_max + 1)) for _ in range(B)]
+    lens[int(rng.integers(0, B))] = t_max
+    dense = (not decode) and rng.random() < 0.15
+    w = W(batch=B, num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=int(rng.choice([64, 128])),
+          seq_len=t_max, q_len=q_len, idx_dim=0 if dense else int(rng.choice([32, 64, 128])),
+          top_k=0 if dense else int(rng.integers(1, 600)),
+          prefix_len=0 if dense or rng.random() < 0.5 else int(rng.integers(1, 11)),
+          page_size=int(rng.choice([64, 128, 256])))
+    kw = dict(seq_lens=lens, spare_pages=int(rng.integers(0, 4)))
+    if not dense and rng.random() < 0.3:
+        kw["num_idx_heads"] = 1
+    if not dense and rng.random() < 0.25:
+        kw["idx_values"] = (-1, 0, 1)
+    return w, kw
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_small_configs_every_row(seed):
+    """Random small workloads (see _random_case) through every path that applies, each against
+    the oracle on every row: decode (two-step and fused selection), or prefill with the two-step
+    lists on gathered rows and on masked tiles, and the fused prefill (automatic and masked
+    paths, with its thresholds), or dense prefill."""
+    w, kw = _random_case(seed)
+    _banner(f"random case {seed}: {w} {kw}")
+    inp = make_inputs(w, seed=500 + seed, device="cpu", **kw).to(DEV)
+    ov = OracleView(inp)
+    rows = all_rows(inp)
+    runs = []
+    if w.dense:
+        runs.append(run_gpu(inp))
+    elif w.q_len == 1:
+        runs += [run_gpu(inp), run_gpu(inp, fused=True)]
+    else:
+        chunk = [None, 64, 96][seed % 3]
+        runs += [run_gpu(inp, q_chunk=chunk), run_gpu(inp, q_chunk=chunk, masked=True),
+                 run_gpu(inp, q_chunk=chunk, prefill_path=fa.SA_PREFILL_AUTO, thresholds=True),
+                 run_gpu(inp, q_chunk=chunk, prefill_path=fa.SA_PREFILL_MASKED)]
+    torch.cuda.synchronize()
+    for r in runs:
+        assert_close(compare_rows(r, ov, rows))
+
+
 def test_fused_prefill_middle_blocks_ragged():
     """Blocks of 160 queries in the middle of sequences of different lengths, with a prefix and
     spare pages: every block through the masked path and the gathered path, every row."""
