@@ -27,6 +27,15 @@
 namespace sa {
 namespace {
 
+// A K or V row piece read with the nontemporal hint: a decode step reads each selected row once,
+// so the rows need not displace cached lines (measured: the 128K step's attention 25.8 -> 24.8
+// us, cold caches).
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
+__device__ __forceinline__ uint4 load_nt(const uint16_t* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSeg = 2048;  // list entries resolved into LDS at a time
@@ -150,8 +159,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_gather(KvView kv, const uint16_
         cok[u] = rid >= 0;
         if (cok[u]) {
           const int64_t o = row_off(rid);
-          ck[u] = *reinterpret_cast<const uint4*>(kbase + o);
-          cv[u] = *reinterpret_cast<const uint4*>(vbase + o);
+          ck[u] = load_nt(kbase + o);
+          cv[u] = load_nt(vbase + o);
         } else {
           ck[u] = make_uint4(0, 0, 0, 0);
           cv[u] = make_uint4(0, 0, 0, 0);

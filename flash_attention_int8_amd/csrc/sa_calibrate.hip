@@ -1,10 +1,11 @@
 // Roofline micro-benchmarks: what one MI355X reaches on the operations the attention path is
 // bound by, measured with the same load and matrix instructions the kernels use. They set the
 // measured denominators of the roofline fractions next to the vendor peaks:
-//   k_calib_read    streaming read of a buffer (16-byte loads, eight in flight per lane)
+//   k_calib_read    streaming read of a buffer (16-byte loads with the nontemporal hint, eight
+//                   in flight per lane; the hint is worth about 13% here, 6.2 -> 7.0 TB/s)
 //   k_calib_gather  random 256-byte rows of a pool (the K or V row of one token at d = 128:
 //                   the decode and sparse-prefill gather unit), 16 lanes per row, eight rows
-//                   in flight per lane group
+//                   in flight per lane group, nontemporal loads as in the decode gather
 //   k_calib_mfma    back-to-back v_mfma_f32_32x32x16_bf16 or v_mfma_i32_32x32x32_i8 on
 //                   register operands, four independent accumulators per wave
 // Each kernel folds what it read or computed into one word per workgroup of `sink`, so the
@@ -18,6 +19,12 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(int)))) int i32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
+
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
 
 constexpr int kCalNT = 256;
 
@@ -45,13 +52,13 @@ __global__ __launch_bounds__(kCalNT) void k_calib_read(const uint4* __restrict__
     const uint4* q = p + c * kChunk + threadIdx.x;
     uint4 v[kCalU];
 #pragma unroll
-    for (int u = 0; u < kCalU; ++u) v[u] = q[u * kCalNT];
+    for (int u = 0; u < kCalU; ++u) v[u] = load_nt(q + u * kCalNT);
 #pragma unroll
     for (int u = 0; u < kCalU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (int64_t i = full * kChunk + (int64_t)blockIdx.x * kCalNT + threadIdx.x; i < n16;
        i += (int64_t)gridDim.x * kCalNT) {
-    const uint4 a = p[i];
+    const uint4 a = load_nt(p + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   fold_to_sink(acc, sink);
@@ -77,12 +84,12 @@ __global__ __launch_bounds__(kCalNT) void k_calib_gather(const uint4* __restrict
     for (int u = 0; u < kCalU; ++u) r[u] = row_of(k + u * ngrp);
     uint4 v[kCalU];
 #pragma unroll
-    for (int u = 0; u < kCalU; ++u) v[u] = pool[r[u] * 16 + lane16];
+    for (int u = 0; u < kCalU; ++u) v[u] = load_nt(pool + r[u] * 16 + lane16);
 #pragma unroll
     for (int u = 0; u < kCalU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; k < n_rows; k += ngrp) {
-    const uint4 a = pool[row_of(k) * 16 + lane16];
+    const uint4 a = load_nt(pool + row_of(k) * 16 + lane16);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   fold_to_sink(acc, sink);

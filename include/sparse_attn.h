@@ -433,7 +433,7 @@ int32_t sparse_attn_check_report(int32_t* report, void* stream);
  * against measured ceilings as well as vendor peaks. The caller times them (e.g. with events on
  * `stream`); each workgroup writes at most one word of `sink` (uint32 [workgroups]).
  *   sparse_attn_calib_read    streams `bytes` (a multiple of 16, >= 16) of `buf` with 16-byte
- *                             loads: bytes / time is the streaming read bandwidth.
+ *                             nontemporal loads: bytes / time is the streaming read bandwidth.
  *   sparse_attn_calib_gather  loads n_rows random 256-byte rows of `pool` (pool_bytes a multiple
  *                             of 256), rows[k] = row number (int32; a number outside the pool
  *                             reads row 0): 256 * n_rows / time is the row-gather bandwidth.
