@@ -66,14 +66,16 @@ __device__ __forceinline__ constexpr int key_off(int mb, int r, int hi) {
   return mb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
 }
 
-// Inclusive prefix sum over the 64 lanes (lane 0 first).
+// Inclusive prefix sum over the 64 lanes (lane 0 first), on DPP: row_shr 1, 2, 4, 8 inside each
+// 16-lane row, then row_bcast:15 and row_bcast:31 carry the row totals forward (no LDS round
+// trip per step, as a shuffle would take).
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
   return v;
 }
 
@@ -88,7 +90,7 @@ __device__ void find_from_top(Get get, int nb, int need, int& bin, int& above, i
   int s = 0;
   for (int x = lo_x; x < hi_x; ++x) s += get(x);
   const int incl = wave_incl_scan(s);
-  total = __shfl(incl, 63, 64);
+  total = __builtin_amdgcn_readlane(incl, 63);
   const uint64_t m = __ballot(incl >= need);
   if (m == 0) {
     bin = -1;
@@ -107,8 +109,8 @@ __device__ void find_from_top(Get get, int nb, int need, int& bin, int& above, i
       run += c;
     }
   }
-  bin = __shfl(b, L, 64);
-  above = __shfl(run, L, 64);
+  bin = __builtin_amdgcn_readlane(b, L);
+  above = __builtin_amdgcn_readlane(run, L);
 }
 
 // For counts c[0..nb) (tokens ascending): the first x with sum_{y <= x} c[y] >= need and the
@@ -135,8 +137,8 @@ __device__ void find_from_bottom(Get get, int nb, int need, int& pos, int& below
       run += c;
     }
   }
-  pos = __shfl(p, L, 64);
-  below = __shfl(run, L, 64);
+  pos = __builtin_amdgcn_readlane(p, L);
+  below = __builtin_amdgcn_readlane(run, L);
 }
 
 template <int DI>
