@@ -864,6 +864,7 @@ def main():
     if calib:
         result["calibration"] = calib
         result["roofline"]["measured_peak"] = calib["hbm_read_gbps"]
+        result["hbm_frac_of_measured"] = result["hbm_gbps"] / calib["hbm_read_gbps"]
         result["roofline"]["frac_of_measured"] = achieved / calib["hbm_read_gbps"]
     if not args.no_prefill:
         del scores
