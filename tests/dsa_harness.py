@@ -21,6 +21,9 @@ MEAN_ABS = 2e-3    # ... mean over elements
 # rounded P is off by at most 2^-8 of itself, so the sum, and exp(LSE), by at most 2^-8:
 # |LSE error| <= ln(1 + 2^-8) = 3.9e-3, reached when one key dominates a short list.
 LSE_ABS = 4e-3
+# The decode attention adds the fp32 P (before its bf16 rounding) into the row sum, so its LSE
+# carries only fp32 rounding; the bound there is the 1e-3 planned for every path.
+LSE_ABS_FP32_SUM = 1e-3
 
 
 class DevicePool:
@@ -61,6 +64,7 @@ class GpuRun:
         self.thresholds = None
         self.out = None
         self.lse = None
+        self.lse_fp32_sum = False  # the row sum of this run's attention adds fp32 P
 
 
 def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
@@ -89,6 +93,7 @@ def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
         r.indices = idx
         r.out, r.lse = fa.decode(kv, inp.q[:, 0].contiguous(), idx[:, 0].contiguous(),
                                  num_splits=num_splits)
+        r.lse_fp32_sum = True
         r.out = r.out.unsqueeze(1)
         r.lse = r.lse.unsqueeze(1)
         return r
@@ -188,7 +193,8 @@ def f64(t: torch.Tensor) -> np.ndarray:
 
 
 def compare_rows(gpu: GpuRun, ov: OracleView, rows, check_lse: bool = True):
-    """Checks the given (b, i, g) rows; returns (max_abs, mean_abs, max_lse) over them."""
+    """Checks the given (b, i, g) rows; returns (max_abs, mean_abs, max_lse, lse_bound) over
+    them, lse_bound being the LSE bar of the run's attention path."""
     w = ov.w
     G = w.group
     errs, lse_errs = [], []
@@ -210,14 +216,17 @@ def compare_rows(gpu: GpuRun, ov: OracleView, rows, check_lse: bool = True):
             lse_errs.append(np.abs(lg - lse))
     e = np.concatenate(errs)
     le = float(np.concatenate(lse_errs).max()) if lse_errs else 0.0
-    return float(e.max()), float(e.mean()), le
+    bound = LSE_ABS_FP32_SUM if getattr(gpu, "lse_fp32_sum", False) else LSE_ABS
+    return float(e.max()), float(e.mean()), le, bound
 
 
 def assert_close(stats):
-    mx, mean, lse = stats
+    """stats = (max_abs, mean_abs, max_lse[, lse_bound]); the bound defaults to LSE_ABS."""
+    mx, mean, lse = stats[:3]
+    bound = stats[3] if len(stats) > 3 else LSE_ABS
     assert mx <= MAX_ABS, f"max abs error {mx}"
     assert mean <= MEAN_ABS, f"mean abs error {mean}"
-    assert lse <= LSE_ABS, f"lse error {lse}"
+    assert lse <= bound, f"lse error {lse} (bound {bound})"
 
 
 def sampled_positions(S: int, n_random: int, edge: int = 64, seed: int = 0) -> list:
@@ -296,4 +305,5 @@ def compare_block(gpu: GpuRun, ov: OracleView, b: int, rows, g: int, want=None):
 
 def merge_stats(stats):
     """Worst max-abs, mean of mean-abs (equal row counts per item), worst LSE error."""
-    return (max(s[0] for s in stats), float(np.mean([s[1] for s in stats])), max(s[2] for s in stats))
+    return (max(s[0] for s in stats), float(np.mean([s[1] for s in stats])), max(s[2] for s in stats),
+            min(s[3] if len(s) > 3 else LSE_ABS for s in stats))
