@@ -21,9 +21,11 @@
 // The heads fill only G of the 16 MFMA columns, so at most G/16 of the matrix work is useful;
 // the matrix units still do the 4*G*d flop per key in a fraction of the time the VALU needs,
 // and the kernel is bound by the gather of the selected rows through L2 and the Infinity Cache.
-// Softmax is base 2 with sm_scale*log2(e) applied in the exponent; P is rounded to bf16 and the
-// row sum adds the rounded values. The running maximum moves only when a score exceeds it by
-// more than 2^8 (exp2 units), which leaves the result unchanged.
+// Softmax is base 2 with sm_scale*log2(e) applied in the exponent; P is rounded to bf16 for P V.
+// Two row sums are kept: the rounded P normalises O (an exact convex combination of the weights
+// P V saw, as in the dense kernel) and the fp32 P gives the LSE (only fp32 rounding); the kernel
+// is bound by its row gathers, so the extra adds are free. The running maximum moves only when
+// a score exceeds it by more than 2^8 (exp2 units), which leaves the result unchanged.
 #include "sa_common.h"
 
 namespace sa {
@@ -102,7 +104,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
   f32x4 o[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
+  float m_run = -INFINITY, l_part = 0.f, l_exact = 0.f;
+  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
 
   // List entry -> pool row in three steps, each issued an iteration before its result is used
   // (lanes 0..31 hold the tile's 32 entries): the entry (token), its page-table entry, and the
@@ -164,7 +167,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
     store_v();
     __syncthreads();
   }
-  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
   for (int t = 0; t < n_tiles; ++t) {
     const int cur = t & 1, nxt = cur ^ 1;
     // S^T for the two 16-key halves of the tile (its K operands were loaded an iteration ago)
@@ -200,6 +202,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
     if (__any((m_new - m_run) * qscale > kRescaleLog2)) {  // wave-uniform, rare
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * qscale);
       l_part *= alpha;
+      l_exact *= alpha;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -223,6 +226,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
       l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pf.u.y), ones, l_part, false);
       l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pf.u.z), ones, l_part, false);
       l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pf.u.w), ones, l_part, false);
+      l_exact += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     }
     // O^T += V^T P^T. Transposed reads: source lane s of group g supplies row 4g + s/4 (and
     // 16 + 4g + s/4), dims nb*16 + 4(s%4) .. +4; lane l receives dim nb*16 + l%16 of the 4 rows.
@@ -253,6 +257,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
   const FPair l16 = lane_pair<16>(l_part);
   const FPair l32 = lane_pair<32>(l16.lo + l16.hi);
   const float l_tot = l32.lo + l32.hi;
+  const FPair e16 = lane_pair<16>(l_exact);
+  const FPair e32 = lane_pair<32>(e16.lo + e16.hi);
+  const float l_ex = e32.lo + e32.hi;
   if (col >= G) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t qh = bi * num_q_heads + (int64_t)g * G + col;
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
     *reinterpret_cast<uint2*>(out + qh * D + nb * 16 + grp * 4) = w;
   }
   if (lse != nullptr && grp == 0)
-    lse[qh] = l_tot > 0.f ? (m_run * qscale + log2f(l_tot)) * kLn2 : -INFINITY;
+    lse[qh] = l_ex > 0.f ? (m_run * qscale + log2f(l_ex)) * kLn2 : -INFINITY;
 }
 
 template <int D, int G>

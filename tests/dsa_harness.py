@@ -21,8 +21,8 @@ MEAN_ABS = 2e-3    # ... mean over elements
 # rounded P is off by at most 2^-8 of itself, so the sum, and exp(LSE), by at most 2^-8:
 # |LSE error| <= ln(1 + 2^-8) = 3.9e-3, reached when one key dominates a short list.
 LSE_ABS = 4e-3
-# The decode attention adds the fp32 P (before its bf16 rounding) into the row sum, so its LSE
-# carries only fp32 rounding; the bound there is the 1e-3 planned for every path.
+# The decode and gathered-row prefill attention add the fp32 P (before its bf16 rounding) into
+# the row sum, so their LSE carries only fp32 rounding; the bound there is the planned 1e-3.
 LSE_ABS_FP32_SUM = 1e-3
 
 
@@ -133,6 +133,8 @@ def run_gpu(inp: Inputs, *, num_splits: int = 0, q_chunk: Optional[int] = None,
         r.indices[:, q0:q0 + c] = idx
         r.out[:, q0:q0 + c] = out
         r.lse[:, q0:q0 + c] = lse
+    # the gathered-row kernel's row sum adds fp32 P; the masked-tile kernel's adds the rounded P
+    r.lse_fp32_sum = (prefill_path is None and not masked) or prefill_path == fa.SA_PREFILL_GATHER
     del T
     return r
 
