@@ -283,6 +283,11 @@ DECODE = {
     "decode_long_didx128": (W(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, idx_dim=128,
                               seq_len=45000, q_len=1, top_k=1000, prefix_len=5),
                             dict(seq_lens=[45000, 17000, 30001])),
+    # long rows on pages of 128 and 256 tokens (two and four 64-token blocks per page)
+    "decode_long_page128": (W(batch=2, seq_len=36000, q_len=1, top_k=1500, prefix_len=7, page_size=128),
+                            dict(seq_lens=[36000, 20000], spare_pages=3)),
+    "decode_long_page256_g8": (W(batch=2, num_q_heads=16, num_kv_heads=2, seq_len=50000, q_len=1,
+                                 top_k=2048, page_size=256), dict(seq_lens=[50000, 33333])),
 }
 
 
@@ -300,7 +305,8 @@ def test_decode_every_row(name, splits):
 @pytest.mark.parametrize("name", ["decode_long_ragged_prefix", "decode_long_ties",
                                   "decode_long_shared_indexer", "decode_long_didx128",
                                   "decode_first_tokens", "decode_large_k",
-                                  "decode_ragged_prefix"])
+                                  "decode_ragged_prefix", "decode_long_page128",
+                                  "decode_long_page256_g8"])
 def test_fused_index_topk_matches(name):
     """The fused indexer + top-K gives the oracle's lists, identical to the two-step path."""
     w, kw = DECODE[name]
