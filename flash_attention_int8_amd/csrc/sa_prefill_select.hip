@@ -16,7 +16,7 @@
 // indexer keys of one head stay in L2), and then writes the masked-dense attention's per-tile
 // lane masks from the same recomputed scores.
 //
-// Passes over the candidate tiles (64 keys each; every wave takes every 8th tile):
+// Passes over the candidate tiles (64 keys each; each of the 16 waves takes every 16th tile):
 //   1. histogram of the top 10 bits of acc = s + d_idx * 2^14 (in [0, 2^RB]: 1025 bins of
 //      32-bit counters per query), then per query the bin holding the K-th largest;
 //   2. the keys of that bin collected into per-query lists in LDS as (low bits, token) keys,
@@ -39,7 +39,10 @@ namespace {
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(int)))) int i32x16;
 
-constexpr int kThWaves = 8;
+// 16 waves (four per SIMD, within 128 VGPRs): against 8 waves the 32K prefill's threshold
+// selection takes 2.46 instead of 3.43 ms, its passes being bound by latency and LDS atomics
+// that more resident waves overlap.
+constexpr int kThWaves = 16;
 constexpr int kThNT = 64 * kThWaves;
 constexpr int kQB = 32;           // queries per workgroup: one 32-query mask block
 constexpr int kTile = 64;         // keys per tile (the dense kernel's key tile)
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(kThNT, 1) void k_sel_thresh(KvView kv, const int8_t
       // ---- pass 2: the keys of each query's coarse bin collected into LDS lists as unique
       //      32-bit keys (fine bits << 17) | (131071 - token): a larger key is a higher score, or
       //      the same score at a lower token. A query's keys come from every wave (each takes
-      //      every 8th tile), so its list is filled through one LDS counter per query.
+      //      every 16th tile), so its list is filled through one LDS counter per query.
       uint32_t* list = hist;
       const int my_bin = st_prefix[l32];  // -1 for queries not searching: never matches
       const int my_off = st_off[l32];
