@@ -317,12 +317,11 @@ double mean_candidates(const sa::KvView& v, int32_t q_len, int32_t q_tail) {
 
 // Path of sparse_attn_prefill_fused: masked-dense tiles when top_k is a large enough share of
 // the block's mean candidate count, else gathered rows. Measured on MI355X (32K context, blocks
-// of 128, 512 and 2048 queries at five positions, top-K 32..2048): for 2048-query blocks the
-// two paths cost the same at a share of about 1/16; shorter blocks need a larger share (about
-// 0.18 at 512 queries, 0.25-0.5 at 128), since the selection then runs few workgroups and the
-// dense tiles of a 256-query workgroup are partly empty. max(1/16, 64/q_len) follows both.
-constexpr double kMaskedMinShare = 1.0 / 16.0;
-constexpr double kMaskedShareQueries = 64.0;
+// of 128, 512 and 2048 queries at five positions, top-K 32..2048, short blocks with key splits):
+// the two paths cost the same at a share of about 1/20 for every block size (between 0.042 and
+// 0.056 for 2048 queries, about 0.06 for 512 and 128); blocks under 64 queries would leave most
+// of a 256-query tile empty and stay on gathered rows.
+constexpr double kMaskedMinShare = 1.0 / 20.0;
 
 int32_t fused_path(const sa::KvView& v, int32_t num_q_heads, int32_t q_len, int32_t q_tail,
                    int32_t top_k, int32_t path) {
@@ -333,14 +332,17 @@ int32_t fused_path(const sa::KvView& v, int32_t num_q_heads, int32_t q_len, int3
   if (path == SA_PREFILL_MASKED) return masked_ok ? SA_PREFILL_MASKED : -1;
   if (!masked_ok) return gather_ok ? SA_PREFILL_GATHER : -1;
   if (!gather_ok) return SA_PREFILL_MASKED;
-  const double share = fmax(kMaskedMinShare, kMaskedShareQueries / q_len);
-  const bool dense_enough = (double)top_k >= share * mean_candidates(v, q_len, q_tail);
+  const bool dense_enough = (double)top_k >= kMaskedMinShare * mean_candidates(v, q_len, q_tail);
   return (dense_enough && q_len >= 64) ? SA_PREFILL_MASKED : SA_PREFILL_GATHER;
 }
 
-size_t fused_bytes(const sa::KvView& v, int32_t q_len, int32_t top_k, int32_t chosen) {
+// Masked path: thresholds, selection records, then (short blocks) the key-split partials.
+size_t fused_bytes(const sa::KvView& v, int32_t num_q_heads, int32_t q_len, int32_t q_tail,
+                   int32_t top_k, int32_t chosen) {
   const size_t rows = (size_t)v.batch * q_len * v.num_idx_heads;
-  if (chosen == SA_PREFILL_MASKED) return align256(rows * 2 * sizeof(int32_t)) + sa::sel_workspace_bytes(v, q_len);
+  if (chosen == SA_PREFILL_MASKED)
+    return align256(rows * 2 * sizeof(int32_t)) + align256(sa::sel_workspace_bytes(v, q_len)) +
+           sa::dense_split_bytes(v, num_q_heads, q_len, sa::dense_splits(v, num_q_heads, q_len, q_tail));
   return align256(rows * ((size_t)v.prefix_len + top_k) * sizeof(int32_t)) + index_topk_bytes(v, q_len, top_k);
 }
 
@@ -354,7 +356,7 @@ size_t sparse_attn_prefill_fused_workspace_size(const sa_paged_kv* kv, int32_t n
   if (num_q_heads < 1 || num_q_heads % v.num_kv_heads != 0 || q_tail < q_len) return 0;
   if (path != SA_PREFILL_AUTO && path != SA_PREFILL_GATHER && path != SA_PREFILL_MASKED) return 0;
   const int32_t chosen = fused_path(v, num_q_heads, q_len, q_tail, top_k, path);
-  return chosen < 0 ? 0 : fused_bytes(v, q_len, top_k, chosen);
+  return chosen < 0 ? 0 : fused_bytes(v, num_q_heads, q_len, q_tail, top_k, chosen);
 }
 
 int32_t sparse_attn_prefill_fused_choice(const sa_paged_kv* kv, int32_t num_q_heads, int32_t q_len,
@@ -383,7 +385,7 @@ int32_t sparse_attn_prefill_fused(const sa_paged_kv* kv, const uint16_t* q, cons
     return SA_ERR_SHAPE;
   const int32_t chosen = fused_path(v, num_q_heads, q_len, q_tail, top_k, path);
   if (chosen < 0) return SA_ERR_UNSUPPORTED;
-  const size_t need = fused_bytes(v, q_len, top_k, chosen);
+  const size_t need = fused_bytes(v, num_q_heads, q_len, q_tail, top_k, chosen);
   if (workspace == nullptr || workspace_bytes < need) return SA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SA_ERR_ALIGN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -392,10 +394,13 @@ int32_t sparse_attn_prefill_fused(const sa_paged_kv* kv, const uint16_t* q, cons
   const size_t rows = (size_t)v.batch * q_len * v.num_idx_heads;
   if (chosen == SA_PREFILL_MASKED) {
     int32_t* thr = reinterpret_cast<int32_t*>(base);
-    uint64_t* sel = reinterpret_cast<uint64_t*>(base + align256(rows * 2 * sizeof(int32_t)));
+    const size_t sel_off = align256(rows * 2 * sizeof(int32_t));
+    uint64_t* sel = reinterpret_cast<uint64_t*>(base + sel_off);
+    float* part = reinterpret_cast<float*>(base + sel_off + align256(sa::sel_workspace_bytes(v, q_len)));
+    const int splits = sa::dense_splits(v, num_q_heads, q_len, q_tail);
     if (sa::launch_sel_thresh(v, q_idx, q_len, q_tail, top_k, thr, sel, s) != hipSuccess) return SA_ERR_HIP;
     return hip_status(sa::launch_attn_masked_records(v, q, num_q_heads, q_len, q_tail, sm_scale, sel,
-                                                     out, lse, s));
+                                                     splits, part, out, lse, s));
   }
   const int32_t width = v.prefix_len + top_k;
   int32_t* lists = reinterpret_cast<int32_t*>(base);

@@ -21,6 +21,9 @@
 // K and V tiles are copied into LDS as they are. Softmax is base 2 with sm_scale*log2(e) applied to
 // the fp32 scores; Q, K and V stay exact bf16, accumulation is fp32, P is rounded to bf16 and
 // the row sum adds the rounded P. Workgroups are ordered for L2 reuse across the 8 XCDs.
+// Key splits (masked attention of blocks too short to fill the chip): each workgroup streams
+// its split's share of the block's causal tiles and writes the unnormalised O, the maximum and
+// the row sum of its queries, which the split merge combines.
 #include "sa_common.h"
 
 namespace sa {
@@ -75,12 +78,12 @@ template <int D, bool MASKED>
 __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     KvView kv, const uint16_t* __restrict__ q, int num_q_heads, int q_len, int q_tail, float qscale,
     uint16_t* __restrict__ out, float* __restrict__ lse, int n_qblocks,
-    const uint64_t* __restrict__ sel, int sel_qblocks, int sel_tiles) {
+    const uint64_t* __restrict__ sel, int sel_qblocks, int sel_tiles, int num_splits,
+    int tiles_per_split, float* __restrict__ part) {
   constexpr int KS = D / 16;     // k-steps of QK^T
   constexpr int DB = D / 32;     // 32-dim blocks of O^T
   constexpr int CPR = D / 8;     // 16-byte chunks per row
   constexpr int KPT = D / 32;    // key rows per thread in the tile loader (half the workgroup)
-  constexpr int KQ = BN / KPT;   // key groups per tile (16)
   constexpr int QW = 32;         // queries per wave
   constexpr int BMQ = kDenseWaves * QW;  // queries per workgroup
   __shared__ DenseShared<D> sh;
@@ -93,9 +96,9 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
 
   // Work order. Workgroups are dealt round-robin to the 8 XCDs, each with its own L2; the
   // remap gives every XCD a contiguous run of the logical order, which is (b, KV head) major,
-  // then query blocks heaviest first (causal work grows with the block index), then the G
-  // query heads of the group. The workgroups resident on one XCD then stream the same KV
-  // prefix and share it in L2.
+  // then query blocks heaviest first (causal work grows with the block index), then key
+  // splits, then the G query heads of the group. The workgroups resident on one XCD then
+  // stream the same KV range and share it in L2.
   const int G = num_q_heads / kv.num_kv_heads;
   int wg;
   {
@@ -104,10 +107,12 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     const int xcd = bid % kNumXcd, r = bid / kNumXcd;
     wg = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + r;
   }
-  const int per_pair = n_qblocks * G;
+  const int per_qblk = num_splits * G;
+  const int per_pair = n_qblocks * per_qblk;
   const int pair = wg / per_pair;
   const int rem = wg - pair * per_pair;
-  const int qblk = n_qblocks - 1 - rem / G;
+  const int qblk = n_qblocks - 1 - rem / per_qblk;
+  const int split = (rem % per_qblk) / G;
   const int b = pair / kv.num_kv_heads;
   const int g = pair - b * kv.num_kv_heads;
   const int h = g * G + rem % G;
@@ -118,9 +123,16 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
   const int i_last_blk = min(q_len, i_blk + BMQ) - 1;
   const int wave_pos_max = pos0 + min(q_len - 1, i_w + QW - 1);
   const int blk_pos_max = pos0 + i_last_blk;
-  if (blk_pos_max < 0) return;
-  const int n_tiles = blk_pos_max / BN + 1;
-  const int last_w = wave_pos_max >= 0 ? wave_pos_max / BN : -1;  // last tile this wave attends
+  if (blk_pos_max < 0 && part == nullptr) return;
+  // Key tiles of this workgroup: [t_lo, t_hi) of the block's causal tiles (all of them without
+  // key splits; with splits, the split's share, possibly none). A split that holds no tile of
+  // a query still writes that query's partial result (empty).
+  const int n_tiles = blk_pos_max >= 0 ? blk_pos_max / BN + 1 : 0;
+  const int t_lo = split * tiles_per_split;
+  const int t_hi = min(n_tiles, t_lo + tiles_per_split);
+  const int n_own = max(0, t_hi - t_lo);  // tiles this workgroup streams (workgroup-uniform)
+  // last tile this wave attends, within the workgroup's range (below t_lo: none)
+  const int last_w = wave_pos_max >= 0 ? min(wave_pos_max / BN, t_hi - 1) : -1;
 
   const int my_i = i_w + l32;
   const int my_pos = pos0 + my_i;
@@ -272,35 +284,12 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
       m_run = m_new;
     }
   };
-  // P^T as B operands: step (mb, kk) takes j = 2kk, 2kk+1 of block mb (8 values). The row sum
-  // adds the bf16-rounded P, the same values the P V product sees.
-  auto softmax = [&](const f32x16 (&s)[2], Frag8 (&pf)[4]) {
-    const float mq = (m_run == -INFINITY) ? 0.f : m_run * qscale;
-    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
-    float psum = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[mb][kk * 8 + e], qscale, -mq));
-        Frag8& f = pf[mb * 2 + kk];
-        f.u.x = pack_bf16x2(p[0], p[1]);
-        f.u.y = pack_bf16x2(p[2], p[3]);
-        f.u.z = pack_bf16x2(p[4], p[5]);
-        f.u.w = pack_bf16x2(p[6], p[7]);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.x), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.y), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.z), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.w), ones, psum, false);
-      }
-    l_run += psum;
-  };
   // QK(next tile) and softmax(current tile) in lock step: k-step ks issues the two MFMAs of
   // S_next (K fragments read one step ahead) and then exponentiates 32/KS of the current
   // scores; a scheduling barrier closes every step, so each step's VALU work sits between
-  // matrix instructions instead of after all of them.
+  // matrix instructions instead of after all of them. P^T is packed into the B operands of
+  // the P V product (step (mb, kk) takes elements 8kk .. 8kk+7 of block mb), and the row sum
+  // adds the bf16-rounded P, the values that product sees.
   auto qk_softmax = [&](int buf, f32x16 (&sn)[2], const f32x16 (&sc)[2], Frag8 (&pf)[4]) {
     constexpr int EPS = 32 / KS;  // score elements per step (4 for d = 128, 8 for d = 64)
     const float mq = (m_run == -INFINITY) ? 0.f : m_run * qscale;
@@ -377,59 +366,63 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
     }
   };
 
-  // Prologue: K(0), V(0) and K(1) in LDS, S(0) computed, masked and its maximum taken.
-  // Each loader role looks its page up one iteration ahead of the load that needs it.
+  // Prologue: K(t_lo), V(t_lo) and K(t_lo+1) in LDS, S(t_lo) computed, masked and its maximum
+  // taken. Each loader role looks its page up one iteration ahead of the load that needs it.
+  // Buffers are indexed by the tile's offset from t_lo.
   uint4 st[KPT];
-  int32_t raw_next;  // page-table entry of the next tile this wave loads
+  int32_t raw_next = 0;  // page-table entry of the next tile this wave loads
   // Whether the page of the tile whose scores the wave masks next is in the table: V loaders
   // look up tile j+1 in iteration j (the tile masked there), K loaders one iteration earlier.
-  bool ok_tile0, ok_ahead = true;
-  if (k_loader) {
-    int64_t ph = phys_page(kv, b, 0);
-    ok_tile0 = ph >= 0;
-    load_rows(kv.k_pool, 0, ph, k_off, st);
-    int lim = valid_rows(0, ph);
-    if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
-    store_k(0, st);
-    if (n_tiles > 1) {
-      ph = phys_page(kv, b, BN);
-      ok_ahead = ph >= 0;
-      load_rows(kv.k_pool, 1, ph, k_off, st);
-      lim = valid_rows(1, ph);
-      if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
-      store_k(1, st);
-    }
-    raw_next = raw_page(2);
-  } else {
-    const int64_t ph = phys_page(kv, b, 0);
-    ok_tile0 = ph >= 0;
-    load_rows(kv.v_pool, 0, ph, k_off, st);
-    const int lim = valid_rows(0, ph);
-    if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
-    store_v(0, st);
-    raw_next = raw_page(1);
-  }
-  __syncthreads();
+  bool ok_tile0 = true, ok_ahead = true;
   f32x16 sa[2], sb[2];
-  if (last_w >= 0) {
+  if (n_own > 0) {  // workgroup-uniform
+    if (k_loader) {
+      int64_t ph = phys_page(kv, b, t_lo * BN);
+      ok_tile0 = ph >= 0;
+      load_rows(kv.k_pool, t_lo, ph, k_off, st);
+      int lim = valid_rows(t_lo, ph);
+      if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
+      store_k(0, st);
+      if (n_own > 1) {
+        ph = phys_page(kv, b, (t_lo + 1) * BN);
+        ok_ahead = ph >= 0;
+        load_rows(kv.k_pool, t_lo + 1, ph, k_off, st);
+        lim = valid_rows(t_lo + 1, ph);
+        if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
+        store_k(1, st);
+      }
+      raw_next = raw_page(t_lo + 2);
+    } else {
+      const int64_t ph = phys_page(kv, b, t_lo * BN);
+      ok_tile0 = ph >= 0;
+      load_rows(kv.v_pool, t_lo, ph, k_off, st);
+      const int lim = valid_rows(t_lo, ph);
+      if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
+      store_v(0, st);
+      raw_next = raw_page(t_lo + 1);
+    }
+    __syncthreads();
+  }
+  if (last_w >= t_lo) {
     qk(0, sa);
-    mask_tile(0, sa, ok_tile0);
+    mask_tile(t_lo, sa, ok_tile0);
     float mx0 = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 32; ++e) mx0 = fmaxf(mx0, sa[e >> 4][e & 15]);
     finish_max(mx0);
   }
 
-  // Iteration j: on entry K buffer (j+1)&1 holds K(j+1), V buffer j&1 holds V(j), sc holds the
-  // masked S(j) and m_run its running maximum. K loaders fetch K(j+2) into registers while the
-  // tile is computed and store it to K buffer j&1; V loaders do the same with V(j+1) and V
-  // buffer (j+1)&1. Neither buffer is read during iteration j.
+  // Iteration j (r = j - t_lo): on entry K buffer (r+1)&1 holds K(j+1), V buffer r&1 holds
+  // V(j), sc holds the masked S(j) and m_run its running maximum. K loaders fetch K(j+2) into
+  // registers while the tile is computed and store it to K buffer r&1; V loaders do the same
+  // with V(j+1) and V buffer (r+1)&1. Neither buffer is read during iteration j.
   auto iter = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int r = j - t_lo;
     // the load past the last tile reads the last tile's slots of page 0 (in bounds) and is
     // never stored
     const int ltile = k_loader ? j + 2 : j + 1;
-    const bool more = ltile < n_tiles;
-    const int lt = more ? ltile : n_tiles - 1;
+    const bool more = ltile < t_hi;
+    const int lt = more ? ltile : t_hi - 1;
     const int64_t ph = more ? checked_page(ltile, raw_next) : 0;
     raw_next = raw_page(ltile + 1);
     bool ok_next;  // page status of tile j+1, whose scores this iteration masks
@@ -454,29 +447,50 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
 #pragma unroll
         for (int k = 0; k < 32; ++k) mw[k] = w[k];
       }
-      qk_softmax((j + 1) & 1, sn, sc, pf);
+      qk_softmax((r + 1) & 1, sn, sc, pf);
       // (masked mode applies the record unconditionally: S(j+1) is not used past last_w, and
       // a conditional use would let the compiler sink the loads to it)
       if constexpr (MASKED) apply_sel(mw, sn, ok_next);
       else if (j + 1 <= last_w) mask_tile(j + 1, sn, ok_next);
-      pv(j & 1, pf, sn, mx);
+      pv(r & 1, pf, sn, mx);
     }
     if (more) {
       if (lim < BN) mask_rows(st, ld_kq * KPT, lim);
-      if (k_loader) store_k(j & 1, st);
-      else store_v((j + 1) & 1, st);
+      if (k_loader) store_k(r & 1, st);
+      else store_v((r + 1) & 1, st);
     }
     if (j + 1 <= last_w) finish_max(mx);
     __syncthreads();
   };
-  for (int j = 0; j < n_tiles; j += 2) {
+  for (int j = t_lo; j < t_hi; j += 2) {
     iter(j, sa, sb);
-    if (j + 1 < n_tiles) iter(j + 1, sb, sa);
+    if (j + 1 < t_hi) iter(j + 1, sb, sa);
   }
 
   // finalize: O^T[db*32 + j*8 + hi*4 + i][query l32]
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!my_valid) return;
+  if (part != nullptr) {
+    // Key splits: this split's unnormalised O, its maximum in exp2 units and its row sum, in
+    // the split-merge layout: [unit][split][head of group][D] accumulators, then
+    // [unit][split][head of group][2] (max, sum), unit = (b, query, KV head).
+    const int64_t units = (int64_t)kv.batch * q_len * kv.num_kv_heads;
+    const int64_t slot = ((((int64_t)b * q_len + my_i) * kv.num_kv_heads + g) * num_splits + split) * G +
+                         (h - g * G);
+    float* acc = part + slot * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(acc + db * 32 + j * 8 + hi * 4) =
+            make_float4(o[db][j * 4 + 0], o[db][j * 4 + 1], o[db][j * 4 + 2], o[db][j * 4 + 3]);
+    if (hi == 0) {
+      float* ml = part + units * num_splits * G * D + slot * 2;
+      ml[0] = (m_run == -INFINITY) ? -INFINITY : m_run * qscale;
+      ml[1] = l_tot;
+    }
+    return;
+  }
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   const int64_t orow = (((int64_t)b * q_len + my_i) * num_q_heads + h) * D;
 #pragma unroll
@@ -493,23 +507,35 @@ __global__ __launch_bounds__(kDenseThreads, 1) void k_attn_dense(
         (l_tot > 0.f) ? (m_run * qscale + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
+// Causal key tiles of the block's last query (host bound from max_seq_len).
+int64_t block_tiles(const KvView& kv, int q_len, int q_tail) {
+  const int64_t last_pos = (int64_t)kv.max_seq_len - q_tail + q_len - 1;
+  return last_pos < 0 ? 0 : last_pos / BN + 1;
+}
+
 template <int D>
 hipError_t launch_dense_d(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                           int q_tail, float sm_scale, uint16_t* out, float* lse,
-                          const uint64_t* sel, hipStream_t stream) {
+                          const uint64_t* sel, int num_splits, float* part, hipStream_t stream) {
   constexpr int BMQ = kDenseWaves * 32;
   const int nqb = (q_len + BMQ - 1) / BMQ;
-  const int64_t wgs = (int64_t)nqb * kv.batch * num_q_heads;
+  const int split = num_splits > 1 ? num_splits : 1;
+  const int64_t wgs = (int64_t)nqb * kv.batch * num_q_heads * split;
+  const int tps = split > 1 ? (int)((block_tiles(kv, q_len, q_tail) + split - 1) / split) : (1 << 30);
+  float* p = split > 1 ? part : nullptr;
   if (sel == nullptr) {
     hipLaunchKernelGGL((k_attn_dense<D, false>), dim3((unsigned)wgs), dim3(kDenseThreads), 0, stream,
                        kv, q, num_q_heads, q_len, q_tail, sm_scale * kLog2e, out, lse, nqb,
-                       (const uint64_t*)nullptr, 0, 0);
+                       (const uint64_t*)nullptr, 0, 0, split, tps, p);
   } else {
     hipLaunchKernelGGL((k_attn_dense<D, true>), dim3((unsigned)wgs), dim3(kDenseThreads), 0, stream,
                        kv, q, num_q_heads, q_len, q_tail, sm_scale * kLog2e, out, lse, nqb, sel,
-                       sel_query_blocks(q_len), sel_tiles(kv));
+                       sel_query_blocks(q_len), sel_tiles(kv), split, tps, p);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || split == 1) return e;
+  const int64_t units = (int64_t)kv.batch * q_len * kv.num_kv_heads;
+  return launch_merge_splits(part, units, split, num_q_heads, kv.num_kv_heads, D, out, lse, stream);
 }
 
 // Selection masks from index lists. One workgroup per (sequence, indexer head, block of 32
@@ -578,6 +604,29 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_masks(KvView kv, int q_len,
 
 }  // namespace
 
+// Key splits of the masked dense attention: a block whose workgroups would leave CUs idle (a
+// short block: one 8-wave workgroup per 256 queries and query head fills a CU) splits its
+// causal key tiles among up to that many workgroups, at least kMinSplitTiles tiles each, and
+// the split results are merged like the decode splits.
+constexpr int kNumCus = 256;  // MI355X
+constexpr int kMinSplitTiles = 8;
+constexpr int kMaxDenseSplits = 64;
+
+int dense_splits(const KvView& kv, int num_q_heads, int q_len, int q_tail) {
+  const int G = num_q_heads / kv.num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return 1;  // group sizes the merge is built for
+  constexpr int BMQ = kDenseWaves * 32;
+  const int64_t wgs = (int64_t)((q_len + BMQ - 1) / BMQ) * kv.batch * num_q_heads;
+  int64_t s = kNumCus / wgs;
+  s = std::min<int64_t>(s, block_tiles(kv, q_len, q_tail) / kMinSplitTiles);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, kMaxDenseSplits));
+}
+
+size_t dense_split_bytes(const KvView& kv, int num_q_heads, int q_len, int num_splits) {
+  if (num_splits <= 1) return 0;
+  return (size_t)kv.batch * q_len * num_q_heads * num_splits * (kv.head_dim + 2) * sizeof(float);
+}
+
 int sel_query_blocks(int q_len) {
   constexpr int BMQ = kDenseWaves * 32;
   return (q_len + BMQ - 1) / BMQ * kDenseWaves;
@@ -593,9 +642,9 @@ hipError_t launch_attn_dense(const KvView& kv, const uint16_t* q, int num_q_head
                              int q_tail, float sm_scale, uint16_t* out, float* lse,
                              hipStream_t stream) {
   if (kv.head_dim == 128)
-    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, nullptr, stream);
+    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, nullptr, 1, nullptr, stream);
   if (kv.head_dim == 64)
-    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, nullptr, stream);
+    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, nullptr, 1, nullptr, stream);
   return hipErrorInvalidValue;
 }
 
@@ -610,19 +659,19 @@ hipError_t launch_attn_masked(const KvView& kv, const uint16_t* q, int num_q_hea
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (kv.head_dim == 128)
-    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, stream);
+    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, 1, nullptr, stream);
   if (kv.head_dim == 64)
-    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, stream);
+    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, 1, nullptr, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_masked_records(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
-                                      int q_tail, float sm_scale, const uint64_t* sel, uint16_t* out,
-                                      float* lse, hipStream_t stream) {
+                                      int q_tail, float sm_scale, const uint64_t* sel, int num_splits,
+                                      float* part, uint16_t* out, float* lse, hipStream_t stream) {
   if (kv.head_dim == 128)
-    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, stream);
+    return launch_dense_d<128>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, num_splits, part, stream);
   if (kv.head_dim == 64)
-    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, stream);
+    return launch_dense_d<64>(kv, q, num_q_heads, q_len, q_tail, sm_scale, out, lse, sel, num_splits, part, stream);
   return hipErrorInvalidValue;
 }
 

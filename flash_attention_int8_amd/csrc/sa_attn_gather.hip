@@ -440,6 +440,27 @@ hipError_t decode_scratch(float** ptr) {
   return hipSuccess;
 }
 
+hipError_t launch_merge_splits(const float* ws, int64_t units, int num_splits, int num_q_heads,
+                               int num_kv_heads, int head_dim, uint16_t* out, float* lse,
+                               hipStream_t stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)units);
+#define SA_MERGE(D, G)                                                                              \
+  hipLaunchKernelGGL((k_merge_splits<D, G>), grid, dim3(256), 0, stream, ws, units, num_splits,    \
+                     num_q_heads, num_kv_heads, out, lse)
+  const int group = num_q_heads / num_kv_heads;
+  if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
+  switch (group) {
+    case 1: if (head_dim == 128) SA_MERGE(128, 1); else SA_MERGE(64, 1); break;
+    case 2: if (head_dim == 128) SA_MERGE(128, 2); else SA_MERGE(64, 2); break;
+    case 4: if (head_dim == 128) SA_MERGE(128, 4); else SA_MERGE(64, 4); break;
+    case 8: if (head_dim == 128) SA_MERGE(128, 8); else SA_MERGE(64, 8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SA_MERGE
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_gather(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                               int q_tail, const int32_t* indices, int index_width, float sm_scale,
                               int num_splits, float* ws, uint16_t* out, float* lse,

@@ -133,6 +133,11 @@ hipError_t launch_attn_gather(const KvView& kv, const uint16_t* q, int num_q_hea
                               int num_splits, float* ws, uint16_t* out, float* lse,
                               hipStream_t stream);
 size_t gather_workspace_bytes(int64_t units, int group, int head_dim, int num_splits);
+// Merge of split partials ([unit][split][G][D] accumulators, then [unit][split][G][2] (max in
+// exp2 units, sum)) into out and lse; unit = (row, KV head), G = num_q_heads / num_kv_heads.
+hipError_t launch_merge_splits(const float* ws, int64_t units, int num_splits, int num_q_heads,
+                               int num_kv_heads, int head_dim, uint16_t* out, float* lse,
+                               hipStream_t stream);
 int auto_splits(int64_t units, int index_width, int head_dim, int group);
 // Static split-partials buffer of sparse_attn_fwd_decode_noalloc: its size, and its device
 // address on the current device (looked up once per device, no allocation).
@@ -181,10 +186,14 @@ size_t sel_workspace_bytes(const KvView& kv, int q_len);
 hipError_t launch_attn_masked(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
                               int q_tail, const int32_t* indices, int index_width, float sm_scale,
                               void* ws, uint16_t* out, float* lse, hipStream_t stream);
-// The masked-dense attention on selection masks already in `sel` (sel_workspace_bytes).
+// The masked-dense attention on selection masks already in `sel` (sel_workspace_bytes), with
+// its causal key tiles split among num_splits workgroups per query block when num_splits > 1
+// (part: dense_split_bytes of split partials, merged by launch_merge_splits).
+int dense_splits(const KvView& kv, int num_q_heads, int q_len, int q_tail);
+size_t dense_split_bytes(const KvView& kv, int num_q_heads, int q_len, int num_splits);
 hipError_t launch_attn_masked_records(const KvView& kv, const uint16_t* q, int num_q_heads, int q_len,
-                                      int q_tail, float sm_scale, const uint64_t* sel, uint16_t* out,
-                                      float* lse, hipStream_t stream);
+                                      int q_tail, float sm_scale, const uint64_t* sel, int num_splits,
+                                      float* part, uint16_t* out, float* lse, hipStream_t stream);
 // Per-row selection thresholds (tau, t_cut) from recomputed indexer scores, and optionally the
 // masked-dense attention's selection masks written from them (sel: sel_workspace_bytes or NULL).
 bool sel_thresh_applies(const KvView& kv);

@@ -241,12 +241,14 @@ int32_t sparse_attn_select_thresholds(const sa_paged_kv* kv, const int8_t* q_idx
  *   SA_PREFILL_MASKED  no index lists: sparse_attn_select_thresholds' (tau, t_cut) per row, the
  *                      dense kernel's selection masks written from indexer scores recomputed
  *                      on the matrix units, then attention over every causal key with the
- *                      unselected ones masked. Cost follows the causal length.
+ *                      unselected ones masked. Cost follows the causal length. A block with
+ *                      too few queries to fill the chip splits its key tiles among several
+ *                      workgroups and merges their results.
  *   SA_PREFILL_GATHER  index lists (sparse_attn_index_topk) and attention over gathered rows.
  *                      Cost follows top_k.
- *   SA_PREFILL_AUTO    masked when q_len >= 64 and top_k is at least max(1/16, 64/q_len) of
- *                      the block's mean candidate count (the crossover measured on MI355X for
- *                      blocks of 128 to 2048 queries); gathered otherwise.
+ *   SA_PREFILL_AUTO    masked when q_len >= 64 and top_k is at least 1/20 of the block's mean
+ *                      candidate count (the crossover measured on MI355X for blocks of 128 to
+ *                      2048 queries); gathered otherwise.
  *                      sparse_attn_prefill_fused_choice tells which path AUTO takes (or -1 if
  *                      none applies).
  * The masked path needs max_seq_len <= 131072; the gathered one a group size H_q/H_kv in

@@ -652,13 +652,14 @@ def test_fused_prefill_other_paths_every_row(name, path):
     assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
 
 
-@pytest.mark.parametrize("top_k,want", [(64, fa.SA_PREFILL_GATHER), (1024, fa.SA_PREFILL_GATHER),
-                                         (2048, fa.SA_PREFILL_MASKED)])
+@pytest.mark.parametrize("top_k,want", [(64, fa.SA_PREFILL_GATHER), (384, fa.SA_PREFILL_GATHER),
+                                         (420, fa.SA_PREFILL_MASKED), (2048, fa.SA_PREFILL_MASKED)])
 def test_fused_prefill_dispatch_both_sides(top_k, want):
-    """A 256-query block at the end of an 8192-token sequence (mean ~8064 candidates): top-64
-    and top-1024 are below the share a 256-query block needs for dense tiles (64/256 of the
-    candidates), top-2048 above it. AUTO takes the expected path, and both paths match the
-    oracle on sampled rows and every KV group; thresholds bit-exact."""
+    """A 256-query block at the end of an 8192-token sequence with a 4-token prefix (mean
+    8060.5 candidates, so the masked share 1/20 is 403 keys): top-64 and top-384 below it,
+    top-420 and top-2048 above it. AUTO takes the expected path, and both paths match the
+    oracle on sampled rows and every KV group (the masked path with key splits: 16 workgroups
+    for 128 tiles); thresholds bit-exact."""
     w = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=8192, q_len=256, top_k=top_k, prefix_len=4)
     _banner(f"fused prefill dispatch top_k={top_k}")
     inp = make_inputs(w, seed=41, device=DEV, seq_lens=[8192, 7000])
@@ -781,6 +782,33 @@ def test_fused_prefill_middle_blocks_ragged():
         gpu = run_gpu(inp, q_chunk=160, prefill_path=path, thresholds=True)
         torch.cuda.synchronize()
         assert_close(compare_rows(gpu, ov, all_rows(inp)))
+
+
+SPLIT_CASES = {
+    # one 128-query block at the end: 16 workgroups, 64 key tiles -> 8 key splits of 8 tiles;
+    # the shorter sequence leaves its last two splits empty
+    "g4_d128_ragged": (W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=4096, q_len=128, top_k=256,
+                         prefix_len=4), dict(seq_lens=[4096, 3000], spare_pages=4), None),
+    # group size 1, head_dim 64: 2 workgroups, 47 tiles -> 5 splits of 10 (the last one 7)
+    "g1_d64": (W(num_q_heads=2, num_kv_heads=2, head_dim=64, idx_dim=32, seq_len=3000, q_len=100,
+                 top_k=200), {}, None),
+    # group size 8, 96-query blocks at four positions (the last block 12 queries)
+    "g8_blocks": (W(num_q_heads=16, num_kv_heads=2, seq_len=2500, q_len=300, top_k=400, prefix_len=3),
+                  {}, 96),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_fused_masked_key_splits_every_row(name):
+    """Short blocks on the masked path split their causal key tiles among several workgroups
+    (too few query blocks to fill the CUs) and merge the split results: every row within the
+    bar, thresholds bit-exact."""
+    w, kw, chunk = SPLIT_CASES[name]
+    _banner(f"fused masked prefill with key splits {name}: {w}")
+    inp = make_inputs(w, seed=43, device="cpu", **kw).to(DEV)
+    gpu = run_gpu(inp, q_chunk=chunk, prefill_path=fa.SA_PREFILL_MASKED, thresholds=True)
+    torch.cuda.synchronize()
+    assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
 
 
 # ------------------------------------------------------------------ int8 minimum, missing pages
