@@ -17,8 +17,8 @@ import torch
 import flash_attention_int8_amd as fa
 import oracle
 from synthetic import CONFIGS, Workload, make_inputs
-from dsa_harness import (OracleView, assert_close, bits, compare_block, compare_rows, make_kv,
-                         merge_stats, run_gpu, f64, sampled_positions)
+from dsa_harness import (LSE_ABS_FP32_SUM, OracleView, assert_close, bits, compare_block,
+                         compare_rows, make_kv, merge_stats, run_gpu, f64, sampled_positions)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -809,6 +809,103 @@ def test_fused_masked_key_splits_every_row(name):
     gpu = run_gpu(inp, q_chunk=chunk, prefill_path=fa.SA_PREFILL_MASKED, thresholds=True)
     torch.cuda.synchronize()
     assert_close(compare_rows(gpu, OracleView(inp), all_rows(inp)))
+
+
+def test_fused_masked_missing_pages_every_row():
+    """Pages missing from the table (entry -1) on the masked path: their keys are not
+    candidates of the selection and take no part in the attention, forced prefix keys
+    included. The expected values come from the oracle's selection and attention over the
+    keys whose pages are present: thresholds bit-exact and every row within the bar, for a
+    block that splits its key tiles (16 workgroups, 64 tiles)."""
+    w = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=4096, q_len=128, top_k=256, prefix_len=4)
+    _banner("fused masked prefill, missing pages")
+    inp = make_inputs(w, seed=44, device="cpu", seq_lens=[4096, 3000], spare_pages=4)
+    inp.page_table[0, 0] = -1    # tokens 0..63 of sequence 0, the forced prefix among them
+    inp.page_table[0, 17] = -1
+    inp.page_table[1, 40] = -1
+    inp.page_table[1, 46] = -1   # the last page of sequence 1, holding the block's last queries
+    inp = inp.to(DEV)
+    gpu = run_gpu(inp, prefill_path=fa.SA_PREFILL_MASKED, thresholds=True)
+    torch.cuda.synchronize()
+    ov = OracleView(inp)
+    G, scale, ps = w.group, 1.0 / math.sqrt(w.head_dim), w.page_size
+    q_idx = inp.q_idx.cpu().numpy()
+    errs, lerrs = [], []
+    for b in range(w.batch):
+        T = inp.seq_lens_host[b]
+        table = np.asarray(ov.table[b])
+        t_all = np.arange(T, dtype=np.int64)
+        present = table[t_all // ps] >= 0
+        for i in range(w.q_len):
+            pos = oracle.query_position(T, w.q_len, i)
+            c = oracle.candidate_keys(pos, w.prefix_len)
+            c = c[present[c]]
+            f = oracle.forced_keys(pos, w.prefix_len)
+            f = f[present[f]]
+            for g in range(w.num_kv_heads):
+                sc = oracle.index_scores(q_idx[b, i, g], oracle.page_rows(ov.kidx, table, ps, g, c))
+                want = oracle.selection_thresholds(sc, c, w.top_k)
+                got = tuple(int(x) for x in gpu.thresholds[b, i, g].cpu())
+                assert got == want, (b, i, g, got, want)
+                keys = np.sort(np.concatenate([f, oracle.topk_select(sc, c, w.top_k)]))
+                sl = slice(g * G, (g + 1) * G)
+                qb = oracle.bf16_to_f64(bits(inp.q[b, i, sl]))
+                kr = oracle.bf16_to_f64(oracle.page_rows(ov.k_pool, table, ps, g, keys))
+                vr = oracle.bf16_to_f64(oracle.page_rows(ov.v_pool, table, ps, g, keys))
+                o_ref, l_ref = oracle.attend(qb, kr, vr, scale)
+                errs.append(np.abs(f64(gpu.out[b, i, sl]) - o_ref).ravel())
+                lerrs.append(np.abs(gpu.lse[b, i, sl].double().cpu().numpy() - l_ref))
+    e = np.concatenate(errs)
+    assert_close((float(e.max()), float(e.mean()), float(np.concatenate(lerrs).max())))
+
+
+def test_fused_decode_missing_pages():
+    """Pages missing from the table in the fused decode selection: keys on them are not
+    candidates (the forced prefix is listed whatever its page) and the decode attention leaves
+    every key on a missing page out. Lists bit-exact against the oracle's selection over the
+    candidates whose pages are present; outputs against the oracle's attention over the listed
+    keys with present pages."""
+    w = W(batch=3, num_q_heads=8, num_kv_heads=2, seq_len=40000, q_len=1, top_k=500, prefix_len=3)
+    _banner("fused decode selection, missing pages")
+    inp = make_inputs(w, seed=45, device="cpu", seq_lens=[40000, 33000, 20000], spare_pages=8)
+    inp.page_table[0, 0] = -1      # the forced prefix's page
+    inp.page_table[0, 130] = -1    # a page inside the second 8192-token chunk
+    inp.page_table[1, 515] = -1    # the page holding the query of sequence 1 (tokens 32960..33023)
+    for p in range(200, 260):      # most of a chunk of sequence 2
+        inp.page_table[2, p] = -1
+    inp = inp.to(DEV)
+    gpu = run_gpu(inp, fused=True)
+    torch.cuda.synchronize()
+    ov = OracleView(inp)
+    G, scale, ps = w.group, 1.0 / math.sqrt(w.head_dim), w.page_size
+    q_idx = inp.q_idx.cpu().numpy()
+    errs, lerrs = [], []
+    for b in range(w.batch):
+        T = inp.seq_lens_host[b]
+        table = np.asarray(ov.table[b])
+        present = table[np.arange(T, dtype=np.int64) // ps] >= 0
+        pos = oracle.query_position(T, 1, 0)
+        c = oracle.candidate_keys(pos, w.prefix_len)
+        c = c[present[c]]
+        f = oracle.forced_keys(pos, w.prefix_len)
+        for g in range(w.num_kv_heads):
+            sc = oracle.index_scores(q_idx[b, 0, g], oracle.page_rows(ov.kidx, table, ps, g, c))
+            keys = np.sort(np.concatenate([f, oracle.topk_select(sc, c, w.top_k)]))
+            want = np.full(w.index_width, -1, dtype=np.int64)
+            want[:keys.size] = keys
+            got = gpu.indices[b, 0, g].cpu().numpy()
+            assert np.array_equal(got, want), (b, g, got[:16], want[:16])
+            keys = keys[present[keys]]
+            sl = slice(g * G, (g + 1) * G)
+            qb = oracle.bf16_to_f64(bits(inp.q[b, 0, sl]))
+            kr = oracle.bf16_to_f64(oracle.page_rows(ov.k_pool, table, ps, g, keys))
+            vr = oracle.bf16_to_f64(oracle.page_rows(ov.v_pool, table, ps, g, keys))
+            o_ref, l_ref = oracle.attend(qb, kr, vr, scale)
+            errs.append(np.abs(f64(gpu.out[b, 0, sl]) - o_ref).ravel())
+            lerrs.append(np.abs(gpu.lse[b, 0, sl].double().cpu().numpy() - l_ref))
+    e = np.concatenate(errs)
+    assert_close((float(e.max()), float(e.mean()), float(np.concatenate(lerrs).max()),
+                  LSE_ABS_FP32_SUM))
 
 
 # ------------------------------------------------------------------ int8 minimum, missing pages
