@@ -29,26 +29,27 @@ MIB = 1 << 20
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs (one process each); only 1 is supported")
+    ap.add_argument("--steps", type=int, default=50, help="timed 128K decode steps")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed decode steps first")
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = auto)")
     ap.add_argument("--warm-cache", action="store_true",
                     help="do not evict the caches between timed steps")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the dense 8K prefill")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the sparse 32K prefill and the 1M-context decode measurements")
-    ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--prefill-reps", type=int, default=20, help="timed calls of each prefill")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--two-step", action="store_true",
                     help="select with sparse_attn_index then sparse_attn_topk (score rows in HBM) "
                          "instead of the fused sparse_attn_index_topk")
-    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=3, help="seed of the 128K decode inputs")
     ap.add_argument("--calibrate", action="store_true",
                     help="only the roofline micro-benchmarks (measured ceilings)")
-    ap.add_argument("--no-calibrate", action="store_true")
+    ap.add_argument("--no-calibrate", action="store_true",
+                    help="skip the roofline micro-benchmarks (measured ceilings)")
     ap.add_argument("--no-layouts", action="store_true",
                     help="skip the 128K selection on adversarial score layouts (kernel traces "
                          "attribute dispatches by kernel and grid, which those runs share)")
