@@ -448,6 +448,41 @@ def test_prefill_fused_dispatch_and_workspace(lib):
     assert ws(2048, 2048, 2048, 9) == 0   # not a path
 
 
+def _align256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_prefill_fused_crossover_and_key_splits(lib):
+    """The measured crossover: masked tiles from top_k = 1/20 of the block's mean candidate
+    count (here the last 2048-query block of 32768 tokens: 31744.5 candidates, so 1587.2), for
+    blocks of 64 queries and more. The masked path's workspace holds the thresholds, the
+    selection records and, for a block whose workgroups (one per 256 queries and query head)
+    would leave CUs idle, the partial results of its key splits: up to 256 / workgroups
+    splits of at least 8 key tiles each, at most 64."""
+    d = desc(max_pages_per_seq=512, max_seq_len=32768, num_pages=1024)
+    ch = lambda q_len, q_tail, k: lib.sparse_attn_prefill_fused_choice(ctypes.byref(d), 32, q_len, q_tail, k)
+    assert ch(2048, 2048, 1587) == fa.SA_PREFILL_GATHER
+    assert ch(2048, 2048, 1588) == fa.SA_PREFILL_MASKED
+    assert ch(64, 64, 32768) == fa.SA_PREFILL_MASKED
+    assert ch(63, 63, 32768) == fa.SA_PREFILL_GATHER
+    for q_len, splits in ((2048, 1), (1024, 1), (512, 2), (128, 4), (64, 4)):
+        # workgroups: ceil(q_len / 256) query blocks x batch 2 x 32 query heads
+        wgs = -(-q_len // 256) * 2 * 32
+        assert splits == max(1, min(256 // wgs, 512 // 8, 64))
+        got = lib.sparse_attn_prefill_fused_workspace_size(ctypes.byref(d), 32, q_len, q_len, 2048,
+                                                           fa.SA_PREFILL_MASKED)
+        want = (_align256(2 * q_len * 8 * 2 * 4)
+                + _align256(lib.sparse_attn_prefill_masked_workspace_size(ctypes.byref(d), q_len)))
+        if splits > 1:
+            want += 2 * q_len * 32 * splits * (128 + 2) * 4
+        assert got == want, (q_len, got, want)
+    # a short context: 15 key tiles, too few for two splits of at least 8
+    ds = desc(max_pages_per_seq=64, max_seq_len=960, num_pages=256)
+    got = lib.sparse_attn_prefill_fused_workspace_size(ctypes.byref(ds), 32, 128, 128, 64, fa.SA_PREFILL_MASKED)
+    assert got == (_align256(2 * 128 * 8 * 2 * 4)
+                   + _align256(lib.sparse_attn_prefill_masked_workspace_size(ctypes.byref(ds), 128)))
+
+
 def call_validate(lib, d, idx=A, width=64, q_len=1, q_tail=1, report=A + 0x500):
     return lib.sparse_attn_validate(None if d is None else ctypes.byref(d), idx, width, q_len, q_tail,
                                     report, None)
