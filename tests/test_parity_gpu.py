@@ -771,6 +771,36 @@ def test_random_small_configs_every_row(seed):
         assert_close(compare_rows(r, ov, rows))
 
 
+@pytest.mark.parametrize("top_k", [1, 2])
+@pytest.mark.parametrize("tied", [False, True])
+def test_degenerate_top_k_every_path(top_k, tied):
+    """Top-1 and top-2 (with every indexer score tied, the lowest candidate tokens win):
+    prefill blocks through the two-step and fused list selections on gathered rows and masked
+    tiles and through the fused prefill (thresholds, masked and automatic paths), and long
+    decode rows through the two-step and fused selections; every row against the oracle."""
+    kw = dict(idx_values=(0,)) if tied else {}
+    _banner(f"top_k={top_k} tied={tied}")
+    w = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=300, q_len=200, top_k=top_k, prefix_len=2)
+    inp = make_inputs(w, seed=46, device="cpu", seq_lens=[300, 260], **kw).to(DEV)
+    ov = OracleView(inp)
+    rows = all_rows(inp)
+    runs = [run_gpu(inp, q_chunk=64), run_gpu(inp, q_chunk=64, fused=True),
+            run_gpu(inp, q_chunk=64, masked=True),
+            run_gpu(inp, q_chunk=64, prefill_path=fa.SA_PREFILL_MASKED, thresholds=True),
+            run_gpu(inp, q_chunk=64, prefill_path=fa.SA_PREFILL_AUTO)]
+    torch.cuda.synchronize()
+    for r in runs:
+        assert_close(compare_rows(r, ov, rows))
+    wd = W(batch=2, num_q_heads=8, num_kv_heads=2, seq_len=20000, q_len=1, top_k=top_k, prefix_len=0)
+    inp = make_inputs(wd, seed=47, device="cpu", seq_lens=[20000, 17000], **kw).to(DEV)
+    ov = OracleView(inp, host_copy=False)
+    runs = [run_gpu(inp), run_gpu(inp, fused=True)]
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0].indices, runs[1].indices)
+    for r in runs:
+        assert_close(compare_rows(r, ov, all_rows(inp)))
+
+
 def test_fused_prefill_middle_blocks_ragged():
     """Blocks of 160 queries in the middle of sequences of different lengths, with a prefix and
     spare pages: every block through the masked path and the gathered path, every row."""
