@@ -306,10 +306,46 @@ def bench_prefill(fa, reps):
     t = [a.elapsed_time(b) for a, b in evs]
     ms = sum(t) / reps
     flops = 4.0 * w.batch * w.num_q_heads * w.head_dim * w.q_len * (w.q_len + 1) / 2
-    del inp, out, lse
+    res = {"workload": w.name, "ms": ms, "ms_percentiles": _pct(t), "reps": reps,
+           "tflops": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS, "flop": flops}
+    # For context: PyTorch's own causal attention (scaled_dot_product_attention, whichever backend
+    # it picks on this build) on the same bf16 inputs, K and V gathered from the pages into
+    # contiguous [B, H, S, d] tensors (the KV heads repeated for each query head of the group).
+    G = w.num_q_heads // w.num_kv_heads
+    pages = inp.page_table[:, :w.q_len // w.page_size].long()
+
+    def dense(pool):
+        x = pool[pages]                       # [B, S/page, Hkv, page, d]
+        x = x.permute(0, 2, 1, 3, 4).reshape(w.batch, w.num_kv_heads, w.q_len, w.head_dim)
+        return x.repeat_interleave(G, dim=1).contiguous()
+    # Only the fused backends are allowed (the unfused one would run batched bf16 products on a
+    # transposed operand); the field is null when neither runs here.
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    qt = inp.q.permute(0, 2, 1, 3).contiguous()
+    kt, vt = dense(inp.k_pool), dense(inp.v_pool)
+    res["torch_sdpa"] = None
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            sdpa = lambda: torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                                            scale=scale)
+            ref = sdpa()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                sdpa()
+            b.record()
+            torch.cuda.synchronize()
+        t_ref = a.elapsed_time(b) / reps
+        diff = (ref.permute(0, 2, 1, 3).float() - out.float()).abs().max().item()
+        res["torch_sdpa"] = {"ms": t_ref, "tflops": flops / t_ref / 1e9, "speedup": t_ref / ms,
+                             "max_abs_diff": diff}
+        del ref
+    except RuntimeError:
+        pass
+    del inp, out, lse, qt, kt, vt
     torch.cuda.empty_cache()
-    return {"workload": w.name, "ms": ms, "ms_percentiles": _pct(t), "reps": reps,
-            "tflops": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS, "flop": flops}
+    return res
 
 
 def bench_tiny(fa, reps=50, warmup=10):
